@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 linear layer on one MI355X.
+
+Workload (one "step"): the decode batch on 7B-like layer shapes at M = 1 -- one
+W4A16 linear for each (K, N) in (4096, 4096), (4096, 11008), (11008, 4096), group size
+128, asymmetric uint4, fp16 scales and zeros, fp16 activations ~ N(0, 1), weights
+~ N(0, 0.02) quantized on the GPU by the library.  Launches cycle through distinct
+copies of the packed weights totalling >= 1 GiB so the 256 MB last-level cache cannot
+serve them: every step streams its weights from HBM.
+
+Metric: effective weight-stream bandwidth = (packed bytes + scale/zero bytes) / time,
+the bytes the method must move (4 bits + 32/g bits per weight).  Also reported: the
+M sweep 1..16, prefill TFLOP/s at M = 4096, the roofline of the dominant kernel and the
+CPU oracle timed on the host (reported baseline, not a target).
+
+Prints ONE JSON line.  ``--gpus N`` with N > 1 is refused: this build runs on one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W4A16 linear: weight-stream GB/s (% HBM peak) at M=1; TFLOP/s at M=4096"
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+SHAPES = [(4096, 4096), (4096, 11008), (11008, 4096)]      # (K, N)
+GROUP = 128
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def weight_bytes(N: int, K: int, g: int) -> int:
+    return N * K // 2 + 4 * N * (K // g)
+
+
+class Layer:
+    """Rotating copies of one packed layer, resident in HBM."""
+
+    def __init__(self, K, N, g, copies, seed, W4, synth, torch):
+        self.K, self.N, self.g = K, N, g
+        W = synth.weights_device(N, K, 0.02, seed)
+        qw, s, z = W4.quantize_pack(W, g, W4.ASYM)
+        self.W_sample_rows = None
+        self.copies = [(qw, s, z)] + [(qw.clone(), s.clone(), z.clone()) for _ in range(copies - 1)]
+        self.W = W      # kept until parity is checked
+        self.bytes = weight_bytes(N, K, g)
+
+
+def parity_check(layer, X_host, X_dev, W4, oracle, torch, np, n_rows=32):
+    """Sampled rows: packing bit-exact and Y within tolerance of the oracle."""
+    rng = np.random.default_rng(layer.N + layer.K)
+    ns = np.unique(np.concatenate([[0, layer.N - 1], rng.choice(layer.N, n_rows, replace=False)]))
+    Wn = layer.W[torch.from_numpy(ns).cuda()].cpu().numpy()
+    codes, s_ref, z_ref = oracle.quantize_asym(Wn, layer.g)
+    qw, s, z = layer.copies[-1]
+    idx = torch.from_numpy(ns).cuda()
+    ok = np.array_equal(qw[idx].cpu().numpy(), oracle.pack(codes))
+    ok &= np.array_equal(s[idx].cpu().numpy().view(np.uint16), s_ref.view(np.uint16))
+    ok &= np.array_equal(z[idx].cpu().numpy().view(np.uint16), z_ref.view(np.uint16))
+    Y = W4.linear(X_dev, qw, s, z, layer.g)
+    ref = oracle.linear_ref(X_host, 0, oracle.pack(codes), s_ref, z_ref, layer.g).astype(np.float64)
+    y = Y[:, idx].float().cpu().numpy().astype(np.float64)
+    fro = float(np.linalg.norm(y - ref) / np.linalg.norm(ref))
+    mx = float(np.abs(y - ref).max() / np.abs(ref).max())
+    return bool(ok) and fro <= 1e-3 and mx <= 1e-2, fro
+
+
+def time_loop(fn, iters, torch):
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(iters):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters   # ms per iteration
+
+
+def cpu_baseline(layers_host, budget_s, np, oracle):
+    """The oracle's linear (fp64 dequantize + BLAS product) on the host cores."""
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    total_bytes = 0
+    t0 = time.perf_counter()
+    steps = 0
+    while True:
+        for (X, qw, s, z, g, nbytes) in layers_host:
+            oracle.linear_ref(X, 0, qw, s, z, g)
+            total_bytes += nbytes
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 50:
+            break
+    return {"value": total_bytes / el / 1e9, "unit": "GB/s", "cores": int(threads),
+            "host_cpus": os.cpu_count(), "kind": "oracle",
+            "sample": f"{steps} oracle step(s) of the same M=1 workload (3 layers, fp64 "
+                      f"dequantize + BLAS matmul), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotate-gib", type=float, default=1.0)
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the W4A16 layer is benchmarked on a single "
+              "MI355X (multi-GPU sharding is a design note, not a measured path).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+    import w4a16_dequant_gemm_amd as W4
+
+    W4.lib()
+    torch.cuda.set_device(0)
+    step_bytes = sum(weight_bytes(N, K, GROUP) for K, N in SHAPES)
+    copies = max(2, int(np.ceil(args.rotate_gib * 2**30 / step_bytes)))
+    log(f"setup: {len(SHAPES)} layers x {copies} copies ({copies * step_bytes / 2**30:.2f} GiB)")
+
+    X_host = synth.activations(1, 4096, synth.FP16, 1015)
+    X_host_k2 = synth.activations(1, 11008, synth.FP16, 1016)
+    layers, xs_host, xs_dev = [], [], []
+    for i, (K, N) in enumerate(SHAPES):
+        layers.append(Layer(K, N, GROUP, copies, 1000 + 10 * 2 + i, W4, synth, torch))
+        xh = X_host if K == 4096 else X_host_k2
+        xs_host.append(xh)
+        xs_dev.append(torch.from_numpy(xh).cuda())
+
+    # parity before timing
+    for L, xh, xd in zip(layers, xs_host, xs_dev):
+        ok, fro = parity_check(L, xh, xd, W4, oracle, torch, np)
+        log(f"parity K={L.K} N={L.N}: ok={ok} rel_fro={fro:.2e}")
+        if not ok:
+            print(json.dumps({"metric": METRIC, "error": f"parity failed K={L.K} N={L.N}"}))
+            sys.exit(1)
+
+    # CPU baseline inputs: host W for the three layers, quantized by the oracle
+    layers_host = []
+    if not args.no_cpu:
+        for L, xh in zip(layers, xs_host):
+            codes, s, z = oracle.quantize_asym(L.W.cpu().numpy(), GROUP)
+            layers_host.append((xh, oracle.pack(codes), s, z, GROUP, L.bytes))
+    for L in layers:
+        del L.W
+    torch.cuda.empty_cache()
+
+    outs = [torch.empty((1, L.N), dtype=torch.float16, device="cuda") for L in layers]
+
+    def step(i):
+        c = i % copies
+        for L, xd, o in zip(layers, xs_dev, outs):
+            qw, s, z = L.copies[c]
+            W4.linear(xd, qw, s, z, GROUP, out=o)
+
+    for i in range(args.warmup):
+        step(i)
+    ms = time_loop(lambda i: step(i + args.warmup), args.steps, torch)
+    value = step_bytes / (ms * 1e-3) / 1e9
+    log(f"step: {ms * 1e3:.1f} us, {value:.1f} GB/s")
+
+    # per-layer launch durations (back-to-back launches of one kernel over the copies)
+    per_layer = []
+    for L, xd, o in zip(layers, xs_dev, outs):
+        def one(i, L=L, xd=xd, o=o):
+            qw, s, z = L.copies[i % copies]
+            W4.linear(xd, qw, s, z, GROUP, out=o)
+        for i in range(10):
+            one(i)
+        t = time_loop(one, max(args.steps, 200), torch)
+        per_layer.append({"K": L.K, "N": L.N, "us": t * 1e3, "bytes": L.bytes,
+                          "GBps": L.bytes / (t * 1e-3) / 1e9,
+                          "path": W4.PATH_NAMES[W4.select_path(1, L.N, L.K, GROUP)]})
+        log(f"  layer K={L.K} N={L.N}: {t * 1e3:.2f} us/launch {per_layer[-1]['GBps']:.0f} GB/s")
+    # dominant kernel: the gemv instantiation with K = 4096 serves two of the three layers
+    dom = [p for p in per_layer if p["K"] == 4096]
+    dom_bytes = sum(p["bytes"] for p in dom) / len(dom)
+    dom_us = sum(p["us"] for p in dom) / len(dom)
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "gemv_kernel (K=4096 instantiation, M=1)",
+                "avg_launch_us": round(dom_us, 3), "bytes_per_launch": dom_bytes}
+
+    extras = {"per_layer_m1": per_layer}
+    if not args.no_extras:
+        extras.update(run_extras(layers, copies, W4, synth, torch, np))
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(layers_host, args.cpu_budget, np, oracle)
+        log(f"cpu oracle: {cpu['value']:.3f} GB/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "decode M=1 on 7B-like layers (K,N) = (4096,4096), "
+                               "(4096,11008), (11008,4096); g=128 asym uint4; fp16 activations",
+                   "M": 1, "group_size": GROUP, "scheme": "asym", "rotating_copies": copies,
+                   "bytes_per_step": step_bytes, "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extras": extras,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_extras(layers, copies, W4, synth, torch, np):
+    out = {}
+    # decode sweep M in 2..16 on the same rotating layers
+    sweep = {}
+    for M in (2, 4, 8, 16):
+        xs = {K: synth.activations_device(M, K, synth.FP16, 2000 + M) for K in (4096, 11008)}
+        outs = [torch.empty((M, L.N), dtype=torch.float16, device="cuda") for L in layers]
+        nbytes = sum(L.bytes for L in layers)
+
+        def step(i):
+            c = i % copies
+            for L, o in zip(layers, outs):
+                qw, s, z = L.copies[c]
+                W4.linear(xs[L.K], qw, s, z, GROUP, out=o)
+        for i in range(5):
+            step(i)
+        ms = time_loop(step, 50, torch)
+        sweep[f"M{M}"] = {"GBps": round(nbytes / (ms * 1e-3) / 1e9, 1), "us_per_step": round(ms * 1e3, 2),
+                          "paths": [W4.PATH_NAMES[W4.select_path(M, L.N, L.K, GROUP)] for L in layers]}
+        log(f"  sweep M={M}: {sweep[f'M{M}']}")
+    out["decode_sweep_fp16_g128"] = sweep
+    # prefill M = 4096
+    pre = {}
+    for (K, N) in [(4096, 11008), (11008, 4096)]:
+        W = synth.weights_device(N, K, 0.02, 3000 + K)
+        qw, s, z = W4.quantize_pack(W, GROUP, W4.ASYM)
+        del W
+        X = synth.activations_device(4096, K, synth.FP16, 3001 + K)
+        Y = torch.empty((4096, N), dtype=torch.float16, device="cuda")
+        for _ in range(3):
+            W4.linear(X, qw, s, z, GROUP, out=Y)
+        ms = time_loop(lambda i: W4.linear(X, qw, s, z, GROUP, out=Y), 10, torch)
+        tf = 2.0 * 4096 * N * K / (ms * 1e-3) / 1e12
+        pre[f"K{K}_N{N}"] = {"TFLOPs": round(tf, 1), "us": round(ms * 1e3, 1),
+                             "frac_mfma_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+        log(f"  prefill M=4096 K={K} N={N}: {tf:.1f} TFLOP/s")
+        del qw, s, z, X, Y
+    out["prefill_m4096_fp16_g128"] = pre
+    return out
+
+
+if __name__ == "__main__":
+    main()

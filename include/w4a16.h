@@ -1,0 +1,148 @@
+/*
+ * w4a16.h -- C ABI of the MI355X (gfx950) W4A16 weight-only linear layer.
+ *
+ * The layer computes Y = X . W_hat^T where W_hat[n][k] = s[n][k/g] * (u[n][k] - z[n][k/g])
+ * is rebuilt inside the kernels from 4-bit codes u, a 16-bit scale s and a 16-bit zero
+ * point z per group of g consecutive input columns, and is never written back to memory.
+ * Sources (five pages on LLM weight quantization):
+ *   - affine quantization q = round(x/s) + z and dequantization x ~ s(q - z):
+ *     page "量化实战深入（GPTQ / AWQ / SmoothQuant / KV 量化）", section 二 (量化的数学本质);
+ *     page "推理优化中“用精度换性能“的核心技术：量化", section 2.3 (核心公式);
+ *   - asymmetric s = (max-min)/(2^b-1), z = round(-min/s) and symmetric absmax
+ *     s = max|x|/(2^(b-1)-1), z = 0: page 4, section 3.3; page 3, section 二;
+ *   - INT4 code ranges [0,15] / [-8,7]: page 4, section 2.2;
+ *   - group-wise granularity, one 16-bit scale and optional 16-bit zero point per 128
+ *     weights (4.25 bits per weight): page 4, section 3.4;
+ *   - weight-only quantization keeps activations in FP16/BF16 and dequantizes the INT4
+ *     weights for the matrix product: page 4, section 3.2; the dequantization belongs
+ *     inside the GEMM, unpacking and scaling in registers or shared memory while the
+ *     INT4 data is read: page "大模型推理中 Weight-only、W8A8 和 FP8 量化有什么区别？如何选型？",
+ *     section 二, and page "LLM 量化中 W4A16 表示什么，它在权重位宽和激活精度上有什么取舍？",
+ *     section 性能取决于 kernel.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library never
+ *     allocates device memory, never frees, never synchronizes the device and keeps no
+ *     state between calls (thread-safe, re-entrant).  Work is enqueued on `stream`
+ *     (a hipStream_t passed as void*; NULL means the default stream) and runs
+ *     asynchronously: the caller keeps every buffer alive until that work completes.
+ *   - Row-major layouts.  W, X, Y, qweight, scales, zeros are dense (no strides).
+ *   - Packed weights: qweight is int32 [N, K/8]; element k of row n is the 4-bit code in
+ *     bits 4*(k%8) .. 4*(k%8)+3 of word qweight[n][k/8] (little-endian nibbles).
+ *   - scales and zeros are IEEE fp16 bit patterns (uint16) of shape [N, K/g].  Symmetric
+ *     weights store codes offset-binary (u = q + 8) with zero point 8; `zeros == NULL` in
+ *     w4a16_linear means "all zero points are 8".
+ *   - Return value: W4A16_OK (0) or a negative w4a16_status.  Argument errors are detected
+ *     on the host before anything is enqueued; W4A16_ERR_HIP reports a failed launch.
+ *   - Inputs must be finite; results for NaN/Inf inputs are unspecified.  X and Y must
+ *     not overlap qweight/scales/zeros or each other.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4A16_ABI_VERSION 1
+
+typedef enum {
+    W4A16_OK = 0,
+    W4A16_ERR_NULL = -1,    /* a required pointer is NULL                          */
+    W4A16_ERR_SHAPE = -2,   /* M, N or K < 1, K % 32 != 0, or a size limit exceeded */
+    W4A16_ERR_GROUP = -3,   /* unsupported group size (see below)                  */
+    W4A16_ERR_ALIGN = -4,   /* a pointer is not aligned as required                 */
+    W4A16_ERR_DTYPE = -5,   /* unknown activation dtype                             */
+    W4A16_ERR_SCHEME = -6,  /* unknown quantization scheme                          */
+    W4A16_ERR_HIP = -7,     /* the HIP runtime reported an error at launch          */
+    W4A16_ERR_PATH = -8     /* a forced kernel path cannot run this problem         */
+} w4a16_status;
+
+typedef enum { W4A16_F16 = 0, W4A16_BF16 = 1 } w4a16_dtype;
+
+typedef enum {
+    W4A16_ASYM_RTN = 0,     /* s = (max-min)/15, z = round(-min/s), codes [0,15]    */
+    W4A16_SYM_ABSMAX = 1    /* s = max|x|/7, signed codes [-8,7] stored as q+8      */
+} w4a16_scheme;
+
+typedef enum {
+    W4A16_PATH_AUTO = 0,    /* dispatcher chooses from (M, N, K, g)                 */
+    W4A16_PATH_GEMV = 1,    /* weight-streaming dot2 kernel, any supported g, M<=8  */
+    W4A16_PATH_SKINNY = 2,  /* weight-streaming MFMA kernel, M <= 64, g % 128 == 0  */
+    W4A16_PATH_PREFILL = 3  /* LDS-tiled MFMA GEMM, g % 64 == 0, K % 64 == 0        */
+} w4a16_path;
+
+/*
+ * Group-size rule for every entry point: g == K, or g is a power of two with
+ * 32 <= g <= K and K % g == 0.  Size limits: 1 <= M, N, K <= 2^31 - 1 and K % 32 == 0.
+ */
+
+/*
+ * w4a16_quantize_pack -- group-wise round-to-nearest INT4 quantization and packing.
+ *   W        [N, K] fp32, device, 16-byte aligned.
+ *   scheme   W4A16_ASYM_RTN or W4A16_SYM_ABSMAX.
+ *   qweight  out [N, K/8] int32, device, 16-byte aligned.
+ *   scales   out [N, K/g] fp16 bits, device, 2-byte aligned.
+ *   zeros    out [N, K/g] fp16 bits, device, 2-byte aligned; may be NULL for the symmetric
+ *            scheme (then nothing is written; pass NULL zeros to w4a16_linear).
+ * Arithmetic per group (IEEE fp32, round-to-nearest-even, this order):
+ *   asymmetric: s32 = (max - min) / 15; s = fp16(s32), or 1.0 if that is 0;
+ *               z = rint(-min / s) + 0.0; q = clamp(rint(x / s) + z, 0, 15);
+ *   symmetric:  s32 = max|x| / 7; s as above; q = clamp(rint(x / s), -8, 7) + 8; z = 8.
+ * The result is bit-identical to that arithmetic.  Preconditions: |z| <= 2048 and a
+ * finite fp16 scale (otherwise the stored values are unspecified).
+ */
+int w4a16_quantize_pack(const float* W, int64_t N, int64_t K, int64_t group_size, int scheme,
+                        int32_t* qweight, uint16_t* scales, uint16_t* zeros, void* stream);
+
+/*
+ * w4a16_linear -- Y[M, N] = X[M, K] . W_hat[N, K]^T with W_hat rebuilt from
+ * (qweight, scales, zeros) inside the kernel; fp32 accumulation; Y is rounded once to
+ * the activation dtype (round-to-nearest-even).
+ *   X        [M, K] fp16 or bf16 (dtype), device, 16-byte aligned.
+ *   qweight  [N, K/8] int32, device, 16-byte aligned.
+ *   scales   [N, K/g] fp16 bits, device, 2-byte aligned.
+ *   zeros    [N, K/g] fp16 bits, device, 2-byte aligned, or NULL (all zero points 8).
+ *            Zero points must be integers with -1024 <= z <= 1024 (the quantizer gives
+ *            z in [0, 15] for every group whose range contains 0).
+ *   Y        out [M, N], same dtype as X, device, 2-byte aligned.
+ */
+int w4a16_linear(const void* X, int dtype, int64_t M, int64_t N, int64_t K, int64_t group_size,
+                 const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                 void* Y, void* stream);
+
+/*
+ * w4a16_linear_ex -- w4a16_linear with an explicit kernel path (w4a16_path).  A forced
+ * path that does not support the problem returns W4A16_ERR_PATH without launching.
+ * Intended for testing every kernel at every size it supports.
+ */
+int w4a16_linear_ex(const void* X, int dtype, int64_t M, int64_t N, int64_t K,
+                    int64_t group_size, const int32_t* qweight, const uint16_t* scales,
+                    const uint16_t* zeros, void* Y, int path, void* stream);
+
+/*
+ * w4a16_select_path -- the path W4A16_PATH_AUTO would take for this problem (host only,
+ * no GPU needed), or a negative status if the arguments are invalid.
+ */
+int w4a16_select_path(int64_t M, int64_t N, int64_t K, int64_t group_size, int dtype);
+
+/*
+ * w4a16_dequantize -- W_hat[N, K] = s * (u - z) as fp32 (exact), for layout checks.
+ *   out [N, K] fp32, device, 16-byte aligned; zeros may be NULL (all 8).
+ */
+int w4a16_dequantize(const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                     int64_t N, int64_t K, int64_t group_size, float* out, void* stream);
+
+/* Human-readable text for a status code (static storage). */
+const char* w4a16_strerror(int status);
+
+/* W4A16_ABI_VERSION of the built library. */
+int w4a16_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -1,0 +1,119 @@
+"""Host-only checks of the C ABI (no GPU): the library loads, exports every function
+declared in include/w4a16.h, and rejects invalid arguments with the documented status
+before anything is enqueued (fake device pointers are never dereferenced)."""
+
+import os
+import re
+
+import pytest
+
+from w4a16_dequant_gemm_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+A = 0x10000       # aligned fake pointers (never dereferenced on these paths)
+B = 0x20000
+C = 0x30000
+D = 0x40000
+MIS = 0x10002     # misaligned for 16-byte requirements
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(w4a16_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        from w4a16_dequant_gemm_amd.build import build
+        build()
+    return L.lib()
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for required in ("w4a16_quantize_pack", "w4a16_linear", "w4a16_linear_ex",
+                     "w4a16_select_path", "w4a16_dequantize", "w4a16_strerror",
+                     "w4a16_abi_version"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_strerror(lib):
+    assert lib.w4a16_abi_version() == 1
+    for st in range(-8, 1):
+        assert lib.w4a16_strerror(st)
+    assert lib.w4a16_strerror(-99) == b"unknown status"
+
+
+def _lin(lib, X=A, dtype=0, M=1, N=64, K=128, g=128, qw=B, s=C, z=D, Y=A + 4096, path=1):
+    return lib.w4a16_linear_ex(X, dtype, M, N, K, g, qw, s, z, Y, path, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), L.ERR_NULL),
+    (dict(qw=None), L.ERR_NULL),
+    (dict(s=None), L.ERR_NULL),
+    (dict(Y=None), L.ERR_NULL),
+    (dict(dtype=2), L.ERR_DTYPE),
+    (dict(M=0), L.ERR_SHAPE),
+    (dict(N=0), L.ERR_SHAPE),
+    (dict(K=0), L.ERR_SHAPE),
+    (dict(K=48, g=48), L.ERR_SHAPE),           # K % 32 != 0
+    (dict(K=192, g=48), L.ERR_GROUP),          # not a power of two, not K
+    (dict(K=128, g=16), L.ERR_GROUP),          # below 32
+    (dict(K=128, g=256), L.ERR_GROUP),         # larger than K
+    (dict(K=384, g=256), L.ERR_GROUP),         # does not divide K
+    (dict(X=MIS), L.ERR_ALIGN),
+    (dict(qw=B + 8), L.ERR_ALIGN),
+    (dict(s=C + 1), L.ERR_ALIGN),
+    (dict(z=D + 1), L.ERR_ALIGN),
+    (dict(Y=A + 4097), L.ERR_ALIGN),
+    (dict(K=96, g=96, path=L.PATH_PREFILL), L.ERR_PATH),   # K % 64 != 0
+    (dict(M=9, path=L.PATH_GEMV), L.ERR_PATH),             # GEMV handles M <= 8
+    (dict(path=17), L.ERR_PATH),
+])
+def test_linear_rejects_invalid_arguments(lib, kw, status):
+    assert _lin(lib, **kw) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 64, 128, 128, 0, B, C, D), L.ERR_NULL),
+    ((A, 64, 128, 128, 5, B, C, D), L.ERR_SCHEME),
+    ((A, 64, 128, 128, 0, B, C, None), L.ERR_NULL),      # asymmetric needs zeros
+    ((A, 64, 100, 100, 0, B, C, D), L.ERR_SHAPE),
+    ((A, 64, 128, 64 + 32, 0, B, C, D), L.ERR_GROUP),
+    ((MIS, 64, 128, 128, 0, B, C, D), L.ERR_ALIGN),
+    ((A, 64, 128, 128, 1, B + 4, C, None), L.ERR_ALIGN),
+])
+def test_quantize_pack_rejects_invalid_arguments(lib, args, status):
+    assert lib.w4a16_quantize_pack(*args, None) == status
+
+
+def test_dequantize_rejects_invalid_arguments(lib):
+    assert lib.w4a16_dequantize(None, C, D, 4, 128, 128, A, None) == L.ERR_NULL
+    assert lib.w4a16_dequantize(B, C, D, 4, 120, 120, A, None) == L.ERR_SHAPE
+    assert lib.w4a16_dequantize(B, C, D, 4, 128, 128, A + 8, None) == L.ERR_ALIGN
+
+
+@pytest.mark.parametrize("M,N,K,g,dtype,path", [
+    (1, 4096, 4096, 128, 0, L.PATH_GEMV),
+    (4, 11008, 4096, 128, 1, L.PATH_GEMV),
+    (1, 8192, 28672, 128, 1, L.PATH_GEMV),
+    (4096, 11008, 4096, 128, 0, L.PATH_PREFILL),
+    (1024, 4096, 11008, 64, 0, L.PATH_PREFILL),
+    (1, 4096, 11008, 11008, 1, L.PATH_GEMV),          # per-channel
+])
+def test_dispatcher_choices(lib, M, N, K, g, dtype, path):
+    assert lib.w4a16_select_path(M, N, K, g, dtype) == path
+
+
+def test_dispatcher_rejects_invalid(lib):
+    assert lib.w4a16_select_path(1, 64, 100, 100, 0) == L.ERR_SHAPE
+    assert lib.w4a16_select_path(1, 64, 128, 128, 3) == L.ERR_DTYPE

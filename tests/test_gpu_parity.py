@@ -1,0 +1,237 @@
+"""GPU parity: every HIP kernel against the CPU oracle, through the C ABI.
+
+* quantize-pack: bit-exact (qweight words, fp16 scale and zero bits);
+* dequantize: exact;
+* linear, every kernel path: relative Frobenius error <= 1e-3 and
+  max |dY| <= 1e-2 * max |Y_ref| against the oracle rounded to the output dtype,
+  plus bit-exact one-hot activations (which select single dequantized weights);
+* full-size problems of every workload family at the launch configuration the
+  benchmark times, on sampled output rows/columns the oracle computes one by one.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import w4a16_dequant_gemm_amd as W4
+from synth import ASYM, BF16, FP16, SYM, Case, activations, config_cases, weights
+from tests.gpu_util import (assert_close, packed_from_torch, ref_bits, ref_to_f64, upload_packed,
+                            x_to_torch, y_bits, y_to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    W4.lib()
+
+
+def _quant_gpu(W: np.ndarray, g: int, scheme: int, write_zeros: bool = True):
+    Wt = torch.from_numpy(W).cuda()
+    return W4.quantize_pack(Wt, g, scheme, write_zeros=write_zeros)
+
+
+def _check_quant(W, g, scheme):
+    qw, s, z = _quant_gpu(W, g, scheme)
+    torch.cuda.synchronize()
+    qn, sn, zn = packed_from_torch(qw, s, z)
+    codes, s_ref, z_ref = oracle.quantize(W, g, scheme)
+    np.testing.assert_array_equal(qn, oracle.pack(codes))
+    np.testing.assert_array_equal(sn.view(np.uint16), s_ref.view(np.uint16))
+    np.testing.assert_array_equal(zn.view(np.uint16), z_ref.view(np.uint16))
+    return qn, sn, zn
+
+
+QCASES = [(64, 256, 32), (37, 512, 64), (100, 1024, 128), (13, 384, 384), (8, 4096, 4096),
+          (300, 11008, 128), (50, 2048, 2048), (3, 96, 96)]
+
+
+@pytest.mark.parametrize("scheme", [ASYM, SYM])
+@pytest.mark.parametrize("N,K,g", QCASES)
+def test_quantize_pack_bit_exact(N, K, g, scheme):
+    W = weights(N, K, 0.02, seed=N * 7 + K, outlier_frac=0.001, outlier_mult=20.0)
+    _check_quant(W, g, scheme)
+
+
+def test_quantize_pack_special_groups():
+    # constant group, hand vectors (ties, non-straddling group, symmetric) tiled to g = 32,
+    # a group with -0.0 and +0.0, and tiny (fp16-subnormal) scales
+    rows = [
+        np.full(32, 0.5, np.float32),
+        np.tile(np.array([-0.75, 3.0, 0.1, 1.3, -0.2, 2.2, 0.0, 0.55], np.float32), 4),
+        np.tile(np.array([0.0, 3.75, 0.625, 0.875, 0, 0, 0, 0], np.float32), 4),
+        np.tile(np.array([1.0, 4.75, 2.0, 3.125, 1.5, 2.625, 4.0, 1.875], np.float32), 4),
+        np.tile(np.array([-0.0, 0.0, -0.0, 1.0, 0.0, -0.0, 0.25, 0.0], np.float32), 4),
+        np.linspace(-1e-6, 2e-6, 32, dtype=np.float32),
+        np.linspace(-3.0, -2.0, 32, dtype=np.float32),
+        np.zeros(32, np.float32),
+    ]
+    W = np.stack(rows).astype(np.float32)
+    for scheme in (ASYM, SYM):
+        _check_quant(W, 32, scheme)
+
+
+def test_quantize_sym_without_zeros():
+    W = weights(16, 512, 0.02, seed=5)
+    qw, s, z = _quant_gpu(W, 128, SYM, write_zeros=False)
+    assert z is None
+    codes, s_ref, _ = oracle.quantize_sym(W, 128)
+    np.testing.assert_array_equal(qw.cpu().numpy(), oracle.pack(codes))
+    np.testing.assert_array_equal(s.cpu().numpy().view(np.uint16), s_ref.view(np.uint16))
+
+
+@pytest.mark.parametrize("N,K,g", [(64, 256, 32), (100, 1024, 128), (13, 384, 384)])
+def test_dequantize_exact(N, K, g):
+    W = weights(N, K, 0.02, seed=11)
+    qw, s, z = _quant_gpu(W, g, ASYM)
+    D = W4.dequantize(qw, s, z, g).cpu().numpy().astype(np.float64)
+    qn, sn, zn = packed_from_torch(qw, s, z)
+    np.testing.assert_array_equal(D, oracle.dequantize(qn, sn, zn, g))
+    D8 = W4.dequantize(qw, s, None, g).cpu().numpy().astype(np.float64)
+    np.testing.assert_array_equal(D8, oracle.dequantize(qn, sn, None, g))
+
+
+# ------------------------------------------------------------------ linear
+def _run_linear(M, N, K, g, scheme, dtype, path, seed, zeros_none=False, x_outliers=False):
+    W = weights(N, K, 0.02, seed=seed)
+    X = activations(M, K, dtype, seed + 1, *(0.01, 100.0) if x_outliers else (0.0, 1.0))
+    codes, s, z = oracle.quantize(W, g, scheme)
+    qw_np = oracle.pack(codes)
+    zz = None if zeros_none else z
+    qw, st, zt = upload_packed(qw_np, s, zz)
+    Y = W4.linear(x_to_torch(X, dtype), qw, st, zt, g, path=path)
+    torch.cuda.synchronize()
+    ref = oracle.linear_ref(X, dtype, qw_np, s, zz, g)
+    return Y, ref
+
+
+GEMV_CASES = [(1, 64, 256, 32), (2, 130, 512, 128), (3, 77, 1024, 1024), (4, 256, 4096, 128),
+              (1, 300, 11008, 128), (5, 100, 2048, 64), (8, 64, 4096, 128), (1, 33, 28672, 128),
+              (2, 50, 11008, 11008), (7, 16, 1024, 256), (1, 1, 32, 32)]
+PREFILL_CASES = [(1, 64, 64, 64), (17, 200, 192, 64), (130, 129, 256, 128), (256, 384, 1024, 128),
+                 (300, 256, 4096, 4096), (64, 128, 11008, 128), (129, 1, 128, 64)]
+
+
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+@pytest.mark.parametrize("M,N,K,g", GEMV_CASES)
+def test_linear_gemv(M, N, K, g, dtype):
+    Y, ref = _run_linear(M, N, K, g, ASYM, dtype, W4.PATH_GEMV, seed=M * 131 + N + K)
+    assert_close(y_to_f64(Y), ref_to_f64(ref, dtype), f"gemv M={M} N={N} K={K} g={g}")
+
+
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+@pytest.mark.parametrize("M,N,K,g", PREFILL_CASES)
+def test_linear_prefill(M, N, K, g, dtype):
+    Y, ref = _run_linear(M, N, K, g, ASYM, dtype, W4.PATH_PREFILL, seed=M * 17 + N + K)
+    assert_close(y_to_f64(Y), ref_to_f64(ref, dtype), f"prefill M={M} N={N} K={K} g={g}")
+
+
+@pytest.mark.parametrize("path", [W4.PATH_GEMV, W4.PATH_PREFILL])
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+def test_linear_symmetric_and_null_zeros(path, dtype):
+    for zeros_none in (False, True):
+        Y, ref = _run_linear(4, 192, 1024, 128, SYM, dtype, path, seed=3, zeros_none=zeros_none)
+        assert_close(y_to_f64(Y), ref_to_f64(ref, dtype), f"sym path={path} zeros_none={zeros_none}")
+
+
+@pytest.mark.parametrize("path", [W4.PATH_GEMV, W4.PATH_PREFILL])
+def test_linear_bf16_outlier_channels(path):
+    Y, ref = _run_linear(4, 256, 8192, 128, ASYM, BF16, path, seed=9, x_outliers=True)
+    assert_close(y_to_f64(Y), ref_to_f64(ref, BF16), f"bf16 outliers path={path}")
+
+
+@pytest.mark.parametrize("path", [W4.PATH_GEMV, W4.PATH_PREFILL])
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+def test_one_hot_bit_exact(path, dtype):
+    # one-hot rows select single dequantized weights: Y[m, n] = round(W_hat[n, k_m]) exactly
+    N, K, g = 200, 1024, 128
+    W = weights(N, K, 0.05, seed=21)
+    codes, s, z = oracle.quantize_asym(W, g)
+    qw_np = oracle.pack(codes)
+    ks = [0, 1, 4, 7, 8, 31, 32, 63, 64, 127, 128, 500, 777, 1023]
+    X64 = np.zeros((len(ks), K))
+    for m, k in enumerate(ks):
+        X64[m, k] = 1.0
+    X = X64.astype(np.float16) if dtype == FP16 else oracle.round_to_bf16_bits(X64)
+    qw, st, zt = upload_packed(qw_np, s, z)
+    ref = oracle.linear_ref(X, dtype, qw_np, s, z, g)
+    rows = 4 if path == W4.PATH_GEMV else len(ks)      # the GEMV kernel serves M <= 8
+    for m0 in range(0, len(ks), rows):
+        Y = W4.linear(x_to_torch(X[m0:m0 + rows], dtype), qw, st, zt, g, path=path)
+        np.testing.assert_array_equal(y_bits(Y), ref_bits(ref[m0:m0 + rows], dtype))
+
+
+def test_auto_dispatch_matches_forced_paths():
+    for M in (1, 4, 16, 64, 300):
+        Y, ref = _run_linear(M, 256, 2048, 128, ASYM, FP16, W4.PATH_AUTO, seed=M)
+        assert_close(y_to_f64(Y), ref_to_f64(ref, FP16), f"auto M={M}")
+
+
+def test_non_default_stream_no_intermediate_sync():
+    W = weights(512, 4096, 0.02, seed=31)
+    X = activations(2, 4096, FP16, 32)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        Wt = torch.from_numpy(W).to("cuda", non_blocking=False)
+        Xt = x_to_torch(X, FP16)
+        qw, sc, z = W4.quantize_pack(Wt, 128, ASYM)
+        Y = W4.linear(Xt, qw, sc, z, 128)
+    s.synchronize()
+    codes, s_ref, z_ref = oracle.quantize_asym(W, 128)
+    ref = oracle.linear_ref(X, FP16, oracle.pack(codes), s_ref, z_ref, 128)
+    assert_close(y_to_f64(Y), ref_to_f64(ref, FP16), "stream")
+
+
+def test_repeat_determinism():
+    W = weights(256, 4096, 0.02, seed=41)
+    X = activations(4, 4096, BF16, 42)
+    Wt = torch.from_numpy(W).cuda()
+    outs = []
+    for _ in range(3):
+        qw, sc, z = W4.quantize_pack(Wt, 128, ASYM)
+        outs.append((qw.clone(), sc.clone(), z.clone(), W4.linear(x_to_torch(X, BF16), qw, sc, z, 128)))
+    for o in outs[1:]:
+        for a, b in zip(o, outs[0]):
+            assert torch.equal(a.view(torch.int16) if a.dtype != torch.int32 else a,
+                               b.view(torch.int16) if b.dtype != torch.int32 else b)
+
+
+# ------------------------------------------------------- full-size workloads
+def _full_size(case: Case, n_rows: int = 48, m_rows: int | None = None):
+    """Full-size problem: GPU quantizes and multiplies the whole layer; the oracle checks
+    sampled output rows n (bit-exact packing and Y columns) and, for large M, sampled
+    activation rows m."""
+    W, X = case.make()
+    Wt = torch.from_numpy(W).cuda()
+    qw, sc, z = W4.quantize_pack(Wt, case.g, case.scheme)
+    del Wt
+    Y = W4.linear(x_to_torch(X, case.dtype), qw, sc, z, case.g)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(case.config * 1000 + case.M)
+    ns = np.unique(np.concatenate([[0, case.N - 1], rng.choice(case.N, n_rows, replace=False)]))
+    ms = np.arange(case.M) if m_rows is None or case.M <= m_rows else \
+        np.unique(np.concatenate([[0, case.M - 1], rng.choice(case.M, m_rows, replace=False)]))
+    codes, s_ref, z_ref = oracle.quantize(W[ns], case.g, case.scheme)
+    qn = qw[torch.from_numpy(ns).cuda()].cpu().numpy()
+    np.testing.assert_array_equal(qn, oracle.pack(codes))
+    np.testing.assert_array_equal(sc[torch.from_numpy(ns).cuda()].cpu().numpy().view(np.uint16),
+                                  s_ref.view(np.uint16))
+    ref = oracle.linear_ref(X[ms], case.dtype, qn, s_ref, z_ref, case.g)
+    y = y_to_f64(Y[torch.from_numpy(ms).cuda()][:, torch.from_numpy(ns).cuda()])
+    assert_close(y, ref_to_f64(ref, case.dtype), case.name)
+
+
+FULL = [c for c in config_cases(1)] + \
+       [c for c in config_cases(2) if c.M in (1, 4, 16)] + \
+       [c for c in config_cases(3) if c.M in (1, 16)] + \
+       [c for c in config_cases(4) if (c.M, c.K, c.g, c.scheme) in
+        [(4096, 4096, 128, ASYM), (256, 11008, 64, SYM), (1024, 4096, 64, ASYM)]]
+
+
+@pytest.mark.parametrize("case", FULL, ids=lambda c: c.name)
+def test_full_size_sampled(case):
+    _full_size(case, m_rows=64)

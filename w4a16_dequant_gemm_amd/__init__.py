@@ -1,0 +1,132 @@
+"""MI355X-native W4A16 weight-only linear layer: Python binding of ``libw4a16.so``.
+
+The binding only marshals arguments: it checks dtypes, shapes and contiguity of torch
+tensors, passes raw device pointers and the current HIP stream to the C ABI and turns
+negative status codes into :class:`W4A16Error`.  Every step of the computation runs in
+the library's HIP kernels; there is no CPU or PyTorch fallback.
+
+``quantize_pack(W, group_size, scheme)`` -> ``(qweight, scales, zeros)``
+    group-wise INT4 RTN quantization of an fp32 ``[N, K]`` CUDA tensor.
+``linear(X, qweight, scales, zeros, group_size, path=PATH_AUTO)`` -> ``Y``
+    ``Y = X . dequant(qweight)^T`` for fp16/bf16 ``X [M, K]``.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from ._lib import (ASYM, BF16, F16, OK, PATH_AUTO, PATH_GEMV, PATH_NAMES, PATH_PREFILL,
+                   PATH_SKINNY, SYM, W4A16Error, check, lib)
+
+__all__ = [
+    "ASYM", "SYM", "F16", "BF16", "PATH_AUTO", "PATH_GEMV", "PATH_SKINNY", "PATH_PREFILL",
+    "PATH_NAMES", "W4A16Error", "quantize_pack", "linear", "dequantize", "select_path",
+    "abi_version", "lib",
+]
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return F16
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"activations must be float16 or bfloat16, got {t.dtype}")
+
+
+def abi_version() -> int:
+    return lib().w4a16_abi_version()
+
+
+def select_path(M: int, N: int, K: int, group_size: int, dtype: int = F16) -> int:
+    """Kernel path the dispatcher picks (host only); raises on invalid arguments."""
+    p = lib().w4a16_select_path(M, N, K, group_size, dtype)
+    if p < 0:
+        raise W4A16Error(p, "select_path")
+    return p
+
+
+def quantize_pack(W: torch.Tensor, group_size: int = 128, scheme: int = ASYM,
+                  write_zeros: bool = True):
+    """Quantize fp32 ``W [N, K]`` on the GPU.
+
+    Returns ``(qweight int32 [N, K/8], scales fp16 [N, K/g], zeros fp16 [N, K/g] or None)``.
+    ``zeros`` is None only for the symmetric scheme with ``write_zeros=False``.
+    """
+    _need(W, "W", torch.float32, 2)
+    N, K = W.shape
+    if K % 8 or group_size <= 0 or K % group_size:
+        raise ValueError("K must be a multiple of 8 and of group_size")
+    G = K // group_size
+    qweight = torch.empty((N, K // 8), dtype=torch.int32, device=W.device)
+    scales = torch.empty((N, G), dtype=torch.float16, device=W.device)
+    zeros = None
+    if scheme == ASYM or write_zeros:
+        zeros = torch.empty((N, G), dtype=torch.float16, device=W.device)
+    st = lib().w4a16_quantize_pack(W.data_ptr(), N, K, group_size, scheme, qweight.data_ptr(),
+                                   scales.data_ptr(), zeros.data_ptr() if zeros is not None else None,
+                                   _stream())
+    check(st, "w4a16_quantize_pack")
+    return qweight, scales, zeros
+
+
+def linear(X: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zeros, group_size: int,
+           path: int = PATH_AUTO, out: torch.Tensor | None = None) -> torch.Tensor:
+    """``Y [M, N] = X [M, K] . dequant(qweight)^T`` in the dtype of ``X``."""
+    dt = _dtype_code(X)
+    _need(X, "X", X.dtype, 2)
+    _need(qweight, "qweight", torch.int32, 2)
+    _need(scales, "scales", torch.float16, 2)
+    if zeros is not None:
+        _need(zeros, "zeros", torch.float16, 2)
+    M, K = X.shape
+    N = qweight.shape[0]
+    if qweight.shape[1] * 8 != K:
+        raise ValueError("qweight must be [N, K/8]")
+    if group_size <= 0 or K % group_size or tuple(scales.shape) != (N, K // group_size):
+        raise ValueError("scales must be [N, K/group_size]")
+    if zeros is not None and zeros.shape != scales.shape:
+        raise ValueError("zeros must match scales")
+    if out is None:
+        out = torch.empty((M, N), dtype=X.dtype, device=X.device)
+    else:
+        _need(out, "out", X.dtype, 2)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out must be [M, N]")
+    st = lib().w4a16_linear_ex(X.data_ptr(), dt, M, N, K, group_size, qweight.data_ptr(),
+                               scales.data_ptr(), zeros.data_ptr() if zeros is not None else None,
+                               out.data_ptr(), path, _stream())
+    check(st, "w4a16_linear")
+    return out
+
+
+def dequantize(qweight: torch.Tensor, scales: torch.Tensor, zeros, group_size: int) -> torch.Tensor:
+    """Exact fp32 ``W_hat [N, K]`` (layout checks and tests)."""
+    _need(qweight, "qweight", torch.int32, 2)
+    _need(scales, "scales", torch.float16, 2)
+    if zeros is not None:
+        _need(zeros, "zeros", torch.float16, 2)
+    N, KW = qweight.shape
+    K = KW * 8
+    out = torch.empty((N, K), dtype=torch.float32, device=qweight.device)
+    st = lib().w4a16_dequantize(qweight.data_ptr(), scales.data_ptr(),
+                                zeros.data_ptr() if zeros is not None else None, N, K, group_size,
+                                out.data_ptr(), _stream())
+    check(st, "w4a16_dequantize")
+    return out

@@ -1,0 +1,199 @@
+// C ABI of the W4A16 library: argument validation, the M-based dispatcher and launches.
+//
+// Every check runs on the host before anything is enqueued, so invalid arguments never
+// reach a kernel and never touch the GPU.  The dispatcher follows the regime split the
+// pages draw: small batches (decode) are bound by reading the weights, large batches
+// (prefill) by the matrix math (page "Quantization & Acceleration: 解释 W8A8 与 W4A16 的差异
+// 与取舍", decode memory-bound / prefill compute-bound; page
+// "大模型推理中 Weight-only、W8A8 和 FP8 量化有什么区别？如何选型？", sections 二 and 五).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/w4a16.h"
+#include "launch.h"
+
+using w4a16::LinearArgs;
+
+namespace {
+
+constexpr int64_t kMaxDim = 2147483647LL;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int log2_exact(int64_t v) {
+    int s = 0;
+    while ((int64_t(1) << s) < v) ++s;
+    return (int64_t(1) << s) == v ? s : -1;
+}
+
+// Shape and group-size rules shared by all entry points.  On success fills g-derived
+// fields (G, gshift).
+int check_shape_group(int64_t N, int64_t K, int64_t g, int* G, int* gshift) {
+    if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim) return W4A16_ERR_SHAPE;
+    if (K % 32 != 0) return W4A16_ERR_SHAPE;
+    if (N * (K / 8) > (int64_t(1) << 40)) return W4A16_ERR_SHAPE;
+    if (g < 1) return W4A16_ERR_GROUP;
+    if (g == K) {
+        *G = 1;
+        *gshift = 31;
+        return W4A16_OK;
+    }
+    const int sh = log2_exact(g);
+    if (sh < 5 || g > K || K % g != 0) return W4A16_ERR_GROUP;
+    *G = (int)(K / g);
+    *gshift = sh;
+    return W4A16_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP; }
+
+int validate_linear(const void* X, int dtype, int64_t M, int64_t N, int64_t K, int64_t g,
+                    const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                    void* Y, LinearArgs* a) {
+    if (!X || !qweight || !scales || !Y) return W4A16_ERR_NULL;
+    if (dtype != W4A16_F16 && dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
+    if (M < 1 || M > kMaxDim) return W4A16_ERR_SHAPE;
+    int G = 0, gshift = 0;
+    const int st = check_shape_group(N, K, g, &G, &gshift);
+    if (st != W4A16_OK) return st;
+    if (M * K > (int64_t(1) << 42) || M * N > (int64_t(1) << 42)) return W4A16_ERR_SHAPE;
+    if (!aligned(X, 16) || !aligned(qweight, 16) || !aligned(scales, 2) || !aligned(Y, 2) ||
+        (zeros && !aligned(zeros, 2)))
+        return W4A16_ERR_ALIGN;
+    a->X = X;
+    a->qw = reinterpret_cast<const uint32_t*>(qweight);
+    a->scales = scales;
+    a->zeros = zeros;
+    a->Y = Y;
+    a->dtype = dtype;
+    a->M = (int)M;
+    a->N = (int)N;
+    a->K = (int)K;
+    a->G = G;
+    a->gshift = gshift;
+    a->g = (int)g;
+    return W4A16_OK;
+}
+
+// M-based dispatch: the weight-streaming GEMV while the dot2 work per weight stays
+// within the VALU budget of the HBM stream, the skinny MFMA kernel for small batches,
+// the tiled MFMA GEMM once the problem is compute-bound.
+int choose_path(const LinearArgs& a) {
+    if (a.M <= 4 && w4a16::gemv_supports(a)) return W4A16_PATH_GEMV;
+    if (a.M <= 64 && w4a16::skinny_supports(a)) return W4A16_PATH_SKINNY;
+    if (w4a16::prefill_supports(a)) return W4A16_PATH_PREFILL;
+    if (w4a16::gemv_supports(a)) return W4A16_PATH_GEMV;
+    if (w4a16::skinny_supports(a)) return W4A16_PATH_SKINNY;
+    return -1;
+}
+
+int run_linear(const LinearArgs& a, int path, hipStream_t s) {
+    hipError_t e;
+    switch (path) {
+        case W4A16_PATH_GEMV:
+            if (!w4a16::gemv_supports(a)) return W4A16_ERR_PATH;
+            e = w4a16::launch_gemv(a, s);
+            break;
+        case W4A16_PATH_SKINNY:
+            if (!w4a16::skinny_supports(a)) return W4A16_ERR_PATH;
+            e = w4a16::launch_skinny(a, s);
+            break;
+        case W4A16_PATH_PREFILL:
+            if (!w4a16::prefill_supports(a)) return W4A16_ERR_PATH;
+            e = w4a16::launch_prefill(a, s);
+            break;
+        default:
+            return W4A16_ERR_PATH;
+    }
+    return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a16_abi_version(void) { return W4A16_ABI_VERSION; }
+
+const char* w4a16_strerror(int status) {
+    switch (status) {
+        case W4A16_OK: return "ok";
+        case W4A16_ERR_NULL: return "a required pointer is NULL";
+        case W4A16_ERR_SHAPE: return "invalid shape (M, N, K >= 1, K % 32 == 0, size limits)";
+        case W4A16_ERR_GROUP:
+            return "unsupported group size (g == K, or a power of two >= 32 dividing K)";
+        case W4A16_ERR_ALIGN: return "misaligned pointer (X, W, qweight 16 B; others 2 B)";
+        case W4A16_ERR_DTYPE: return "unknown activation dtype";
+        case W4A16_ERR_SCHEME: return "unknown quantization scheme";
+        case W4A16_ERR_HIP: return "HIP runtime error at launch";
+        case W4A16_ERR_PATH: return "the requested kernel path does not support this problem";
+        default: return "unknown status";
+    }
+}
+
+int w4a16_quantize_pack(const float* W, int64_t N, int64_t K, int64_t group_size, int scheme,
+                        int32_t* qweight, uint16_t* scales, uint16_t* zeros, void* stream) {
+    if (!W || !qweight || !scales) return W4A16_ERR_NULL;
+    if (scheme != W4A16_ASYM_RTN && scheme != W4A16_SYM_ABSMAX) return W4A16_ERR_SCHEME;
+    if (scheme == W4A16_ASYM_RTN && !zeros) return W4A16_ERR_NULL;
+    int G = 0, gshift = 0;
+    const int st = check_shape_group(N, K, group_size, &G, &gshift);
+    if (st != W4A16_OK) return st;
+    if (!aligned(W, 16) || !aligned(qweight, 16) || !aligned(scales, 2) ||
+        (zeros && !aligned(zeros, 2)))
+        return W4A16_ERR_ALIGN;
+    const hipError_t e = w4a16::launch_quantize_pack(
+        W, (int)N, (int)K, (int)group_size, gshift, scheme, reinterpret_cast<uint32_t*>(qweight),
+        scales, zeros, static_cast<hipStream_t>(stream));
+    return hip_status(e);
+}
+
+int w4a16_dequantize(const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                     int64_t N, int64_t K, int64_t group_size, float* out, void* stream) {
+    if (!qweight || !scales || !out) return W4A16_ERR_NULL;
+    int G = 0, gshift = 0;
+    const int st = check_shape_group(N, K, group_size, &G, &gshift);
+    if (st != W4A16_OK) return st;
+    if (!aligned(qweight, 16) || !aligned(out, 16) || !aligned(scales, 2) ||
+        (zeros && !aligned(zeros, 2)))
+        return W4A16_ERR_ALIGN;
+    const hipError_t e = w4a16::launch_dequantize(reinterpret_cast<const uint32_t*>(qweight),
+                                                  scales, zeros, (int)N, (int)K, (int)group_size,
+                                                  gshift, out, static_cast<hipStream_t>(stream));
+    return hip_status(e);
+}
+
+int w4a16_select_path(int64_t M, int64_t N, int64_t K, int64_t group_size, int dtype) {
+    // Fake, aligned, non-null pointers: only shapes are examined.
+    alignas(16) static const unsigned char dummy[16] = {0};
+    LinearArgs a;
+    const int st = validate_linear(dummy, dtype, M, N, K, group_size,
+                                   reinterpret_cast<const int32_t*>(dummy),
+                                   reinterpret_cast<const uint16_t*>(dummy), nullptr,
+                                   const_cast<unsigned char*>(dummy), &a);
+    if (st != W4A16_OK) return st;
+    const int p = choose_path(a);
+    return p < 0 ? W4A16_ERR_PATH : p;
+}
+
+int w4a16_linear_ex(const void* X, int dtype, int64_t M, int64_t N, int64_t K,
+                    int64_t group_size, const int32_t* qweight, const uint16_t* scales,
+                    const uint16_t* zeros, void* Y, int path, void* stream) {
+    LinearArgs a;
+    const int st = validate_linear(X, dtype, M, N, K, group_size, qweight, scales, zeros, Y, &a);
+    if (st != W4A16_OK) return st;
+    if (path == W4A16_PATH_AUTO) {
+        path = choose_path(a);
+        if (path < 0) return W4A16_ERR_PATH;
+    }
+    return run_linear(a, path, static_cast<hipStream_t>(stream));
+}
+
+int w4a16_linear(const void* X, int dtype, int64_t M, int64_t N, int64_t K, int64_t group_size,
+                 const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros, void* Y,
+                 void* stream) {
+    return w4a16_linear_ex(X, dtype, M, N, K, group_size, qweight, scales, zeros, Y,
+                           W4A16_PATH_AUTO, stream);
+}
+
+}  // extern "C"

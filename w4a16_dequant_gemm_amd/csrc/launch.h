@@ -1,0 +1,36 @@
+// Internal launcher interface between the C ABI (api.cpp) and the kernels (*.hip).
+// Every launcher assumes its arguments were validated by the caller and only enqueues.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+struct LinearArgs {
+    const void* X;          // [M, K] fp16/bf16
+    const uint32_t* qw;     // [N, K/8]
+    const uint16_t* scales; // [N, G]
+    const uint16_t* zeros;  // [N, G] or nullptr (all 8)
+    void* Y;                // [M, N]
+    int dtype;              // 0 fp16, 1 bf16
+    int M, N, K;
+    int G;                  // groups per row, K / g
+    int gshift;             // log2(g), or 31 when g == K
+    int g;                  // group size
+};
+
+// Host-side shape support checks of each kernel family (no GPU needed).
+bool gemv_supports(const LinearArgs& a);
+bool skinny_supports(const LinearArgs& a);
+bool prefill_supports(const LinearArgs& a);
+
+hipError_t launch_quantize_pack(const float* W, int N, int K, int g, int gshift, int scheme,
+                                uint32_t* qw, uint16_t* scales, uint16_t* zeros, hipStream_t s);
+hipError_t launch_dequantize(const uint32_t* qw, const uint16_t* scales, const uint16_t* zeros,
+                             int N, int K, int g, int gshift, float* out, hipStream_t s);
+hipError_t launch_gemv(const LinearArgs& a, hipStream_t s);
+hipError_t launch_skinny(const LinearArgs& a, hipStream_t s);
+hipError_t launch_prefill(const LinearArgs& a, hipStream_t s);
+
+}  // namespace w4a16
