@@ -75,7 +75,33 @@ def parity_check(layer, X_host, X_dev, W4, oracle, torch, np, n_rows=32):
     return bool(ok) and fro <= 1e-3 and mx <= 1e-2, fro
 
 
-def time_loop(fn, iters, torch):
+def capture(fn, iters, torch):
+    """HIP graph holding ``iters`` back-to-back calls fn(0..iters-1) (launch overhead of
+    the Python binding is paid once, at capture)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(iters):
+            fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, iters, torch):
+    """ms per iteration of a graph that holds ``iters`` iterations."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    g.replay()                     # warm replay
+    torch.cuda.synchronize()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def time_loop(fn, iters, torch, graph=True):
+    if graph:
+        return time_graph(capture(fn, iters, torch), iters, torch)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -178,9 +204,27 @@ def main():
 
     for i in range(args.warmup):
         step(i)
-    ms = time_loop(lambda i: step(i + args.warmup), args.steps, torch)
+    # The timed region is one replay of a graph holding exactly `steps` steps, bracketed
+    # by synchronize + events; warm-up steps run eagerly and as one warm graph replay.
+    g_main = capture(lambda i: step(i + args.warmup), args.steps, torch)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    g_main.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    g_main.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
     value = step_bytes / (ms * 1e-3) / 1e9
     log(f"step: {ms * 1e3:.1f} us, {value:.1f} GB/s")
+    # the graph replays must reproduce the eager result of the last step
+    last = [o.clone() for o in outs]
+    step(args.warmup + args.steps - 1)
+    torch.cuda.synchronize()
+    if not all(torch.equal(a, b) for a, b in zip(last, outs)):
+        print(json.dumps({"metric": METRIC, "error": "graph replay differs from eager launch"}))
+        sys.exit(1)
 
     # per-layer launch durations (back-to-back launches of one kernel over the copies)
     per_layer = []

@@ -111,7 +111,8 @@ def _run_linear(M, N, K, g, scheme, dtype, path, seed, zeros_none=False, x_outli
 
 GEMV_CASES = [(1, 64, 256, 32), (2, 130, 512, 128), (3, 77, 1024, 1024), (4, 256, 4096, 128),
               (1, 300, 11008, 128), (5, 100, 2048, 64), (8, 64, 4096, 128), (1, 33, 28672, 128),
-              (2, 50, 11008, 11008), (7, 16, 1024, 256), (1, 1, 32, 32)]
+              (2, 50, 11008, 11008), (7, 16, 1024, 256), (1, 1, 32, 32),
+              (1, 9477, 4096, 128), (2, 5000, 2048, 64), (4, 3000, 1024, 1024), (3, 2600, 6144, 128)]
 PREFILL_CASES = [(1, 64, 64, 64), (17, 200, 192, 64), (130, 129, 256, 128), (256, 384, 1024, 128),
                  (300, 256, 4096, 4096), (64, 128, 11008, 128), (129, 1, 128, 64)]
 

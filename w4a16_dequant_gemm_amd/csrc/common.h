@@ -2,24 +2,26 @@
 //
 // Code layout.  A 32-bit word of the packed weight row holds 8 consecutive input
 // columns k0..k7, element k_t in bits 4t..4t+3.  The kernels never rebuild the natural
-// order: a word is split into four 16-bit pairs (k0,k4) (k1,k5) (k2,k6) (k3,k7) with one
-// AND/OR each (the "exponent-bias" trick: OR-ing a nibble into the mantissa of a
-// 16-bit float whose exponent makes one ulp equal to 1 yields bias + code exactly).
-// Activations are permuted the same way once, when they are loaded, so every
-// dot product sees matching pairs: per 8-column block the activation order is
-// x0 x4 x1 x5 x2 x6 x3 x7.
+// column order: a word is split into four 32-bit registers, each holding two codes in
+// its two 16-bit halves, with one or two integer instructions per register.  The
+// activations are permuted the same way once, when they are loaded, so every
+// dot product / MFMA sees matching pairs (a dot product is invariant under a
+// permutation of k applied to both operands).
 //
 // Dequantization x_hat = s * (u - z) (page "推理优化中“用精度换性能“的核心技术：量化",
 // section 2.3; page "量化实战深入（GPTQ / AWQ / SmoothQuant / KV 量化）", section 二) is
-// applied in two parts: the integer part (u - z) enters the dot products / MFMAs, the
-// per-group scale s multiplies the fp32 partial sum of the group afterwards, so no
-// rounded fp16/bf16 weight is ever formed.
-//   fp16 activations: the pair holds the exact small integers (u - z); the bias 1024 and
-//     the zero point are removed with one packed fp16 add (or fma), which is exact for
-//     |z| <= 1024.
-//   bf16 activations: gfx950 has no packed bf16 add, so the pair holds 128 + u (exact in
-//     bf16); the MFMA/dot result is sum x*(128+u) and the group epilogue subtracts
-//     (128 + z) * sum(x) in fp32.
+// split so that no rounded 16-bit weight is ever formed:
+//   sum_k x_k s (u_k - z) = s * ( sum_k x_k u_k  -  z * sum_k x_k ),
+// the first sum is computed by v_dot2 / MFMA on exact codes, the activation sum is
+// computed once per chunk or group, and the per-group scale multiplies the fp32 result.
+// Exact codes in a 16-bit float:
+//   fp16: a nibble u in the low bits of an fp16 with zero exponent is the subnormal
+//     u * 2^-24; both v_dot2_f32_f16 and the fp16 MFMAs multiply subnormals exactly, so
+//     masking alone yields the operand (products are exact in fp32).  A nibble at bits
+//     4..7 is still subnormal (16u * 2^-24), which the GEMV uses to skip a shift.
+//   bf16: bf16 subnormals would push the fp32 products below the normal range, so the
+//     nibble is OR-ed into the mantissa of 128.0 (0x4300), giving 128 + u exactly; the
+//     bias 128 is removed with the activation sum: s * (sum x (128+u) - (128+z) sum x).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -67,8 +69,8 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 }
 
 // Natural-order activations of one 8-column block, as four 32-bit pairs
-// r0=(x0,x1) r1=(x2,x3) r2=(x4,x5) r3=(x6,x7), to kernel order
-// (x0,x4) (x1,x5) (x2,x6) (x3,x7).
+// r0=(x0,x1) r1=(x2,x3) r2=(x4,x5) r3=(x6,x7), to "mask order"
+// (x0,x4) (x1,x5) (x2,x6) (x3,x7) -- the pair order of unpack_mask_f16.
 __device__ __forceinline__ void permute_x8(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
                                           uint32_t out[4]) {
     out[0] = perm(r2, r0, 0x05040100u);
@@ -77,51 +79,59 @@ __device__ __forceinline__ void permute_x8(uint32_t r0, uint32_t r1, uint32_t r2
     out[3] = perm(r3, r1, 0x07060302u);
 }
 
-// Per-group constants used by the unpack routines.
-struct ZeroConst {
-    uint32_t sub;    // fp16 pair (-(1024+z), -(1024+z)), or unused for bf16
-    uint32_t sub16;  // fp16 pair (-(64+z), -(64+z)), or unused for bf16
-};
-
-__device__ __forceinline__ ZeroConst make_zero_const_f16(float z) {
-    ZeroConst c;
-    _Float16 a = (_Float16)(-(1024.0f + z));
-    _Float16 b = (_Float16)(-(64.0f + z));
-    uint32_t ab = __builtin_bit_cast(uint16_t, a);
-    uint32_t bb = __builtin_bit_cast(uint16_t, b);
-    c.sub = ab | (ab << 16);
-    c.sub16 = bb | (bb << 16);
-    return c;
+// Natural order to "byte order" (x0,x2) (x4,x6) (x1,x3) (x5,x7) -- the pair order of
+// unpack_byte.
+__device__ __forceinline__ void permute_x8_byte(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
+                                               uint32_t out[4]) {
+    out[0] = perm(r1, r0, 0x05040100u);   // x0, x2
+    out[1] = perm(r3, r2, 0x05040100u);   // x4, x6
+    out[2] = perm(r1, r0, 0x07060302u);   // x1, x3
+    out[3] = perm(r3, r2, 0x07060302u);   // x5, x7
 }
 
-// fp16: word -> four pairs of exact codes (u - z) in kernel order.
-__device__ __forceinline__ void unpack_f16(uint32_t w, const ZeroConst& zc, uint32_t out[4]) {
-    const uint32_t MAGIC = 0x64006400u;                 // 1024.0 in both halves
-    const f16x2 inv16 = {(_Float16)0.0625f, (_Float16)0.0625f};
-    uint32_t p0 = (w & 0x000F000Fu) | MAGIC;           // 1024 + u0 | 1024 + u4
-    uint32_t p1 = (w & 0x00F000F0u) | MAGIC;           // 1024 + 16 u1 | 1024 + 16 u5
-    uint32_t w8 = w >> 8;
-    uint32_t p2 = (w8 & 0x000F000Fu) | MAGIC;          // 1024 + u2 | 1024 + u6
-    uint32_t p3 = (w8 & 0x00F000F0u) | MAGIC;          // 1024 + 16 u3 | 1024 + 16 u7
-    f16x2 s = __builtin_bit_cast(f16x2, zc.sub);
-    f16x2 s16 = __builtin_bit_cast(f16x2, zc.sub16);
-    f16x2 r0 = __builtin_bit_cast(f16x2, p0) + s;
-    f16x2 r1 = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, p1), inv16, s16);
-    f16x2 r2 = __builtin_bit_cast(f16x2, p2) + s;
-    f16x2 r3 = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, p3), inv16, s16);
-    out[0] = __builtin_bit_cast(uint32_t, r0);
-    out[1] = __builtin_bit_cast(uint32_t, r1);
-    out[2] = __builtin_bit_cast(uint32_t, r2);
-    out[3] = __builtin_bit_cast(uint32_t, r3);
+// fp16, GEMV form: four registers of subnormal codes in mask order,
+// (u0,u4) (16u1,16u5) (u2,u6) (16u3,16u7) times 2^-24.  Five integer instructions.
+__device__ __forceinline__ void unpack_mask_f16(uint32_t w, uint32_t out[4]) {
+    const uint32_t w8 = w >> 8;
+    out[0] = w & 0x000F000Fu;
+    out[1] = w & 0x00F000F0u;
+    out[2] = w8 & 0x000F000Fu;
+    out[3] = w8 & 0x00F000F0u;
 }
 
-// bf16: word -> four pairs of biased codes 128 + u (exact in bf16), kernel order.
-__device__ __forceinline__ void unpack_bf16(uint32_t w, uint32_t out[4]) {
-    const uint32_t MAGIC = 0x43004300u;                 // 128.0 in both halves
-    out[0] = (w & 0x000F000Fu) | MAGIC;
-    out[1] = ((w >> 4) & 0x000F000Fu) | MAGIC;
-    out[2] = ((w >> 8) & 0x000F000Fu) | MAGIC;
-    out[3] = ((w >> 12) & 0x000F000Fu) | MAGIC;
+// Byte form for either dtype: codes in byte order (u0,u2) (u4,u6) (u1,u3) (u5,u7), each
+// half = MAGIC_HI byte : code byte.  MAGIC = 0 gives fp16 subnormals u * 2^-24,
+// MAGIC = 0x43 gives bf16 128 + u.  Seven instructions (two masks, one shift, four
+// byte permutes).
+template <uint32_t MAGIC>
+__device__ __forceinline__ void unpack_byte(uint32_t w, uint32_t out[4]) {
+    const uint32_t t0 = w & 0x0F0F0F0Fu;           // u0 u2 u4 u6
+    const uint32_t t1 = (w >> 4) & 0x0F0F0F0Fu;    // u1 u3 u5 u7
+    const uint32_t mag = MAGIC * 0x01010101u;
+    // selector bytes 0..3 pick from the low operand, 4..7 from the high operand
+    out[0] = perm(mag, t0, 0x04010400u);
+    out[1] = perm(mag, t0, 0x04030402u);
+    out[2] = perm(mag, t1, 0x04010400u);
+    out[3] = perm(mag, t1, 0x04030402u);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL,
+                                                             0xF, 0xF, true));
+}
+
+// Sum over a 64-lane wave with DPP row operations; the total is returned in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp_mov<0x141>(v);   // row_half_mirror
+    v += dpp_mov<0x140>(v);   // row_mirror: every lane holds its 16-lane row sum
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 // fp32 += a.x*b.x + a.y*b.y on 16-bit pairs (v_dot2_f32_f16 / v_dot2_f32_bf16).

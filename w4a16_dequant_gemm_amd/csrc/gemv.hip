@@ -1,23 +1,24 @@
-// Decode-regime W4A16 kernel: weight-streaming GEMV for small M (dot2 on the VALU).
+// Decode-regime W4A16 kernel: weight-streaming GEMV for small M (v_dot2 on the VALU).
 //
-// At decode the layer reads every weight once per token while doing two flops per
-// weight per activation row, so it is bound by the weight stream from HBM, not by
-// arithmetic (page "推理优化中“用精度换性能“的核心技术：量化", section 一; page
-// "Quantization & Acceleration: 解释 W8A8 与 W4A16 的差异与取舍", decode vs prefill).
-// The kernel therefore (i) reads each packed weight row exactly once with coalesced
-// 128-bit loads, (ii) dequantizes in registers only (page
+// At decode the layer reads every weight once per token and does two flops per weight
+// per activation row, so it is bound by the weight stream from HBM, not by arithmetic
+// (page "推理优化中“用精度换性能“的核心技术：量化", section 一; page
+// "Quantization & Acceleration: 解释 W8A8 与 W4A16 的差异与取舍", decode vs prefill).  The
+// kernel (i) reads each packed weight row exactly once with coalesced 128-bit loads, all
+// issued before any arithmetic so the whole per-block share of the stream is in flight
+// at once, (ii) dequantizes in registers only (page
 // "大模型推理中 Weight-only、W8A8 和 FP8 量化有什么区别？如何选型？", section 二) and
-// (iii) keeps the activations resident in registers for the life of the block.
+// (iii) keeps the activations in registers.
 //
-// Mapping.  A block of NT threads (NT a multiple of 64, <= 1024) owns RB consecutive
-// output rows and the whole K range.  Thread t owns the 32-column chunks
-// c = t + NT*i (i < CPL) of every row: its activation chunks (M x 32 values, permuted to
-// the pair order of the unpack) are loaded once into registers, then for each row the
-// thread streams one 16-byte weight chunk per owned chunk.  One 16-byte chunk (32
-// columns) always lies inside one group because g is a multiple of 32, so the group's
-// scale multiplies the chunk's fp32 partial sum once.  Partial sums are reduced across
-// the wave with shuffles and across waves through LDS; one thread per (row, m) rounds
-// to the output dtype.
+// Mapping.  A block of NT threads (a multiple of 64) owns RB consecutive output rows and
+// the whole K range.  Thread t owns the 32-column chunks c = t + NT*i (i < CPL) of every
+// row; a 16-byte chunk never straddles a group (g is a multiple of 32), so each chunk
+// contributes s * (sum x*u - z * sum x) with one scale and one zero point.
+//   fp16: codes are fp16 subnormals from two masks (unpack_mask_f16); the x1 and x16
+//     pairs go to two v_dot2 accumulators; 2^24 is folded into the scale.
+//   bf16: codes are 128 + u from byte permutes (unpack_byte<0x43>); the bias leaves with
+//     the chunk's activation sum.
+// Partial sums are reduced across the wave with DPP and across waves through LDS.
 #include "common.h"
 #include "launch.h"
 
@@ -25,18 +26,20 @@ namespace w4a16 {
 
 namespace {
 
-// Threads per block the kernel is compiled for: configurations that hold many
-// activation registers get 256 VGPRs (512 threads), the others 128 (1024 threads).
-constexpr int launch_limit(int M, int CPL) { return (M * CPL <= 2 || (CPL == 1 && M <= 4)) ? 1024 : 512; }
+// Conservative VGPR estimate of one configuration; it decides the launch bound.
+constexpr int gemv_regs(int M, int CPL, int RB) {
+    return 6 * RB * CPL + 16 * M * CPL + 3 * RB * M + 40;
+}
+constexpr int launch_limit(int M, int CPL, int RB) {
+    return gemv_regs(M, CPL, RB) <= 128 ? 1024 : (gemv_regs(M, CPL, RB) <= 256 ? 512 : 0);
+}
 
 template <int DT, int M, int CPL, int RB>
-__global__ __launch_bounds__(launch_limit(M, CPL)) void gemv_kernel(const uint16_t* __restrict__ X,
-                                                    const uint32_t* __restrict__ qw,
-                                                    const uint16_t* __restrict__ scales,
-                                                    const uint16_t* __restrict__ zeros,
-                                                    uint16_t* __restrict__ Y, int N, int K, int G,
-                                                    int gshift) {
-    __shared__ float red[16][RB][M];
+__global__ __launch_bounds__(launch_limit(M, CPL, RB)) void gemv_kernel(
+    const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int has_zeros,
+    uint16_t* __restrict__ Y, int N, int K, int G, int gshift) {
+    __shared__ float red[16][RB * M];
     const int tid = threadIdx.x;
     const int NT = blockDim.x;
     const int lane = tid & 63;
@@ -44,169 +47,476 @@ __global__ __launch_bounds__(launch_limit(M, CPL)) void gemv_kernel(const uint16
     const int nwaves = NT >> 6;
     const int C = K >> 5;
     const int KW = K >> 3;
+    const int row0 = blockIdx.x * RB;
+    // A NULL zero-point array reads the scales instead (always valid memory); the value
+    // is replaced by 8 below.  Keeps every load unconditional.
+    const uint16_t* zsrc = has_zeros ? zeros : scales;
 
-    // Activation chunks, permuted, in registers.
-    uint32_t xr[M][CPL][16];
-    float xs[M][CPL];
-    int cg[CPL];
+    int cc[CPL], cg[CPL];
     bool cval[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int c = tid + NT * i;
         cval[i] = c < C;
-        cg[i] = group_of(c << 5, gshift);
+        cc[i] = cval[i] ? c : 0;      // chunks past the row end re-read chunk 0 ...
+        cg[i] = group_of(cc[i] << 5, gshift);
+    }
+
+    // 1. Activations first (vmcnt waits are in issue order and they are needed first),
+    //    then the whole weight share of this block.  Rows past N are clamped to N-1 (their
+    //    results are not stored).
+    u32x4 xv[M][CPL][4];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                xv[m][i][b] = reinterpret_cast<const u32x4*>(X + (size_t)m * K + ((size_t)cc[i] << 5))[b];
+    u32x4 wv[RB][CPL];
+    uint16_t sraw[RB][CPL], zraw[RB][CPL];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        const int n = min(row0 + r, N - 1);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            wv[r][i] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(qw + (size_t)n * KW + ((size_t)cc[i] << 2)));
+            sraw[r][i] = scales[(size_t)n * G + cg[i]];
+            zraw[r][i] = zsrc[(size_t)n * G + cg[i]];
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. Activations to pair order; chunk sums.  ... and get zero activations, so they
+    //    contribute nothing whatever weights they meet.
+    uint32_t xr[M][CPL][16];
+    float xs[M][CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            xs[m][i] = 0.0f;
-            if (cval[i]) {
-                const u32x4* src = reinterpret_cast<const u32x4*>(X + (size_t)m * K + ((size_t)c << 5));
+            float sum = 0.0f;
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const u32x4 v = src[b];
-                    uint32_t o[4];
+            for (int b = 0; b < 4; ++b) {
+                const u32x4 v = xv[m][i][b];
+                uint32_t o[4];
+                if constexpr (DT == DT_F16)
                     permute_x8(v.x, v.y, v.z, v.w, o);
+                else
+                    permute_x8_byte(v.x, v.y, v.z, v.w, o);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) xr[m][i][4 * b + q] = o[q];
-                    if constexpr (DT == DT_BF16) {
-                        xs[m][i] += (pair_sum<DT>(v.x) + pair_sum<DT>(v.y)) +
-                                    (pair_sum<DT>(v.z) + pair_sum<DT>(v.w));
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int q = 0; q < 16; ++q) xr[m][i][q] = 0u;
+                for (int q = 0; q < 4; ++q) xr[m][i][4 * b + q] = cval[i] ? o[q] : 0u;
+                sum += (pair_sum<DT>(v.x) + pair_sum<DT>(v.y)) + (pair_sum<DT>(v.z) + pair_sum<DT>(v.w));
             }
+            // fp16 works in units of 2^-24 (the subnormal code scale)
+            xs[m][i] = cval[i] ? (DT == DT_F16 ? sum * 5.9604644775390625e-8f : sum) : 0.0f;
         }
     }
 
-    for (int row0 = blockIdx.x * RB; row0 < N; row0 += gridDim.x * RB) {
-        u32x4 wv[RB][CPL];
-        float sc[RB][CPL], zc[RB][CPL];
+    // 3. Dot products.
+    float acc[RB][M];
 #pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            const int n = row0 + r;
+    for (int r = 0; r < RB; ++r) {
 #pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                const int c = tid + NT * i;
-                if (n < N && cval[i]) {
-                    wv[r][i] = *reinterpret_cast<const u32x4*>(qw + (size_t)n * KW + ((size_t)c << 2));
-                    sc[r][i] = h2f(scales[(size_t)n * G + cg[i]]);
-                    zc[r][i] = zeros ? h2f(zeros[(size_t)n * G + cg[i]]) : 8.0f;
-                } else {
-                    wv[r][i] = u32x4{0u, 0u, 0u, 0u};
-                    sc[r][i] = 0.0f;
-                    zc[r][i] = 0.0f;
-                }
-            }
-        }
-
-        float acc[RB][M];
+        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 #pragma unroll
-        for (int r = 0; r < RB; ++r) {
+        for (int i = 0; i < CPL; ++i) {
+            const float s = h2f(sraw[r][i]);
+            const float z = has_zeros ? h2f(zraw[r][i]) : 8.0f;
+            if constexpr (DT == DT_F16) {
+                float pa[M], pb[M];
 #pragma unroll
-            for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                float part[M];
-#pragma unroll
-                for (int m = 0; m < M; ++m) part[m] = 0.0f;
-                ZeroConst zk;
-                if constexpr (DT == DT_F16) zk = make_zero_const_f16(zc[r][i]);
+                for (int m = 0; m < M; ++m) pa[m] = pb[m] = 0.0f;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     uint32_t cd[4];
-                    if constexpr (DT == DT_F16)
-                        unpack_f16(wv[r][i][q], zk, cd);
-                    else
-                        unpack_bf16(wv[r][i][q], cd);
+                    unpack_mask_f16(wv[r][i][q], cd);
 #pragma unroll
                     for (int m = 0; m < M; ++m) {
-                        float p = part[m];
-                        p = dot2<DT>(xr[m][i][4 * q + 0], cd[0], p);
-                        p = dot2<DT>(xr[m][i][4 * q + 1], cd[1], p);
-                        p = dot2<DT>(xr[m][i][4 * q + 2], cd[2], p);
-                        p = dot2<DT>(xr[m][i][4 * q + 3], cd[3], p);
-                        part[m] = p;
+                        pa[m] = dot2<DT>(xr[m][i][4 * q + 0], cd[0], pa[m]);
+                        pb[m] = dot2<DT>(xr[m][i][4 * q + 1], cd[1], pb[m]);
+                        pa[m] = dot2<DT>(xr[m][i][4 * q + 2], cd[2], pa[m]);
+                        pb[m] = dot2<DT>(xr[m][i][4 * q + 3], cd[3], pb[m]);
+                    }
+                }
+                const float s24 = s * 16777216.0f;     // 2^24: exact
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    float t = fmaf(pb[m], 0.0625f, pa[m]);   // sum x*u * 2^-24
+                    t = fmaf(-z, xs[m][i], t);
+                    acc[r][m] = fmaf(s24, t, acc[r][m]);
+                }
+            } else {
+                float p[M];
+#pragma unroll
+                for (int m = 0; m < M; ++m) p[m] = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    uint32_t cd[4];
+                    unpack_byte<0x43>(wv[r][i][q], cd);
+#pragma unroll
+                    for (int m = 0; m < M; ++m) {
+                        p[m] = dot2<DT>(xr[m][i][4 * q + 0], cd[0], p[m]);
+                        p[m] = dot2<DT>(xr[m][i][4 * q + 1], cd[1], p[m]);
+                        p[m] = dot2<DT>(xr[m][i][4 * q + 2], cd[2], p[m]);
+                        p[m] = dot2<DT>(xr[m][i][4 * q + 3], cd[3], p[m]);
                     }
                 }
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
-                    if constexpr (DT == DT_F16) {
-                        acc[r][m] = fmaf(sc[r][i], part[m], acc[r][m]);
-                    } else {
-                        const float corr = fmaf(-(128.0f + zc[r][i]), xs[m][i], part[m]);
-                        acc[r][m] = fmaf(sc[r][i], corr, acc[r][m]);
-                    }
+                    const float t = fmaf(-(128.0f + z), xs[m][i], p[m]);
+                    acc[r][m] = fmaf(s, t, acc[r][m]);
                 }
             }
         }
+    }
 
-        // Reduce over the 64 lanes of each wave, then over the waves.
+    // 4. Reduce over the wave (DPP) and over the waves (LDS); round once to the output.
+    if (nwaves == 1) {
 #pragma unroll
-        for (int r = 0; r < RB; ++r) {
+        for (int r = 0; r < RB; ++r)
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-                float v = acc[r][m];
-#pragma unroll
-                for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-                if (lane == 0) red[wave][r][m] = v;
+                const float v = wave_sum(acc[r][m]);
+                if (lane == 0 && row0 + r < N) Y[(size_t)m * N + row0 + r] = f2out<DT>(v);
             }
+        return;
+    }
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float v = wave_sum(acc[r][m]);
+            if (lane == 0) red[wave][r * M + m] = v;
         }
-        __syncthreads();
-        if (tid < RB * M) {
-            const int r = tid / M;
-            const int m = tid % M;
-            const int n = row0 + r;
-            float v = 0.0f;
-            for (int w = 0; w < nwaves; ++w) v += red[w][r][m];
-            if (n < N) Y[(size_t)m * N + n] = f2out<DT>(v);
-        }
-        __syncthreads();
+    __syncthreads();
+    if (tid < RB * M) {
+        const int r = tid / M;
+        const int m = tid % M;
+        float v = 0.0f;
+        for (int w = 0; w < nwaves; ++w) v += red[w][tid];
+        if (row0 + r < N) Y[(size_t)m * N + row0 + r] = f2out<DT>(v);
     }
 }
 
-constexpr int kRB = 4;
+// ---------------------------------------------------------------------------------
+// Streaming variant (used whenever the activations fit in LDS).  The grid is a fixed,
+// balanced set of persistent blocks: block b owns a contiguous range of about N / grid
+// rows.  The block stages the permuted activations and their 32-column chunk sums in
+// LDS once; then wave w of the block walks the rows row_begin + w*RB + i*W*RB
+// (batches of RB rows), lane l handling chunks l + 64 c of each row.  Weight loads of
+// the next batch are issued before the current batch is computed (two register
+// buffers), so the arithmetic of one batch overlaps the HBM stream of the next.  Each
+// wave owns whole rows: one DPP reduction per row, no cross-wave traffic.
+constexpr int kLdsBudget = 65536;
+
+__host__ __device__ constexpr int lds_bytes(int M, int CPL) { return (M * CPL * 64 + 1) * (64 + 4); }
+
+template <int DT, int M, int CPL, int RB>
+struct RowBatch {
+    u32x4 w[RB][CPL];
+    uint16_t s[RB][CPL], z[RB][CPL];
+};
+
+// Buffer loads: the row offset is wave-uniform (an SGPR soffset) and the lane's chunk
+// offset never changes between rows (voffset), so a load costs no address arithmetic.
+// A batch past the wave's last one loads through `none` (num_records = 0): buffer loads
+// out of range return zeros without touching memory, so every prefetch can be issued
+// unconditionally.
+struct StreamSrc {
+    __amdgpu_buffer_rsrc_t w, s, z, none;
+    int row_bytes_w, row_bytes_sz;
+};
+
+template <int DT, int M, int CPL, int RB>
+__device__ __forceinline__ void load_batch(RowBatch<DT, M, CPL, RB>& bt, const StreamSrc& src, int row,
+                                           bool live, int N, const int vw[CPL], const int vsz[CPL]) {
+    const __amdgpu_buffer_rsrc_t rw = live ? src.w : src.none;   // wave-uniform selects
+    const __amdgpu_buffer_rsrc_t rs = live ? src.s : src.none;
+    const __amdgpu_buffer_rsrc_t rz = live ? src.z : src.none;
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        const int n = min(row + r, N - 1);          // wave-uniform
+        const int ow = n * src.row_bytes_w;
+        const int osz = n * src.row_bytes_sz;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            bt.w[r][i] = __builtin_amdgcn_raw_buffer_load_b128(rw, vw[i], ow, 2 /* nt */);
+            bt.s[r][i] = __builtin_amdgcn_raw_buffer_load_b16(rs, vsz[i], osz, 0);
+            bt.z[r][i] = __builtin_amdgcn_raw_buffer_load_b16(rz, vsz[i], osz, 0);
+        }
+    }
+}
+
+template <int DT, int M, int CPL, int RB>
+__device__ __forceinline__ void compute_batch(const RowBatch<DT, M, CPL, RB>& bt, const uint32_t* xp,
+                                              const float* xsum, int lane, int has_zeros,
+                                              float acc[RB][M]) {
+    constexpr int CH = CPL * 64;
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = lane + 64 * i;
+        uint32_t xr[M][16];
+        float xs[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            // piece-major layout [m][piece][chunk]: a wave reads 64 consecutive 16-byte slots
+            const u32x4* src = reinterpret_cast<const u32x4*>(xp) + (size_t)m * 4 * CH + c;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const u32x4 v = src[b * CH];
+                xr[m][4 * b + 0] = v.x;
+                xr[m][4 * b + 1] = v.y;
+                xr[m][4 * b + 2] = v.z;
+                xr[m][4 * b + 3] = v.w;
+            }
+            xs[m] = xsum[m * CH + c];
+        }
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const float s = h2f(bt.s[r][i]);
+            const float z = has_zeros ? h2f(bt.z[r][i]) : 8.0f;
+            if constexpr (DT == DT_F16) {
+                float pa[M], pb[M];
+#pragma unroll
+                for (int m = 0; m < M; ++m) pa[m] = pb[m] = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    uint32_t cd[4];
+                    unpack_mask_f16(bt.w[r][i][q], cd);
+#pragma unroll
+                    for (int m = 0; m < M; ++m) {
+                        pa[m] = dot2<DT>(xr[m][4 * q + 0], cd[0], pa[m]);
+                        pb[m] = dot2<DT>(xr[m][4 * q + 1], cd[1], pb[m]);
+                        pa[m] = dot2<DT>(xr[m][4 * q + 2], cd[2], pa[m]);
+                        pb[m] = dot2<DT>(xr[m][4 * q + 3], cd[3], pb[m]);
+                    }
+                }
+                const float s24 = s * 16777216.0f;
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    float t = fmaf(pb[m], 0.0625f, pa[m]);
+                    t = fmaf(-z, xs[m], t);
+                    acc[r][m] = fmaf(s24, t, acc[r][m]);
+                }
+            } else {
+                float p[M];
+#pragma unroll
+                for (int m = 0; m < M; ++m) p[m] = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    uint32_t cd[4];
+                    unpack_byte<0x43>(bt.w[r][i][q], cd);
+#pragma unroll
+                    for (int m = 0; m < M; ++m) {
+                        p[m] = dot2<DT>(xr[m][4 * q + 0], cd[0], p[m]);
+                        p[m] = dot2<DT>(xr[m][4 * q + 1], cd[1], p[m]);
+                        p[m] = dot2<DT>(xr[m][4 * q + 2], cd[2], p[m]);
+                        p[m] = dot2<DT>(xr[m][4 * q + 3], cd[3], p[m]);
+                    }
+                }
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    const float t = fmaf(-(128.0f + z), xs[m], p[m]);
+                    acc[r][m] = fmaf(s, t, acc[r][m]);
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);   // one chunk of activations live at a time
+    }
+}
+
+// Rows at or past row_end belong to the next block (or do not exist) and are not stored.
+template <int DT, int M, int RB>
+__device__ __forceinline__ void store_batch(const float acc[RB][M], int row, int row_end, int N,
+                                            int lane, uint16_t* __restrict__ Y) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float v = wave_sum(acc[r][m]);
+            if (lane == 0 && row + r < row_end) Y[(size_t)m * N + row + r] = f2out<DT>(v);
+        }
+}
+
+template <int DT, int M, int CPL, int RB, int W>
+__global__ __launch_bounds__(64 * W) void gemv_stream_kernel(
+    const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int has_zeros,
+    uint16_t* __restrict__ Y, int N, int K, int G, int gshift, int rows_per_block) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+    constexpr int CH = CPL * 64;                       // padded chunks per activation row
+    constexpr int NT = 64 * W;
+    constexpr int JOBS = M * CH * 4;                   // 8-column staging jobs
+    constexpr int JPT = (JOBS + NT - 1) / NT;
+    uint32_t* xp = lds;                  // [M][4 pieces][CH] x 16 B pairs, then one spare slot
+    float* xsum = reinterpret_cast<float*>(lds + (M * CH + 1) * 16);   // [M*CH + 1]
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int C = K >> 5;
+    const int KW = K >> 3;
+    const int row_begin = blockIdx.x * rows_per_block;
+    const int row_end = min(N, row_begin + rows_per_block);
+    const int first = row_begin + wave * RB;
+    const int nbatch = first < row_end ? (row_end - first + W * RB - 1) / (W * RB) : 0;
+
+    StreamSrc src;
+    src.w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(qw), 0, 0x7FFFFFFF, 0x00020000);
+    src.s = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(scales), 0, 0x7FFFFFFF, 0x00020000);
+    // NULL zeros: read the scales (valid memory); the value is replaced by 8
+    src.z = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(has_zeros ? zeros : scales), 0,
+                                              0x7FFFFFFF, 0x00020000);
+    src.none = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(qw), 0, 0, 0x00020000);
+    src.row_bytes_w = KW * 4;
+    src.row_bytes_sz = G * 2;
+    int vw[CPL], vsz[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = lane + 64 * i;
+        const int cc = c < C ? c : 0;     // chunks past the row end re-read chunk 0 (zero activations)
+        vw[i] = cc * 16;
+        vsz[i] = group_of(cc << 5, gshift) * 2;
+    }
+
+    // 1. Issue order = need order (vmcnt waits are in issue order): activation staging
+    //    loads, then the first two weight batches.  All loads unconditional.
+    u32x4 xv[JPT];
+#pragma unroll
+    for (int j = 0; j < JPT; ++j) {
+        const int job = min(tid + NT * j, JOBS - 1);
+        const int m = job / (CH * 4);
+        const int e = job % (CH * 4);                  // 8-column block within the padded row
+        const int c = e >> 2;
+        xv[j] = reinterpret_cast<const u32x4*>(X + (size_t)m * K + ((size_t)(c < C ? c : 0) << 5))[e & 3];
+    }
+    RowBatch<DT, M, CPL, RB> buf0, buf1;
+    load_batch<DT, M, CPL, RB>(buf0, src, first, nbatch > 0, N, vw, vsz);
+    load_batch<DT, M, CPL, RB>(buf1, src, first + W * RB, nbatch > 1, N, vw, vsz);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. Stage activations: permute each 8-column block, chunk sums by a quad reduction
+    //    (the four blocks of a chunk sit in four consecutive lanes).  Branch-free except
+    //    the predicated sum store; threads without a job write the spare slot.
+#pragma unroll
+    for (int j = 0; j < JPT; ++j) {
+        const int job0 = tid + NT * j;
+        const bool real = job0 < JOBS;
+        const int job = real ? job0 : JOBS;            // spare: 4 slots past the last chunk
+        const int e = job % (CH * 4);
+        const bool ok = real && (e >> 2) < C;
+        const u32x4 v = xv[j];
+        uint32_t o[4];
+        if constexpr (DT == DT_F16)
+            permute_x8(v.x, v.y, v.z, v.w, o);
+        else
+            permute_x8_byte(v.x, v.y, v.z, v.w, o);
+        const uint32_t ones = DT == DT_F16 ? 0x3C003C00u : 0x3F803F80u;
+        float sum = dot2<DT>(v.x, ones, 0.0f);
+        sum = dot2<DT>(v.y, ones, sum);
+        sum = dot2<DT>(v.z, ones, sum);
+        sum = dot2<DT>(v.w, ones, sum);
+        sum += dpp_mov<0xB1>(sum);                     // quad_perm [1,0,3,2]
+        sum += dpp_mov<0x4E>(sum);                     // quad_perm [2,3,0,1]
+        const int slot = real ? job >> 2 : M * CH;
+        const int mrow = job / (CH * 4);
+        const int piece_major = (mrow * 4 + (e & 3)) * CH + (e >> 2);
+        reinterpret_cast<u32x4*>(xp)[real ? piece_major : 4 * M * CH] =
+            ok ? u32x4{o[0], o[1], o[2], o[3]} : u32x4{0u, 0u, 0u, 0u};
+        if ((job0 & 3) == 0)
+            xsum[slot] = ok ? (DT == DT_F16 ? sum * 5.9604644775390625e-8f : sum) : 0.0f;
+    }
+    __syncthreads();
+
+    // 3. Row batches, two in flight.  Prefetches and computes are unconditional (a batch
+    //    past the end loads zeros through `none` and stores nothing): a conditional
+    //    prefetch would turn each buffer into a merge of old and new values and the
+    //    compiler would shuffle registers, waiting on every load to do so.
+    float acc[RB][M];
+    for (int b = 0; b < nbatch; b += 2) {
+        compute_batch<DT, M, CPL, RB>(buf0, xp, xsum, lane, has_zeros, acc);
+        load_batch<DT, M, CPL, RB>(buf0, src, first + (b + 2) * W * RB, b + 2 < nbatch, N, vw, vsz);
+        store_batch<DT, M, RB>(acc, first + b * W * RB, row_end, N, lane, Y);
+        compute_batch<DT, M, CPL, RB>(buf1, xp, xsum, lane, has_zeros, acc);
+        load_batch<DT, M, CPL, RB>(buf1, src, first + (b + 3) * W * RB, b + 3 < nbatch, N, vw, vsz);
+        store_batch<DT, M, RB>(acc, first + (b + 1) * W * RB, row_end, N, lane, Y);
+    }
+}
 
 struct GemvCfg {
     int nt = 0;
     int cpl = 0;
+    int rb = 0;
 };
 
-int cpl_max(int M) { return M >= 4 ? 1 : (M == 3 ? 1 : 4 / M); }
+constexpr int kMaxM = 8;
+constexpr int cpl_max(int M) { return M == 1 ? 4 : (M == 2 ? 2 : 1); }
 
-GemvCfg pick(int M, int K) {
+// Choose chunks-per-thread (best lane utilisation, then more chunks per thread) and
+// rows-per-block (most rows that still give >= 2048 waves, i.e. 8 per CU; else 2).
+GemvCfg pick(int M, int N, int K) {
     const int C = K / 32;
     GemvCfg best;
     double best_util = -1.0;
     for (int cpl = 1; cpl <= cpl_max(M); ++cpl) {
-        int nt = ((C + cpl - 1) / cpl + 63) / 64 * 64;
-        if (nt > launch_limit(M, cpl)) continue;
-        double util = (double)C / ((double)nt * cpl);
+        const int nt = ((C + cpl - 1) / cpl + 63) / 64 * 64;
+        if (nt > 1024 || nt > launch_limit(M, cpl, 2)) continue;
+        const double util = (double)C / ((double)nt * cpl);
         if (util > best_util + 1e-9 || (util > best_util - 1e-9 && cpl > best.cpl)) {
             best_util = util;
             best.nt = nt;
             best.cpl = cpl;
         }
     }
+    if (best.nt == 0) return best;
+    const int waves_per_block = best.nt / 64;
+    int rb = 2;
+    for (int cand : {8, 4}) {
+        const long long waves = (long long)((N + cand - 1) / cand) * waves_per_block;
+        if (waves >= 2048 && best.nt <= launch_limit(M, best.cpl, cand)) {
+            rb = cand;
+            break;
+        }
+    }
+    best.rb = rb;
     return best;
 }
 
+template <int DT, int M, int CPL, int RB>
+hipError_t run3(const LinearArgs& a, int nt, hipStream_t st) {
+    if constexpr (launch_limit(M, CPL, RB) == 0) {
+        return hipErrorInvalidValue;
+    } else {
+        const int blocks = (a.N + RB - 1) / RB;
+        hipLaunchKernelGGL((gemv_kernel<DT, M, CPL, RB>), dim3(blocks), dim3(nt), 0, st,
+                           static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros,
+                           a.zeros ? 1 : 0, static_cast<uint16_t*>(a.Y), a.N, a.K, a.G, a.gshift);
+        return hipGetLastError();
+    }
+}
+
 template <int DT, int M, int CPL>
-hipError_t run(const LinearArgs& a, int nt, hipStream_t st) {
-    const int blocks = (a.N + kRB - 1) / kRB;
-    hipLaunchKernelGGL((gemv_kernel<DT, M, CPL, kRB>), dim3(blocks), dim3(nt), 0, st,
-                       static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros,
-                       static_cast<uint16_t*>(a.Y), a.N, a.K, a.G, a.gshift);
-    return hipGetLastError();
+hipError_t run2(const LinearArgs& a, const GemvCfg& c, hipStream_t st) {
+    switch (c.rb) {
+        case 2: return run3<DT, M, CPL, 2>(a, c.nt, st);
+        case 4: return run3<DT, M, CPL, 4>(a, c.nt, st);
+        case 8: return run3<DT, M, CPL, 8>(a, c.nt, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <int DT, int M>
 hipError_t run_m(const LinearArgs& a, const GemvCfg& c, hipStream_t st) {
     switch (c.cpl) {
-        case 1: return run<DT, M, 1>(a, c.nt, st);
-        case 2: if constexpr (M <= 2) return run<DT, M, 2>(a, c.nt, st); break;
-        case 3: if constexpr (M == 1) return run<DT, M, 3>(a, c.nt, st); break;
-        case 4: if constexpr (M == 1) return run<DT, M, 4>(a, c.nt, st); break;
+        case 1: return run2<DT, M, 1>(a, c, st);
+        case 2: if constexpr (cpl_max(M) >= 2) return run2<DT, M, 2>(a, c, st); break;
+        case 3: if constexpr (cpl_max(M) >= 3) return run2<DT, M, 3>(a, c, st); break;
+        case 4: if constexpr (cpl_max(M) >= 4) return run2<DT, M, 4>(a, c, st); break;
     }
     return hipErrorInvalidValue;
 }
@@ -226,15 +536,78 @@ hipError_t run_dt(const LinearArgs& a, const GemvCfg& c, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
+// Rows per batch of the streaming variant: two rows while a row is short, one row once
+// a lane streams >= 4 chunks per row (two batches are in flight per wave).
+constexpr int lds_rb(int M, int CPL) { return M * CPL >= 4 ? 1 : 2; }
+constexpr int lds_max_cpl(int M) {
+    return M == 1 ? 6 : (M == 2 ? 4 : (M == 3 ? 3 : (M == 4 ? 2 : 0)));
+}
+constexpr int kStreamWaves = 8;       // waves per block: two per SIMD
+
+struct LdsCfg {
+    int cpl = 0;
+    int blocks = 0;
+    int rows_per_block = 0;
+};
+
+// One block per CU (256) when N allows, each owning ceil(N / 256) rows.
+LdsCfg pick_lds(int M, int N, int K) {
+    LdsCfg c;
+    if (M < 1 || M > 4) return c;
+    const int cpl = (K / 32 + 63) / 64;
+    if (cpl > lds_max_cpl(M) || lds_bytes(M, cpl) > kLdsBudget) return c;
+    // 32-bit buffer offsets: the packed weights must stay below 2 GiB
+    if ((long long)N * (K / 2) >= (1LL << 31)) return c;
+    c.cpl = cpl;
+    const int want = 256;
+    c.rows_per_block = (N + want - 1) / want;
+    c.blocks = (N + c.rows_per_block - 1) / c.rows_per_block;
+    return c;
+}
+
+template <int DT, int M, int CPL>
+hipError_t run_lds3(const LinearArgs& a, const LdsCfg& c, hipStream_t st) {
+    constexpr int RB = lds_rb(M, CPL);
+    hipLaunchKernelGGL((gemv_stream_kernel<DT, M, CPL, RB, kStreamWaves>), dim3(c.blocks),
+                       dim3(64 * kStreamWaves), lds_bytes(M, CPL), st,
+                       static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, a.zeros ? 1 : 0,
+                       static_cast<uint16_t*>(a.Y), a.N, a.K, a.G, a.gshift, c.rows_per_block);
+    return hipGetLastError();
+}
+
+template <int DT, int M, int CPL>
+hipError_t run_lds_cpl(const LinearArgs& a, const LdsCfg& c, hipStream_t st) {
+    if constexpr (CPL > lds_max_cpl(M)) {
+        return hipErrorInvalidValue;
+    } else {
+        if (c.cpl == CPL) return run_lds3<DT, M, CPL>(a, c, st);
+        return run_lds_cpl<DT, M, CPL + 1>(a, c, st);
+    }
+}
+
+template <int DT>
+hipError_t run_lds(const LinearArgs& a, const LdsCfg& c, hipStream_t st) {
+    switch (a.M) {
+        case 1: return run_lds_cpl<DT, 1, 1>(a, c, st);
+        case 2: return run_lds_cpl<DT, 2, 1>(a, c, st);
+        case 3: return run_lds_cpl<DT, 3, 1>(a, c, st);
+        case 4: return run_lds_cpl<DT, 4, 1>(a, c, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 bool gemv_supports(const LinearArgs& a) {
-    if (a.M < 1 || a.M > 8) return false;
-    return pick(a.M, a.K).nt > 0;
+    if (a.M < 1 || a.M > kMaxM) return false;
+    return pick_lds(a.M, a.N, a.K).cpl > 0 || pick(a.M, a.N, a.K).nt > 0;
 }
 
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t st) {
-    const GemvCfg c = pick(a.M, a.K);
+    const LdsCfg lc = pick_lds(a.M, a.N, a.K);
+    if (lc.cpl > 0)
+        return a.dtype == DT_F16 ? run_lds<DT_F16>(a, lc, st) : run_lds<DT_BF16>(a, lc, st);
+    const GemvCfg c = pick(a.M, a.N, a.K);
     if (c.nt == 0) return hipErrorInvalidValue;
     return a.dtype == DT_F16 ? run_dt<DT_F16>(a, c, st) : run_dt<DT_BF16>(a, c, st);
 }

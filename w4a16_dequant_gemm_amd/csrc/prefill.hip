@@ -18,10 +18,12 @@
 //     columns k0 + 32h + 8kk + {0,4,1,5,2,6,3,7}, and the A lane (m, h) reads the same
 //     columns from LDS.  Each MFMA therefore stays inside one 64-column window, so a
 //     group size that is a multiple of 64 never splits an MFMA across groups.
+//   Codes: byte-permute unpack (fp16 subnormals u * 2^-24, or bf16 128 + u), so the
+//     activation tile is staged in the matching "byte order".
 //   Groups: the MFMAs of one group accumulate into acc_g starting from zero; at the
-//     group's last step acc += s[n] * acc_g (fp16: exact codes u - z), or
-//     acc += s[n] * (acc_g - (128 + z[n]) * S_g[m]) (bf16: biased codes, S_g = sum of the
-//     group's activations of row m).
+//     group's last step acc += s'[n] * (acc_g - c[n] * S_g[m]) with S_g the group's
+//     activation sum of row m (computed while staging), fp16: s' = s * 2^24, c = z and S_g
+//     in units of 2^-24; bf16: s' = s, c = 128 + z.
 #include "common.h"
 #include "launch.h"
 
@@ -58,6 +60,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restr
                                                          const uint32_t* __restrict__ qw,
                                                          const uint16_t* __restrict__ scales,
                                                          const uint16_t* __restrict__ zeros,
+                                                         int has_zeros,
                                                          uint16_t* __restrict__ Y, int M, int N,
                                                          int K, int G, int steps_per_group) {
     __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * LDS_STRIDE];
@@ -80,30 +83,25 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restr
     const int nsteps = K / BK;
 
     // Staging role: thread t loads row t/2, columns 32*(t%2) .. +31 of the tile.
+    // Rows past M / N are clamped to the last valid row: every load is unconditional and
+    // the results of those rows are never stored.
     const int srow = tid >> 1;
     const int shalf = tid & 1;
-    const bool srow_ok = (m0 + srow) < M;
-    const uint16_t* xsrc = X + (size_t)(m0 + (srow_ok ? srow : 0)) * K + 32 * shalf;
+    const uint16_t* xsrc = X + (size_t)min(m0 + srow, M - 1) * K + 32 * shalf;
+    const uint16_t* zsrc = has_zeros ? zeros : scales;   // NULL zeros: value replaced by 8
 
     // Weight rows this lane feeds (one per n sub-tile).
     int wrow[2];
-    bool wok[2];
 #pragma unroll
-    for (int ns = 0; ns < 2; ++ns) {
-        const int n = n0 + wn * 64 + ns * 32 + l32;
-        wok[ns] = n < N;
-        wrow[ns] = wok[ns] ? n : 0;
-    }
+    for (int ns = 0; ns < 2; ++ns) wrow[ns] = min(n0 + wn * 64 + ns * 32 + l32, N - 1);
 
     u32x4 xreg[4];
-    float s_acc = 0.0f;   // bf16: running group sum of this staging row
+    float s_acc = 0.0f;   // running group sum of this staging row
 
     auto load_x = [&](int step) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            xreg[b] = srow_ok ? *reinterpret_cast<const u32x4*>(xsrc + (size_t)step * BK + 8 * b)
-                              : u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int b = 0; b < 4; ++b)
+            xreg[b] = *reinterpret_cast<const u32x4*>(xsrc + (size_t)step * BK + 8 * b);
     };
     auto store_x = [&](int buf, int step) {
         uint16_t* dst = &xs[buf][srow * LDS_STRIDE + 32 * shalf];
@@ -111,30 +109,27 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restr
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             uint32_t o[4];
-            permute_x8(xreg[b].x, xreg[b].y, xreg[b].z, xreg[b].w, o);
+            permute_x8_byte(xreg[b].x, xreg[b].y, xreg[b].z, xreg[b].w, o);
             *reinterpret_cast<u32x4*>(dst + 8 * b) = u32x4{o[0], o[1], o[2], o[3]};
-            if constexpr (DT == DT_BF16)
-                part += (pair_sum<DT>(xreg[b].x) + pair_sum<DT>(xreg[b].y)) +
-                        (pair_sum<DT>(xreg[b].z) + pair_sum<DT>(xreg[b].w));
+            part += (pair_sum<DT>(xreg[b].x) + pair_sum<DT>(xreg[b].y)) +
+                    (pair_sum<DT>(xreg[b].z) + pair_sum<DT>(xreg[b].w));
         }
-        if constexpr (DT == DT_BF16) {
-            part += __shfl_xor(part, 1, 64);
-            s_acc += part;
-            if ((step + 1) % steps_per_group == 0) {
-                if (shalf == 0) sg[(step / steps_per_group) & 1][srow] = s_acc;
-                s_acc = 0.0f;
-            }
+        part += __shfl_xor(part, 1, 64);
+        s_acc += part;
+        if ((step + 1) % steps_per_group == 0) {
+            // fp16 codes are in units of 2^-24; scale the sum the same way (exact)
+            const float sv = DT == DT_F16 ? s_acc * 5.9604644775390625e-8f : s_acc;
+            if (shalf == 0) sg[(step / steps_per_group) & 1][srow] = sv;
+            s_acc = 0.0f;
         }
     };
 
     u32x4 wreg[2];
     auto load_w = [&](int step) {
 #pragma unroll
-        for (int ns = 0; ns < 2; ++ns) {
-            wreg[ns] = wok[ns] ? *reinterpret_cast<const u32x4*>(qw + (size_t)wrow[ns] * KW +
-                                                                (size_t)step * (BK / 8) + 4 * h)
-                               : u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int ns = 0; ns < 2; ++ns)
+            wreg[ns] = *reinterpret_cast<const u32x4*>(qw + (size_t)wrow[ns] * KW +
+                                                       (size_t)step * (BK / 8) + 4 * h);
     };
 
     f32x16 acc[2][2], accg[2][2];
@@ -145,8 +140,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restr
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    float gs[2] = {0.0f, 0.0f}, gz[2] = {0.0f, 0.0f};
-    ZeroConst zk[2];
+    float gs[2] = {0.0f, 0.0f}, gc[2] = {0.0f, 0.0f};
 
     load_x(0);
     store_x(0, 0);
@@ -161,9 +155,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restr
         if (gfirst) {
 #pragma unroll
             for (int ns = 0; ns < 2; ++ns) {
-                gs[ns] = wok[ns] ? h2f(scales[(size_t)wrow[ns] * G + grp]) : 0.0f;
-                gz[ns] = wok[ns] ? (zeros ? h2f(zeros[(size_t)wrow[ns] * G + grp]) : 8.0f) : 0.0f;
-                if constexpr (DT == DT_F16) zk[ns] = make_zero_const_f16(gz[ns]);
+                const float sv = h2f(scales[(size_t)wrow[ns] * G + grp]);
+                const float zr = h2f(zsrc[(size_t)wrow[ns] * G + grp]);
+                const float zv = has_zeros ? zr : 8.0f;
+                gs[ns] = DT == DT_F16 ? sv * 16777216.0f : sv;     // fp16: fold 2^24 (exact)
+                gc[ns] = DT == DT_F16 ? zv : 128.0f + zv;
             }
         }
         // Dequantize this step's weights into B operands.
@@ -171,18 +167,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restr
 #pragma unroll
         for (int ns = 0; ns < 2; ++ns) {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                if constexpr (DT == DT_F16)
-                    unpack_f16(wreg[ns][kk], zk[ns], bop[ns][kk]);
-                else
-                    unpack_bf16(wreg[ns][kk], bop[ns][kk]);
-            }
+            for (int kk = 0; kk < 4; ++kk) unpack_byte<DT == DT_F16 ? 0u : 0x43u>(wreg[ns][kk], bop[ns][kk]);
         }
         // Prefetch the next step.
         if (step + 1 < nsteps) {
             load_x(step + 1);
             load_w(step + 1);
         }
+        __builtin_amdgcn_sched_barrier(0);
         // MFMAs.
         const uint16_t* xb = xs[buf];
 #pragma unroll
@@ -213,11 +205,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restr
                 for (int ns = 0; ns < 2; ++ns) {
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
-                        float v = accg[ms][ns][e];
-                        if constexpr (DT == DT_BF16) {
-                            const int r = wm * 64 + ms * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-                            v = fmaf(-(128.0f + gz[ns]), sg[grp & 1][r], v);
-                        }
+                        const int r = wm * 64 + ms * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+                        const float v = fmaf(-gc[ns], sg[grp & 1][r], accg[ms][ns][e]);
                         acc[ms][ns][e] = fmaf(gs[ns], v, acc[ms][ns][e]);
                     }
                 }
@@ -253,13 +242,14 @@ bool prefill_supports(const LinearArgs& a) {
 hipError_t launch_prefill(const LinearArgs& a, hipStream_t st) {
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     const int spg = a.g / BK;
+    const int hz = a.zeros ? 1 : 0;
     if (a.dtype == DT_F16)
         hipLaunchKernelGGL(prefill_kernel<DT_F16>, dim3(tiles), dim3(256), 0, st,
-                           static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros,
+                           static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, hz,
                            static_cast<uint16_t*>(a.Y), a.M, a.N, a.K, a.G, spg);
     else
         hipLaunchKernelGGL(prefill_kernel<DT_BF16>, dim3(tiles), dim3(256), 0, st,
-                           static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros,
+                           static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, hz,
                            static_cast<uint16_t*>(a.Y), a.M, a.N, a.K, a.G, spg);
     return hipGetLastError();
 }
