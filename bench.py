@@ -295,6 +295,27 @@ def run_extras(layers, copies, W4, synth, torch, np):
                           "paths": [W4.PATH_NAMES[W4.select_path(M, L.N, L.K, GROUP)] for L in layers]}
         log(f"  sweep M={M}: {sweep[f'M{M}']}")
     out["decode_sweep_fp16_g128"] = sweep
+    # each kernel path forced, per M (same layers, same rotation)
+    per_path = {}
+    for M in (1, 2, 4, 8, 16):
+        xs = {K: synth.activations_device(M, K, synth.FP16, 2100 + M) for K in (4096, 11008)}
+        outs = [torch.empty((M, L.N), dtype=torch.float16, device="cuda") for L in layers]
+        nbytes = sum(L.bytes for L in layers)
+        for path in (W4.PATH_GEMV, W4.PATH_SKINNY):
+            if path == W4.PATH_GEMV and M > 8:
+                continue
+
+            def step(i, path=path):
+                c = i % copies
+                for L, o in zip(layers, outs):
+                    qw, s, z = L.copies[c]
+                    W4.linear(xs[L.K], qw, s, z, GROUP, path=path, out=o)
+            for i in range(3):
+                step(i)
+            ms = time_loop(step, 50, torch)
+            per_path[f"M{M}_{W4.PATH_NAMES[path]}"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    log(f"  per-path GB/s: {per_path}")
+    out["decode_per_path_GBps"] = per_path
     # prefill M = 4096
     pre = {}
     for (K, N) in [(4096, 11008), (11008, 4096)]:

@@ -70,8 +70,8 @@ typedef enum {
 typedef enum {
     W4A16_PATH_AUTO = 0,    /* dispatcher chooses from (M, N, K, g)                 */
     W4A16_PATH_GEMV = 1,    /* weight-streaming dot2 kernel, any supported g, M<=8  */
-    W4A16_PATH_SKINNY = 2,  /* weight-streaming MFMA kernel, M <= 64, g % 128 == 0  */
-    W4A16_PATH_PREFILL = 3  /* LDS-tiled MFMA GEMM, g % 64 == 0, K % 64 == 0        */
+    W4A16_PATH_SKINNY = 2,  /* weight-streaming MFMA kernel, M <= 32, g % 128 == 0  */
+    W4A16_PATH_PREFILL = 3  /* LDS-tiled MFMA GEMM; bf16 needs g % 64 == 0, K % 64 == 0 */
 } w4a16_path;
 
 /*
@@ -105,8 +105,9 @@ int w4a16_quantize_pack(const float* W, int64_t N, int64_t K, int64_t group_size
  *   qweight  [N, K/8] int32, device, 16-byte aligned.
  *   scales   [N, K/g] fp16 bits, device, 2-byte aligned.
  *   zeros    [N, K/g] fp16 bits, device, 2-byte aligned, or NULL (all zero points 8).
- *            Zero points must be integers with -1024 <= z <= 1024 (the quantizer gives
- *            z in [0, 15] for every group whose range contains 0).
+ *            Zero points must be integers with -480 <= z <= 480 (the quantizer gives
+ *            z in [0, 15] for every group whose range contains 0; larger |z| only arise
+ *            for a group far narrower than its distance from 0).
  *   Y        out [M, N], same dtype as X, device, 2-byte aligned.
  */
 int w4a16_linear(const void* X, int dtype, int64_t M, int64_t N, int64_t K, int64_t group_size,

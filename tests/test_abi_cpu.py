@@ -75,7 +75,7 @@ def _lin(lib, X=A, dtype=0, M=1, N=64, K=128, g=128, qw=B, s=C, z=D, Y=A + 4096,
     (dict(s=C + 1), L.ERR_ALIGN),
     (dict(z=D + 1), L.ERR_ALIGN),
     (dict(Y=A + 4097), L.ERR_ALIGN),
-    (dict(K=96, g=96, path=L.PATH_PREFILL), L.ERR_PATH),   # K % 64 != 0
+    (dict(K=96, g=96, dtype=L.BF16, path=L.PATH_PREFILL), L.ERR_PATH),   # bf16: K % 64 != 0
     (dict(M=9, path=L.PATH_GEMV), L.ERR_PATH),             # GEMV handles M <= 8
     (dict(path=17), L.ERR_PATH),
 ])

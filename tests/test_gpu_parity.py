@@ -113,8 +113,13 @@ GEMV_CASES = [(1, 64, 256, 32), (2, 130, 512, 128), (3, 77, 1024, 1024), (4, 256
               (1, 300, 11008, 128), (5, 100, 2048, 64), (8, 64, 4096, 128), (1, 33, 28672, 128),
               (2, 50, 11008, 11008), (7, 16, 1024, 256), (1, 1, 32, 32),
               (1, 9477, 4096, 128), (2, 5000, 2048, 64), (4, 3000, 1024, 1024), (3, 2600, 6144, 128)]
+SKINNY_CASES = [(1, 64, 128, 128), (5, 100, 1024, 128), (16, 256, 4096, 128), (17, 77, 2048, 256),
+                (32, 300, 11008, 128), (31, 129, 1024, 1024), (8, 4096, 4096, 128), (2, 50, 11008, 11008),
+                (12, 1000, 28672, 128)]
 PREFILL_CASES = [(1, 64, 64, 64), (17, 200, 192, 64), (130, 129, 256, 128), (256, 384, 1024, 128),
                  (300, 256, 4096, 4096), (64, 128, 11008, 128), (129, 1, 128, 64)]
+# fp16 prefill also takes K % 64 == 32 and g == 32 (bf16 prefill needs multiples of 64)
+PREFILL_F16_CASES = [(40, 150, 96, 32), (257, 300, 160, 32), (70, 64, 96, 96), (513, 260, 2080, 32)]
 
 
 @pytest.mark.parametrize("dtype", [FP16, BF16])
@@ -125,13 +130,48 @@ def test_linear_gemv(M, N, K, g, dtype):
 
 
 @pytest.mark.parametrize("dtype", [FP16, BF16])
+@pytest.mark.parametrize("M,N,K,g", SKINNY_CASES)
+def test_linear_skinny(M, N, K, g, dtype):
+    Y, ref = _run_linear(M, N, K, g, ASYM, dtype, W4.PATH_SKINNY, seed=M * 71 + N + K)
+    assert_close(y_to_f64(Y), ref_to_f64(ref, dtype), f"skinny M={M} N={N} K={K} g={g}")
+
+
+@pytest.mark.parametrize("dtype", [FP16, BF16])
 @pytest.mark.parametrize("M,N,K,g", PREFILL_CASES)
 def test_linear_prefill(M, N, K, g, dtype):
     Y, ref = _run_linear(M, N, K, g, ASYM, dtype, W4.PATH_PREFILL, seed=M * 17 + N + K)
     assert_close(y_to_f64(Y), ref_to_f64(ref, dtype), f"prefill M={M} N={N} K={K} g={g}")
 
 
-@pytest.mark.parametrize("path", [W4.PATH_GEMV, W4.PATH_PREFILL])
+@pytest.mark.parametrize("M,N,K,g", PREFILL_F16_CASES)
+def test_linear_prefill_f16_k32(M, N, K, g):
+    Y, ref = _run_linear(M, N, K, g, ASYM, FP16, W4.PATH_PREFILL, seed=M * 19 + N + K)
+    assert_close(y_to_f64(Y), ref_to_f64(ref, FP16), f"prefill f16 M={M} N={N} K={K} g={g}")
+
+
+ALL_PATHS = [W4.PATH_GEMV, W4.PATH_SKINNY, W4.PATH_PREFILL]
+
+
+@pytest.mark.parametrize("path", ALL_PATHS)
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+def test_linear_offset_groups(path, dtype):
+    # groups that do not straddle zero: asymmetric zero points far outside 0..15
+    N, K, g = 192, 1024, 128
+    W = weights(N, K, 0.01, seed=51)
+    W[: N // 2] += 0.5
+    W[N // 2:] -= 0.5
+    codes, s, z = oracle.quantize_asym(W, g)
+    assert z.min() < -60 and z.max() > 60 and np.abs(z).max() <= 480
+    qw_np = oracle.pack(codes)
+    qw, st, zt = upload_packed(qw_np, s, z)
+    M = 4 if path == W4.PATH_GEMV else 24
+    X = activations(M, K, dtype, 52)
+    Y = W4.linear(x_to_torch(X, dtype), qw, st, zt, g, path=path)
+    ref = oracle.linear_ref(X, dtype, qw_np, s, z, g)
+    assert_close(y_to_f64(Y), ref_to_f64(ref, dtype), f"offset groups path={path}")
+
+
+@pytest.mark.parametrize("path", ALL_PATHS)
 @pytest.mark.parametrize("dtype", [FP16, BF16])
 def test_linear_symmetric_and_null_zeros(path, dtype):
     for zeros_none in (False, True):
@@ -139,13 +179,13 @@ def test_linear_symmetric_and_null_zeros(path, dtype):
         assert_close(y_to_f64(Y), ref_to_f64(ref, dtype), f"sym path={path} zeros_none={zeros_none}")
 
 
-@pytest.mark.parametrize("path", [W4.PATH_GEMV, W4.PATH_PREFILL])
+@pytest.mark.parametrize("path", ALL_PATHS)
 def test_linear_bf16_outlier_channels(path):
     Y, ref = _run_linear(4, 256, 8192, 128, ASYM, BF16, path, seed=9, x_outliers=True)
     assert_close(y_to_f64(Y), ref_to_f64(ref, BF16), f"bf16 outliers path={path}")
 
 
-@pytest.mark.parametrize("path", [W4.PATH_GEMV, W4.PATH_PREFILL])
+@pytest.mark.parametrize("path", ALL_PATHS)
 @pytest.mark.parametrize("dtype", [FP16, BF16])
 def test_one_hot_bit_exact(path, dtype):
     # one-hot rows select single dequantized weights: Y[m, n] = round(W_hat[n, k_m]) exactly

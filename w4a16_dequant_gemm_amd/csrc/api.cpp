@@ -81,7 +81,7 @@ int validate_linear(const void* X, int dtype, int64_t M, int64_t N, int64_t K, i
 // the tiled MFMA GEMM once the problem is compute-bound.
 int choose_path(const LinearArgs& a) {
     if (a.M <= 4 && w4a16::gemv_supports(a)) return W4A16_PATH_GEMV;
-    if (a.M <= 64 && w4a16::skinny_supports(a)) return W4A16_PATH_SKINNY;
+    if (a.M <= 32 && w4a16::skinny_supports(a)) return W4A16_PATH_SKINNY;
     if (w4a16::prefill_supports(a)) return W4A16_PATH_PREFILL;
     if (w4a16::gemv_supports(a)) return W4A16_PATH_GEMV;
     if (w4a16::skinny_supports(a)) return W4A16_PATH_SKINNY;

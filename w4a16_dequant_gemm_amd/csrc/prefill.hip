@@ -231,26 +231,178 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restr
     }
 }
 
+// ---------------------------------------------------------------------------------
+// fp16 kernel: dequantize once per block into LDS.
+//
+// Block tile 256 (M) x 128 (N), k-step 32, 256 threads = 4 waves in a 2 x 2 grid, wave
+// tile 128 x 64 = 4 x 2 MFMA 32x32x16 tiles.  Per k-step every thread
+//   - loads 64 bytes of one activation row (its 32 columns) and stores them to LDS
+//     unchanged (natural column order),
+//   - loads 8 bytes = 16 codes of one weight row and writes the dequantized fp16 weights
+//     s * (u - z) to LDS: the code pair (u, u') is built as the fp16 bits of
+//     1536 + (u - z) by one packed 16-bit integer add (exact while |u - z| < 512), then
+//     1536 is subtracted (exact) and the pair is multiplied by s (one rounding),
+// so every weight is dequantized exactly once per block -- the pages' "dequantize the
+// INT4 weight to FP16, then multiply" with the FP16 weight living only in LDS.  The
+// MFMAs read both operands from LDS in natural order; rows are padded by 16 bytes,
+// which makes the 32-lane column reads conflict-free.  LDS is double-buffered, one
+// barrier per k-step.
+constexpr int F_BM = 256, F_BN = 128, F_BK = 32;
+constexpr int F_LDA = F_BK + 8;      // halves per LDS row
+
+__global__ __launch_bounds__(256, 2) void prefill_f16_kernel(
+    const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int has_zeros,
+    uint16_t* __restrict__ Y, int M, int N, int K, int G, int gshift) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][F_BM * F_LDA];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][F_BN * F_LDA];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1;
+    const int wn = wave & 1;
+    const int l32 = lane & 31;
+    const int h = lane >> 5;
+    const int tiles_n = (N + F_BN - 1) / F_BN;
+    const int m0 = (blockIdx.x / tiles_n) * F_BM;
+    const int n0 = (blockIdx.x % tiles_n) * F_BN;
+    const int KW = K >> 3;
+    const int nsteps = K / F_BK;
+
+    // Staging roles.  Activations: thread t owns row t of the tile.  Weights: thread t
+    // owns row t/2, columns 16*(t%2) .. +15 of the step (two words).  Rows past M / N are
+    // clamped (loads stay in bounds; their results are never stored).
+    const uint16_t* xrow = X + (size_t)min(m0 + tid, M - 1) * K;
+    const int wr = tid >> 1;
+    const int wh = tid & 1;
+    const int wrow = min(n0 + wr, N - 1);
+    const uint32_t* wsrc = qw + (size_t)wrow * KW + 2 * wh;
+    const uint16_t* zsrc = has_zeros ? zeros : scales;    // NULL zeros: value replaced by 8
+
+    u32x4 xa[4];
+    uint32_t wq[2];
+    auto load_step = [&](int step) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            xa[b] = *reinterpret_cast<const u32x4*>(xrow + (size_t)step * F_BK + 8 * b);
+        const uint2 v = *reinterpret_cast<const uint2*>(wsrc + (size_t)step * (F_BK / 8));
+        wq[0] = v.x;
+        wq[1] = v.y;
+    };
+    // dequantization constants of the current group: (0x6600 - z) pair and s pair
+    uint32_t zbias = 0, spair = 0;
+    int cur_group = -1;
+    auto store_step = [&](int buf, int step) {
+        const int grp = group_of(step * F_BK, gshift);
+        if (grp != cur_group) {
+            cur_group = grp;
+            const uint16_t sb = scales[(size_t)wrow * G + grp];
+            const float z = has_zeros ? h2f(zsrc[(size_t)wrow * G + grp]) : 8.0f;
+            const uint32_t zb = (uint32_t)(0x6600 - (int)z) & 0xFFFFu;
+            zbias = zb | (zb << 16);
+            spair = (uint32_t)sb | ((uint32_t)sb << 16);
+        }
+        uint16_t* arow = &As[buf][tid * F_LDA];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) *reinterpret_cast<u32x4*>(arow + 8 * b) = xa[b];
+        const f16x2 bias = {(_Float16)1536.0f, (_Float16)1536.0f};
+        const f16x2 sv = __builtin_bit_cast(f16x2, spair);
+        uint32_t d[8];
+#pragma unroll
+        for (int wi = 0; wi < 2; ++wi) {
+            const uint32_t w = wq[wi];
+            const uint32_t t0 = w & 0x0F0F0F0Fu;          // u0 u2 u4 u6 (as bytes)
+            const uint32_t t1 = (w >> 4) & 0x0F0F0F0Fu;   // u1 u3 u5 u7
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                // (u_{2p}, u_{2p+1}) as 16-bit integers, then the fp16 bits of 1536 + u - z
+                const uint32_t uu = perm(t1, t0, 0x0C040C00u + 0x00010001u * p);
+                const uint32_t biased = __builtin_bit_cast(uint32_t,
+                    __builtin_bit_cast(u16x2, uu) + __builtin_bit_cast(u16x2, zbias));
+                const f16x2 code = __builtin_bit_cast(f16x2, biased) - bias;    // exact
+                d[4 * wi + p] = __builtin_bit_cast(uint32_t, code * sv);        // one rounding
+            }
+        }
+        uint16_t* brow = &Bs[buf][wr * F_LDA + 16 * wh];
+        *reinterpret_cast<u32x4*>(brow) = u32x4{d[0], d[1], d[2], d[3]};
+        *reinterpret_cast<u32x4*>(brow + 8) = u32x4{d[4], d[5], d[6], d[7]};
+    };
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    load_step(0);
+    store_step(0, 0);
+    __syncthreads();
+    for (int step = 0; step < nsteps; ++step) {
+        const int buf = step & 1;
+        if (step + 1 < nsteps) load_step(step + 1);
+        const uint16_t* A = As[buf];
+        const uint16_t* B = Bs[buf];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            uint32_t bf[2][4];
+#pragma unroll
+            for (int ns = 0; ns < 2; ++ns) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(
+                    B + (wn * 64 + ns * 32 + l32) * F_LDA + 16 * ks + 8 * h);
+                bf[ns][0] = v.x; bf[ns][1] = v.y; bf[ns][2] = v.z; bf[ns][3] = v.w;
+            }
+#pragma unroll
+            for (int ms = 0; ms < 4; ++ms) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(
+                    A + (wm * 128 + ms * 32 + l32) * F_LDA + 16 * ks + 8 * h);
+                const uint32_t af[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int ns = 0; ns < 2; ++ns) acc[ms][ns] = Mfma<DT_F16>::run(af, bf[ns], acc[ms][ns]);
+            }
+        }
+        if (step + 1 < nsteps) store_step(buf ^ 1, step + 1);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms) {
+#pragma unroll
+        for (int ns = 0; ns < 2; ++ns) {
+            const int n = n0 + wn * 64 + ns * 32 + l32;
+            if (n >= N) continue;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int m = m0 + wm * 128 + ms * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+                if (m < M) Y[(size_t)m * N + n] = f2h_bits(acc[ms][ns][e]);
+            }
+        }
+    }
+}
+
 }  // namespace
 
 bool prefill_supports(const LinearArgs& a) {
-    if (a.K % BK != 0) return false;
-    if (a.g % BK != 0) return false;
-    return true;
+    if (a.dtype == DT_F16) return a.K % F_BK == 0 && a.g % F_BK == 0;   // any supported g
+    return a.K % BK == 0 && a.g % BK == 0;
 }
 
 hipError_t launch_prefill(const LinearArgs& a, hipStream_t st) {
+    const int hz = a.zeros ? 1 : 0;
+    if (a.dtype == DT_F16) {
+        const int tiles = ((a.M + F_BM - 1) / F_BM) * ((a.N + F_BN - 1) / F_BN);
+        hipLaunchKernelGGL(prefill_f16_kernel, dim3(tiles), dim3(256), 0, st,
+                           static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, hz,
+                           static_cast<uint16_t*>(a.Y), a.M, a.N, a.K, a.G, a.gshift);
+        return hipGetLastError();
+    }
     const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     const int spg = a.g / BK;
-    const int hz = a.zeros ? 1 : 0;
-    if (a.dtype == DT_F16)
-        hipLaunchKernelGGL(prefill_kernel<DT_F16>, dim3(tiles), dim3(256), 0, st,
-                           static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, hz,
-                           static_cast<uint16_t*>(a.Y), a.M, a.N, a.K, a.G, spg);
-    else
-        hipLaunchKernelGGL(prefill_kernel<DT_BF16>, dim3(tiles), dim3(256), 0, st,
-                           static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, hz,
-                           static_cast<uint16_t*>(a.Y), a.M, a.N, a.K, a.G, spg);
+    hipLaunchKernelGGL(prefill_kernel<DT_BF16>, dim3(tiles), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, hz,
+                       static_cast<uint16_t*>(a.Y), a.M, a.N, a.K, a.G, spg);
     return hipGetLastError();
 }
 
