@@ -115,7 +115,11 @@ GEMV_CASES = [(1, 64, 256, 32), (2, 130, 512, 128), (3, 77, 1024, 1024), (4, 256
               (1, 9477, 4096, 128), (2, 5000, 2048, 64), (4, 3000, 1024, 1024), (3, 2600, 6144, 128)]
 SKINNY_CASES = [(1, 64, 128, 128), (5, 100, 1024, 128), (16, 256, 4096, 128), (17, 77, 2048, 256),
                 (32, 300, 11008, 128), (31, 129, 1024, 1024), (8, 4096, 4096, 128), (2, 50, 11008, 11008),
-                (12, 1000, 28672, 128)]
+                (12, 1000, 28672, 128),
+                # M <= 4: the k-split decode kernel (1..4 tiles per block, short and long K)
+                (1, 4096, 4096, 128), (2, 11008, 4096, 128), (3, 4096, 11008, 128),
+                (4, 1000, 2048, 256), (1, 16000, 1024, 128), (1, 300, 28672, 128),
+                (4, 700, 8192, 8192), (1, 50, 11008, 11008), (3, 17, 128, 128), (2, 5000, 1408, 128)]
 PREFILL_CASES = [(1, 64, 64, 64), (17, 200, 192, 64), (130, 129, 256, 128), (256, 384, 1024, 128),
                  (300, 256, 4096, 4096), (64, 128, 11008, 128), (129, 1, 128, 64)]
 # fp16 prefill also takes K % 64 == 32 and g == 32 (bf16 prefill needs multiples of 64)
@@ -181,8 +185,9 @@ def test_linear_symmetric_and_null_zeros(path, dtype):
 
 @pytest.mark.parametrize("path", ALL_PATHS)
 def test_linear_bf16_outlier_channels(path):
-    Y, ref = _run_linear(4, 256, 8192, 128, ASYM, BF16, path, seed=9, x_outliers=True)
-    assert_close(y_to_f64(Y), ref_to_f64(ref, BF16), f"bf16 outliers path={path}")
+    for K in (8192, 4096):
+        Y, ref = _run_linear(4, 256, K, 128, ASYM, BF16, path, seed=9, x_outliers=True)
+        assert_close(y_to_f64(Y), ref_to_f64(ref, BF16), f"bf16 outliers path={path} K={K}")
 
 
 @pytest.mark.parametrize("path", ALL_PATHS)
@@ -200,10 +205,12 @@ def test_one_hot_bit_exact(path, dtype):
     X = X64.astype(np.float16) if dtype == FP16 else oracle.round_to_bf16_bits(X64)
     qw, st, zt = upload_packed(qw_np, s, z)
     ref = oracle.linear_ref(X, dtype, qw_np, s, z, g)
-    rows = 4 if path == W4.PATH_GEMV else len(ks)      # the GEMV kernel serves M <= 8
-    for m0 in range(0, len(ks), rows):
-        Y = W4.linear(x_to_torch(X[m0:m0 + rows], dtype), qw, st, zt, g, path=path)
-        np.testing.assert_array_equal(y_bits(Y), ref_bits(ref[m0:m0 + rows], dtype))
+    # GEMV serves M <= 8; the MFMA decode kernel takes M <= 4 and the skinny kernel larger M
+    sizes = {W4.PATH_GEMV: [4], W4.PATH_SKINNY: [4, len(ks)]}.get(path, [len(ks)])
+    for rows in sizes:
+        for m0 in range(0, len(ks), rows):
+            Y = W4.linear(x_to_torch(X[m0:m0 + rows], dtype), qw, st, zt, g, path=path)
+            np.testing.assert_array_equal(y_bits(Y), ref_bits(ref[m0:m0 + rows], dtype))
 
 
 def test_auto_dispatch_matches_forced_paths():

@@ -216,7 +216,6 @@ __host__ __device__ constexpr int lds_bytes(int M, int CPL) { return (M * CPL * 
 template <int DT, int M, int CPL, int RB>
 struct RowBatch {
     u32x4 w[RB][CPL];
-    uint16_t s[RB][CPL], z[RB][CPL];
 };
 
 // Buffer loads: the row offset is wave-uniform (an SGPR soffset) and the lane's chunk
@@ -226,33 +225,29 @@ struct RowBatch {
 // unconditionally.
 struct StreamSrc {
     __amdgpu_buffer_rsrc_t w, s, z, none;
-    int row_bytes_w, row_bytes_sz;
+    int row_bytes_w;
 };
 
 template <int DT, int M, int CPL, int RB>
 __device__ __forceinline__ void load_batch(RowBatch<DT, M, CPL, RB>& bt, const StreamSrc& src, int row,
-                                           bool live, int N, const int vw[CPL], const int vsz[CPL]) {
-    const __amdgpu_buffer_rsrc_t rw = live ? src.w : src.none;   // wave-uniform selects
-    const __amdgpu_buffer_rsrc_t rs = live ? src.s : src.none;
-    const __amdgpu_buffer_rsrc_t rz = live ? src.z : src.none;
+                                           bool live, int N, const int vw[CPL]) {
+    const __amdgpu_buffer_rsrc_t rw = live ? src.w : src.none;   // wave-uniform select
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-        const int n = min(row + r, N - 1);          // wave-uniform
-        const int ow = n * src.row_bytes_w;
-        const int osz = n * src.row_bytes_sz;
+    for (int i = 0; i < CPL; ++i) {
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            bt.w[r][i] = __builtin_amdgcn_raw_buffer_load_b128(rw, vw[i], ow, 2 /* nt */);
-            bt.s[r][i] = __builtin_amdgcn_raw_buffer_load_b16(rs, vsz[i], osz, 0);
-            bt.z[r][i] = __builtin_amdgcn_raw_buffer_load_b16(rz, vsz[i], osz, 0);
+        for (int r = 0; r < RB; ++r) {
+            const int n = min(row + r, N - 1);          // wave-uniform
+            bt.w[r][i] = __builtin_amdgcn_raw_buffer_load_b128(rw, vw[i], n * src.row_bytes_w, 2 /* nt */);
         }
     }
 }
 
+// szl: the block's (scale, zero point) fp16 pairs, one 32-bit word per (row, group),
+// rows relative to the block; szrow = LDS word index of the batch's first row.
 template <int DT, int M, int CPL, int RB>
 __device__ __forceinline__ void compute_batch(const RowBatch<DT, M, CPL, RB>& bt, const uint32_t* xp,
-                                              const float* xsum, int lane, int has_zeros,
-                                              float acc[RB][M]) {
+                                              const float* xsum, const uint32_t* szl, int szrow, int G,
+                                              const int lgrp[CPL], int lane, float acc[RB][M]) {
     constexpr int CH = CPL * 64;
 #pragma unroll
     for (int r = 0; r < RB; ++r)
@@ -279,8 +274,9 @@ __device__ __forceinline__ void compute_batch(const RowBatch<DT, M, CPL, RB>& bt
         }
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-            const float s = h2f(bt.s[r][i]);
-            const float z = has_zeros ? h2f(bt.z[r][i]) : 8.0f;
+            const uint32_t sz = szl[szrow + r * G + lgrp[i]];
+            const float s = h2f((uint16_t)(sz & 0xFFFFu));
+            const float z = h2f((uint16_t)(sz >> 16));
             if constexpr (DT == DT_F16) {
                 float pa[M], pb[M];
 #pragma unroll
@@ -344,7 +340,11 @@ __device__ __forceinline__ void store_batch(const float acc[RB][M], int row, int
         }
 }
 
-template <int DT, int M, int CPL, int RB, int W>
+// Byte offset of the (scale, zero point) words in the stream kernel's LDS.
+__host__ __device__ constexpr int sz_lds_offset(int M, int CPL) { return (lds_bytes(M, CPL) + 15) & ~15; }
+constexpr int kSzPiecesPerThread = 2;     // 16-byte pieces of scales (and of zeros) per thread
+
+template <int DT, int M, int CPL, int RB, int W, int NB>
 __global__ __launch_bounds__(64 * W) void gemv_stream_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int has_zeros,
@@ -354,8 +354,10 @@ __global__ __launch_bounds__(64 * W) void gemv_stream_kernel(
     constexpr int NT = 64 * W;
     constexpr int JOBS = M * CH * 4;                   // 8-column staging jobs
     constexpr int JPT = (JOBS + NT - 1) / NT;
+    constexpr int JSZ = kSzPiecesPerThread;
     uint32_t* xp = lds;                  // [M][4 pieces][CH] x 16 B pairs, then one spare slot
     float* xsum = reinterpret_cast<float*>(lds + (M * CH + 1) * 16);   // [M*CH + 1]
+    uint32_t* szs = lds + sz_lds_offset(M, CPL) / 4;   // staged (scale | zero << 16) words
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -366,26 +368,40 @@ __global__ __launch_bounds__(64 * W) void gemv_stream_kernel(
     const int first = row_begin + wave * RB;
     const int nbatch = first < row_end ? (row_end - first + W * RB - 1) / (W * RB) : 0;
 
+    // The block's scales (and zeros) are one contiguous run of (row_end - row_begin) * G
+    // halves; it is staged in 16-byte pieces from the 16-byte boundary at or below its
+    // start.  Pieces that lie wholly inside the arrays are loaded with 16-byte loads; the
+    // last (N * G) % 8 halves of the arrays, if any, with 2-byte loads.
+    const int total = N * G;
+    const int full_end = total & ~7;
     StreamSrc src;
     src.w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(qw), 0, 0x7FFFFFFF, 0x00020000);
-    src.s = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(scales), 0, 0x7FFFFFFF, 0x00020000);
     // NULL zeros: read the scales (valid memory); the value is replaced by 8
-    src.z = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(has_zeros ? zeros : scales), 0,
-                                              0x7FFFFFFF, 0x00020000);
+    const uint16_t* zsrc = has_zeros ? zeros : scales;
+    src.s = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(scales), 0, full_end * 2, 0x00020000);
+    src.z = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(zsrc), 0, full_end * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t s_all =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(scales), 0, total * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t z_all =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(zsrc), 0, total * 2, 0x00020000);
     src.none = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(qw), 0, 0, 0x00020000);
     src.row_bytes_w = KW * 4;
-    src.row_bytes_sz = G * 2;
-    int vw[CPL], vsz[CPL];
+    int vw[CPL], lgrp[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int c = lane + 64 * i;
         const int cc = c < C ? c : 0;     // chunks past the row end re-read chunk 0 (zero activations)
         vw[i] = cc * 16;
-        vsz[i] = group_of(cc << 5, gshift) * 2;
+        lgrp[i] = group_of(cc << 5, gshift);
     }
+    const int sz_first = row_begin * G;
+    const int sz_al = sz_first & ~7;
+    const int sz_pieces = ((row_end - row_begin) * G + (sz_first - sz_al) + 7) >> 3;
+    const int szrow0 = sz_first - sz_al;               // LDS word of (row_begin, group 0)
 
     // 1. Issue order = need order (vmcnt waits are in issue order): activation staging
-    //    loads, then the first two weight batches.  All loads unconditional.
+    //    loads, scale / zero staging loads, then the first weight batches.  All loads
+    //    unconditional.
     u32x4 xv[JPT];
 #pragma unroll
     for (int j = 0; j < JPT; ++j) {
@@ -395,9 +411,20 @@ __global__ __launch_bounds__(64 * W) void gemv_stream_kernel(
         const int c = e >> 2;
         xv[j] = reinterpret_cast<const u32x4*>(X + (size_t)m * K + ((size_t)(c < C ? c : 0) << 5))[e & 3];
     }
-    RowBatch<DT, M, CPL, RB> buf0, buf1;
-    load_batch<DT, M, CPL, RB>(buf0, src, first, nbatch > 0, N, vw, vsz);
-    load_batch<DT, M, CPL, RB>(buf1, src, first + W * RB, nbatch > 1, N, vw, vsz);
+    u32x4 sv[JSZ], zv[JSZ];
+#pragma unroll
+    for (int j = 0; j < JSZ; ++j) {
+        const int off = (sz_al + 8 * min(tid + NT * j, sz_pieces - 1)) * 2;
+        sv[j] = __builtin_amdgcn_raw_buffer_load_b128(src.s, off, 0, 0);
+        zv[j] = __builtin_amdgcn_raw_buffer_load_b128(src.z, off, 0, 0);
+    }
+    const int tail = min(full_end + (tid & 7), total - 1);
+    const uint16_t st = __builtin_amdgcn_raw_buffer_load_b16(s_all, tail * 2, 0, 0);
+    const uint16_t zt = __builtin_amdgcn_raw_buffer_load_b16(z_all, tail * 2, 0, 0);
+    RowBatch<DT, M, CPL, RB> buf[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+        load_batch<DT, M, CPL, RB>(buf[i], src, first + i * W * RB, nbatch > i, N, vw);
     __builtin_amdgcn_sched_barrier(0);
 
     // 2. Stage activations: permute each 8-column block, chunk sums by a quad reduction
@@ -431,20 +458,55 @@ __global__ __launch_bounds__(64 * W) void gemv_stream_kernel(
         if ((job0 & 3) == 0)
             xsum[slot] = ok ? (DT == DT_F16 ? sum * 5.9604644775390625e-8f : sum) : 0.0f;
     }
+    //    Scales and zero points: one (s | z << 16) word per (row, group); NULL zeros
+    //    become 8.0 (0x4800).
+#pragma unroll
+    for (int j = 0; j < JSZ; ++j) {
+        const int p = tid + NT * j;
+        const u32x4 sw = sv[j];
+        const u32x4 zw = has_zeros ? zv[j] : u32x4{0x48004800u, 0x48004800u, 0x48004800u, 0x48004800u};
+        if (p < sz_pieces && sz_al + 8 * p + 8 <= total) {
+            u32x4* dst = reinterpret_cast<u32x4*>(szs + 8 * p);
+            dst[0] = u32x4{perm(zw.x, sw.x, 0x05040100u), perm(zw.x, sw.x, 0x07060302u),
+                           perm(zw.y, sw.y, 0x05040100u), perm(zw.y, sw.y, 0x07060302u)};
+            dst[1] = u32x4{perm(zw.z, sw.z, 0x05040100u), perm(zw.z, sw.z, 0x07060302u),
+                           perm(zw.w, sw.w, 0x05040100u), perm(zw.w, sw.w, 0x07060302u)};
+        }
+    }
+    {
+        const int h = full_end + tid;            // tail half of this thread (tid < 8)
+        if (tid < 8 && h < total && h >= sz_al && h < sz_al + 8 * sz_pieces)
+            szs[h - sz_al] = (uint32_t)st | ((uint32_t)(has_zeros ? zt : (uint16_t)0x4800) << 16);
+    }
     __syncthreads();
 
-    // 3. Row batches, two in flight.  Prefetches and computes are unconditional (a batch
-    //    past the end loads zeros through `none` and stores nothing): a conditional
-    //    prefetch would turn each buffer into a merge of old and new values and the
-    //    compiler would shuffle registers, waiting on every load to do so.
+    // 3. Row batches, NB in flight.  Prefetches are unconditional (a batch past the end
+    //    loads zeros through `none`): a conditional prefetch would turn each buffer into a
+    //    merge of old and new values and the compiler would shuffle registers, waiting on
+    //    every load to do so.  The main loop runs while another round follows; the last
+    //    round (the tail) only computes what is in flight, so a wave issues at most NB - 1
+    //    empty batches.
     float acc[RB][M];
-    for (int b = 0; b < nbatch; b += 2) {
-        compute_batch<DT, M, CPL, RB>(buf0, xp, xsum, lane, has_zeros, acc);
-        load_batch<DT, M, CPL, RB>(buf0, src, first + (b + 2) * W * RB, b + 2 < nbatch, N, vw, vsz);
-        store_batch<DT, M, RB>(acc, first + b * W * RB, row_end, N, lane, Y);
-        compute_batch<DT, M, CPL, RB>(buf1, xp, xsum, lane, has_zeros, acc);
-        load_batch<DT, M, CPL, RB>(buf1, src, first + (b + 3) * W * RB, b + 3 < nbatch, N, vw, vsz);
-        store_batch<DT, M, RB>(acc, first + (b + 1) * W * RB, row_end, N, lane, Y);
+    int b = 0;
+    for (; b + NB < nbatch; b += NB) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int row = first + (b + i) * W * RB;
+            compute_batch<DT, M, CPL, RB>(buf[i], xp, xsum, szs, szrow0 + (row - row_begin) * G, G, lgrp,
+                                          lane, acc);
+            load_batch<DT, M, CPL, RB>(buf[i], src, first + (b + i + NB) * W * RB, b + i + NB < nbatch,
+                                       N, vw);
+            store_batch<DT, M, RB>(acc, row, row_end, N, lane, Y);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        if (b + i < nbatch) {
+            const int row = first + (b + i) * W * RB;
+            compute_batch<DT, M, CPL, RB>(buf[i], xp, xsum, szs, szrow0 + (row - row_begin) * G, G, lgrp,
+                                          lane, acc);
+            store_batch<DT, M, RB>(acc, row, row_end, N, lane, Y);
+        }
     }
 }
 
@@ -548,31 +610,48 @@ struct LdsCfg {
     int cpl = 0;
     int blocks = 0;
     int rows_per_block = 0;
+    int lds = 0;               // dynamic LDS bytes
 };
 
-// One block per CU (256) when N allows, each owning ceil(N / 256) rows.
-LdsCfg pick_lds(int M, int N, int K) {
+// One block per CU (256) when N allows, each owning ceil(N / 256) rows.  The block's
+// activations, chunk sums and (scale, zero) words must fit the LDS budget.
+LdsCfg pick_lds(int M, int N, int K, int G) {
     LdsCfg c;
     if (M < 1 || M > 4) return c;
     const int cpl = (K / 32 + 63) / 64;
-    if (cpl > lds_max_cpl(M) || lds_bytes(M, cpl) > kLdsBudget) return c;
+    if (cpl > lds_max_cpl(M)) return c;
     // 32-bit buffer offsets: the packed weights must stay below 2 GiB
     if ((long long)N * (K / 2) >= (1LL << 31)) return c;
-    c.cpl = cpl;
     const int want = 256;
-    c.rows_per_block = (N + want - 1) / want;
-    c.blocks = (N + c.rows_per_block - 1) / c.rows_per_block;
+    const int rpb = (N + want - 1) / want;
+    const long long pieces = ((long long)rpb * G + 7) / 8 + 1;      // 16-byte staging pieces
+    if (pieces > (long long)kSzPiecesPerThread * 64 * kStreamWaves) return c;
+    const long long lds = sz_lds_offset(M, cpl) + 32 * pieces;
+    if (lds > kLdsBudget) return c;
+    c.cpl = cpl;
+    c.rows_per_block = rpb;
+    c.blocks = (N + rpb - 1) / rpb;
+    c.lds = (int)lds;
     return c;
+}
+
+// Two rows per wave or fewer (and registers for them): one batch of two rows, nothing to
+// prefetch.  Otherwise batches of lds_rb rows, two in flight.
+template <int DT, int M, int CPL, int RB, int NB>
+hipError_t run_lds4(const LinearArgs& a, const LdsCfg& c, hipStream_t st) {
+    hipLaunchKernelGGL((gemv_stream_kernel<DT, M, CPL, RB, kStreamWaves, NB>), dim3(c.blocks),
+                       dim3(64 * kStreamWaves), c.lds, st,
+                       static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, a.zeros ? 1 : 0,
+                       static_cast<uint16_t*>(a.Y), a.N, a.K, a.G, a.gshift, c.rows_per_block);
+    return hipGetLastError();
 }
 
 template <int DT, int M, int CPL>
 hipError_t run_lds3(const LinearArgs& a, const LdsCfg& c, hipStream_t st) {
-    constexpr int RB = lds_rb(M, CPL);
-    hipLaunchKernelGGL((gemv_stream_kernel<DT, M, CPL, RB, kStreamWaves>), dim3(c.blocks),
-                       dim3(64 * kStreamWaves), lds_bytes(M, CPL), st,
-                       static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, a.zeros ? 1 : 0,
-                       static_cast<uint16_t*>(a.Y), a.N, a.K, a.G, a.gshift, c.rows_per_block);
-    return hipGetLastError();
+    if constexpr (M * CPL <= 6) {       // register budget of a two-row batch
+        if (c.rows_per_block <= 2 * kStreamWaves) return run_lds4<DT, M, CPL, 2, 1>(a, c, st);
+    }
+    return run_lds4<DT, M, CPL, lds_rb(M, CPL), 2>(a, c, st);
 }
 
 template <int DT, int M, int CPL>
@@ -600,11 +679,11 @@ hipError_t run_lds(const LinearArgs& a, const LdsCfg& c, hipStream_t st) {
 
 bool gemv_supports(const LinearArgs& a) {
     if (a.M < 1 || a.M > kMaxM) return false;
-    return pick_lds(a.M, a.N, a.K).cpl > 0 || pick(a.M, a.N, a.K).nt > 0;
+    return pick_lds(a.M, a.N, a.K, a.G).cpl > 0 || pick(a.M, a.N, a.K).nt > 0;
 }
 
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t st) {
-    const LdsCfg lc = pick_lds(a.M, a.N, a.K);
+    const LdsCfg lc = pick_lds(a.M, a.N, a.K, a.G);
     if (lc.cpl > 0)
         return a.dtype == DT_F16 ? run_lds<DT_F16>(a, lc, st) : run_lds<DT_BF16>(a, lc, st);
     const GemvCfg c = pick(a.M, a.N, a.K);

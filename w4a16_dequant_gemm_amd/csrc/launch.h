@@ -23,6 +23,7 @@ struct LinearArgs {
 // Host-side shape support checks of each kernel family (no GPU needed).
 bool gemv_supports(const LinearArgs& a);
 bool skinny_supports(const LinearArgs& a);
+bool decode_supports(const LinearArgs& a);
 bool prefill_supports(const LinearArgs& a);
 
 hipError_t launch_quantize_pack(const float* W, int N, int K, int g, int gshift, int scheme,
@@ -31,6 +32,7 @@ hipError_t launch_dequantize(const uint32_t* qw, const uint16_t* scales, const u
                              int N, int K, int g, int gshift, float* out, hipStream_t s);
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t s);
 hipError_t launch_skinny(const LinearArgs& a, hipStream_t s);
+hipError_t launch_decode(const LinearArgs& a, hipStream_t s);
 hipError_t launch_prefill(const LinearArgs& a, hipStream_t s);
 
 }  // namespace w4a16

@@ -279,6 +279,7 @@ bool skinny_supports(const LinearArgs& a) {
 }
 
 hipError_t launch_skinny(const LinearArgs& a, hipStream_t st) {
+    if (decode_supports(a)) return launch_decode(a, st);     // 1 <= M <= 4
     const SkinnyCfg c = pick_skinny(a);
     return a.dtype == DT_F16 ? run_dt<DT_F16>(a, c, st) : run_dt<DT_BF16>(a, c, st);
 }
