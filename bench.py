@@ -35,8 +35,44 @@ SHAPES = [(4096, 4096), (4096, 11008), (11008, 4096)]      # (K, N)
 GROUP = 128
 
 
+# Kernel instantiation serving each layer at M = 1 (fp16, g = 128), as rocprofv3 names it.
+KERNEL_NAMES = {(4096, 4096): "gemv_stream_kernel<0, 1, 2, 2, 8, 1>",
+                (4096, 11008): "gemv_stream_kernel<0, 1, 2, 2, 8, 2>",
+                (11008, 4096): "gemv_stream_kernel<0, 1, 6, 2, 8, 1>"}
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = [os.path.join(ROOT, "w4a16_dequant_gemm_amd", "csrc", f)
+                  for f in ("gemv.hip", "common.h")]
+COPY_MIB = 256          # calibration copy: reads and writes COPY_MIB MiB
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_file(K: int, N: int) -> str:
+    return os.path.join(PROFILES, f"traffic_gemv_stream_m1_k{K}_n{N}.json")
+
+
+def traffic_record(K: int, N: int):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    current kernel source (else None)."""
+    path = traffic_file(K, N)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256") != source_hash():
+        return None
+    return {"bytes_per_launch": rec["traffic_bytes_per_launch"], "source": os.path.relpath(path, ROOT)}
 
 
 def weight_bytes(N: int, K: int, g: int) -> int:
@@ -54,25 +90,6 @@ class Layer:
         self.copies = [(qw, s, z)] + [(qw.clone(), s.clone(), z.clone()) for _ in range(copies - 1)]
         self.W = W      # kept until parity is checked
         self.bytes = weight_bytes(N, K, g)
-
-
-def parity_check(layer, X_host, X_dev, W4, oracle, torch, np, n_rows=32):
-    """Sampled rows: packing bit-exact and Y within tolerance of the oracle."""
-    rng = np.random.default_rng(layer.N + layer.K)
-    ns = np.unique(np.concatenate([[0, layer.N - 1], rng.choice(layer.N, n_rows, replace=False)]))
-    Wn = layer.W[torch.from_numpy(ns).cuda()].cpu().numpy()
-    codes, s_ref, z_ref = oracle.quantize_asym(Wn, layer.g)
-    qw, s, z = layer.copies[-1]
-    idx = torch.from_numpy(ns).cuda()
-    ok = np.array_equal(qw[idx].cpu().numpy(), oracle.pack(codes))
-    ok &= np.array_equal(s[idx].cpu().numpy().view(np.uint16), s_ref.view(np.uint16))
-    ok &= np.array_equal(z[idx].cpu().numpy().view(np.uint16), z_ref.view(np.uint16))
-    Y = W4.linear(X_dev, qw, s, z, layer.g)
-    ref = oracle.linear_ref(X_host, 0, oracle.pack(codes), s_ref, z_ref, layer.g).astype(np.float64)
-    y = Y[:, idx].float().cpu().numpy().astype(np.float64)
-    fro = float(np.linalg.norm(y - ref) / np.linalg.norm(ref))
-    mx = float(np.abs(y - ref).max() / np.abs(ref).max())
-    return bool(ok) and fro <= 1e-3 and mx <= 1e-2, fro
 
 
 def capture(fn, iters, torch):
@@ -113,28 +130,122 @@ def time_loop(fn, iters, torch, graph=True):
     return e0.elapsed_time(e1) / iters   # ms per iteration
 
 
-def cpu_baseline(layers_host, budget_s, np, oracle):
-    """The oracle's linear (fp64 dequantize + BLAS product) on the host cores."""
+def cpu_baseline(layers, w_host, xs_host, y_gpu, budget_s, np, torch):
+    """The oracle beside the GPU path, on the host cores: quantize each layer (checked
+    bit-exact against the GPU packing on sampled rows), then time the oracle's linear
+    (fp64 dequantize + BLAS product) on the same M = 1 workload and check the GPU
+    outputs of the timed step against its result."""
+    import oracle
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
+    host = []
+    packing_ok = True
+    for L, W in zip(layers, w_host):
+        codes, s, z = oracle.quantize_asym(W, GROUP)
+        qw = oracle.pack(codes)
+        rng = np.random.default_rng(L.N + L.K)
+        ns = np.unique(np.concatenate([[0, L.N - 1], rng.choice(L.N, 64, replace=False)]))
+        idx = torch.from_numpy(ns).cuda()
+        qg, sg, zg = L.copies[0]
+        packing_ok &= bool(np.array_equal(qg[idx].cpu().numpy(), qw[ns]))
+        packing_ok &= bool(np.array_equal(sg[idx].cpu().numpy().view(np.uint16), s[ns].view(np.uint16)))
+        packing_ok &= bool(np.array_equal(zg[idx].cpu().numpy().view(np.uint16), z[ns].view(np.uint16)))
+        host.append((qw, s, z, L.bytes))
     total_bytes = 0
+    refs = None
     t0 = time.perf_counter()
     steps = 0
     while True:
-        for (X, qw, s, z, g, nbytes) in layers_host:
-            oracle.linear_ref(X, 0, qw, s, z, g)
-            total_bytes += nbytes
+        ys = [oracle.linear_ref(X, 0, qw, s, z, GROUP) for X, (qw, s, z, _) in zip(xs_host, host)]
+        total_bytes += sum(h[3] for h in host)
+        refs = refs or ys
         steps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or steps >= 50:
             break
+    fro, mx = [], []
+    for y, r in zip(y_gpu, refs):
+        y = y.float().cpu().numpy().astype(np.float64)
+        r = r.astype(np.float64)
+        fro.append(float(np.linalg.norm(y - r) / np.linalg.norm(r)))
+        mx.append(float(np.abs(y - r).max() / np.abs(r).max()))
+    parity = {"packing_bit_exact_sampled_rows": packing_ok, "rel_fro": fro, "max_rel": mx,
+              "ok": packing_ok and max(fro) <= 1e-3 and max(mx) <= 1e-2}
     return {"value": total_bytes / el / 1e9, "unit": "GB/s", "cores": int(threads),
             "host_cpus": os.cpu_count(), "kind": "oracle",
             "sample": f"{steps} oracle step(s) of the same M=1 workload (3 layers, fp64 "
-                      f"dequantize + BLAS matmul), {el:.1f} s"}
+                      f"dequantize + BLAS matmul), {el:.1f} s",
+            "parity_vs_gpu": parity}
+
+
+def traffic_run(K: int, N: int, W4, synth, torch, np):
+    """Workload for the two counter passes: a plain elementwise copy (y = -x) of COPY_MIB
+    MiB (calibration: known bytes read and written) five times, then 20 launches of the
+    layer's kernel at M = 1 over rotating weight copies."""
+    nbytes = weight_bytes(N, K, GROUP)
+    copies = max(2, int(np.ceil(2**30 / nbytes)))
+    L = Layer(K, N, GROUP, copies, 1000 + 10 * 2 + SHAPES.index((K, N)), W4, synth, torch)
+    del L.W
+    X = synth.activations_device(1, K, synth.FP16, 1015)
+    Y = torch.empty((1, N), dtype=torch.float16, device="cuda")
+    src = torch.ones(COPY_MIB << 19, dtype=torch.float16, device="cuda")
+    dst = torch.empty_like(src)
+    for i in range(3):
+        W4.linear(X, *L.copies[i % copies], GROUP, out=Y)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        torch.neg(src, out=dst)          # one elementwise kernel: reads and writes COPY_MIB MiB
+    torch.cuda.synchronize()
+    for i in range(20):
+        W4.linear(X, *L.copies[(i + 3) % copies], GROUP, out=Y)
+    torch.cuda.synchronize()
+    log(f"traffic run done: K={K} N={N}, {copies} weight copies, copy {COPY_MIB} MiB x5")
+
+
+def _counter_means(run_dir: str, counter: str):
+    """Mean per-dispatch value of `counter` for each kernel name in a rocprofv3 csv run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    vals = {}
+    for r in csv.DictReader(open(files[0])):
+        if r.get("Counter_Name") != counter:
+            continue
+        vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return vals
+
+
+def traffic_parse(fetch_dir: str, write_dir: str, K: int, N: int, commands, out_path=None):
+    """Turn the FETCH_SIZE / WRITE_SIZE passes of traffic_run into HBM bytes per launch
+    of the layer's kernel, scaled by what the counters read for the known-size copy."""
+    kname = KERNEL_NAMES[(K, N)]
+    out = {"kernel": kname, "M": 1, "K": K, "N": N, "group_size": GROUP,
+           "source_sha256": source_hash(), "copy_bytes": COPY_MIB << 20,
+           "algorithmic_bytes_per_launch": weight_bytes(N, K, GROUP), "commands": commands}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals = _counter_means(d, counter)
+        kv = [v for name, vs in vals.items() if kname in name for v in vs]
+        cv = [v for name, vs in vals.items() if "neg_kernel" in name for v in vs]
+        if not kv or not cv:
+            raise SystemExit(f"{counter}: kernel or copy dispatches not found in {d}: {list(vals)}")
+        kv = kv[3:] if len(kv) > 6 else kv          # the first dispatches are warm-up
+        key = counter.split("_")[0].lower()
+        out[f"{key}_kib_per_launch"] = sum(kv) / len(kv)
+        out[f"copy_{key}_kib"] = sum(cv) / len(cv)
+        out[f"factor_{key}"] = out["copy_bytes"] / (out[f"copy_{key}_kib"] * 1024.0)
+    out["traffic_bytes_per_launch"] = round(out["fetch_kib_per_launch"] * 1024 * out["factor_fetch"] +
+                                            out["write_kib_per_launch"] * 1024 * out["factor_write"])
+    out["traffic_over_algorithmic"] = out["traffic_bytes_per_launch"] / out["algorithmic_bytes_per_launch"]
+    out_path = out_path or traffic_file(K, N)
+    os.makedirs(os.path.dirname(out_path), exist_ok=True)
+    with open(out_path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
 
 
 def main():
@@ -146,7 +257,18 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--traffic-run", nargs=2, type=int, metavar=("K", "N"),
+                    help="counter workload: calibration copy + the layer's kernel at M = 1")
+    ap.add_argument("--traffic-parse", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "K", "N"),
+                    help="write profiles/traffic_*.json from the two counter passes")
+    ap.add_argument("--traffic-commands", nargs="*", default=[],
+                    help="the profiler command lines, recorded in the traffic file")
+    ap.add_argument("--traffic-out", default=None, help="output path of --traffic-parse")
     args = ap.parse_args()
+    if args.traffic_parse:
+        f, w, K, N = args.traffic_parse
+        traffic_parse(f, w, int(K), int(N), args.traffic_commands, args.traffic_out)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the W4A16 layer is benchmarked on a single "
@@ -157,12 +279,14 @@ def main():
     import numpy as np
     import torch
 
-    import oracle
     import synth
     import w4a16_dequant_gemm_amd as W4
 
     W4.lib()
     torch.cuda.set_device(0)
+    if args.traffic_run:
+        traffic_run(args.traffic_run[0], args.traffic_run[1], W4, synth, torch, np)
+        return
     step_bytes = sum(weight_bytes(N, K, GROUP) for K, N in SHAPES)
     copies = max(2, int(np.ceil(args.rotate_gib * 2**30 / step_bytes)))
     log(f"setup: {len(SHAPES)} layers x {copies} copies ({copies * step_bytes / 2**30:.2f} GiB)")
@@ -176,20 +300,8 @@ def main():
         xs_host.append(xh)
         xs_dev.append(torch.from_numpy(xh).cuda())
 
-    # parity before timing
-    for L, xh, xd in zip(layers, xs_host, xs_dev):
-        ok, fro = parity_check(L, xh, xd, W4, oracle, torch, np)
-        log(f"parity K={L.K} N={L.N}: ok={ok} rel_fro={fro:.2e}")
-        if not ok:
-            print(json.dumps({"metric": METRIC, "error": f"parity failed K={L.K} N={L.N}"}))
-            sys.exit(1)
-
-    # CPU baseline inputs: host W for the three layers, quantized by the oracle
-    layers_host = []
-    if not args.no_cpu:
-        for L, xh in zip(layers, xs_host):
-            codes, s, z = oracle.quantize_asym(L.W.cpu().numpy(), GROUP)
-            layers_host.append((xh, oracle.pack(codes), s, z, GROUP, L.bytes))
+    # host copies of the weights for the oracle leg (the oracle runs after the timing)
+    w_host = [L.W.cpu().numpy() for L in layers] if not args.no_cpu else None
     for L in layers:
         del L.W
     torch.cuda.empty_cache()
@@ -237,17 +349,20 @@ def main():
         t = time_loop(one, max(args.steps, 200), torch)
         per_layer.append({"K": L.K, "N": L.N, "us": t * 1e3, "bytes": L.bytes,
                           "GBps": L.bytes / (t * 1e-3) / 1e9,
-                          "path": W4.PATH_NAMES[W4.select_path(1, L.N, L.K, GROUP)]})
+                          "path": W4.PATH_NAMES[W4.select_path(1, L.N, L.K, GROUP)],
+                          "kernel": KERNEL_NAMES.get((L.K, L.N), "?")})
         log(f"  layer K={L.K} N={L.N}: {t * 1e3:.2f} us/launch {per_layer[-1]['GBps']:.0f} GB/s")
-    # dominant kernel: the gemv instantiation with K = 4096 serves two of the three layers
-    dom = [p for p in per_layer if p["K"] == 4096]
-    dom_bytes = sum(p["bytes"] for p in dom) / len(dom)
-    dom_us = sum(p["us"] for p in dom) / len(dom)
-    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    # dominant kernel: the layer with the longest launches (each layer runs one kernel)
+    dom = max(per_layer, key=lambda p: p["us"])
+    achieved = dom["bytes"] / (dom["us"] * 1e-6) / 1e9
+    traffic = traffic_record(dom["K"], dom["N"])
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "gemv_kernel (K=4096 instantiation, M=1)",
-                "avg_launch_us": round(dom_us, 3), "bytes_per_launch": dom_bytes}
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic["bytes_per_launch"] if traffic else None,
+                "kernel": f"{dom['kernel']} (M=1, K={dom['K']}, N={dom['N']})",
+                "avg_launch_us": round(dom["us"], 3), "bytes_per_launch": dom["bytes"]}
+    if traffic:
+        roofline["traffic_source"] = traffic["source"]
 
     extras = {"per_layer_m1": per_layer}
     if not args.no_extras:
@@ -255,8 +370,13 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(layers_host, args.cpu_budget, np, oracle)
-        log(f"cpu oracle: {cpu['value']:.3f} GB/s on {cpu['cores']} threads")
+        cpu = cpu_baseline(layers, w_host, xs_host, last, args.cpu_budget, np, torch)
+        log(f"cpu oracle: {cpu['value']:.3f} GB/s on {cpu['cores']} threads; "
+            f"parity vs GPU: {cpu['parity_vs_gpu']}")
+        if not cpu["parity_vs_gpu"]["ok"]:
+            print(json.dumps({"metric": METRIC, "error": "GPU output differs from the oracle",
+                              "parity": cpu["parity_vs_gpu"]}))
+            sys.exit(1)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
