@@ -382,6 +382,210 @@ __global__ __launch_bounds__(256, 2) void prefill_f16_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------------
+// fp16 kernel, wide variant (K % 128 == 0): block tile 256 (M) x 256 (N), k-step 64,
+// 4 waves side by side along N, wave tile 256 x 64 = 8 x 2 MFMA 32x32x16 tiles.
+//   Activations: the block's 256 x 64 tile goes global -> LDS directly (16-byte buffer
+//     loads with the LDS destination: lane l of an instruction writes slot base + l), two
+//     buffers.  Row r is 8 slots of 16 bytes; column piece c of row r sits in slot
+//     c ^ ((r / 2) % 8), which keeps the 32-row fragment reads free of bank conflicts.
+//     Every wave reads all 256 rows; the LDS carries only activations.
+//   Weights: each wave dequantizes exactly the 64 weight rows it multiplies, in
+//     registers (none goes through LDS, none is dequantized twice): lane (n, h) loads the
+//     16 bytes holding columns 32 h .. 32 h + 31 of the step for each of its two rows, one
+//     step ahead, and turns word j into the fp16 B fragment of MFMA j with the 1536-bias
+//     construction (exact 1536 + u - z, exact subtraction, one rounding in the multiply
+//     by s).  MFMA j covers columns 8 j .. 8 j + 7 and 32 + 8 j .. + 7; the activation
+//     fragment of lane (m, h) reads the same columns.  The next step's dequantization is
+//     interleaved with this step's MFMAs.
+//   Block order: consecutive block indices run on different XCDs; blocks are renumbered
+//     so that each XCD works through consecutive tiles (a few 256-row activation panels,
+//     held in that XCD's L2).
+constexpr int W_BM = 256, W_BN = 256, W_BK = 64;     // K % 128 == 0: steps in pairs
+
+template <bool HZ>
+__global__ __launch_bounds__(256, 1) void prefill_f16_wide_kernel(
+    const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros,
+    uint16_t* __restrict__ Y, int M, int N, int K, int G, int gshift) {
+    __shared__ __attribute__((aligned(16))) u32x4 As[2][W_BM * 8];     // 2 x 32 KB
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l32 = lane & 31;
+    const int h = lane >> 5;
+    const int tiles_n = (N + W_BN - 1) / W_BN;
+    const int tiles = ((M + W_BM - 1) / W_BM) * tiles_n;
+    // XCD-aware renumbering: hardware block b runs on XCD b % 8; the blocks of XCD x take
+    // tiles x * per_xcd + rank (the grid is padded to 8 * per_xcd)
+    const int per_xcd = (tiles + 7) / 8;
+    const int tile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (tile >= tiles) return;
+    const int m0 = (tile / tiles_n) * W_BM;
+    const int n0 = (tile % tiles_n) * W_BN;
+    const int nsteps = K / W_BK;
+
+    // Buffer loads: per-lane 32-bit offsets fixed for the whole K loop, the step's offset
+    // as the wave-uniform soffset.  Rows past M / N are clamped (loaded, never stored).
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X), 0, 0x7FFFFFFF, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(qw), 0, 0x7FFFFFFF, 0x00020000);
+    const uint16_t* zsrc = HZ ? zeros : scales;           // NULL zeros: value replaced by 8
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(scales), 0, 0x7FFFFFFF, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rz =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(zsrc), 0, 0x7FFFFFFF, 0x00020000);
+
+    // activation staging: instruction j of wave w fills slots (8 w + j) * 64 + lane, i.e.
+    // row r = (8 w + j) * 8 + lane / 8, slot lane % 8, which holds column piece
+    // (lane % 8) ^ ((r / 2) % 8)
+    int xoff[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int r = (8 * wave + j) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
+        xoff[j] = (min(m0 + r, M - 1) * K + 8 * c) * 2;
+    }
+    int woff[2], szoff[2];
+#pragma unroll
+    for (int ns = 0; ns < 2; ++ns) {
+        const int wrow = min(n0 + 64 * wave + 32 * ns + l32, N - 1);
+        woff[ns] = wrow * (K / 2) + 16 * h;
+        szoff[ns] = wrow * G * 2;
+    }
+    auto load_a = [&](int buf, int step) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rx, (__attribute__((address_space(3))) void*)&As[buf][(8 * wave + j) * 64], 16,
+                xoff[j], step * W_BK * 2, 0, 0);
+    };
+    struct WStage {
+        u32x4 w[2];
+        uint16_t s[2], z[2];
+    };
+    auto load_w = [&](WStage& st, int step) {
+        const int grp2 = group_of(step * W_BK + 32 * h, gshift) * 2;
+#pragma unroll
+        for (int ns = 0; ns < 2; ++ns) {
+            st.w[ns] = __builtin_amdgcn_raw_buffer_load_b128(rw, woff[ns], step * (W_BK / 2), 0);
+            st.s[ns] = __builtin_amdgcn_raw_buffer_load_b16(rs, szoff[ns] + grp2, 0, 0);
+            st.z[ns] = __builtin_amdgcn_raw_buffer_load_b16(rz, szoff[ns] + grp2, 0, 0);
+        }
+    };
+    // word j of both rows of a stage -> the fp16 B fragments of MFMA j: b[ns][j][4]
+    auto dequant_word = [&](const WStage& st, int j, uint32_t b[2][4][4]) {
+        const f16x2 bias = {(_Float16)1536.0f, (_Float16)1536.0f};
+#pragma unroll
+        for (int ns = 0; ns < 2; ++ns) {
+            const float z = HZ ? h2f(st.z[ns]) : 8.0f;
+            const uint32_t zb = (uint32_t)(0x6600 - (int)z) & 0xFFFFu;
+            const u16x2 zbias = __builtin_bit_cast(u16x2, zb | (zb << 16));
+            const f16x2 sv = __builtin_bit_cast(f16x2, (uint32_t)st.s[ns] | ((uint32_t)st.s[ns] << 16));
+            const uint32_t w = st.w[ns][j];
+            const uint32_t t0 = w & 0x0F0F0F0Fu;          // u0 u2 u4 u6 (as bytes)
+            const uint32_t t1 = (w >> 4) & 0x0F0F0F0Fu;   // u1 u3 u5 u7
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const uint32_t uu = perm(t1, t0, 0x0C040C00u + 0x00010001u * p);
+                const u16x2 biased = __builtin_bit_cast(u16x2, uu) + zbias;     // 1536 + u - z
+                const f16x2 code = __builtin_bit_cast(f16x2, biased) - bias;    // exact
+                b[ns][j][p] = __builtin_bit_cast(uint32_t, code * sv);          // one rounding
+            }
+        }
+    };
+
+    f32x16 acc[8][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    // fragment slots: row m = 32 ms + l32, piece c = 4 h + j -> slot m * 8 + (c ^ (m / 2 % 8))
+    int fslot[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fslot[j] = l32 * 8 + ((4 * h + j) ^ ((l32 >> 1) & 7));
+
+    // One step: MFMAs on the activations in LDS buffer `buf` and the dequantized weights
+    // `bc`, while the next step's packed weights `nx` are dequantized into `bn`, one word
+    // per MFMA group so the VALU work hides under the matrix instructions.
+    auto compute = [&](int buf, const uint32_t bc[2][4][4], const WStage& nx, uint32_t bn[2][4][4]) {
+        const u32x4* A = As[buf];
+        u32x4 fa[8], fb[8];        // activation fragments one MFMA group ahead
+#pragma unroll
+        for (int ms = 0; ms < 8; ++ms) fa[ms] = A[ms * 256 + fslot[0]];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            u32x4* cur = (j & 1) ? fb : fa;
+            u32x4* nxt = (j & 1) ? fa : fb;
+            if (j < 3) {
+#pragma unroll
+                for (int ms = 0; ms < 8; ++ms) nxt[ms] = A[ms * 256 + fslot[j + 1]];
+            }
+#pragma unroll
+            for (int ms = 0; ms < 8; ++ms) {
+                const uint32_t af[4] = {cur[ms].x, cur[ms].y, cur[ms].z, cur[ms].w};
+#pragma unroll
+                for (int ns = 0; ns < 2; ++ns) acc[ms][ns] = Mfma<DT_F16>::run(af, bc[ns][j], acc[ms][ns]);
+            }
+            dequant_word(nx, j, bn);
+            // interleave: one fragment read and a few dequant instructions per MFMA pair
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (j < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);              // VALU
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Pipeline: activations one step ahead (global -> LDS), packed weights one step ahead
+    // and dequantized weights one step ahead (registers).  The LDS-destination loads are
+    // complete when vmcnt drains; each step ends with that wait and a barrier.  Loads past
+    // the last step re-read it (harmless, unused).
+    WStage p0, p1;
+    uint32_t b0[2][4][4], b1[2][4][4];
+    load_a(0, 0);
+    load_w(p0, 0);
+    load_w(p1, min(1, nsteps - 1));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dequant_word(p0, j, b0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int step = 0; step < nsteps; step += 2) {
+        load_a(1, min(step + 1, nsteps - 1));
+        load_w(p0, min(step + 2, nsteps - 1));
+        compute(0, b0, p1, b1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        load_a(0, min(step + 2, nsteps - 1));
+        load_w(p1, min(step + 3, nsteps - 1));
+        compute(1, b1, p0, b0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int ms = 0; ms < 8; ++ms) {
+#pragma unroll
+        for (int ns = 0; ns < 2; ++ns) {
+            const int n = n0 + 64 * wave + 32 * ns + l32;
+            if (n >= N) continue;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int m = m0 + 32 * ms + 8 * (e >> 2) + 4 * h + (e & 3);
+                if (m < M) Y[(size_t)m * N + n] = f2h_bits(acc[ms][ns][e]);
+            }
+        }
+    }
+}
+
 }  // namespace
 
 bool prefill_supports(const LinearArgs& a) {
@@ -391,6 +595,19 @@ bool prefill_supports(const LinearArgs& a) {
 
 hipError_t launch_prefill(const LinearArgs& a, hipStream_t st) {
     const int hz = a.zeros ? 1 : 0;
+    if (a.dtype == DT_F16 && a.K % (2 * W_BK) == 0) {
+        const int tiles = ((a.M + W_BM - 1) / W_BM) * ((a.N + W_BN - 1) / W_BN);
+        const int grid = 8 * ((tiles + 7) / 8);
+        if (hz)
+            hipLaunchKernelGGL(prefill_f16_wide_kernel<true>, dim3(grid), dim3(256), 0, st,
+                               static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros,
+                               static_cast<uint16_t*>(a.Y), a.M, a.N, a.K, a.G, a.gshift);
+        else
+            hipLaunchKernelGGL(prefill_f16_wide_kernel<false>, dim3(grid), dim3(256), 0, st,
+                               static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros,
+                               static_cast<uint16_t*>(a.Y), a.M, a.N, a.K, a.G, a.gshift);
+        return hipGetLastError();
+    }
     if (a.dtype == DT_F16) {
         const int tiles = ((a.M + F_BM - 1) / F_BM) * ((a.N + F_BN - 1) / F_BN);
         hipLaunchKernelGGL(prefill_f16_kernel, dim3(tiles), dim3(256), 0, st,
