@@ -242,11 +242,13 @@ __device__ __forceinline__ void load_batch(RowBatch<DT, M, CPL, RB>& bt, const S
     }
 }
 
-// szl: the block's (scale, zero point) fp16 pairs, one 32-bit word per (row, group),
-// rows relative to the block; szrow = LDS word index of the batch's first row.
+// szl: the block's group factors, one (s', c) float pair per (row, group), rows relative
+// to the block (szrow = index of the batch's first row): a chunk adds s' * P + c * S to
+// its row (P its dot product, S its activation sum); fp16: s' = s * 2^24, c = -z * s'
+// (P and S in units of 2^-24); bf16: s' = s, c = -(128 + z) * s.  Both are exact in fp32.
 template <int DT, int M, int CPL, int RB>
 __device__ __forceinline__ void compute_batch(const RowBatch<DT, M, CPL, RB>& bt, const uint32_t* xp,
-                                              const float* xsum, const uint32_t* szl, int szrow, int G,
+                                              const float* xsum, const float2* szl, int szrow, int G,
                                               const int lgrp[CPL], int lane, float acc[RB][M]) {
     constexpr int CH = CPL * 64;
 #pragma unroll
@@ -274,53 +276,42 @@ __device__ __forceinline__ void compute_batch(const RowBatch<DT, M, CPL, RB>& bt
         }
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-            const uint32_t sz = szl[szrow + r * G + lgrp[i]];
-            const float s = h2f((uint16_t)(sz & 0xFFFFu));
-            const float z = h2f((uint16_t)(sz >> 16));
+            const float2 f = szl[szrow + r * G + lgrp[i]];
             if constexpr (DT == DT_F16) {
                 float pa[M], pb[M];
-#pragma unroll
-                for (int m = 0; m < M; ++m) pa[m] = pb[m] = 0.0f;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     uint32_t cd[4];
                     unpack_mask_f16(bt.w[r][i][q], cd);
 #pragma unroll
                     for (int m = 0; m < M; ++m) {
-                        pa[m] = dot2<DT>(xr[m][4 * q + 0], cd[0], pa[m]);
-                        pb[m] = dot2<DT>(xr[m][4 * q + 1], cd[1], pb[m]);
+                        pa[m] = dot2<DT>(xr[m][4 * q + 0], cd[0], q == 0 ? 0.0f : pa[m]);
+                        pb[m] = dot2<DT>(xr[m][4 * q + 1], cd[1], q == 0 ? 0.0f : pb[m]);
                         pa[m] = dot2<DT>(xr[m][4 * q + 2], cd[2], pa[m]);
                         pb[m] = dot2<DT>(xr[m][4 * q + 3], cd[3], pb[m]);
                     }
                 }
-                const float s24 = s * 16777216.0f;
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
-                    float t = fmaf(pb[m], 0.0625f, pa[m]);
-                    t = fmaf(-z, xs[m], t);
-                    acc[r][m] = fmaf(s24, t, acc[r][m]);
+                    const float t = fmaf(pb[m], 0.0625f, pa[m]);     // sum x*u * 2^-24
+                    acc[r][m] = fmaf(f.y, xs[m], fmaf(f.x, t, acc[r][m]));
                 }
             } else {
                 float p[M];
-#pragma unroll
-                for (int m = 0; m < M; ++m) p[m] = 0.0f;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     uint32_t cd[4];
                     unpack_byte<0x43>(bt.w[r][i][q], cd);
 #pragma unroll
                     for (int m = 0; m < M; ++m) {
-                        p[m] = dot2<DT>(xr[m][4 * q + 0], cd[0], p[m]);
+                        p[m] = dot2<DT>(xr[m][4 * q + 0], cd[0], q == 0 ? 0.0f : p[m]);
                         p[m] = dot2<DT>(xr[m][4 * q + 1], cd[1], p[m]);
                         p[m] = dot2<DT>(xr[m][4 * q + 2], cd[2], p[m]);
                         p[m] = dot2<DT>(xr[m][4 * q + 3], cd[3], p[m]);
                     }
                 }
 #pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    const float t = fmaf(-(128.0f + z), xs[m], p[m]);
-                    acc[r][m] = fmaf(s, t, acc[r][m]);
-                }
+                for (int m = 0; m < M; ++m) acc[r][m] = fmaf(f.y, xs[m], fmaf(f.x, p[m], acc[r][m]));
             }
         }
         __builtin_amdgcn_sched_barrier(0);   // one chunk of activations live at a time
@@ -357,7 +348,7 @@ __global__ __launch_bounds__(64 * W) void gemv_stream_kernel(
     constexpr int JSZ = kSzPiecesPerThread;
     uint32_t* xp = lds;                  // [M][4 pieces][CH] x 16 B pairs, then one spare slot
     float* xsum = reinterpret_cast<float*>(lds + (M * CH + 1) * 16);   // [M*CH + 1]
-    uint32_t* szs = lds + sz_lds_offset(M, CPL) / 4;   // staged (scale | zero << 16) words
+    float2* szs = reinterpret_cast<float2*>(lds + sz_lds_offset(M, CPL) / 4);   // staged group factors
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -458,25 +449,31 @@ __global__ __launch_bounds__(64 * W) void gemv_stream_kernel(
         if ((job0 & 3) == 0)
             xsum[slot] = ok ? (DT == DT_F16 ? sum * 5.9604644775390625e-8f : sum) : 0.0f;
     }
-    //    Scales and zero points: one (s | z << 16) word per (row, group); NULL zeros
-    //    become 8.0 (0x4800).
+    //    Group factors (s', c) per (row, group), see compute_batch; NULL zeros mean z = 8.
+    auto factors = [&](uint32_t s_bits, uint32_t z_bits) {
+        const float sv = h2f((uint16_t)s_bits);
+        const float zv = has_zeros ? h2f((uint16_t)z_bits) : 8.0f;
+        const float sp = DT == DT_F16 ? sv * 16777216.0f : sv;
+        return float2{sp, -(DT == DT_F16 ? zv : 128.0f + zv) * sp};
+    };
 #pragma unroll
     for (int j = 0; j < JSZ; ++j) {
         const int p = tid + NT * j;
-        const u32x4 sw = sv[j];
-        const u32x4 zw = has_zeros ? zv[j] : u32x4{0x48004800u, 0x48004800u, 0x48004800u, 0x48004800u};
         if (p < sz_pieces && sz_al + 8 * p + 8 <= total) {
-            u32x4* dst = reinterpret_cast<u32x4*>(szs + 8 * p);
-            dst[0] = u32x4{perm(zw.x, sw.x, 0x05040100u), perm(zw.x, sw.x, 0x07060302u),
-                           perm(zw.y, sw.y, 0x05040100u), perm(zw.y, sw.y, 0x07060302u)};
-            dst[1] = u32x4{perm(zw.z, sw.z, 0x05040100u), perm(zw.z, sw.z, 0x07060302u),
-                           perm(zw.w, sw.w, 0x05040100u), perm(zw.w, sw.w, 0x07060302u)};
+            const uint32_t sw[4] = {sv[j].x, sv[j].y, sv[j].z, sv[j].w};
+            const uint32_t zw[4] = {zv[j].x, zv[j].y, zv[j].z, zv[j].w};
+            float2* dst = szs + 8 * p;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                dst[2 * d] = factors(sw[d] & 0xFFFFu, zw[d] & 0xFFFFu);
+                dst[2 * d + 1] = factors(sw[d] >> 16, zw[d] >> 16);
+            }
         }
     }
     {
         const int h = full_end + tid;            // tail half of this thread (tid < 8)
         if (tid < 8 && h < total && h >= sz_al && h < sz_al + 8 * sz_pieces)
-            szs[h - sz_al] = (uint32_t)st | ((uint32_t)(has_zeros ? zt : (uint16_t)0x4800) << 16);
+            szs[h - sz_al] = factors(st, zt);
     }
     __syncthreads();
 
@@ -626,7 +623,7 @@ LdsCfg pick_lds(int M, int N, int K, int G) {
     const int rpb = (N + want - 1) / want;
     const long long pieces = ((long long)rpb * G + 7) / 8 + 1;      // 16-byte staging pieces
     if (pieces > (long long)kSzPiecesPerThread * 64 * kStreamWaves) return c;
-    const long long lds = sz_lds_offset(M, cpl) + 32 * pieces;
+    const long long lds = sz_lds_offset(M, cpl) + 64 * pieces;       // 8 float pairs per piece
     if (lds > kLdsBudget) return c;
     c.cpl = cpl;
     c.rows_per_block = rpb;
