@@ -448,10 +448,17 @@ def run_extras(layers, copies, W4, synth, torch, np):
             W4.linear(X, qw, s, z, GROUP, out=Y)
         ms = time_loop(lambda i: W4.linear(X, qw, s, z, GROUP, out=Y), 10, torch)
         tf = 2.0 * 4096 * N * K / (ms * 1e-3) / 1e12
+        # context: a dense fp16 GEMM of the same shape with fp16 weights (torch / hipBLASLt)
+        Wd = torch.randn(N, K, dtype=torch.float16, device="cuda")
+        for _ in range(3):
+            torch.matmul(X, Wd.t(), out=Y)
+        ms_d = time_loop(lambda i: torch.matmul(X, Wd.t(), out=Y), 10, torch, graph=False)
+        tf_d = 2.0 * 4096 * N * K / (ms_d * 1e-3) / 1e12
         pre[f"K{K}_N{N}"] = {"TFLOPs": round(tf, 1), "us": round(ms * 1e3, 1),
-                             "frac_mfma_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
-        log(f"  prefill M=4096 K={K} N={N}: {tf:.1f} TFLOP/s")
-        del qw, s, z, X, Y
+                             "frac_mfma_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                             "dense_fp16_torch_TFLOPs": round(tf_d, 1)}
+        log(f"  prefill M=4096 K={K} N={N}: {tf:.1f} TFLOP/s (dense fp16 torch.matmul {tf_d:.1f})")
+        del qw, s, z, X, Y, Wd
     out["prefill_m4096_fp16_g128"] = pre
     return out
 
