@@ -158,6 +158,35 @@ ALL_PATHS = [W4.PATH_GEMV, W4.PATH_SKINNY, W4.PATH_PREFILL]
 
 @pytest.mark.parametrize("path", ALL_PATHS)
 @pytest.mark.parametrize("dtype", [FP16, BF16])
+@pytest.mark.parametrize("offset", [1, 3])
+def test_linear_unaligned_metadata(path, dtype, offset):
+    # scales / zeros need only 2-byte alignment: pass views that start `offset` halves into
+    # larger buffers (the kernels stage them with 16-byte loads from arbitrary offsets)
+    N, K, g = 301, 1024, 128
+    G = K // g
+    W = weights(N, K, 0.02, seed=61)
+    M = {W4.PATH_GEMV: 2, W4.PATH_SKINNY: 3, W4.PATH_PREFILL: 70}[path]
+    X = activations(M, K, dtype, 62)
+
+    def view_at_offset(a: np.ndarray) -> torch.Tensor:
+        buf = torch.zeros(N * G + 2 * offset, dtype=torch.float16, device="cuda")
+        buf[offset:offset + N * G] = torch.from_numpy(a.astype(np.float16).reshape(-1)).cuda()
+        v = buf[offset:offset + N * G].view(N, G)
+        assert v.data_ptr() % 16 != 0
+        return v
+
+    for scheme in (ASYM, SYM):
+        codes, s, z = oracle.quantize(W, g, scheme)
+        qw_np = oracle.pack(codes)
+        zz = z if scheme == ASYM else None           # symmetric: NULL zeros (all 8)
+        Y = W4.linear(x_to_torch(X, dtype), torch.from_numpy(qw_np).cuda(), view_at_offset(s),
+                      view_at_offset(zz) if zz is not None else None, g, path=path)
+        ref = oracle.linear_ref(X, dtype, qw_np, s, zz, g)
+        assert_close(y_to_f64(Y), ref_to_f64(ref, dtype), f"unaligned metadata path={path} scheme={scheme}")
+
+
+@pytest.mark.parametrize("path", ALL_PATHS)
+@pytest.mark.parametrize("dtype", [FP16, BF16])
 def test_linear_offset_groups(path, dtype):
     # groups that do not straddle zero: asymmetric zero points far outside 0..15
     N, K, g = 192, 1024, 128
