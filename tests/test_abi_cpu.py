@@ -106,8 +106,11 @@ def test_dequantize_rejects_invalid_arguments(lib):
     (1, 4096, 4096, 128, 0, L.PATH_GEMV),
     (2, 4096, 11008, 128, 0, L.PATH_GEMV),
     (4, 11008, 4096, 128, 1, L.PATH_SKINNY),          # MFMA decode kernel
+    (4, 4096, 11008, 128, 0, L.PATH_SKINNY),          # long K: activations streamed
     (3, 4096, 4096, 64, 0, L.PATH_GEMV),              # g = 64: the MFMA kernels need g % 128 == 0
     (16, 4096, 4096, 128, 0, L.PATH_SKINNY),
+    (8, 4096, 11008, 128, 1, L.PATH_SKINNY),          # MFMA decode kernel, 5 <= M <= 16
+    (17, 4096, 4096, 128, 0, L.PATH_SKINNY),
     (1, 8192, 28672, 128, 1, L.PATH_GEMV),
     (4096, 11008, 4096, 128, 0, L.PATH_PREFILL),
     (1024, 4096, 11008, 64, 0, L.PATH_PREFILL),

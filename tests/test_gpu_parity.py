@@ -119,7 +119,11 @@ SKINNY_CASES = [(1, 64, 128, 128), (5, 100, 1024, 128), (16, 256, 4096, 128), (1
                 # M <= 4: the k-split decode kernel (1..4 tiles per block, short and long K)
                 (1, 4096, 4096, 128), (2, 11008, 4096, 128), (3, 4096, 11008, 128),
                 (4, 1000, 2048, 256), (1, 16000, 1024, 128), (1, 300, 28672, 128),
-                (4, 700, 8192, 8192), (1, 50, 11008, 11008), (3, 17, 128, 128), (2, 5000, 1408, 128)]
+                (4, 700, 8192, 8192), (1, 50, 11008, 11008), (3, 17, 128, 128), (2, 5000, 1408, 128),
+                # 5 <= M <= 16: activations streamed next to the weights (1..4 tiles per block)
+                (5, 4100, 2048, 128), (16, 12300, 512, 128), (9, 8200, 1024, 256), (13, 33, 11008, 128),
+                (16, 4096, 11008, 128), (7, 3000, 8192, 8192), (11, 1, 256, 128), (16, 17, 4352, 128),
+                (4, 4096, 11008, 128), (3, 300, 28672, 128)]
 PREFILL_CASES = [(1, 64, 64, 64), (17, 200, 192, 64), (130, 129, 256, 128), (256, 384, 1024, 128),
                  (300, 256, 4096, 4096), (64, 128, 11008, 128), (129, 1, 128, 64)]
 # fp16 prefill also takes K % 64 == 32 and g == 32 (bf16 prefill needs multiples of 64)
@@ -207,16 +211,22 @@ def test_linear_offset_groups(path, dtype):
 @pytest.mark.parametrize("path", ALL_PATHS)
 @pytest.mark.parametrize("dtype", [FP16, BF16])
 def test_linear_symmetric_and_null_zeros(path, dtype):
-    for zeros_none in (False, True):
-        Y, ref = _run_linear(4, 192, 1024, 128, SYM, dtype, path, seed=3, zeros_none=zeros_none)
-        assert_close(y_to_f64(Y), ref_to_f64(ref, dtype), f"sym path={path} zeros_none={zeros_none}")
+    for M in (4, 9):
+        if path == W4.PATH_GEMV and M > 8:
+            continue
+        for zeros_none in (False, True):
+            Y, ref = _run_linear(M, 192, 1024, 128, SYM, dtype, path, seed=3, zeros_none=zeros_none)
+            assert_close(y_to_f64(Y), ref_to_f64(ref, dtype),
+                         f"sym M={M} path={path} zeros_none={zeros_none}")
 
 
 @pytest.mark.parametrize("path", ALL_PATHS)
 def test_linear_bf16_outlier_channels(path):
-    for K in (8192, 4096):
-        Y, ref = _run_linear(4, 256, K, 128, ASYM, BF16, path, seed=9, x_outliers=True)
-        assert_close(y_to_f64(Y), ref_to_f64(ref, BF16), f"bf16 outliers path={path} K={K}")
+    for M, K in ((4, 8192), (4, 4096), (16, 8192)):
+        if path == W4.PATH_GEMV and M > 8:
+            continue
+        Y, ref = _run_linear(M, 256, K, 128, ASYM, BF16, path, seed=9, x_outliers=True)
+        assert_close(y_to_f64(Y), ref_to_f64(ref, BF16), f"bf16 outliers M={M} path={path} K={K}")
 
 
 @pytest.mark.parametrize("path", ALL_PATHS)
@@ -234,8 +244,8 @@ def test_one_hot_bit_exact(path, dtype):
     X = X64.astype(np.float16) if dtype == FP16 else oracle.round_to_bf16_bits(X64)
     qw, st, zt = upload_packed(qw_np, s, z)
     ref = oracle.linear_ref(X, dtype, qw_np, s, z, g)
-    # GEMV serves M <= 8; the MFMA decode kernel takes M <= 4 and the skinny kernel larger M
-    sizes = {W4.PATH_GEMV: [4], W4.PATH_SKINNY: [4, len(ks)]}.get(path, [len(ks)])
+    # GEMV serves M <= 8; the MFMA decode kernels take M <= 16 (K % 256 == 0)
+    sizes = {W4.PATH_GEMV: [4], W4.PATH_SKINNY: [4, 7, len(ks)]}.get(path, [len(ks)])
     for rows in sizes:
         for m0 in range(0, len(ks), rows):
             Y = W4.linear(x_to_torch(X[m0:m0 + rows], dtype), qw, st, zt, g, path=path)

@@ -1,5 +1,7 @@
-// Decode-regime W4A16 kernel on CDNA4 matrix cores, 1 <= M <= 4 (MFMA 16x16x32);
-// K % 256 == 0 and g % 128 == 0.
+// Decode-regime W4A16 kernels on CDNA4 matrix cores, 1 <= M <= 16 (MFMA 16x16x32);
+// K % 256 == 0 and g % 128 == 0.  decode_kernel (M <= 4) stages the activations in LDS;
+// decode16_kernel (M <= 16; used from 5 rows, or when the activations do not fit the LDS)
+// streams them from memory next to the weights.
 //
 // At decode the layer streams every packed weight once per token (page
 // "推理优化中“用精度换性能“的核心技术：量化", section 一), so the kernel is built around the
@@ -367,12 +369,286 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------------
+// Up to 16 rows: the same weight stream, tiles and k-split, with all sixteen MFMA rows in
+// use.  The activations no longer fit the LDS (16 rows of K), so each wave loads the
+// activation fragments of its k-block pairs straight from memory (L2-resident: every
+// block reads all of X), P pairs ahead together with the weights; lane (n, q) loads row
+// n (zeros for n >= M), columns 128 kb + 32 q .. + 31 of each k-block and puts them in
+// the unpack's pair order in registers.  The k-block activation sums come from four more
+// MFMAs against a constant B operand (2^-24 in the x1 slots and 16 * 2^-24 in the x16
+// slots for fp16, 1.0 for bf16), so they land in the accumulator layout: lane (n, q)
+// element j holds row 4 q + j.
+struct XStage {
+    u32x4 x[2][4];
+};
+
+template <int DT, int T, int P, int W>
+__global__ __launch_bounds__(64 * W) void decode16_kernel(
+    const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int has_zeros,
+    uint16_t* __restrict__ Y, int M, int N, int K, int G, int gshift, int NT, int nblk, int KSP,
+    int off_wt) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t dlds[];
+    constexpr int NTH = 64 * W;
+    const int KB = K >> 7;
+    unsigned char* lbase = reinterpret_cast<unsigned char*>(dlds);
+    uint32_t* szs = dlds;                                                  // (s | z << 16) words
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    u32x4* wt = reinterpret_cast<u32x4*>(lbase + off_wt) + wave * 128;     // 2 KB per wave
+    const int n16 = lane & 15;
+    const int q = lane >> 4;
+
+    const int tile0 = (int)(((long long)blockIdx.x * NT) / nblk);
+    const int ntiles = (int)(((long long)(blockIdx.x + 1) * NT) / nblk) - tile0;
+    const int row_begin = tile0 * 16;
+    const int row_end = min(N, row_begin + ntiles * 16);
+    const int kp0 = wave * KSP;
+    const int kp1 = min(KB / 2, kp0 + KSP);
+    const int np = max(0, kp1 - kp0);
+
+    const __amdgpu_buffer_rsrc_t rw =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(qw), 0, 0x7FFFFFFF, 0x00020000);
+    const __amdgpu_buffer_rsrc_t none =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(qw), 0, 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X), 0, M * K * 2, 0x00020000);
+    const uint16_t* zsrc = has_zeros ? zeros : scales;
+    const int total = N * G;
+    const int full_end = total & ~7;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(scales), 0, full_end * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rz =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(zsrc), 0, full_end * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_all =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(scales), 0, total * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rz_all =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(zsrc), 0, total * 2, 0x00020000);
+
+    int vw[T][2], wslot[2], rslot[2];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int n = min((tile0 + t) * 16 + 8 * h + (lane >> 3), N - 1);
+            vw[t][h] = n * (K >> 1) + 16 * (lane & 7);
+        }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int r = 8 * h + (lane >> 3);
+        wslot[h] = 8 * r + ((lane & 7) ^ ((r >> 1) & 7));
+        const int c = 4 * h + q;
+        rslot[h] = 8 * n16 + (c ^ ((n16 >> 1) & 7));
+    }
+    // activation fragment offset of this lane; rows >= M point past the buffer (zeros)
+    const int xoff = n16 < M ? (n16 * K + 32 * q) * 2 : 0x40000000;
+    auto load_x = [&](XStage& xs, int kp, bool live) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                xs.x[e][j] = __builtin_amdgcn_raw_buffer_load_b128(live ? rx : none, xoff + e * 256 + 16 * j,
+                                                                   kp * 512, 0);
+    };
+
+    // 1. (scale, zero) staging loads first, then P pairs of activations and weights
+    const int sz_first = row_begin * G;
+    const int sz_al = sz_first & ~7;
+    const int sz_pieces = ((row_end - row_begin) * G + (sz_first - sz_al) + 7) >> 3;
+    u32x4 sv[kSzPieces], zv[kSzPieces];
+#pragma unroll
+    for (int j = 0; j < kSzPieces; ++j) {
+        const int off = (sz_al + 8 * min(tid + NTH * j, sz_pieces - 1)) * 2;
+        sv[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        zv[j] = __builtin_amdgcn_raw_buffer_load_b128(rz, off, 0, 0);
+    }
+    const int tail = min(full_end + (tid & 7), total - 1);
+    const uint16_t s_tail = __builtin_amdgcn_raw_buffer_load_b16(rs_all, tail * 2, 0, 0);
+    const uint16_t z_tail = __builtin_amdgcn_raw_buffer_load_b16(rz_all, tail * 2, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    XStage xst[P];
+    Stage<T> st[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        load_x(xst[p], kp0 + p, p < np);
+        load_stage<T>(st[p], rw, none, kp0 + p, p < np, vw, ntiles);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. (scale | zero << 16) words; NULL zeros become 8.0 (0x4800)
+#pragma unroll
+    for (int j = 0; j < kSzPieces; ++j) {
+        const int p = tid + NTH * j;
+        const u32x4 sw = sv[j];
+        const u32x4 zw = has_zeros ? zv[j] : u32x4{0x48004800u, 0x48004800u, 0x48004800u, 0x48004800u};
+        if (p < sz_pieces && sz_al + 8 * p + 8 <= total) {
+            u32x4* dst = reinterpret_cast<u32x4*>(szs + 8 * p);
+            dst[0] = u32x4{perm(zw.x, sw.x, 0x05040100u), perm(zw.x, sw.x, 0x07060302u),
+                           perm(zw.y, sw.y, 0x05040100u), perm(zw.y, sw.y, 0x07060302u)};
+            dst[1] = u32x4{perm(zw.z, sw.z, 0x05040100u), perm(zw.z, sw.z, 0x07060302u),
+                           perm(zw.w, sw.w, 0x05040100u), perm(zw.w, sw.w, 0x07060302u)};
+        }
+    }
+    {
+        const int h = full_end + tid;
+        if (tid < 8 && h < total && h >= sz_al && h < sz_al + 8 * sz_pieces)
+            szs[h - sz_al] = (uint32_t)s_tail | ((uint32_t)(has_zeros ? z_tail : (uint16_t)0x4800) << 16);
+    }
+    __syncthreads();
+
+    int szo[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) szo[t] = (sz_first - sz_al) + (t * 16 + n16) * G;
+    f32x4 tile[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) tile[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // constant B operand of the activation-sum MFMAs
+    const uint32_t ones_lo = DT == DT_F16 ? 0x00010001u : 0x3F803F80u;
+    const uint32_t ones_hi = DT == DT_F16 ? 0x00100010u : 0x3F803F80u;
+    const uint32_t ones[4] = {ones_lo, ones_hi, ones_lo, ones_hi};
+
+    // One k-block pair, k-block by k-block (fewer live registers): activation fragments in
+    // pair order, their sums, then for each tile the lanes holding k-block e of the unit
+    // pass it through the transpose slots.
+    const bool my_half[2] = {(lane & 7) < 4, (lane & 7) >= 4};
+    auto compute = [&](const XStage& xs, const Stage<T>& sw, int kp) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            uint32_t a[4][4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const u32x4 v = xs.x[e][j];
+                if constexpr (DT == DT_F16) {
+                    permute_x8(v.x, v.y, v.z, v.w, a[j]);
+                    const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+                    a[j][1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a[j][1]) * sixteenth);
+                    a[j][3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a[j][3]) * sixteenth);
+                } else {
+                    permute_x8_byte(v.x, v.y, v.z, v.w, a[j]);
+                }
+            }
+            f32x4 S = mfma16<DT>(a[0], ones, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+            for (int j = 1; j < 4; ++j) S = mfma16<DT>(a[j], ones, S);
+            const int grp = ((2 * kp + e) << 7) >> gshift;
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                if (my_half[e]) {
+                    wt[wslot[0]] = sw.w[t][0];
+                    wt[wslot[1]] = sw.w[t][1];
+                }
+                __builtin_amdgcn_wave_barrier();
+                const u32x4 wb = wt[rslot[e]];
+                __builtin_amdgcn_wave_barrier();
+                uint32_t bq[4][4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if constexpr (DT == DT_F16)
+                        unpack_mask_f16(wb[j], bq[j]);
+                    else
+                        unpack_byte<0x43>(wb[j], bq[j]);
+                }
+                f32x4 acc = mfma16<DT>(a[0], bq[0], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+                for (int j = 1; j < 4; ++j) acc = mfma16<DT>(a[j], bq[j], acc);
+                const uint32_t sz = szs[szo[t] + grp];
+                const float s = h2f((uint16_t)(sz & 0xFFFFu));
+                const float z = h2f((uint16_t)(sz >> 16));
+                const float sp = DT == DT_F16 ? s * 16777216.0f : s;
+                const float c = DT == DT_F16 ? z : 128.0f + z;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) tile[t][j] = fmaf(sp, fmaf(-c, S[j], acc[j]), tile[t][j]);
+            }
+        }
+    };
+
+    // 3. k-block pairs of the slice, P in flight; the last round computes what is in flight
+    int i = 0;
+    for (; i + P < np; i += P) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            compute(xst[p], st[p], kp0 + i + p);
+            load_x(xst[p], kp0 + i + p + P, i + p + P < np);
+            load_stage<T>(st[p], rw, none, kp0 + i + p + P, i + p + P < np, vw, ntiles);
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+        if (i + p < np) compute(xst[p], st[p], kp0 + i + p);
+
+    // 4. sum the waves' partial tiles in the LDS; lane (n, q) element j is row 4 q + j
+    __syncthreads();
+    f32x4* red = reinterpret_cast<f32x4*>(lbase);
+#pragma unroll
+    for (int t = 0; t < T; ++t) red[(wave * T + t) * 64 + lane] = tile[t];
+    __syncthreads();
+    for (int idx = tid; idx < T * 64; idx += NTH) {
+        const int t = idx >> 6;
+        const int l = idx & 63;
+        f32x4 v = red[t * 64 + l];
+        for (int w = 1; w < W; ++w) {
+            const f32x4 u = red[(w * T + t) * 64 + l];
+            v[0] += u[0]; v[1] += u[1]; v[2] += u[2]; v[3] += u[3];
+        }
+        const int n = (tile0 + t) * 16 + (l & 15);
+        if (t < ntiles && n < N) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int m = 4 * (l >> 4) + j;
+                if (m < M) Y[(size_t)m * N + n] = f2out<DT>(v[j]);
+            }
+        }
+    }
+}
+
 struct DecCfg {
-    int t = 0, p = 0, ksp = 0, nblk = 0;
+    int t = 0, p = 0, ksp = 0, nblk = 0, xreg = 0;
     int sk = 0, spare = 0, szs = 0, wt = 0, lds = 0;
 };
 
+// 5 <= M <= 16 (decode16_kernel): no activation staging; LDS = (scale, zero) words, the
+// per-wave transpose buffers, and later the partial tiles.
+DecCfg pick_decode16(const LinearArgs& a) {
+    DecCfg c;
+    if (a.M < 1 || a.M > 16 || a.K % 256 != 0 || a.g % 128 != 0) return c;
+    if ((long long)a.N * (a.K / 2) >= (1LL << 31) || (long long)a.M * a.K * 2 >= (1LL << 30)) return c;
+    if ((long long)a.N * a.G * 2 >= (1LL << 31)) return c;
+    const int NT = (a.N + 15) / 16;
+    const int KB = a.K / 128;
+    int t = (NT + 255) / 256;
+    if (t > 4) t = 4;
+    const long long pieces = ((long long)t * 16 * a.G + 7) / 8 + 1;
+    if (pieces > (long long)kSzPieces * 64 * kWaves) return c;
+    c.wt = align16((int)pieces * 32);
+    long long lds = (long long)c.wt + (long long)kWaves * 2048;
+    const long long red = (long long)kWaves * t * 1024;
+    if (red > lds) lds = red;
+    if (lds > kLdsBudget) return c;
+    c.lds = (int)lds;
+    c.t = t;
+    c.p = t == 4 ? 1 : 2;            // register budget of two waves per SIMD
+    c.ksp = (KB / 2 + kWaves - 1) / kWaves;
+    c.nblk = (NT + t - 1) / t;
+    return c;
+}
+
+DecCfg pick_decode_staged(const LinearArgs& a);
+
+// M <= 4 prefers the activation-staging kernel; when the activations do not fit its LDS
+// (long K), or M > 4, the streaming one (c.xreg).
 DecCfg pick_decode(const LinearArgs& a) {
+    if (a.M <= 4) {
+        const DecCfg c = pick_decode_staged(a);
+        if (c.t > 0) return c;
+    }
+    DecCfg c = pick_decode16(a);
+    c.xreg = 1;
+    return c;
+}
+
+DecCfg pick_decode_staged(const LinearArgs& a) {
     DecCfg c;
     if (a.M < 1 || a.M > 4 || a.K % 256 != 0 || a.g % 128 != 0) return c;
     // 32-bit buffer offsets
@@ -432,8 +708,26 @@ hipError_t run_m(const LinearArgs& a, const DecCfg& c, hipStream_t st) {
     }
 }
 
+template <int DT, int T, int P>
+hipError_t run16(const LinearArgs& a, const DecCfg& c, hipStream_t st) {
+    hipLaunchKernelGGL((decode16_kernel<DT, T, P, kWaves>), dim3(c.nblk), dim3(64 * kWaves), c.lds, st,
+                       static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, a.zeros ? 1 : 0,
+                       static_cast<uint16_t*>(a.Y), a.M, a.N, a.K, a.G, a.gshift, (a.N + 15) / 16, c.nblk,
+                       c.ksp, c.wt);
+    return hipGetLastError();
+}
+
 template <int DT>
 hipError_t run_dt(const LinearArgs& a, const DecCfg& c, hipStream_t st) {
+    if (c.xreg) {
+        switch (c.t) {
+            case 1: return run16<DT, 1, 2>(a, c, st);
+            case 2: return run16<DT, 2, 2>(a, c, st);
+            case 3: return run16<DT, 3, 2>(a, c, st);
+            case 4: return run16<DT, 4, 1>(a, c, st);
+        }
+        return hipErrorInvalidValue;
+    }
     switch (a.M) {
         case 1: return run_m<DT, 1>(a, c, st);
         case 2: return run_m<DT, 2>(a, c, st);

@@ -228,16 +228,25 @@ struct StreamSrc {
     int row_bytes_w;
 };
 
-template <int DT, int M, int CPL, int RB>
+// CLIP: rows at or past `row_lim` (another wave's) load zeros through `none`; otherwise
+// rows are clamped to row_lim - 1 (rows past the block's end re-read valid memory and their
+// results are not stored).
+template <int DT, int M, int CPL, int RB, bool CLIP>
 __device__ __forceinline__ void load_batch(RowBatch<DT, M, CPL, RB>& bt, const StreamSrc& src, int row,
-                                           bool live, int N, const int vw[CPL]) {
+                                           bool live, int row_lim, const int vw[CPL]) {
     const __amdgpu_buffer_rsrc_t rw = live ? src.w : src.none;   // wave-uniform select
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-            const int n = min(row + r, N - 1);          // wave-uniform
-            bt.w[r][i] = __builtin_amdgcn_raw_buffer_load_b128(rw, vw[i], n * src.row_bytes_w, 2 /* nt */);
+            if constexpr (CLIP) {
+                const bool in = live && row + r < row_lim;              // wave-uniform
+                bt.w[r][i] = __builtin_amdgcn_raw_buffer_load_b128(in ? src.w : src.none, vw[i],
+                                                                   (in ? row + r : 0) * src.row_bytes_w, 2);
+            } else {
+                const int n = min(row + r, row_lim - 1);                // wave-uniform
+                bt.w[r][i] = __builtin_amdgcn_raw_buffer_load_b128(rw, vw[i], n * src.row_bytes_w, 2 /* nt */);
+            }
         }
     }
 }
@@ -249,7 +258,7 @@ __device__ __forceinline__ void load_batch(RowBatch<DT, M, CPL, RB>& bt, const S
 template <int DT, int M, int CPL, int RB>
 __device__ __forceinline__ void compute_batch(const RowBatch<DT, M, CPL, RB>& bt, const uint32_t* xp,
                                               const float* xsum, const float2* szl, int szrow, int G,
-                                              const int lgrp[CPL], int lane, float acc[RB][M]) {
+                                              int nrows, const int lgrp[CPL], int lane, float acc[RB][M]) {
     constexpr int CH = CPL * 64;
 #pragma unroll
     for (int r = 0; r < RB; ++r)
@@ -276,7 +285,9 @@ __device__ __forceinline__ void compute_batch(const RowBatch<DT, M, CPL, RB>& bt
         }
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-            const float2 f = szl[szrow + r * G + lgrp[i]];
+            // rows past the batch's last real row (zeros loaded, result not stored) read
+            // that row's factors, so every LDS read stays inside the staged words
+            const float2 f = szl[szrow + (r < nrows ? r : nrows - 1) * G + lgrp[i]];
             if constexpr (DT == DT_F16) {
                 float pa[M], pb[M];
 #pragma unroll
@@ -323,12 +334,14 @@ template <int DT, int M, int RB>
 __device__ __forceinline__ void store_batch(const float acc[RB][M], int row, int row_end, int N,
                                             int lane, uint16_t* __restrict__ Y) {
 #pragma unroll
-    for (int r = 0; r < RB; ++r)
+    for (int r = 0; r < RB; ++r) {
+        if (row + r >= row_end) break;                 // wave-uniform
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             const float v = wave_sum(acc[r][m]);
-            if (lane == 0 && row + r < row_end) Y[(size_t)m * N + row + r] = f2out<DT>(v);
+            if (lane == 0) Y[(size_t)m * N + row + r] = f2out<DT>(v);
         }
+    }
 }
 
 // Byte offset of the (scale, zero point) words in the stream kernel's LDS.
@@ -356,8 +369,15 @@ __global__ __launch_bounds__(64 * W) void gemv_stream_kernel(
     const int KW = K >> 3;
     const int row_begin = blockIdx.x * rows_per_block;
     const int row_end = min(N, row_begin + rows_per_block);
-    const int first = row_begin + wave * RB;
-    const int nbatch = first < row_end ? (row_end - first + W * RB - 1) / (W * RB) : 0;
+    // NB == 0: one batch per wave holding all of its rows, an even split of the block's
+    // rows (wave w: rows_w .. rows_{w+1} - 1); otherwise batches of RB rows strided by W * RB.
+    constexpr bool ONE = NB == 0;
+    constexpr int NBUF = ONE ? 1 : NB;
+    const int nrows_blk = row_end - row_begin;
+    const int first = ONE ? row_begin + (wave * nrows_blk) / W : row_begin + wave * RB;
+    const int wave_end = ONE ? row_begin + ((wave + 1) * nrows_blk) / W : row_end;
+    const int nbatch = ONE ? (first < wave_end ? 1 : 0)
+                           : (first < row_end ? (row_end - first + W * RB - 1) / (W * RB) : 0);
 
     // The block's scales (and zeros) are one contiguous run of (row_end - row_begin) * G
     // halves; it is staged in 16-byte pieces from the 16-byte boundary at or below its
@@ -412,10 +432,10 @@ __global__ __launch_bounds__(64 * W) void gemv_stream_kernel(
     const int tail = min(full_end + (tid & 7), total - 1);
     const uint16_t st = __builtin_amdgcn_raw_buffer_load_b16(s_all, tail * 2, 0, 0);
     const uint16_t zt = __builtin_amdgcn_raw_buffer_load_b16(z_all, tail * 2, 0, 0);
-    RowBatch<DT, M, CPL, RB> buf[NB];
+    RowBatch<DT, M, CPL, RB> buf[NBUF];
 #pragma unroll
-    for (int i = 0; i < NB; ++i)
-        load_batch<DT, M, CPL, RB>(buf[i], src, first + i * W * RB, nbatch > i, N, vw);
+    for (int i = 0; i < NBUF; ++i)
+        load_batch<DT, M, CPL, RB, ONE>(buf[i], src, first + i * W * RB, nbatch > i, ONE ? wave_end : N, vw);
     __builtin_amdgcn_sched_barrier(0);
 
     // 2. Stage activations: permute each 8-column block, chunk sums by a quad reduction
@@ -484,25 +504,34 @@ __global__ __launch_bounds__(64 * W) void gemv_stream_kernel(
     //    round (the tail) only computes what is in flight, so a wave issues at most NB - 1
     //    empty batches.
     float acc[RB][M];
-    int b = 0;
-    for (; b + NB < nbatch; b += NB) {
+    if constexpr (ONE) {
+        // all loads are in flight; compute in load order so each chunk waits only for itself
+        if (nbatch > 0) {
+            compute_batch<DT, M, CPL, RB>(buf[0], xp, xsum, szs, szrow0 + (first - row_begin) * G, G,
+                                          wave_end - first, lgrp, lane, acc);
+            store_batch<DT, M, RB>(acc, first, wave_end, N, lane, Y);
+        }
+    } else {
+        int b = 0;
+        for (; b + NB < nbatch; b += NB) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const int row = first + (b + i) * W * RB;
+                compute_batch<DT, M, CPL, RB>(buf[i], xp, xsum, szs, szrow0 + (row - row_begin) * G, G,
+                                              row_end - row, lgrp, lane, acc);
+                load_batch<DT, M, CPL, RB, false>(buf[i], src, first + (b + i + NB) * W * RB,
+                                                  b + i + NB < nbatch, N, vw);
+                store_batch<DT, M, RB>(acc, row, row_end, N, lane, Y);
+            }
+        }
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            const int row = first + (b + i) * W * RB;
-            compute_batch<DT, M, CPL, RB>(buf[i], xp, xsum, szs, szrow0 + (row - row_begin) * G, G, lgrp,
-                                          lane, acc);
-            load_batch<DT, M, CPL, RB>(buf[i], src, first + (b + i + NB) * W * RB, b + i + NB < nbatch,
-                                       N, vw);
-            store_batch<DT, M, RB>(acc, row, row_end, N, lane, Y);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        if (b + i < nbatch) {
-            const int row = first + (b + i) * W * RB;
-            compute_batch<DT, M, CPL, RB>(buf[i], xp, xsum, szs, szrow0 + (row - row_begin) * G, G, lgrp,
-                                          lane, acc);
-            store_batch<DT, M, RB>(acc, row, row_end, N, lane, Y);
+            if (b + i < nbatch) {
+                const int row = first + (b + i) * W * RB;
+                compute_batch<DT, M, CPL, RB>(buf[i], xp, xsum, szs, szrow0 + (row - row_begin) * G, G,
+                                              row_end - row, lgrp, lane, acc);
+                store_batch<DT, M, RB>(acc, row, row_end, N, lane, Y);
+            }
         }
     }
 }
@@ -632,8 +661,11 @@ LdsCfg pick_lds(int M, int N, int K, int G) {
     return c;
 }
 
-// Two rows per wave or fewer (and registers for them): one batch of two rows, nothing to
-// prefetch.  Otherwise batches of lds_rb rows, two in flight.
+// When a wave owns at most two rows and they fit in registers (at most kOneShotLoads
+// 16-byte loads per lane), the wave loads all of them at once (NB = 0, one batch);
+// otherwise batches of lds_rb rows, two in flight (measured faster for longer row runs).
+constexpr int kOneShotLoads = 12;
+constexpr int kOneShotRows = 2;
 template <int DT, int M, int CPL, int RB, int NB>
 hipError_t run_lds4(const LinearArgs& a, const LdsCfg& c, hipStream_t st) {
     hipLaunchKernelGGL((gemv_stream_kernel<DT, M, CPL, RB, kStreamWaves, NB>), dim3(c.blocks),
@@ -643,12 +675,19 @@ hipError_t run_lds4(const LinearArgs& a, const LdsCfg& c, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <int DT, int M, int CPL, int RB>
+hipError_t run_one(const LinearArgs& a, const LdsCfg& c, hipStream_t st) {
+    if constexpr (RB > kOneShotRows || RB * M * CPL > kOneShotLoads) {
+        return run_lds4<DT, M, CPL, lds_rb(M, CPL), 2>(a, c, st);
+    } else {
+        if (c.rows_per_block <= RB * kStreamWaves) return run_lds4<DT, M, CPL, RB, 0>(a, c, st);
+        return run_one<DT, M, CPL, RB + 1>(a, c, st);
+    }
+}
+
 template <int DT, int M, int CPL>
 hipError_t run_lds3(const LinearArgs& a, const LdsCfg& c, hipStream_t st) {
-    if constexpr (M * CPL <= 6) {       // register budget of a two-row batch
-        if (c.rows_per_block <= 2 * kStreamWaves) return run_lds4<DT, M, CPL, 2, 1>(a, c, st);
-    }
-    return run_lds4<DT, M, CPL, lds_rb(M, CPL), 2>(a, c, st);
+    return run_one<DT, M, CPL, 1>(a, c, st);
 }
 
 template <int DT, int M, int CPL>
