@@ -104,7 +104,8 @@ def test_dequantize_rejects_invalid_arguments(lib):
 
 @pytest.mark.parametrize("M,N,K,g,dtype,path", [
     (1, 4096, 4096, 128, 0, L.PATH_GEMV),
-    (2, 4096, 11008, 128, 0, L.PATH_GEMV),
+    (2, 11008, 4096, 128, 0, L.PATH_GEMV),
+    (2, 4096, 11008, 128, 0, L.PATH_SKINNY),          # two rows, long K: MFMA decode
     (4, 11008, 4096, 128, 1, L.PATH_SKINNY),          # MFMA decode kernel
     (4, 4096, 11008, 128, 0, L.PATH_SKINNY),          # long K: activations streamed
     (3, 4096, 4096, 64, 0, L.PATH_GEMV),              # g = 64: the MFMA kernels need g % 128 == 0

@@ -80,9 +80,9 @@ int validate_linear(const void* X, int dtype, int64_t M, int64_t N, int64_t K, i
 // within the VALU budget of the HBM stream, the skinny MFMA kernel for small batches,
 // the tiled MFMA GEMM once the problem is compute-bound.
 int choose_path(const LinearArgs& a) {
-    // measured on MI355X: the v_dot2 GEMV leads for one or two rows, the MFMA decode
-    // kernels (skinny path, 1 <= M <= 16) from three rows on
-    if (a.M <= 2 && w4a16::gemv_supports(a)) return W4A16_PATH_GEMV;
+    // measured on MI355X: the v_dot2 GEMV leads for one row and for two rows of short K
+    // (K <= 4096), the MFMA decode kernels (skinny path, 1 <= M <= 16) from there on
+    if ((a.M == 1 || (a.M == 2 && a.K <= 4096)) && w4a16::gemv_supports(a)) return W4A16_PATH_GEMV;
     if (a.M <= 16 && w4a16::decode_supports(a)) return W4A16_PATH_SKINNY;
     if (a.M <= 4 && w4a16::gemv_supports(a)) return W4A16_PATH_GEMV;
     if (a.M <= 32 && w4a16::skinny_supports(a)) return W4A16_PATH_SKINNY;
