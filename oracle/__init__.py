@@ -22,9 +22,13 @@ What it computes (sources are the five pages on W4A16 quantization):
   16-bit activations (page 4, §3.2 Weight-only 量化; page
   "大模型推理中 Weight-only、W8A8 和 FP8 量化有什么区别？如何选型？", §二).
 
+* GPTQ (``gptq.py``): ``H = 2 X^T X`` from calibration activations and the column-wise
+  quantization with the optimal-brain-surgeon compensation of the columns still free
+  (page 4, section 四 GPTQ; page "量化实战深入（GPTQ / AWQ / SmoothQuant / KV 量化）", 4.1).
+
 Readings where the pages are silent (tie rule, clamping, which scale feeds the
 zero point, nibble order, symmetric storage) are listed in the docstrings of
-``quant.py`` and ``linear.py``.
+``quant.py``, ``linear.py`` and ``gptq.py``.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against hand-worked vectors, closed forms, exact rational arithmetic or an

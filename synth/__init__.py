@@ -77,6 +77,29 @@ def activations(M: int, K: int, dtype: int, seed: int,
     raise ValueError(f"unknown dtype {dtype}")
 
 
+def calibration(n: int, K: int, dtype: int, seed: int, n_factors: int = 16,
+                factor_scale: float = 0.5, outlier_frac: float = 0.01,
+                outlier_mult: float = 10.0) -> np.ndarray:
+    """Calibration activations ``[n, K]`` with correlated channels: i.i.d. N(0, 1) plus
+    ``n_factors`` shared Gaussian factors (loadings ~ N(0, factor_scale^2)); a fraction
+    ``outlier_frac`` of the channels (at least one) is multiplied by ``outlier_mult``.
+    fp16 array, or bf16 bit patterns."""
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((n, K), dtype=np.float32)
+    F = rng.standard_normal((n, n_factors), dtype=np.float32)
+    L = rng.standard_normal((n_factors, K), dtype=np.float32) * np.float32(factor_scale)
+    X += F @ L
+    n_ch = max(1, int(round(outlier_frac * K))) if outlier_frac > 0 else 0
+    if n_ch:
+        ch = rng.choice(K, size=n_ch, replace=False)
+        X[:, ch] *= np.float32(outlier_mult)
+    if dtype == FP16:
+        return X.astype(np.float16)
+    if dtype == BF16:
+        return f32_to_bf16_bits(X)
+    raise ValueError(f"unknown dtype {dtype}")
+
+
 @dataclass(frozen=True)
 class Case:
     """One W4A16 linear problem: shapes, dtype, group size, scheme, distributions."""
