@@ -136,6 +136,53 @@ int w4a16_select_path(int64_t M, int64_t N, int64_t K, int64_t group_size, int d
 int w4a16_dequantize(const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                      int64_t N, int64_t K, int64_t group_size, float* out, void* stream);
 
+/*
+ * GPTQ: column-by-column INT4 quantization with second-order error compensation, writing
+ * the same packed format as w4a16_quantize_pack.  Page "推理优化中“用精度换性能“的核心技术：
+ * 量化", section 四 (4.2 algorithm: H = 2 X^T X, columns quantized in order, every later
+ * column j corrected by -dw * Hinv[i, j] / Hinv[i, i]; 4.4 natural column order, Cholesky
+ * factor, group_size); page "量化实战深入（GPTQ / AWQ / SmoothQuant / KV 量化）", 4.1.
+ * Hinv is the inverse Hessian of the columns not yet quantized; with H^-1 = U^T U (U upper
+ * triangular) the correction ratio is U[i, j] / U[i, i].  All compensation arithmetic is
+ * fp64; codes, scales and zero points follow the RTN rules of w4a16_quantize_pack applied,
+ * at each group's first column, to the group's current (compensated) weights rounded to
+ * fp32.  Calls are asynchronous on `stream` like every entry point; the caller owns all
+ * buffers.  Typical use: hessian (once, or once per calibration batch with accumulate = 1),
+ * factor, quantize.
+ */
+
+/*
+ * w4a16_gptq_hessian -- H (=, or += when accumulate != 0) 2 X^T X.
+ *   X  [n_samples, K] fp16 or bf16 (dtype) calibration activations of the layer, device,
+ *      2-byte aligned.
+ *   H  [K, K] fp64, device, 8-byte aligned.  Only the lower triangle (i >= j) is defined
+ *      on return; the strictly upper part is unspecified.  K <= 46340.
+ */
+int w4a16_gptq_hessian(const void* X, int dtype, int64_t n_samples, int64_t K, double* H,
+                       int accumulate, void* stream);
+
+/*
+ * w4a16_gptq_factor -- U = upper Cholesky factor of (H + lambda I)^-1, H^-1 = U^T U, with
+ * lambda = damp * mean(diag H) (damp = 0 leaves H as is; 0.01 is customary when the
+ * calibration set is small).
+ *   H  [K, K] fp64, device: reads the lower triangle; DESTROYED (used as workspace).
+ *   U  [K, K] fp64 out, device: upper triangle, zeros below the diagonal.
+ * If H + lambda I is not numerically positive definite U contains NaN.
+ */
+int w4a16_gptq_factor(double* H, int64_t K, double damp, double* U, void* stream);
+
+/*
+ * w4a16_gptq_quantize -- GPTQ of W [N, K] fp32 (device, 4-byte aligned) with the factor U
+ * from w4a16_gptq_factor.  group_size and scheme as in w4a16_quantize_pack.
+ *   work     device fp64 workspace of N * K + 64 * N elements (8-byte aligned).
+ *   qweight  out [N, K/8] int32; scales, zeros out [N, K/g] fp16 bits (zeros may be NULL
+ *            for the symmetric scheme, else all 8.0).
+ * Limits: N * K <= 2^34, K <= 46340.
+ */
+int w4a16_gptq_quantize(const float* W, int64_t N, int64_t K, int64_t group_size, int scheme,
+                        const double* U, double* work, int32_t* qweight, uint16_t* scales,
+                        uint16_t* zeros, void* stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* w4a16_strerror(int status);
 

@@ -88,7 +88,7 @@ def _code(x64: np.ndarray, s_h: np.ndarray, z_h: np.ndarray, scheme: int) -> np.
     return q.astype(np.uint8)
 
 
-def _run(W, g: int, scheme: int, coef, trace=None):
+def _run(W, g: int, scheme: int, coef, trace=None, pre=None):
     W = np.asarray(W, dtype=np.float32)
     N, K = W.shape
     if g <= 0 or K % g:
@@ -102,6 +102,8 @@ def _run(W, g: int, scheme: int, coef, trace=None):
             s_h, z_h = _group_params(Wc[:, i:i + g], scheme)
             scales[:, i // g] = s_h
             zeros[:, i // g] = z_h
+        if pre is not None:
+            pre[:, i] = Wc[:, i]
         q = _code(Wc[:, i], s_h, z_h, scheme)
         codes[:, i] = q
         w_hat = s_h.astype(np.float64) * (q.astype(np.float64) - z_h.astype(np.float64))
@@ -114,16 +116,17 @@ def _run(W, g: int, scheme: int, coef, trace=None):
     return codes, scales, zeros
 
 
-def gptq_quantize(W, U: np.ndarray, g: int, scheme: int = ASYM, trace=None):
+def gptq_quantize(W, U: np.ndarray, g: int, scheme: int = ASYM, trace=None, pre=None):
     """GPTQ with the Cholesky factor ``U`` of ``H^-1`` (``H^-1 = U^T U``, G1).
 
     Returns ``(codes uint8 [N, K], scales fp16 [N, K/g], zeros fp16 [N, K/g])`` in the
     layout of ``quant.quantize`` (pack with ``quant.pack``).  ``trace``, if a list,
     receives the compensated weights after every column (with the quantized columns
-    replaced by their dequantized values).
+    replaced by their dequantized values); ``pre``, if an fp64 ``[N, K]`` array, receives
+    the value each weight had when it was quantized.  Rows are independent given ``U``.
     """
     U = np.asarray(U, dtype=np.float64)
-    return _run(W, g, scheme, lambda i: U[i, i + 1:] / U[i, i], trace)
+    return _run(W, g, scheme, lambda i: U[i, i + 1:] / U[i, i], trace, pre)
 
 
 def gptq_obs(W, H: np.ndarray, g: int, scheme: int = ASYM, trace=None):

@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
     names = _declared()
     for required in ("w4a16_quantize_pack", "w4a16_linear", "w4a16_linear_ex",
                      "w4a16_select_path", "w4a16_dequantize", "w4a16_strerror",
-                     "w4a16_abi_version"):
+                     "w4a16_abi_version", "w4a16_gptq_hessian", "w4a16_gptq_factor",
+                     "w4a16_gptq_quantize"):
         assert required in names
 
 
@@ -124,3 +125,27 @@ def test_dispatcher_choices(lib, M, N, K, g, dtype, path):
 def test_dispatcher_rejects_invalid(lib):
     assert lib.w4a16_select_path(1, 64, 100, 100, 0) == L.ERR_SHAPE
     assert lib.w4a16_select_path(1, 64, 128, 128, 3) == L.ERR_DTYPE
+
+
+def test_gptq_rejects_invalid_arguments(lib):
+    assert lib.w4a16_gptq_hessian(None, 0, 16, 64, A, 0, None) == L.ERR_NULL
+    assert lib.w4a16_gptq_hessian(A, 2, 16, 64, B, 0, None) == L.ERR_DTYPE
+    assert lib.w4a16_gptq_hessian(A, 0, 0, 64, B, 0, None) == L.ERR_SHAPE
+    assert lib.w4a16_gptq_hessian(A, 0, 16, 50000, B, 0, None) == L.ERR_SHAPE
+    assert lib.w4a16_gptq_hessian(A + 1, 0, 16, 64, B, 0, None) == L.ERR_ALIGN
+    assert lib.w4a16_gptq_factor(None, 64, 0.01, B, None) == L.ERR_NULL
+    assert lib.w4a16_gptq_factor(A, 1, 0.01, B, None) == L.ERR_SHAPE
+    assert lib.w4a16_gptq_factor(A, 64, -1.0, B, None) == L.ERR_SHAPE
+    assert lib.w4a16_gptq_factor(A, 64, float("nan"), B, None) == L.ERR_SHAPE
+    assert lib.w4a16_gptq_factor(A + 4, 64, 0.01, B, None) == L.ERR_ALIGN
+    q = lambda **kw: lib.w4a16_gptq_quantize(kw.get("W", A), 64, kw.get("K", 128), kw.get("g", 128),
+                                             kw.get("scheme", 0), kw.get("U", B), kw.get("work", C),
+                                             kw.get("qw", D), kw.get("s", D + 4096), kw.get("z", D + 8192),
+                                             None)
+    assert q(W=None) == L.ERR_NULL
+    assert q(work=None) == L.ERR_NULL
+    assert q(z=None) == L.ERR_NULL                  # asymmetric needs zeros
+    assert q(scheme=3) == L.ERR_SCHEME
+    assert q(K=100, g=100) == L.ERR_SHAPE
+    assert q(g=48) == L.ERR_GROUP
+    assert q(U=B + 4) == L.ERR_ALIGN

@@ -9,6 +9,9 @@ the library's HIP kernels; there is no CPU or PyTorch fallback.
     group-wise INT4 RTN quantization of an fp32 ``[N, K]`` CUDA tensor.
 ``linear(X, qweight, scales, zeros, group_size, path=PATH_AUTO)`` -> ``Y``
     ``Y = X . dequant(qweight)^T`` for fp16/bf16 ``X [M, K]``.
+``gptq_hessian(X, H=None)`` / ``gptq_factor(H, damp)`` / ``gptq_quantize(W, U, group_size, scheme)``
+    GPTQ: ``H = 2 X^T X`` (fp64, lower triangle), the upper Cholesky factor ``U`` of the
+    damped inverse, and the compensated column-wise quantization in the packed format.
 """
 
 from __future__ import annotations
@@ -21,7 +24,7 @@ from ._lib import (ASYM, BF16, F16, OK, PATH_AUTO, PATH_GEMV, PATH_NAMES, PATH_P
 __all__ = [
     "ASYM", "SYM", "F16", "BF16", "PATH_AUTO", "PATH_GEMV", "PATH_SKINNY", "PATH_PREFILL",
     "PATH_NAMES", "W4A16Error", "quantize_pack", "linear", "dequantize", "select_path",
-    "abi_version", "lib",
+    "abi_version", "lib", "gptq_hessian", "gptq_factor", "gptq_quantize",
 ]
 
 
@@ -130,3 +133,59 @@ def dequantize(qweight: torch.Tensor, scales: torch.Tensor, zeros, group_size: i
                                 out.data_ptr(), _stream())
     check(st, "w4a16_dequantize")
     return out
+
+
+def gptq_hessian(X: torch.Tensor, H: torch.Tensor | None = None) -> torch.Tensor:
+    """``H = 2 X^T X`` (``H += 2 X^T X`` when ``H`` is given) for fp16/bf16 calibration
+    activations ``X [n, K]``; fp64 ``[K, K]``, lower triangle defined."""
+    dt = _dtype_code(X)
+    _need(X, "X", X.dtype, 2)
+    n, K = X.shape
+    acc = H is not None
+    if H is None:
+        H = torch.empty((K, K), dtype=torch.float64, device=X.device)
+    else:
+        _need(H, "H", torch.float64, 2)
+        if tuple(H.shape) != (K, K):
+            raise ValueError("H must be [K, K]")
+    check(lib().w4a16_gptq_hessian(X.data_ptr(), dt, n, K, H.data_ptr(), 1 if acc else 0, _stream()),
+          "w4a16_gptq_hessian")
+    return H
+
+
+def gptq_factor(H: torch.Tensor, damp: float = 0.01) -> torch.Tensor:
+    """Upper ``U`` with ``(H + damp * mean(diag H) I)^-1 = U^T U``; ``H`` is overwritten."""
+    _need(H, "H", torch.float64, 2)
+    K = H.shape[0]
+    if tuple(H.shape) != (K, K):
+        raise ValueError("H must be square")
+    U = torch.empty_like(H)
+    check(lib().w4a16_gptq_factor(H.data_ptr(), K, float(damp), U.data_ptr(), _stream()),
+          "w4a16_gptq_factor")
+    return U
+
+
+def gptq_quantize(W: torch.Tensor, U: torch.Tensor, group_size: int = 128, scheme: int = ASYM,
+                  work: torch.Tensor | None = None):
+    """GPTQ of fp32 ``W [N, K]`` with the factor ``U``; returns ``(qweight, scales, zeros)``
+    in the layout of :func:`quantize_pack` (zeros all 8 for the symmetric scheme)."""
+    _need(W, "W", torch.float32, 2)
+    _need(U, "U", torch.float64, 2)
+    N, K = W.shape
+    if tuple(U.shape) != (K, K):
+        raise ValueError("U must be [K, K]")
+    if K % 8 or group_size <= 0 or K % group_size:
+        raise ValueError("K must be a multiple of 8 and of group_size")
+    need = N * K + 64 * N
+    if work is None:
+        work = torch.empty(need, dtype=torch.float64, device=W.device)
+    elif work.dtype != torch.float64 or work.numel() < need or not work.is_contiguous():
+        raise ValueError(f"work must be a contiguous fp64 tensor of >= {need} elements")
+    G = K // group_size
+    qweight = torch.empty((N, K // 8), dtype=torch.int32, device=W.device)
+    scales = torch.empty((N, G), dtype=torch.float16, device=W.device)
+    zeros = torch.empty((N, G), dtype=torch.float16, device=W.device)
+    check(lib().w4a16_gptq_quantize(W.data_ptr(), N, K, group_size, scheme, U.data_ptr(),
+                                    work.data_ptr(), qweight.data_ptr(), scales.data_ptr(),
+                                    zeros.data_ptr(), _stream()), "w4a16_gptq_quantize")
+    return qweight, scales, zeros

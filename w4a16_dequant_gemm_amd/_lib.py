@@ -55,6 +55,12 @@ def lib() -> ctypes.CDLL:
     L.w4a16_select_path.argtypes = [i64, i64, i64, i64, i32]
     L.w4a16_dequantize.restype = i32
     L.w4a16_dequantize.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp]
+    L.w4a16_gptq_hessian.restype = i32
+    L.w4a16_gptq_hessian.argtypes = [vp, i32, i64, i64, vp, i32, vp]
+    L.w4a16_gptq_factor.restype = i32
+    L.w4a16_gptq_factor.argtypes = [vp, i64, ctypes.c_double, vp, vp]
+    L.w4a16_gptq_quantize.restype = i32
+    L.w4a16_gptq_quantize.argtypes = [vp, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp]
     _lib = L
     return L
 

@@ -18,6 +18,7 @@ using w4a16::LinearArgs;
 namespace {
 
 constexpr int64_t kMaxDim = 2147483647LL;
+constexpr int64_t kGptqMaxK = 46340;      // K * K fp64 elements indexable in 31 bits
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -165,6 +166,43 @@ int w4a16_dequantize(const int32_t* qweight, const uint16_t* scales, const uint1
                                                   scales, zeros, (int)N, (int)K, (int)group_size,
                                                   gshift, out, static_cast<hipStream_t>(stream));
     return hip_status(e);
+}
+
+int w4a16_gptq_hessian(const void* X, int dtype, int64_t n_samples, int64_t K, double* H,
+                       int accumulate, void* stream) {
+    if (!X || !H) return W4A16_ERR_NULL;
+    if (dtype != W4A16_F16 && dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
+    if (n_samples < 1 || K < 1 || n_samples > kMaxDim || K > kGptqMaxK) return W4A16_ERR_SHAPE;
+    if (n_samples * K > (int64_t(1) << 40)) return W4A16_ERR_SHAPE;
+    if (!aligned(X, 2) || !aligned(H, 8)) return W4A16_ERR_ALIGN;
+    return hip_status(w4a16::launch_gptq_hessian(X, dtype, (int)n_samples, (int)K, H, accumulate != 0,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_gptq_factor(double* H, int64_t K, double damp, double* U, void* stream) {
+    if (!H || !U) return W4A16_ERR_NULL;
+    if (K < 2 || K > kGptqMaxK) return W4A16_ERR_SHAPE;
+    if (!(damp >= 0.0) || damp > 1e6) return W4A16_ERR_SHAPE;
+    if (!aligned(H, 8) || !aligned(U, 8)) return W4A16_ERR_ALIGN;
+    return hip_status(w4a16::launch_gptq_factor(H, (int)K, damp, U, static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_gptq_quantize(const float* W, int64_t N, int64_t K, int64_t group_size, int scheme,
+                        const double* U, double* work, int32_t* qweight, uint16_t* scales,
+                        uint16_t* zeros, void* stream) {
+    if (!W || !U || !work || !qweight || !scales) return W4A16_ERR_NULL;
+    if (scheme != W4A16_ASYM_RTN && scheme != W4A16_SYM_ABSMAX) return W4A16_ERR_SCHEME;
+    if (scheme == W4A16_ASYM_RTN && !zeros) return W4A16_ERR_NULL;
+    int G = 0, gshift = 0;
+    const int st = check_shape_group(N, K, group_size, &G, &gshift);
+    if (st != W4A16_OK) return st;
+    if (K > kGptqMaxK || N * K > (int64_t(1) << 34)) return W4A16_ERR_SHAPE;
+    if (!aligned(W, 4) || !aligned(U, 8) || !aligned(work, 8) || !aligned(qweight, 4) ||
+        !aligned(scales, 2) || (zeros && !aligned(zeros, 2)))
+        return W4A16_ERR_ALIGN;
+    return hip_status(w4a16::launch_gptq_quantize(W, (int)N, (int)K, (int)group_size, scheme, U, work,
+                                                  reinterpret_cast<uint32_t*>(qweight), scales, zeros,
+                                                  static_cast<hipStream_t>(stream)));
 }
 
 int w4a16_select_path(int64_t M, int64_t N, int64_t K, int64_t group_size, int dtype) {

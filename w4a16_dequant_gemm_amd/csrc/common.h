@@ -64,6 +64,33 @@ __device__ __forceinline__ float in2f(uint32_t b16) {
     return DT == DT_F16 ? h2f((uint16_t)b16) : bf2f(b16);
 }
 
+// RTN group parameters (fp32, round-to-nearest-even, this order): asymmetric from the
+// group's min and max, s = fp16((max - min) / 15) (1.0 if that is 0), z = rint(-min/s) + 0;
+// symmetric from max|x|, s = fp16(max|x| / 7), z = 8 (offset-binary storage).
+template <int SCHEME>
+__device__ __forceinline__ void rtn_params(float mn, float mx, _Float16& sh, float& s, float& z) {
+    const float s32 = (SCHEME == 0) ? (mx - mn) / 15.0f : mx / 7.0f;
+    sh = (_Float16)s32;
+    s = (float)sh;
+    if (s == 0.0f) { s = 1.0f; sh = (_Float16)1.0f; }
+    z = (SCHEME == 0) ? (__builtin_rintf((-mn) / s) + 0.0f) : 8.0f;
+}
+
+// The stored 4-bit code of x with those parameters: clamp(rint(x/s) + z, 0, 15), or
+// clamp(rint(x/s), -8, 7) + 8 for the symmetric scheme.
+template <int SCHEME>
+__device__ __forceinline__ uint32_t rtn_code(float x, float s, float z) {
+    float q;
+    if (SCHEME == 0) {
+        q = __builtin_rintf(x / s) + z;
+        q = fminf(fmaxf(q, 0.0f), 15.0f);
+    } else {
+        q = __builtin_rintf(x / s);
+        q = fminf(fmaxf(q, -8.0f), 7.0f) + 8.0f;
+    }
+    return (uint32_t)(int)q;
+}
+
 // Byte permute: result byte i = byte sel_i of the 8-byte value {hi:lo}.
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
     return __builtin_amdgcn_perm(hi, lo, sel);

@@ -1,0 +1,392 @@
+// GPTQ on the GPU: the layer Hessian from calibration activations, the Cholesky factor of
+// its (damped) inverse, and the column-by-column INT4 quantization with second-order
+// compensation of the columns not yet quantized.
+//
+// Method (page "推理优化中“用精度换性能“的核心技术：量化", section 四 GPTQ, 4.2 and 4.4):
+// H = 2 X^T X; columns are quantized in their natural order; after column i the columns
+// j > i move by -dw * Hinv[i, j] / Hinv[i, i], Hinv being the inverse Hessian of the columns
+// still free.  With H^-1 = U^T U (U upper triangular) that ratio is U[i, j] / U[i, i], so
+// the loop needs only the rows of U (the Cholesky factor the page mentions).  Group
+// parameters are the RTN ones of the group's current weights when the loop reaches the
+// group's first column.  Everything but the code decision (fp32 RTN, as in quantize.hip)
+// is fp64.
+//
+// GPU structure.
+//   * fp64 GEMM (64 x 64 tiles, 16-deep k chunks through LDS, 4 x 4 outputs per thread)
+//     over strided operands: the Hessian, the Cholesky trailing updates, the triangular
+//     inverse and the GPTQ batch updates are all instances of it.
+//   * U without an explicit inverse of H: with P the index reversal, P H P = L L^T
+//     (lower Cholesky) gives H = (P L P)(P L P)^T, so U = P L^-1 P.  The matrix is
+//     reversed once, factored by blocks of 64 (one-workgroup diagonal factorization and
+//     inverse, a row-parallel panel solve, a lower-tile GEMM for the trailing matrix),
+//     L^-1 is built block row by block row from GEMMs, and reversed back into U.
+//   * The column loop runs in batches of B = 64 (or 32) columns: one lane per weight row
+//     holds the batch in registers and applies the in-batch compensation sequentially; the
+//     batch's scaled errors then update all later columns in one GEMM (the order of the
+//     additions changes, the arithmetic does not).
+#include "common.h"
+#include "launch.h"
+
+namespace w4a16 {
+
+namespace {
+
+// ------------------------------------------------------------------ fp64 GEMM
+constexpr int GT = 64;      // tile edge
+constexpr int GKC = 16;     // k chunk
+
+// element loaders: 0 = fp64, 1 = fp16 bits, 2 = bf16 bits
+template <int T>
+__device__ __forceinline__ double ld_elem(const void* p, long long i) {
+    if constexpr (T == 0) return static_cast<const double*>(p)[i];
+    else if constexpr (T == 1) return (double)h2f(static_cast<const uint16_t*>(p)[i]);
+    else return (double)bf2f(static_cast<const uint16_t*>(p)[i]);
+}
+
+// C = beta * C + alpha * A B with A(m, k) = A[m sam + k sak], B(k, n) = B[k sbk + n sbn],
+// C(m, n) = C[m scm + n scn].  MODE bit 0: only tiles touching the lower triangle
+// (m >= n) are computed; bit 1: B is lower triangular (B(k, n) = 0 for k < n), so the
+// contraction of a tile starts at its first column.  beta == 0 never reads C.
+template <int AT, int BT, int MODE>
+__global__ __launch_bounds__(256) void gemm_f64_kernel(int M, int N, int K, double alpha,
+                                                       const void* __restrict__ A, long long sam,
+                                                       long long sak, const void* __restrict__ B,
+                                                       long long sbk, long long sbn, double beta,
+                                                       double* __restrict__ C, long long scm,
+                                                       long long scn) {
+    const int m0 = blockIdx.y * GT;
+    const int n0 = blockIdx.x * GT;
+    if ((MODE & 1) && n0 > m0 + GT - 1) return;
+    __shared__ double As[GKC][GT + 1];
+    __shared__ double Bs[GKC][GT + 1];
+    const int tid = threadIdx.x;
+    const int tx = tid & 15;
+    const int ty = tid >> 4;
+    double acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+    const int kbeg = (MODE & 2) ? (n0 / GKC) * GKC : 0;
+    const bool a_krow = sak == 1;      // k contiguous in A
+    const bool b_ncol = sbn == 1;      // n contiguous in B
+    for (int k0 = kbeg; k0 < K; k0 += GKC) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int e = tid + 256 * r;
+            int m, k;
+            if (a_krow) { m = e >> 4; k = e & 15; } else { k = e >> 6; m = e & 63; }
+            const int gm = m0 + m, gk = k0 + k;
+            As[k][m] = (gm < M && gk < K) ? ld_elem<AT>(A, (long long)gm * sam + (long long)gk * sak) : 0.0;
+            int n, kb;
+            if (b_ncol) { kb = e >> 6; n = e & 63; } else { n = e >> 4; kb = e & 15; }
+            const int gn = n0 + n, gkb = k0 + kb;
+            Bs[kb][n] = (gn < N && gkb < K) ? ld_elem<BT>(B, (long long)gkb * sbk + (long long)gn * sbn) : 0.0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < GKC; ++kk) {
+            double a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = As[kk][ty + 16 * i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx + 16 * j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int gm = m0 + ty + 16 * i, gn = n0 + tx + 16 * j;
+            if (gm < M && gn < N) {
+                double* c = C + (long long)gm * scm + (long long)gn * scn;
+                *c = beta == 0.0 ? alpha * acc[i][j] : fma(alpha, acc[i][j], beta * *c);
+            }
+        }
+}
+
+template <int AT, int BT, int MODE>
+hipError_t gemm(int M, int N, int K, double alpha, const void* A, long long sam, long long sak,
+                const void* B, long long sbk, long long sbn, double beta, double* C, long long scm,
+                long long scn, hipStream_t st) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    const dim3 grid((N + GT - 1) / GT, (M + GT - 1) / GT);
+    hipLaunchKernelGGL((gemm_f64_kernel<AT, BT, MODE>), grid, dim3(256), 0, st, M, N, K, alpha, A, sam,
+                       sak, B, sbk, sbn, beta, C, scm, scn);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------- damping, reversal, Cholesky
+// lambda = damp * mean(diag H), stored in H[0][1] (strictly upper: never read as data)
+__global__ __launch_bounds__(1024) void damp_kernel(double* H, long long K, double damp) {
+    __shared__ double part[1024];
+    double s = 0.0;
+    for (long long i = threadIdx.x; i < K; i += 1024) s += H[i * K + i];
+    part[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 512; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) H[1] = damp * (part[0] / (double)K);
+}
+
+// dst[i][j] = src[K-1-i][K-1-j], reading only the lower triangle of the symmetric src;
+// DAMP adds lambda (src[0][1]) on the diagonal; UPPER_OUT zeroes dst below the diagonal.
+template <bool DAMP, bool UPPER_OUT>
+__global__ __launch_bounds__(256) void reverse_kernel(const double* __restrict__ src, double* __restrict__ dst,
+                                                      long long K) {
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= K * K) return;
+    const long long i = idx / K, j = idx % K;
+    if (UPPER_OUT && j < i) { dst[idx] = 0.0; return; }
+    long long a = K - 1 - i, b = K - 1 - j;
+    if (b > a) { const long long t = a; a = b; b = t; }
+    double v = src[a * K + b];
+    if (DAMP && i == j) v += src[1];
+    dst[idx] = v;
+}
+
+// One diagonal block (jb <= 64) of the lower Cholesky factorization, in place, by one
+// workgroup; its inverse (lower, zeros above the diagonal) goes to Dinv.
+__global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ A, long long lda, int jb,
+                                                         double* __restrict__ Dinv, long long ldd) {
+    __shared__ double a[64][65];
+    __shared__ double inv[64][65];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < jb * jb; e += 256) a[e / jb][e % jb] = A[(long long)(e / jb) * lda + e % jb];
+    __syncthreads();
+    for (int k = 0; k < jb; ++k) {
+        if (tid == 0) a[k][k] = sqrt(a[k][k]);
+        __syncthreads();
+        if (tid > k && tid < jb) a[tid][k] /= a[k][k];
+        __syncthreads();
+        for (int e = tid; e < jb * jb; e += 256) {
+            const int i = e / jb, j = e % jb;
+            if (j > k && i >= j) a[i][j] -= a[i][k] * a[j][k];
+        }
+        __syncthreads();
+    }
+    if (tid < jb) {                   // column c of L^-1 by forward substitution
+        const int c = tid;
+        for (int i = 0; i < jb; ++i) {
+            if (i < c) { inv[i][c] = 0.0; continue; }
+            double s = i == c ? 1.0 : 0.0;
+            for (int k = c; k < i; ++k) s -= a[i][k] * inv[k][c];
+            inv[i][c] = s / a[i][i];
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < jb * jb; e += 256) {
+        const int i = e / jb, j = e % jb;
+        if (j <= i) A[(long long)i * lda + j] = a[i][j];
+        Dinv[(long long)i * ldd + j] = inv[i][j];
+    }
+}
+
+// Panel solve, 16 rows per workgroup: row <- row * Dinv^T (Dinv lower, jb <= 64).
+__global__ __launch_bounds__(256) void trsm_rows_kernel(double* __restrict__ A, long long lda, int rows, int jb,
+                                                        const double* __restrict__ Dinv, long long ldd) {
+    __shared__ double d[64][65];
+    __shared__ double r[16][65];
+    const int tid = threadIdx.x;
+    const int row0 = blockIdx.x * 16;
+    for (int e = tid; e < jb * jb; e += 256) d[e / jb][e % jb] = Dinv[(long long)(e / jb) * ldd + e % jb];
+    for (int e = tid; e < 16 * jb; e += 256) {
+        const int rr = e / jb, k = e % jb;
+        r[rr][k] = row0 + rr < rows ? A[(long long)(row0 + rr) * lda + k] : 0.0;
+    }
+    __syncthreads();
+    const int rr = tid >> 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int c = (tid & 15) + 16 * q;
+        if (c < jb && row0 + rr < rows) {
+            double x = 0.0;
+            for (int k = 0; k <= c; ++k) x = fma(r[rr][k], d[c][k], x);
+            A[(long long)(row0 + rr) * lda + c] = x;
+        }
+    }
+}
+
+// ------------------------------------------------------------- column loop
+__global__ __launch_bounds__(256) void to_f64_kernel(const float* __restrict__ W, double* __restrict__ Wd,
+                                                     long long n) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) Wd[i] = (double)W[i];
+}
+
+// RTN parameters of group [c0, c0 + g) of every row from the current weights (fp32).
+template <int SCHEME>
+__global__ __launch_bounds__(256) void group_params_kernel(const double* __restrict__ Wd, int N, int K,
+                                                           int c0, int g, int G, uint16_t* __restrict__ scales,
+                                                           uint16_t* __restrict__ zeros) {
+    const int lane = threadIdx.x & 63;
+    const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (n >= N) return;
+    const double* row = Wd + (long long)n * K + c0;
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+    for (int k = lane; k < g; k += 64) {
+        const float x = (float)row[k];
+        if (SCHEME == 0) { mn = fminf(mn, x); mx = fmaxf(mx, x); }
+        else mx = fmaxf(mx, fabsf(x));
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+        mn = fminf(mn, __shfl_xor(mn, off, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    }
+    if (lane == 0) {
+        _Float16 sh;
+        float s, z;
+        rtn_params<SCHEME>(mn, mx, sh, s, z);
+        scales[(long long)n * G + c0 / g] = __builtin_bit_cast(uint16_t, sh);
+        if (zeros) zeros[(long long)n * G + c0 / g] = __builtin_bit_cast(uint16_t, (_Float16)z);
+    }
+}
+
+// One batch of B columns [c0, c0 + B) (inside one group), one lane per weight row: codes,
+// errors scaled by 1 / U[i][i] (to E, for the GEMM that updates the later columns) and the
+// in-batch compensation, column by column.
+template <int B, int SCHEME>
+__global__ __launch_bounds__(64) void gptq_batch_kernel(double* __restrict__ Wd, const double* __restrict__ U,
+                                                        int N, int K, int c0, int g, int G,
+                                                        const uint16_t* __restrict__ scales,
+                                                        const uint16_t* __restrict__ zeros,
+                                                        uint32_t* __restrict__ qw, double* __restrict__ E) {
+    __shared__ double Us[B][B + 1];
+    const int lane = threadIdx.x;
+    for (int e = lane; e < B * B; e += 64) {
+        const int i = e / B, j = e % B;
+        Us[i][j] = j >= i ? U[(long long)(c0 + i) * K + c0 + j] : 0.0;
+    }
+    __syncthreads();
+    const int n = blockIdx.x * 64 + lane;
+    if (n >= N) return;
+    double* row = Wd + (long long)n * K + c0;
+    double w[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) w[j] = row[j];
+    const int grp = c0 / g;
+    const float s = h2f(scales[(long long)n * G + grp]);
+    const float z = SCHEME == 0 ? h2f(zeros[(long long)n * G + grp]) : 8.0f;
+    const double sd = (double)s, zd = (double)z;
+    uint32_t words[B / 8];
+#pragma unroll
+    for (int t = 0; t < B / 8; ++t) words[t] = 0u;
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+        const uint32_t q = rtn_code<SCHEME>((float)w[i], s, z);
+        words[i / 8] |= (q & 0xFu) << (4 * (i % 8));
+        const double e = (w[i] - sd * ((double)q - zd)) / Us[i][i];
+        E[(long long)n * B + i] = e;
+#pragma unroll
+        for (int j = i + 1; j < B; ++j) w[j] = fma(-e, Us[i][j], w[j]);
+    }
+#pragma unroll
+    for (int t = 0; t < B / 8; ++t) qw[(long long)n * (K / 8) + c0 / 8 + t] = words[t];
+}
+
+template <int B, int SCHEME>
+hipError_t gptq_loop(const float* W, int N, int K, int g, const double* U, double* Wd, double* E,
+                     uint32_t* qw, uint16_t* scales, uint16_t* zeros, hipStream_t st) {
+    const int G = K / g;
+    const long long nk = (long long)N * K;
+    hipLaunchKernelGGL(to_f64_kernel, dim3((unsigned)((nk + 255) / 256)), dim3(256), 0, st, W, Wd, nk);
+    for (int c0 = 0; c0 < K; c0 += B) {
+        if (c0 % g == 0)
+            hipLaunchKernelGGL(group_params_kernel<SCHEME>, dim3((N + 3) / 4), dim3(256), 0, st, Wd, N, K, c0,
+                               g, G, scales, SCHEME == 0 ? zeros : nullptr);
+        hipLaunchKernelGGL((gptq_batch_kernel<B, SCHEME>), dim3((N + 63) / 64), dim3(64), 0, st, Wd, U, N, K,
+                           c0, g, G, scales, zeros, qw, E);
+        const int rest = K - c0 - B;
+        if (rest > 0) {
+            const hipError_t e = gemm<0, 0, 0>(N, rest, B, -1.0, E, B, 1, U + (long long)c0 * K + c0 + B, K, 1,
+                                               1.0, Wd + c0 + B, K, 1, st);
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void fill_u16_kernel(uint16_t* __restrict__ p, long long n, uint16_t v) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+}  // namespace
+
+hipError_t launch_gptq_hessian(const void* X, int dtype, int n, int K, double* H, bool accumulate,
+                               hipStream_t st) {
+    // lower-triangle tiles of H (+)= 2 X^T X; A(m, k) = X[k][m], B(k, n) = X[k][n]
+    const double beta = accumulate ? 1.0 : 0.0;
+    if (dtype == DT_F16)
+        return gemm<1, 1, 1>(K, K, n, 2.0, X, 1, K, X, K, 1, beta, H, K, 1, st);
+    return gemm<2, 2, 1>(K, K, n, 2.0, X, 1, K, X, K, 1, beta, H, K, 1, st);
+}
+
+hipError_t launch_gptq_factor(double* H, int K, double damp, double* U, hipStream_t st) {
+    constexpr int NB = 64;
+    const long long kk = (long long)K * K;
+    const unsigned blocks = (unsigned)((kk + 255) / 256);
+    // 1. lambda into H[0][1]; U = P (H + lambda I) P
+    hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(1024), 0, st, H, (long long)K, damp);
+    hipLaunchKernelGGL((reverse_kernel<true, false>), dim3(blocks), dim3(256), 0, st, H, U, (long long)K);
+    // 2. lower Cholesky of U in place; the diagonal blocks' inverses go to H (block I, I)
+    for (int j0 = 0; j0 < K; j0 += NB) {
+        const int jb = min(NB, K - j0);
+        double* Ajj = U + (long long)j0 * K + j0;
+        double* Djj = H + (long long)j0 * K + j0;
+        hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(256), 0, st, Ajj, (long long)K, jb, Djj, (long long)K);
+        const int rows = K - j0 - jb;
+        if (rows > 0) {
+            double* A21 = U + (long long)(j0 + jb) * K + j0;
+            hipLaunchKernelGGL(trsm_rows_kernel, dim3((rows + 15) / 16), dim3(256), 0, st, A21, (long long)K, rows,
+                               jb, Djj, (long long)K);
+            const hipError_t e = gemm<0, 0, 1>(rows, rows, jb, -1.0, A21, K, 1, A21, 1, K, 1.0,
+                                               U + (long long)(j0 + jb) * K + j0 + jb, K, 1, st);
+            if (e != hipSuccess) return e;
+        }
+    }
+    // 3. L^-1 in H, block row by block row: T = L[I, 0:r0] L^-1[0:r0, 0:r0] (stored transposed
+    //    in U's strictly upper block column I), L^-1[I, 0:r0] = -Dinv_I T
+    for (int r0 = NB; r0 < K; r0 += NB) {
+        const int ib = min(NB, K - r0);
+        hipError_t e = gemm<0, 0, 2>(ib, r0, r0, 1.0, U + (long long)r0 * K, K, 1, H, K, 1, 0.0, U + r0, 1, K, st);
+        if (e != hipSuccess) return e;
+        e = gemm<0, 0, 0>(ib, r0, ib, -1.0, H + (long long)r0 * K + r0, K, 1, U + r0, 1, K, 0.0,
+                          H + (long long)r0 * K, K, 1, st);
+        if (e != hipSuccess) return e;
+    }
+    // 4. U = P L^-1 P (upper; zeros below the diagonal)
+    hipLaunchKernelGGL((reverse_kernel<false, true>), dim3(blocks), dim3(256), 0, st, H, U, (long long)K);
+    return hipGetLastError();
+}
+
+hipError_t launch_gptq_quantize(const float* W, int N, int K, int g, int scheme, const double* U,
+                                double* work, uint32_t* qw, uint16_t* scales, uint16_t* zeros,
+                                hipStream_t st) {
+    double* Wd = work;
+    double* E = work + (long long)N * K;
+    const bool b64 = g % 64 == 0 && K % 64 == 0;
+    hipError_t e;
+    if (scheme == 0)
+        e = b64 ? gptq_loop<64, 0>(W, N, K, g, U, Wd, E, qw, scales, zeros, st)
+                : gptq_loop<32, 0>(W, N, K, g, U, Wd, E, qw, scales, zeros, st);
+    else
+        e = b64 ? gptq_loop<64, 1>(W, N, K, g, U, Wd, E, qw, scales, zeros, st)
+                : gptq_loop<32, 1>(W, N, K, g, U, Wd, E, qw, scales, zeros, st);
+    if (e != hipSuccess) return e;
+    if (scheme == 1 && zeros) {
+        const long long n = (long long)N * (K / g);
+        hipLaunchKernelGGL(fill_u16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, zeros, n,
+                           (uint16_t)0x4800);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace w4a16

@@ -35,4 +35,12 @@ hipError_t launch_skinny(const LinearArgs& a, hipStream_t s);
 hipError_t launch_decode(const LinearArgs& a, hipStream_t s);
 hipError_t launch_prefill(const LinearArgs& a, hipStream_t s);
 
+// GPTQ (gptq.hip)
+hipError_t launch_gptq_hessian(const void* X, int dtype, int n, int K, double* H, bool accumulate,
+                               hipStream_t s);
+hipError_t launch_gptq_factor(double* H, int K, double damp, double* U, hipStream_t s);
+hipError_t launch_gptq_quantize(const float* W, int N, int K, int g, int scheme, const double* U,
+                                double* work, uint32_t* qw, uint16_t* scales, uint16_t* zeros,
+                                hipStream_t s);
+
 }  // namespace w4a16

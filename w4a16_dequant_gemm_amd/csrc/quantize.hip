@@ -61,11 +61,9 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
     if (!active_group) return;
 
     // Scale (rounded to fp16 and used from then on) and zero point.
-    float s32 = (SCHEME == 0) ? (mx - mn) / 15.0f : mx / 7.0f;
-    _Float16 sh = (_Float16)s32;
-    float s = (float)sh;
-    if (s == 0.0f) { s = 1.0f; sh = (_Float16)1.0f; }
-    float z = (SCHEME == 0) ? (__builtin_rintf((-mn) / s) + 0.0f) : 8.0f;
+    _Float16 sh;
+    float s, z;
+    rtn_params<SCHEME>(mn, mx, sh, s, z);
 
     for (int it = 0; it < words_per_lane; ++it) {
         const int w = gl + it * seg;
@@ -75,17 +73,7 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
             const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
             uint32_t word = 0;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                float q;
-                if (SCHEME == 0) {
-                    q = __builtin_rintf(x[t] / s) + z;
-                    q = fminf(fmaxf(q, 0.0f), 15.0f);
-                } else {
-                    q = __builtin_rintf(x[t] / s);
-                    q = fminf(fmaxf(q, -8.0f), 7.0f) + 8.0f;
-                }
-                word |= ((uint32_t)(int)q & 0xFu) << (4 * t);
-            }
+            for (int t = 0; t < 8; ++t) word |= (rtn_code<SCHEME>(x[t], s, z) & 0xFu) << (4 * t);
             qw[(size_t)n * (K >> 3) + (size_t)j * (g >> 3) + w] = word;
         }
     }
