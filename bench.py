@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 
 METRIC = "W4A16 linear: weight-stream GB/s (% HBM peak) at M=1; TFLOP/s at M=4096"
 HBM_PEAK_GBS = 8000.0
+FP64_PEAK_TFLOPS = 78.6             # MI355X dense fp64
 MFMA_F16_PEAK_TFLOPS = 2500.0
 SHAPES = [(4096, 4096), (4096, 11008), (11008, 4096)]      # (K, N)
 GROUP = 128
@@ -460,7 +461,45 @@ def run_extras(layers, copies, W4, synth, torch, np):
         log(f"  prefill M=4096 K={K} N={N}: {tf:.1f} TFLOP/s (dense fp16 torch.matmul {tf_d:.1f})")
         del qw, s, z, X, Y, Wd
     out["prefill_m4096_fp16_g128"] = pre
+    out["gptq_4096x4096_g128"] = run_gptq(W4, synth, torch)
     return out
+
+
+def run_gptq(W4, synth, torch, n=2048, K=4096, N=4096, reps=3):
+    """GPTQ of one 4096 x 4096 layer from 2048 calibration rows: each entry point timed with
+    events on its own; algorithmic fp64 flops: Hessian lower triangle n K (K + 1), factor
+    (Cholesky + triangular inverse) 2 K^3 / 3, column compensation N K (K - 1)."""
+    X = synth.activations_device(n, K, synth.FP16, 4001)
+    W = synth.weights_device(N, K, 0.02, 4002)
+
+    def timed(fn, prep=None):
+        best = None
+        for _ in range(reps):
+            arg = prep() if prep else None
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            r = fn(arg)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        return best, r
+
+    ms_h, H = timed(lambda _: W4.gptq_hessian(X))
+    ms_f, U = timed(lambda Hc: W4.gptq_factor(Hc, 0.01), prep=lambda: H.clone())
+    work = torch.empty(N * K + 64 * N, dtype=torch.float64, device="cuda")
+    ms_q, _ = timed(lambda _: W4.gptq_quantize(W, U, GROUP, W4.ASYM, work=work))
+    res = {}
+    for name, ms, flops in (("hessian", ms_h, n * K * (K + 1)), ("factor", ms_f, 2 * K ** 3 / 3),
+                            ("quantize", ms_q, N * K * (K - 1))):
+        tf = flops / (ms * 1e-3) / 1e12
+        res[name] = {"ms": round(ms, 3), "fp64_TFLOPs": round(tf, 2),
+                     "frac_fp64_peak": round(tf / FP64_PEAK_TFLOPS, 4)}
+    res["total_ms"] = round(ms_h + ms_f + ms_q, 3)
+    log(f"  gptq 4096x4096 (n=2048): {res}")
+    del X, W, H, U, work
+    return res
 
 
 if __name__ == "__main__":

@@ -46,7 +46,8 @@ __device__ __forceinline__ double ld_elem(const void* p, long long i) {
 // C = beta * C + alpha * A B with A(m, k) = A[m sam + k sak], B(k, n) = B[k sbk + n sbn],
 // C(m, n) = C[m scm + n scn].  MODE bit 0: only tiles touching the lower triangle
 // (m >= n) are computed; bit 1: B is lower triangular (B(k, n) = 0 for k < n), so the
-// contraction of a tile starts at its first column.  beta == 0 never reads C.
+// contraction of a tile starts at its first column; bit 2: A is lower triangular
+// (A(m, k) = 0 for k > m), so it ends after the tile's last row.  beta == 0 never reads C.
 template <int AT, int BT, int MODE>
 __global__ __launch_bounds__(256) void gemm_f64_kernel(int M, int N, int K, double alpha,
                                                        const void* __restrict__ A, long long sam,
@@ -68,9 +69,10 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(int M, int N, int K, doub
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
     const int kbeg = (MODE & 2) ? (n0 / GKC) * GKC : 0;
+    const int kend = (MODE & 4) ? min(K, m0 + GT) : K;
     const bool a_krow = sak == 1;      // k contiguous in A
     const bool b_ncol = sbn == 1;      // n contiguous in B
-    for (int k0 = kbeg; k0 < K; k0 += GKC) {
+    for (int k0 = kbeg; k0 < kend; k0 += GKC) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int e = tid + 256 * r;
@@ -153,39 +155,78 @@ __global__ __launch_bounds__(256) void reverse_kernel(const double* __restrict__
 }
 
 // One diagonal block (jb <= 64) of the lower Cholesky factorization, in place, by one
-// workgroup; its inverse (lower, zeros above the diagonal) goes to Dinv.
+// workgroup; its inverse (lower, zeros above the diagonal) goes to Dinv.  Thread t owns
+// row i = t / 4, columns 16 (t % 4) .. + 15 of the block in registers for both
+// right-looking sweeps; the pivot column (Cholesky) or pivot row (inverse) of each step is
+// published through LDS (double-buffered: one barrier per step).  The updates are
+// branch-free: a zero multiplier leaves an element exactly as it is.  Rows and columns
+// past jb hold the identity, which factors and inverts to itself.
 __global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ A, long long lda, int jb,
                                                          double* __restrict__ Dinv, long long ldd) {
-    __shared__ double a[64][65];
-    __shared__ double inv[64][65];
+    __shared__ double col[2][64];
+    __shared__ double L[64][65];
+    __shared__ double rdiag[64];
     const int tid = threadIdx.x;
-    for (int e = tid; e < jb * jb; e += 256) a[e / jb][e % jb] = A[(long long)(e / jb) * lda + e % jb];
+    const int i = tid >> 2;
+    const int q = tid & 3;
+    double r[16];
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+        const int j = q * 16 + jj;
+        r[jj] = (i < jb && j < jb) ? A[(long long)i * lda + j] : (i == j ? 1.0 : 0.0);
+    }
+    // Cholesky: l_k = a[:, k] / sqrt(a[k][k]); a[i][j] -= l_i l_j for k < j <= i
+    for (int kq = 0; kq < 4; ++kq) {
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            const int k = kq * 16 + kk;
+            const int buf = k & 1;
+            if (q == kq) col[buf][i] = r[kk];
+            __syncthreads();
+            const double d = sqrt(col[buf][k]);
+            const double rd = 1.0 / d;
+            const double li = i == k ? d : (i > k ? col[buf][i] * rd : 0.0);
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) {
+                const int j = q * 16 + jj;
+                const double lj = (j > k && j <= i) ? col[buf][j] * rd : 0.0;
+                r[jj] = fma(-li, lj, r[jj]);
+            }
+            if (q == kq && i >= k) r[kk] = li;
+        }
+    }
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) L[i][q * 16 + jj] = r[jj];
     __syncthreads();
-    for (int k = 0; k < jb; ++k) {
-        if (tid == 0) a[k][k] = sqrt(a[k][k]);
-        __syncthreads();
-        if (tid > k && tid < jb) a[tid][k] /= a[k][k];
-        __syncthreads();
-        for (int e = tid; e < jb * jb; e += 256) {
-            const int i = e / jb, j = e % jb;
-            if (j > k && i >= j) a[i][j] -= a[i][k] * a[j][k];
+    if (tid < 64) rdiag[tid] = 1.0 / L[tid][tid];
+    // inverse: X = I; row k *= 1 / L[k][k]; rows i > k -= L[i][k] * row k
+    double x[16];
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) x[jj] = (i == q * 16 + jj) ? 1.0 : 0.0;
+    __syncthreads();
+    for (int k = 0; k < 64; ++k) {
+        const int buf = k & 1;
+        if (i == k) {
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) {
+                x[jj] *= rdiag[k];
+                col[buf][q * 16 + jj] = x[jj];
+            }
         }
         __syncthreads();
+        const double lik = i > k ? L[i][k] : 0.0;
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) x[jj] = fma(-lik, col[buf][q * 16 + jj], x[jj]);
     }
-    if (tid < jb) {                   // column c of L^-1 by forward substitution
-        const int c = tid;
-        for (int i = 0; i < jb; ++i) {
-            if (i < c) { inv[i][c] = 0.0; continue; }
-            double s = i == c ? 1.0 : 0.0;
-            for (int k = c; k < i; ++k) s -= a[i][k] * inv[k][c];
-            inv[i][c] = s / a[i][i];
+    if (i < jb) {
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+            const int j = q * 16 + jj;
+            if (j < jb) {
+                if (j <= i) A[(long long)i * lda + j] = r[jj];
+                Dinv[(long long)i * ldd + j] = j <= i ? x[jj] : 0.0;
+            }
         }
-    }
-    __syncthreads();
-    for (int e = tid; e < jb * jb; e += 256) {
-        const int i = e / jb, j = e % jb;
-        if (j <= i) A[(long long)i * lda + j] = a[i][j];
-        Dinv[(long long)i * ldd + j] = inv[i][j];
     }
 }
 
@@ -249,46 +290,81 @@ __global__ __launch_bounds__(256) void group_params_kernel(const double* __restr
     }
 }
 
-// One batch of B columns [c0, c0 + B) (inside one group), one lane per weight row: codes,
-// errors scaled by 1 / U[i][i] (to E, for the GEMM that updates the later columns) and the
-// in-batch compensation, column by column.
+// One batch of B columns [c0, c0 + B) (inside one group).  Four lanes share a weight row,
+// lane q of the quad holding columns q B/4 .. + B/4 - 1 in registers.  For each column the
+// owning lane decides the code and the error scaled by 1 / U[i][i], the quad takes it by a
+// DPP broadcast, and every lane compensates its later columns.  The scaled errors go to E
+// for the GEMM that updates the columns after the batch.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 template <int B, int SCHEME>
-__global__ __launch_bounds__(64) void gptq_batch_kernel(double* __restrict__ Wd, const double* __restrict__ U,
-                                                        int N, int K, int c0, int g, int G,
-                                                        const uint16_t* __restrict__ scales,
-                                                        const uint16_t* __restrict__ zeros,
-                                                        uint32_t* __restrict__ qw, double* __restrict__ E) {
+__global__ __launch_bounds__(256) void gptq_batch_kernel(double* __restrict__ Wd, const double* __restrict__ U,
+                                                         int N, int K, int c0, int g, int G,
+                                                         const uint16_t* __restrict__ scales,
+                                                         const uint16_t* __restrict__ zeros,
+                                                         uint32_t* __restrict__ qw, double* __restrict__ E) {
+    constexpr int Q = B / 4;            // columns per lane
     __shared__ double Us[B][B + 1];
-    const int lane = threadIdx.x;
-    for (int e = lane; e < B * B; e += 64) {
+    __shared__ double rinv[B];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < B * B; e += 256) {           // strictly upper part only
         const int i = e / B, j = e % B;
-        Us[i][j] = j >= i ? U[(long long)(c0 + i) * K + c0 + j] : 0.0;
+        Us[i][j] = j > i ? U[(long long)(c0 + i) * K + c0 + j] : 0.0;
     }
+    if (tid < B) rinv[tid] = 1.0 / U[(long long)(c0 + tid) * K + c0 + tid];
     __syncthreads();
-    const int n = blockIdx.x * 64 + lane;
-    if (n >= N) return;
-    double* row = Wd + (long long)n * K + c0;
-    double w[B];
+    const int q = tid & 3;
+    const int n_raw = blockIdx.x * 64 + (tid >> 2);
+    const bool live = n_raw < N;
+    const int n = live ? n_raw : N - 1;            // dead rows compute, never store
+    double* row = Wd + (long long)n * K + c0 + q * Q;
+    double w[Q], eown[Q];
 #pragma unroll
-    for (int j = 0; j < B; ++j) w[j] = row[j];
+    for (int j = 0; j < Q; ++j) w[j] = row[j];
     const int grp = c0 / g;
     const float s = h2f(scales[(long long)n * G + grp]);
     const float z = SCHEME == 0 ? h2f(zeros[(long long)n * G + grp]) : 8.0f;
     const double sd = (double)s, zd = (double)z;
-    uint32_t words[B / 8];
+    uint32_t words[Q / 8];
 #pragma unroll
-    for (int t = 0; t < B / 8; ++t) words[t] = 0u;
+    for (int t = 0; t < Q / 8; ++t) words[t] = 0u;
+    // column i = o Q + ii belongs to lane o of the quad; the (uniform) loop over o keeps
+    // every register index static
+    for (int o = 0; o < 4; ++o) {
 #pragma unroll
-    for (int i = 0; i < B; ++i) {
-        const uint32_t q = rtn_code<SCHEME>((float)w[i], s, z);
-        words[i / 8] |= (q & 0xFu) << (4 * (i % 8));
-        const double e = (w[i] - sd * ((double)q - zd)) / Us[i][i];
-        E[(long long)n * B + i] = e;
+        for (int ii = 0; ii < Q; ++ii) {
+            const int i = o * Q + ii;
+            // every lane evaluates its own column ii; only the owner's result is used
+            const uint32_t qc = rtn_code<SCHEME>((float)w[ii], s, z);
+            const double e_mine = (w[ii] - sd * ((double)qc - zd)) * rinv[i];
+            double e;       // quad_perm broadcast of lane o
+            switch (o) {
+                case 0: e = dpp_f64<0x00>(e_mine); break;
+                case 1: e = dpp_f64<0x55>(e_mine); break;
+                case 2: e = dpp_f64<0xAA>(e_mine); break;
+                default: e = dpp_f64<0xFF>(e_mine); break;
+            }
+            if (q == o) {
+                words[ii / 8] |= (qc & 0xFu) << (4 * (ii % 8));
+                eown[ii] = e;
+            }
+            // Us holds zeros on and below the diagonal: earlier columns stay exact
 #pragma unroll
-        for (int j = i + 1; j < B; ++j) w[j] = fma(-e, Us[i][j], w[j]);
+            for (int jj = 0; jj < Q; ++jj) w[jj] = fma(-e, Us[i][q * Q + jj], w[jj]);
+        }
     }
+    if (live) {
 #pragma unroll
-    for (int t = 0; t < B / 8; ++t) qw[(long long)n * (K / 8) + c0 / 8 + t] = words[t];
+        for (int jj = 0; jj < Q; ++jj) E[(long long)n * B + q * Q + jj] = eown[jj];
+#pragma unroll
+        for (int t = 0; t < Q / 8; ++t) qw[(long long)n * (K / 8) + c0 / 8 + q * (Q / 8) + t] = words[t];
+    }
 }
 
 template <int B, int SCHEME>
@@ -301,8 +377,8 @@ hipError_t gptq_loop(const float* W, int N, int K, int g, const double* U, doubl
         if (c0 % g == 0)
             hipLaunchKernelGGL(group_params_kernel<SCHEME>, dim3((N + 3) / 4), dim3(256), 0, st, Wd, N, K, c0,
                                g, G, scales, SCHEME == 0 ? zeros : nullptr);
-        hipLaunchKernelGGL((gptq_batch_kernel<B, SCHEME>), dim3((N + 63) / 64), dim3(64), 0, st, Wd, U, N, K,
-                           c0, g, G, scales, zeros, qw, E);
+        hipLaunchKernelGGL((gptq_batch_kernel<B, SCHEME>), dim3((N + 63) / 64), dim3(256), 0, st, Wd, U, N,
+                           K, c0, g, G, scales, zeros, qw, E);
         const int rest = K - c0 - B;
         if (rest > 0) {
             const hipError_t e = gemm<0, 0, 0>(N, rest, B, -1.0, E, B, 1, U + (long long)c0 * K + c0 + B, K, 1,
@@ -329,6 +405,31 @@ hipError_t launch_gptq_hessian(const void* X, int dtype, int n, int K, double* H
     return gemm<2, 2, 1>(K, K, n, 2.0, X, 1, K, X, K, 1, beta, H, K, 1, st);
 }
 
+namespace {
+
+// Inverse of the lower-triangular L (lower part of U) on the diagonal block [o, o + n), by
+// halves: with L = [A 0; B C], L^-1 = [A^-1 0; -C^-1 B A^-1  C^-1].  A^-1 and C^-1 first
+// (recursively; 64-blocks come from the diagonal factorization), then T = B A^-1, stored
+// transposed in U's strictly upper part of the block, and -C^-1 T into H.
+hipError_t trtri_lower(double* U, double* H, int K, int o, int n, hipStream_t st) {
+    if (n <= 64) return hipSuccess;
+    const int n1 = ((n / 2 + 63) / 64) * 64;
+    const int n2 = n - n1;
+    hipError_t e = trtri_lower(U, H, K, o, n1, st);
+    if (e != hipSuccess) return e;
+    e = trtri_lower(U, H, K, o + n1, n2, st);
+    if (e != hipSuccess) return e;
+    const long long lk = K;
+    double* T = U + (long long)o * K + o + n1;          // T(m, n) at T[n K + m]
+    e = gemm<0, 0, 2>(n2, n1, n1, 1.0, U + (long long)(o + n1) * K + o, lk, 1, H + (long long)o * K + o, lk, 1,
+                      0.0, T, 1, lk, st);
+    if (e != hipSuccess) return e;
+    return gemm<0, 0, 4>(n2, n1, n2, -1.0, H + (long long)(o + n1) * K + o + n1, lk, 1, T, 1, lk, 0.0,
+                         H + (long long)(o + n1) * K + o, lk, 1, st);
+}
+
+}  // namespace
+
 hipError_t launch_gptq_factor(double* H, int K, double damp, double* U, hipStream_t st) {
     constexpr int NB = 64;
     const long long kk = (long long)K * K;
@@ -352,16 +453,9 @@ hipError_t launch_gptq_factor(double* H, int K, double damp, double* U, hipStrea
             if (e != hipSuccess) return e;
         }
     }
-    // 3. L^-1 in H, block row by block row: T = L[I, 0:r0] L^-1[0:r0, 0:r0] (stored transposed
-    //    in U's strictly upper block column I), L^-1[I, 0:r0] = -Dinv_I T
-    for (int r0 = NB; r0 < K; r0 += NB) {
-        const int ib = min(NB, K - r0);
-        hipError_t e = gemm<0, 0, 2>(ib, r0, r0, 1.0, U + (long long)r0 * K, K, 1, H, K, 1, 0.0, U + r0, 1, K, st);
-        if (e != hipSuccess) return e;
-        e = gemm<0, 0, 0>(ib, r0, ib, -1.0, H + (long long)r0 * K + r0, K, 1, U + r0, 1, K, 0.0,
-                          H + (long long)r0 * K, K, 1, st);
-        if (e != hipSuccess) return e;
-    }
+    // 3. L^-1 in H (lower; the 64-blocks on the diagonal are already there)
+    hipError_t e = trtri_lower(U, H, K, 0, K, st);
+    if (e != hipSuccess) return e;
     // 4. U = P L^-1 P (upper; zeros below the diagonal)
     hipLaunchKernelGGL((reverse_kernel<false, true>), dim3(blocks), dim3(256), 0, st, H, U, (long long)K);
     return hipGetLastError();
