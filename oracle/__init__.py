@@ -26,9 +26,13 @@ What it computes (sources are the five pages on W4A16 quantization):
   quantization with the optimal-brain-surgeon compensation of the columns still free
   (page 4, section 四 GPTQ; page "量化实战深入（GPTQ / AWQ / SmoothQuant / KV 量化）", 4.1).
 
+* AWQ (``awq.py``): per-input-channel rescaling ``W x = (W diag(1/s)) (diag(s) x)`` with
+  ``s`` from the channels' mean activation magnitude, chosen by a grid search on the
+  quantized layer's output error (page 4, section 五 AWQ).
+
 Readings where the pages are silent (tie rule, clamping, which scale feeds the
 zero point, nibble order, symmetric storage) are listed in the docstrings of
-``quant.py``, ``linear.py`` and ``gptq.py``.
+``quant.py``, ``linear.py``, ``gptq.py`` and ``awq.py``.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against hand-worked vectors, closed forms, exact rational arithmetic or an

@@ -1,0 +1,97 @@
+"""Pins for the AWQ oracle (CPU only).
+
+* the channel statistic against a brute-force loop;
+* candidate scales against an independent power function, the normalization (geometric
+  centre 1), reciprocal symmetry and the exact identity at a = 0;
+* the output error of the E-form equals the error of the page's rescaled product
+  (W diag(1/s)) (diag(s) x), so the transform's direction is consistent everywhere;
+* a = 0 is plain RTN (codes and loss); the search returns the first minimum;
+* on calibration data with outlier channels the search beats RTN by enlarging the
+  salient channels' weights (a < 0);
+* the scaled activations are rounded once (exact rational check).
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import awq as A
+from oracle import formats as F
+from oracle import gptq as G
+from synth import BF16, FP16, calibration, weights
+
+
+def test_channel_mean_abs_brute_force():
+    X = calibration(9, 6, FP16, seed=1)
+    got = A.channel_mean_abs(X, FP16)
+    for k in range(6):
+        ref = sum(abs(float(X[t, k])) for t in range(9)) / 9.0
+        assert got[k] == np.float32(ref)
+
+
+def test_candidate_scales():
+    xm = np.array([0.5, 2.0, 8.0, 1e-9, 3.0], dtype=np.float32)
+    r = A.candidate_ratio(xm)
+    # clamp at 1e-6 * max, geometric centre of the extremes at 1
+    assert r[3] == pytest.approx(8e-6 / np.sqrt(8.0 * 8e-6), rel=1e-6)
+    assert np.sqrt(float(r.max()) * float(r.min())) == pytest.approx(1.0, rel=2e-7)
+    np.testing.assert_array_equal(A.candidate_scales(xm, 0), np.ones(5, np.float32))
+    for a in A.GRID:
+        s = A.candidate_scales(xm, a).astype(np.float64)
+        np.testing.assert_allclose(s, r.astype(np.float64) ** (a / 4.0), rtol=6e-7)
+        s_neg = A.candidate_scales(xm, -a).astype(np.float64)
+        np.testing.assert_allclose(s * s_neg, 1.0, rtol=1e-6)
+
+
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+def test_loss_is_error_of_rescaled_product(dtype):
+    X = calibration(64, 128, dtype, seed=2)
+    W = weights(24, 128, 0.02, seed=3)
+    xm = A.channel_mean_abs(X, dtype)
+    for a in (-3, 2):
+        s = A.candidate_scales(xm, a)
+        codes, sc, z = oracle.quantize((W / s[None, :]).astype(np.float32), 32, oracle.ASYM)
+        x = oracle.linear._x64(X, dtype)
+        y_ref = x @ W.astype(np.float64).T
+        y_q = (x * s.astype(np.float64)[None, :]) @ oracle.dequantize(oracle.pack(codes), sc, z, 32).T
+        direct = float(np.sum((y_ref - y_q) ** 2))
+        assert A.awq_loss(X, dtype, W, s, codes, sc, z, 32) == pytest.approx(direct, rel=1e-9)
+
+
+def test_zero_exponent_is_rtn_and_first_minimum():
+    X = calibration(128, 256, FP16, seed=4)
+    W = weights(32, 256, 0.02, seed=5)
+    xm = A.channel_mean_abs(X, FP16)
+    best, losses, s, codes, sc, z = A.awq_search(W, X, FP16, xm, 128, oracle.ASYM)
+    rc, rs, rz = oracle.quantize(W, 128, oracle.ASYM)
+    i0 = A.GRID.index(0)
+    rtn_loss = G.layer_error(X, FP16, W, oracle.dequantize(oracle.pack(rc), rs, rz, 128)) / 1.0
+    assert losses[i0] == pytest.approx(rtn_loss, rel=1e-12)
+    assert losses[best] <= losses[i0]
+    assert best == int(np.flatnonzero(losses == losses.min())[0])
+
+
+@pytest.mark.parametrize("scheme", [oracle.ASYM, oracle.SYM])
+def test_outlier_channels_favour_enlarged_salient_weights(scheme):
+    X = calibration(256, 512, FP16, seed=6, outlier_frac=0.01, outlier_mult=20.0)
+    W = weights(64, 512, 0.02, seed=7)
+    xm = A.channel_mean_abs(X, FP16)
+    best, losses, s, codes, sc, z = A.awq_search(W, X, FP16, xm, 128, scheme)
+    assert A.GRID[best] < 0
+    assert losses[best] < 0.8 * losses[A.GRID.index(0)]
+    # the salient channels' weights were enlarged: the quantizer sees W / s with s < 1
+    top = np.argsort(xm)[-5:]
+    assert np.all(s[top] < 1.0)
+    # and the page's literal direction (s > 1 on salient channels, a > 0) is worse than RTN
+    assert np.all(losses[A.GRID.index(1):] > losses[A.GRID.index(0)])
+
+
+def test_scaled_activations_round_once():
+    X = np.array([[1.0009765625, -3.0, 65504.0 / 4]], dtype=np.float16)
+    s = np.array([1.3333333, 0.1, 3.0], dtype=np.float32)
+    got = A.scale_activations(X, FP16, s)
+    for k in range(3):
+        exact = Fraction(float(X[0, k])) * Fraction(float(s[k]))
+        assert float(got[0, k]) == F.round_fraction_to_format(exact, F.F16)
