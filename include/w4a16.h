@@ -183,6 +183,56 @@ int w4a16_gptq_quantize(const float* W, int64_t N, int64_t K, int64_t group_size
                         const double* U, double* work, int32_t* qweight, uint16_t* scales,
                         uint16_t* zeros, void* stream);
 
+/*
+ * AWQ: activation-aware per-input-channel scaling before group-wise RTN.  Page
+ * "推理优化中“用精度换性能“的核心技术：量化", section 五 (5.1 channel importance from the mean
+ * activation magnitude on calibration data; 5.2 the exact rescaling
+ * W x = (W diag(1/s)) (diag(s) x), the scale chosen by a grid search on the quantized
+ * layer's output error; 5.3 plain per-group quantization afterwards); page "量化实战深入
+ * （GPTQ / AWQ / SmoothQuant / KV 量化）", 4.2.  Candidates are s = r^(a/4), a = -4 .. 4, with
+ * r = xc / sqrt(max xc * min xc), xc = max(xmean, 1e-6 * max xmean); a = 0 is plain RTN.
+ * The quantizer sees the fp32 quotient W / s; at inference the activations must be
+ * multiplied by s (w4a16_awq_scale, or folded into the preceding operator).
+ */
+
+/* Number of fp64 elements of the w4a16_awq_search workspace (host only), or a negative
+ * status. */
+int64_t w4a16_awq_workspace(int64_t N, int64_t K, int64_t n_samples);
+
+/*
+ * w4a16_awq_stats -- xmean[k] = mean over the n_samples rows of |X[t][k]| (fp64 sum, fp32
+ * result).  X [n_samples, K] fp16/bf16 device (2-byte aligned); xmean [K] fp32 device.
+ */
+int w4a16_awq_stats(const void* X, int dtype, int64_t n_samples, int64_t K, float* xmean,
+                    void* stream);
+
+/*
+ * w4a16_awq_search -- for each of the nine candidates quantize W / s with the RTN rules of
+ * w4a16_quantize_pack and measure ||X W^T - (X diag(s)) (W_hat')^T||_F^2 in fp64 on the
+ * calibration rows X [n_samples, K]; keep the first minimum.
+ *   W        [N, K] fp32 device (4-byte aligned).
+ *   xmean    [K] fp32 device, from w4a16_awq_stats (or any positive channel statistic).
+ *   work     fp64 device workspace of w4a16_awq_workspace(N, K, n_samples) elements.
+ *   losses   out [9] fp64 device: the error of each candidate, a = -4 .. 4.
+ *   best     out [1] int32 device: index into losses of the chosen candidate.
+ *   s_out    out [K] fp32 device: the chosen scales s.
+ *   qweight, scales, zeros: out, the packed quantization of W / s (zeros may be NULL for
+ *            the symmetric scheme).
+ * Limits: N * K <= 2^34, n_samples * N <= 2^34.
+ */
+int w4a16_awq_search(const float* W, int64_t N, int64_t K, const void* X, int dtype,
+                     int64_t n_samples, const float* xmean, int64_t group_size, int scheme,
+                     double* work, double* losses, int32_t* best, float* s_out, int32_t* qweight,
+                     uint16_t* scales, uint16_t* zeros, void* stream);
+
+/*
+ * w4a16_awq_scale -- Y[m][k] = X[m][k] * s[k] rounded once to the dtype of X (the exact
+ * product, round-to-nearest-even).  X, Y [M, K] fp16/bf16 device (2-byte aligned, may be the
+ * same buffer); s [K] fp32 device.
+ */
+int w4a16_awq_scale(const void* X, int dtype, int64_t M, int64_t K, const float* s, void* Y,
+                    void* stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* w4a16_strerror(int status);
 

@@ -21,7 +21,7 @@ MIS = 0x10002     # misaligned for 16-byte requirements
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(w4a16_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|const char\*)\s+(w4a16_\w+)\s*\(", text, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -37,7 +37,8 @@ def test_header_declares_the_boundary():
     for required in ("w4a16_quantize_pack", "w4a16_linear", "w4a16_linear_ex",
                      "w4a16_select_path", "w4a16_dequantize", "w4a16_strerror",
                      "w4a16_abi_version", "w4a16_gptq_hessian", "w4a16_gptq_factor",
-                     "w4a16_gptq_quantize"):
+                     "w4a16_gptq_quantize", "w4a16_awq_workspace", "w4a16_awq_stats",
+                     "w4a16_awq_search", "w4a16_awq_scale"):
         assert required in names
 
 
@@ -149,3 +150,27 @@ def test_gptq_rejects_invalid_arguments(lib):
     assert q(K=100, g=100) == L.ERR_SHAPE
     assert q(g=48) == L.ERR_GROUP
     assert q(U=B + 4) == L.ERR_ALIGN
+
+
+def test_awq_workspace_and_invalid_arguments(lib):
+    assert lib.w4a16_awq_workspace(64, 128, 32) >= 64 * 128 + 32 * 64 + 9 * 128 // 2
+    assert lib.w4a16_awq_workspace(0, 128, 32) == L.ERR_SHAPE
+    assert lib.w4a16_awq_stats(None, 0, 8, 64, A, None) == L.ERR_NULL
+    assert lib.w4a16_awq_stats(A, 2, 8, 64, B, None) == L.ERR_DTYPE
+    assert lib.w4a16_awq_stats(A, 0, 0, 64, B, None) == L.ERR_SHAPE
+    assert lib.w4a16_awq_stats(A, 0, 8, 64, B + 2, None) == L.ERR_ALIGN
+    s = lambda **kw: lib.w4a16_awq_search(kw.get("W", A), 64, kw.get("K", 128), kw.get("X", B), kw.get("dt", 0),
+                                          32, kw.get("xm", C), kw.get("g", 128), kw.get("scheme", 0),
+                                          kw.get("work", D), D + 0x100000, D + 0x200000, D + 0x300000,
+                                          D + 0x400000, D + 0x500000, kw.get("z", D + 0x600000), None)
+    assert s(W=None) == L.ERR_NULL
+    assert s(xm=None) == L.ERR_NULL
+    assert s(z=None) == L.ERR_NULL
+    assert s(dt=5) == L.ERR_DTYPE
+    assert s(scheme=2) == L.ERR_SCHEME
+    assert s(K=100, g=100) == L.ERR_SHAPE
+    assert s(g=96) == L.ERR_GROUP
+    assert s(work=D + 4) == L.ERR_ALIGN
+    assert lib.w4a16_awq_scale(A, 0, 4, 64, None, B, None) == L.ERR_NULL
+    assert lib.w4a16_awq_scale(A, 0, 0, 64, C, B, None) == L.ERR_SHAPE
+    assert lib.w4a16_awq_scale(A + 1, 0, 4, 64, C, B, None) == L.ERR_ALIGN

@@ -12,6 +12,9 @@ the library's HIP kernels; there is no CPU or PyTorch fallback.
 ``gptq_hessian(X, H=None)`` / ``gptq_factor(H, damp)`` / ``gptq_quantize(W, U, group_size, scheme)``
     GPTQ: ``H = 2 X^T X`` (fp64, lower triangle), the upper Cholesky factor ``U`` of the
     damped inverse, and the compensated column-wise quantization in the packed format.
+``awq_stats(X)`` / ``awq_search(W, X, xmean, group_size, scheme)`` / ``awq_scale(X, s)``
+    AWQ: per-channel activation statistic, grid search over channel scalings, and the
+    activation side of the rescaling.
 """
 
 from __future__ import annotations
@@ -24,7 +27,8 @@ from ._lib import (ASYM, BF16, F16, OK, PATH_AUTO, PATH_GEMV, PATH_NAMES, PATH_P
 __all__ = [
     "ASYM", "SYM", "F16", "BF16", "PATH_AUTO", "PATH_GEMV", "PATH_SKINNY", "PATH_PREFILL",
     "PATH_NAMES", "W4A16Error", "quantize_pack", "linear", "dequantize", "select_path",
-    "abi_version", "lib", "gptq_hessian", "gptq_factor", "gptq_quantize",
+    "abi_version", "lib", "gptq_hessian", "gptq_factor", "gptq_quantize", "awq_stats",
+    "awq_search", "awq_scale",
 ]
 
 
@@ -189,3 +193,64 @@ def gptq_quantize(W: torch.Tensor, U: torch.Tensor, group_size: int = 128, schem
                                     work.data_ptr(), qweight.data_ptr(), scales.data_ptr(),
                                     zeros.data_ptr(), _stream()), "w4a16_gptq_quantize")
     return qweight, scales, zeros
+
+
+def awq_stats(X: torch.Tensor) -> torch.Tensor:
+    """Mean ``|x|`` per input channel of calibration activations ``X [n, K]`` (fp32 ``[K]``)."""
+    dt = _dtype_code(X)
+    _need(X, "X", X.dtype, 2)
+    n, K = X.shape
+    out = torch.empty(K, dtype=torch.float32, device=X.device)
+    check(lib().w4a16_awq_stats(X.data_ptr(), dt, n, K, out.data_ptr(), _stream()), "w4a16_awq_stats")
+    return out
+
+
+def awq_search(W: torch.Tensor, X: torch.Tensor, xmean: torch.Tensor, group_size: int = 128,
+               scheme: int = ASYM):
+    """Grid search of the channel scaling; returns ``(qweight, scales, zeros, s, losses,
+    best)`` (``s`` fp32 ``[K]``, ``losses`` fp64 ``[9]``, ``best`` int32 ``[1]``, all on the
+    GPU)."""
+    _need(W, "W", torch.float32, 2)
+    dt = _dtype_code(X)
+    _need(X, "X", X.dtype, 2)
+    _need(xmean, "xmean", torch.float32, 1)
+    N, K = W.shape
+    n = X.shape[0]
+    if X.shape[1] != K or xmean.shape[0] != K:
+        raise ValueError("X must be [n, K] and xmean [K]")
+    if K % 8 or group_size <= 0 or K % group_size:
+        raise ValueError("K must be a multiple of 8 and of group_size")
+    L = lib()
+    need = L.w4a16_awq_workspace(N, K, n)
+    if need < 0:
+        raise W4A16Error(int(need), "w4a16_awq_workspace")
+    work = torch.empty(need, dtype=torch.float64, device=W.device)
+    G = K // group_size
+    qweight = torch.empty((N, K // 8), dtype=torch.int32, device=W.device)
+    scales = torch.empty((N, G), dtype=torch.float16, device=W.device)
+    zeros = torch.empty((N, G), dtype=torch.float16, device=W.device)
+    s = torch.empty(K, dtype=torch.float32, device=W.device)
+    losses = torch.empty(9, dtype=torch.float64, device=W.device)
+    best = torch.empty(1, dtype=torch.int32, device=W.device)
+    check(L.w4a16_awq_search(W.data_ptr(), N, K, X.data_ptr(), dt, n, xmean.data_ptr(), group_size,
+                             scheme, work.data_ptr(), losses.data_ptr(), best.data_ptr(), s.data_ptr(),
+                             qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(), _stream()),
+          "w4a16_awq_search")
+    return qweight, scales, zeros, s, losses, best
+
+
+def awq_scale(X: torch.Tensor, s: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """``X * s`` per input channel, rounded once to the dtype of ``X``."""
+    dt = _dtype_code(X)
+    _need(X, "X", X.dtype, 2)
+    _need(s, "s", torch.float32, 1)
+    M, K = X.shape
+    if s.shape[0] != K:
+        raise ValueError("s must be [K]")
+    if out is None:
+        out = torch.empty_like(X)
+    else:
+        _need(out, "out", X.dtype, 2)
+    check(lib().w4a16_awq_scale(X.data_ptr(), dt, M, K, s.data_ptr(), out.data_ptr(), _stream()),
+          "w4a16_awq_scale")
+    return out

@@ -59,6 +59,15 @@ def lib() -> ctypes.CDLL:
     L.w4a16_gptq_hessian.argtypes = [vp, i32, i64, i64, vp, i32, vp]
     L.w4a16_gptq_factor.restype = i32
     L.w4a16_gptq_factor.argtypes = [vp, i64, ctypes.c_double, vp, vp]
+    L.w4a16_awq_workspace.restype = i64
+    L.w4a16_awq_workspace.argtypes = [i64, i64, i64]
+    L.w4a16_awq_stats.restype = i32
+    L.w4a16_awq_stats.argtypes = [vp, i32, i64, i64, vp, vp]
+    L.w4a16_awq_search.restype = i32
+    L.w4a16_awq_search.argtypes = [vp, i64, i64, vp, i32, i64, vp, i64, i32, vp, vp, vp, vp, vp, vp,
+                                   vp, vp]
+    L.w4a16_awq_scale.restype = i32
+    L.w4a16_awq_scale.argtypes = [vp, i32, i64, i64, vp, vp, vp]
     L.w4a16_gptq_quantize.restype = i32
     L.w4a16_gptq_quantize.argtypes = [vp, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp]
     _lib = L

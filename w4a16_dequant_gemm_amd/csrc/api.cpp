@@ -205,6 +205,58 @@ int w4a16_gptq_quantize(const float* W, int64_t N, int64_t K, int64_t group_size
                                                   static_cast<hipStream_t>(stream)));
 }
 
+int64_t w4a16_awq_workspace(int64_t N, int64_t K, int64_t n_samples) {
+    if (N < 1 || K < 1 || n_samples < 1) return W4A16_ERR_SHAPE;
+    return w4a16::awq_workspace_doubles(N, K, n_samples);
+}
+
+int w4a16_awq_stats(const void* X, int dtype, int64_t n_samples, int64_t K, float* xmean,
+                    void* stream) {
+    if (!X || !xmean) return W4A16_ERR_NULL;
+    if (dtype != W4A16_F16 && dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
+    if (n_samples < 1 || K < 1 || n_samples > kMaxDim || K > kMaxDim) return W4A16_ERR_SHAPE;
+    if (n_samples * K > (int64_t(1) << 40)) return W4A16_ERR_SHAPE;
+    if (!aligned(X, 2) || !aligned(xmean, 4)) return W4A16_ERR_ALIGN;
+    return hip_status(w4a16::launch_awq_stats(X, dtype, (int)n_samples, (int)K, xmean,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_awq_search(const float* W, int64_t N, int64_t K, const void* X, int dtype,
+                     int64_t n_samples, const float* xmean, int64_t group_size, int scheme,
+                     double* work, double* losses, int32_t* best, float* s_out, int32_t* qweight,
+                     uint16_t* scales, uint16_t* zeros, void* stream) {
+    if (!W || !X || !xmean || !work || !losses || !best || !s_out || !qweight || !scales)
+        return W4A16_ERR_NULL;
+    if (dtype != W4A16_F16 && dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
+    if (scheme != W4A16_ASYM_RTN && scheme != W4A16_SYM_ABSMAX) return W4A16_ERR_SCHEME;
+    if (scheme == W4A16_ASYM_RTN && !zeros) return W4A16_ERR_NULL;
+    int G = 0, gshift = 0;
+    const int st = check_shape_group(N, K, group_size, &G, &gshift);
+    if (st != W4A16_OK) return st;
+    if (n_samples < 1 || n_samples > kMaxDim || N * K > (int64_t(1) << 34) ||
+        n_samples * N > (int64_t(1) << 34))
+        return W4A16_ERR_SHAPE;
+    if (!aligned(W, 4) || !aligned(X, 2) || !aligned(xmean, 4) || !aligned(work, 8) ||
+        !aligned(losses, 8) || !aligned(best, 4) || !aligned(s_out, 4) || !aligned(qweight, 4) ||
+        !aligned(scales, 2) || (zeros && !aligned(zeros, 2)))
+        return W4A16_ERR_ALIGN;
+    return hip_status(w4a16::launch_awq_search(
+        W, (int)N, (int)K, X, dtype, (int)n_samples, xmean, (int)group_size, scheme, work, losses,
+        reinterpret_cast<int*>(best), s_out, reinterpret_cast<uint32_t*>(qweight), scales, zeros,
+        static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_awq_scale(const void* X, int dtype, int64_t M, int64_t K, const float* s, void* Y,
+                    void* stream) {
+    if (!X || !s || !Y) return W4A16_ERR_NULL;
+    if (dtype != W4A16_F16 && dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
+    if (M < 1 || K < 1 || M > kMaxDim || K > kMaxDim || M * K > (int64_t(1) << 42))
+        return W4A16_ERR_SHAPE;
+    if (!aligned(X, 2) || !aligned(s, 4) || !aligned(Y, 2)) return W4A16_ERR_ALIGN;
+    return hip_status(w4a16::launch_awq_scale(X, dtype, M, (int)K, s, Y,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 int w4a16_select_path(int64_t M, int64_t N, int64_t K, int64_t group_size, int dtype) {
     // Fake, aligned, non-null pointers: only shapes are examined.
     alignas(16) static const unsigned char dummy[16] = {0};

@@ -39,6 +39,15 @@ hipError_t launch_prefill(const LinearArgs& a, hipStream_t s);
 hipError_t launch_gptq_hessian(const void* X, int dtype, int n, int K, double* H, bool accumulate,
                                hipStream_t s);
 hipError_t launch_gptq_factor(double* H, int K, double damp, double* U, hipStream_t s);
+// AWQ (awq.hip)
+long long awq_workspace_doubles(long long N, long long K, long long n);
+hipError_t launch_awq_stats(const void* X, int dtype, int n, int K, float* xmean, hipStream_t s);
+hipError_t launch_awq_search(const float* W, int N, int K, const void* X, int dtype, int n,
+                             const float* xmean, int g, int scheme, double* work, double* losses,
+                             int* best, float* s_out, uint32_t* qw, uint16_t* scales,
+                             uint16_t* zeros, hipStream_t s);
+hipError_t launch_awq_scale(const void* X, int dtype, long long M, int K, const float* s, void* Y,
+                            hipStream_t st);
 hipError_t launch_gptq_quantize(const float* W, int N, int K, int g, int scheme, const double* U,
                                 double* work, uint32_t* qw, uint16_t* scales, uint16_t* zeros,
                                 hipStream_t s);
