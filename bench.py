@@ -37,9 +37,9 @@ GROUP = 128
 
 
 # Kernel instantiation serving each layer at M = 1 (fp16, g = 128), as rocprofv3 names it.
-KERNEL_NAMES = {(4096, 4096): "gemv_stream_kernel<0, 1, 2, 2, 8, 1>",
+KERNEL_NAMES = {(4096, 4096): "gemv_stream_kernel<0, 1, 2, 2, 8, 0>",
                 (4096, 11008): "gemv_stream_kernel<0, 1, 2, 2, 8, 2>",
-                (11008, 4096): "gemv_stream_kernel<0, 1, 6, 2, 8, 1>"}
+                (11008, 4096): "gemv_stream_kernel<0, 1, 6, 2, 8, 0>"}
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "w4a16_dequant_gemm_amd", "csrc", f)
                   for f in ("gemv.hip", "common.h")]
@@ -462,6 +462,40 @@ def run_extras(layers, copies, W4, synth, torch, np):
         del qw, s, z, X, Y, Wd
     out["prefill_m4096_fp16_g128"] = pre
     out["gptq_4096x4096_g128"] = run_gptq(W4, synth, torch)
+    out["awq_4096x4096_g128"] = run_awq(W4, synth, torch)
+    return out
+
+
+def run_awq(W4, synth, torch, n=512, K=4096, N=4096, reps=3):
+    """AWQ of one 4096 x 4096 layer from 512 calibration rows with outlier channels: the
+    statistic and the nine-candidate search timed with events; algorithmic fp64 flops of the
+    search are its nine output-error products, 9 * 2 n N K."""
+    X = synth.calibration_device(n, K, synth.FP16, 5001, outlier_frac=0.01, outlier_mult=20.0)
+    W = synth.weights_device(N, K, 0.02, 5002)
+    best_ms = {"stats": None, "search": None}
+    res = None
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        xm = W4.awq_stats(X)
+        e[1].record()
+        res = W4.awq_search(W, X, xm, GROUP, W4.ASYM)
+        e[2].record()
+        torch.cuda.synchronize()
+        for k, (a, b) in (("stats", (0, 1)), ("search", (1, 2))):
+            ms = e[a].elapsed_time(e[b])
+            best_ms[k] = ms if best_ms[k] is None else min(best_ms[k], ms)
+    losses = res[4].cpu().numpy()
+    best = int(res[5].cpu().numpy()[0])
+    flops = 9 * 2.0 * n * N * K
+    tf = flops / (best_ms["search"] * 1e-3) / 1e12
+    out = {"stats_ms": round(best_ms["stats"], 3), "search_ms": round(best_ms["search"], 3),
+           "search_fp64_TFLOPs": round(tf, 2), "frac_fp64_peak": round(tf / FP64_PEAK_TFLOPS, 4),
+           "best_exponent_quarters": best - 4,
+           "loss_vs_rtn": round(float(losses[best] / losses[4]), 4)}
+    log(f"  awq 4096x4096 (n=512): {out}")
+    del X, W, res
     return out
 
 

@@ -180,6 +180,15 @@ def weights_device(N: int, K: int, sigma: float, seed: int, device="cuda",
     return W
 
 
+def calibration_device(n: int, K: int, dtype: int, seed: int, device="cuda", **kw):
+    """:func:`calibration` uploaded as a torch tensor (fp16, or bf16 viewed from the bits)."""
+    import torch
+    X = calibration(n, K, dtype, seed, **kw)
+    if dtype == FP16:
+        return torch.from_numpy(X).to(device)
+    return torch.from_numpy(X.view(np.int16)).to(device).view(torch.bfloat16)
+
+
 def activations_device(M: int, K: int, dtype: int, seed: int, device="cuda",
                        outlier_frac: float = 0.0, outlier_mult: float = 1.0):
     """``[M, K]`` fp16 or bf16 activations on the GPU (torch's RNE casts)."""
