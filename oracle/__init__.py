@@ -30,9 +30,14 @@ What it computes (sources are the five pages on W4A16 quantization):
   ``s`` from the channels' mean activation magnitude, chosen by a grid search on the
   quantized layer's output error (page 4, section 五 AWQ).
 
+* W8A8 with SmoothQuant (``w8a8.py``): the smoothing ``Y = (X/s)(sW)`` with
+  ``s_j = max|X_j|^alpha / max|W_j|^(1-alpha)``, per-channel INT8 weights, per-token dynamic
+  INT8 activations and the integer product with a float epilogue (page 2, section 三;
+  page 4, section 六; page 1 on per-token dynamic quantization).
+
 Readings where the pages are silent (tie rule, clamping, which scale feeds the
 zero point, nibble order, symmetric storage) are listed in the docstrings of
-``quant.py``, ``linear.py``, ``gptq.py`` and ``awq.py``.
+``quant.py``, ``linear.py``, ``gptq.py``, ``awq.py`` and ``w8a8.py``.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against hand-worked vectors, closed forms, exact rational arithmetic or an
