@@ -233,6 +233,51 @@ int w4a16_awq_search(const float* W, int64_t N, int64_t K, const void* X, int dt
 int w4a16_awq_scale(const void* X, int dtype, int64_t M, int64_t K, const float* s, void* Y,
                     void* stream);
 
+/*
+ * W8A8 with SmoothQuant: both operands in INT8 for the integer matrix units, the activation
+ * outlier channels migrated into the weights.  Page "大模型推理中 Weight-only、W8A8 和 FP8 量化有
+ * 什么区别？如何选型？", section 三 (Y = (X/s)(sW), INT8 matrix units); page "推理优化中“用精度换
+ * 性能“的核心技术：量化", 6.2 (s_j = max|X_j|^alpha / max|W_j|^(1-alpha), alpha = 0.5), 3.3-3.4
+ * (symmetric absmax scales, per channel for weights, per token for activations); page
+ * "Quantization & Acceleration: 解释 W8A8 与 W4A16 的差异与取舍" (per-token dynamic activation
+ * scales).  All fp32 arithmetic follows one fixed order, so codes, scales and outputs are
+ * bit-reproducible: alpha = alpha_quarters / 4 with powers formed from square roots and
+ * products; w * s_j and x / s_j rounded once; scale = amax / 127 (1.0 if amax is 0); code =
+ * clamp(rint(v / scale), -128, 127); Y = out(fp32(fp32(acc) * xscale[m]) * wscale[n]) from
+ * the exact int32 sum acc.  Scales are fp32.
+ */
+
+/*
+ * w4a16_w8a8_smooth -- s[j] = max_t |X[t][j]|^alpha / max_n |W[n][j]|^(1-alpha) (1.0 for a
+ * channel whose activation or weight maximum is 0).  X [n_samples, K] fp16/bf16 calibration
+ * activations; W [N, K] fp32; s [K] fp32 out; all device.  alpha_quarters in 0..4.
+ */
+int w4a16_w8a8_smooth(const void* X, int dtype, int64_t n_samples, const float* W, int64_t N,
+                      int64_t K, int alpha_quarters, float* s, void* stream);
+
+/*
+ * w4a16_w8a8_quantize_weight -- qweight[n][k] = INT8 of W[n][k] * s[k] with one scale per
+ * output row n (wscale [N] fp32 out).  W [N, K] fp32, qweight [N, K] int8, device.
+ */
+int w4a16_w8a8_quantize_weight(const float* W, int64_t N, int64_t K, const float* s,
+                               int8_t* qweight, float* wscale, void* stream);
+
+/*
+ * w4a16_w8a8_quantize_act -- per-token dynamic INT8 of X[m][k] / s[k] (xscale [M] fp32 out).
+ * X [M, K] fp16/bf16, qx [M, K] int8, device.
+ */
+int w4a16_w8a8_quantize_act(const void* X, int dtype, int64_t M, int64_t K, const float* s,
+                            int8_t* qx, float* xscale, void* stream);
+
+/*
+ * w4a16_w8a8_linear -- Y[m][n] = out((sum_k qx[m][k] qweight[n][k]) * xscale[m] * wscale[n])
+ * on the INT8 matrix cores.  qx [M, K] and qweight [N, K] int8 (16-byte aligned), K % 128 == 0,
+ * M * K and N * K < 2^31; Y [M, N] in dtype (fp16/bf16), 2-byte aligned.
+ */
+int w4a16_w8a8_linear(const int8_t* qx, const float* xscale, int64_t M, int64_t N, int64_t K,
+                      const int8_t* qweight, const float* wscale, void* Y, int dtype,
+                      void* stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* w4a16_strerror(int status);
 

@@ -38,7 +38,8 @@ def test_header_declares_the_boundary():
                      "w4a16_select_path", "w4a16_dequantize", "w4a16_strerror",
                      "w4a16_abi_version", "w4a16_gptq_hessian", "w4a16_gptq_factor",
                      "w4a16_gptq_quantize", "w4a16_awq_workspace", "w4a16_awq_stats",
-                     "w4a16_awq_search", "w4a16_awq_scale"):
+                     "w4a16_awq_search", "w4a16_awq_scale", "w4a16_w8a8_smooth",
+                     "w4a16_w8a8_quantize_weight", "w4a16_w8a8_quantize_act", "w4a16_w8a8_linear"):
         assert required in names
 
 
@@ -174,3 +175,20 @@ def test_awq_workspace_and_invalid_arguments(lib):
     assert lib.w4a16_awq_scale(A, 0, 4, 64, None, B, None) == L.ERR_NULL
     assert lib.w4a16_awq_scale(A, 0, 0, 64, C, B, None) == L.ERR_SHAPE
     assert lib.w4a16_awq_scale(A + 1, 0, 4, 64, C, B, None) == L.ERR_ALIGN
+
+
+def test_w8a8_rejects_invalid_arguments(lib):
+    assert lib.w4a16_w8a8_smooth(None, 0, 8, B, 16, 64, 2, C, None) == L.ERR_NULL
+    assert lib.w4a16_w8a8_smooth(A, 0, 8, B, 16, 64, 5, C, None) == L.ERR_SHAPE
+    assert lib.w4a16_w8a8_smooth(A, 3, 8, B, 16, 64, 2, C, None) == L.ERR_DTYPE
+    assert lib.w4a16_w8a8_quantize_weight(A, 16, 64, None, B, C, None) == L.ERR_NULL
+    assert lib.w4a16_w8a8_quantize_weight(A + 2, 16, 64, B, C, D, None) == L.ERR_ALIGN
+    assert lib.w4a16_w8a8_quantize_act(A, 0, 0, 64, B, C, D, None) == L.ERR_SHAPE
+    lin = lambda **kw: lib.w4a16_w8a8_linear(kw.get("qx", A), kw.get("sx", B), kw.get("M", 64), 64,
+                                             kw.get("K", 256), kw.get("qw", C), kw.get("sw", D),
+                                             kw.get("Y", D + 4096), kw.get("dt", 0), None)
+    assert lin(qx=None) == L.ERR_NULL
+    assert lin(K=200) == L.ERR_SHAPE                 # K % 128 != 0
+    assert lin(M=1 << 24, K=1 << 8) == L.ERR_SHAPE   # M * K >= 2^31
+    assert lin(qw=C + 8) == L.ERR_ALIGN
+    assert lin(dt=4) == L.ERR_DTYPE

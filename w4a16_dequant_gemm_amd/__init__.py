@@ -15,6 +15,8 @@ the library's HIP kernels; there is no CPU or PyTorch fallback.
 ``awq_stats(X)`` / ``awq_search(W, X, xmean, group_size, scheme)`` / ``awq_scale(X, s)``
     AWQ: per-channel activation statistic, grid search over channel scalings, and the
     activation side of the rescaling.
+``w8a8_smooth`` / ``w8a8_quantize_weight`` / ``w8a8_quantize_act`` / ``w8a8_linear``
+    W8A8 with SmoothQuant on the INT8 matrix cores.
 """
 
 from __future__ import annotations
@@ -28,7 +30,8 @@ __all__ = [
     "ASYM", "SYM", "F16", "BF16", "PATH_AUTO", "PATH_GEMV", "PATH_SKINNY", "PATH_PREFILL",
     "PATH_NAMES", "W4A16Error", "quantize_pack", "linear", "dequantize", "select_path",
     "abi_version", "lib", "gptq_hessian", "gptq_factor", "gptq_quantize", "awq_stats",
-    "awq_search", "awq_scale",
+    "awq_search", "awq_scale", "w8a8_smooth", "w8a8_quantize_weight", "w8a8_quantize_act",
+    "w8a8_linear",
 ]
 
 
@@ -253,4 +256,63 @@ def awq_scale(X: torch.Tensor, s: torch.Tensor, out: torch.Tensor | None = None)
         _need(out, "out", X.dtype, 2)
     check(lib().w4a16_awq_scale(X.data_ptr(), dt, M, K, s.data_ptr(), out.data_ptr(), _stream()),
           "w4a16_awq_scale")
+    return out
+
+
+def w8a8_smooth(X: torch.Tensor, W: torch.Tensor, alpha_quarters: int = 2) -> torch.Tensor:
+    """SmoothQuant factors ``s [K]`` from calibration activations ``X [n, K]`` and ``W [N, K]``."""
+    dt = _dtype_code(X)
+    _need(X, "X", X.dtype, 2)
+    _need(W, "W", torch.float32, 2)
+    n, K = X.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("W must be [N, K]")
+    s = torch.empty(K, dtype=torch.float32, device=X.device)
+    check(lib().w4a16_w8a8_smooth(X.data_ptr(), dt, n, W.data_ptr(), N, K, alpha_quarters, s.data_ptr(),
+                                  _stream()), "w4a16_w8a8_smooth")
+    return s
+
+
+def w8a8_quantize_weight(W: torch.Tensor, s: torch.Tensor):
+    """``(qweight int8 [N, K], wscale fp32 [N])`` of the smoothed weights ``W * s``."""
+    _need(W, "W", torch.float32, 2)
+    _need(s, "s", torch.float32, 1)
+    N, K = W.shape
+    q = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    sw = torch.empty(N, dtype=torch.float32, device=W.device)
+    check(lib().w4a16_w8a8_quantize_weight(W.data_ptr(), N, K, s.data_ptr(), q.data_ptr(), sw.data_ptr(),
+                                           _stream()), "w4a16_w8a8_quantize_weight")
+    return q, sw
+
+
+def w8a8_quantize_act(X: torch.Tensor, s: torch.Tensor):
+    """``(qx int8 [M, K], xscale fp32 [M])``: per-token INT8 of ``X / s``."""
+    dt = _dtype_code(X)
+    _need(X, "X", X.dtype, 2)
+    _need(s, "s", torch.float32, 1)
+    M, K = X.shape
+    q = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    sx = torch.empty(M, dtype=torch.float32, device=X.device)
+    check(lib().w4a16_w8a8_quantize_act(X.data_ptr(), dt, M, K, s.data_ptr(), q.data_ptr(), sx.data_ptr(),
+                                        _stream()), "w4a16_w8a8_quantize_act")
+    return q, sx
+
+
+def w8a8_linear(qx: torch.Tensor, sx: torch.Tensor, qw: torch.Tensor, sw: torch.Tensor,
+                dtype=torch.float16, out: torch.Tensor | None = None) -> torch.Tensor:
+    """``Y [M, N]`` from INT8 operands and their fp32 scales, on the INT8 matrix cores."""
+    _need(qx, "qx", torch.int8, 2)
+    _need(qw, "qweight", torch.int8, 2)
+    _need(sx, "xscale", torch.float32, 1)
+    _need(sw, "wscale", torch.float32, 1)
+    M, K = qx.shape
+    N = qw.shape[0]
+    if qw.shape[1] != K or sx.shape[0] != M or sw.shape[0] != N:
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty((M, N), dtype=dtype, device=qx.device)
+    dt = _dtype_code(out)
+    check(lib().w4a16_w8a8_linear(qx.data_ptr(), sx.data_ptr(), M, N, K, qw.data_ptr(), sw.data_ptr(),
+                                  out.data_ptr(), dt, _stream()), "w4a16_w8a8_linear")
     return out

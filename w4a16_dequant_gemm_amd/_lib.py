@@ -68,6 +68,14 @@ def lib() -> ctypes.CDLL:
                                    vp, vp]
     L.w4a16_awq_scale.restype = i32
     L.w4a16_awq_scale.argtypes = [vp, i32, i64, i64, vp, vp, vp]
+    L.w4a16_w8a8_smooth.restype = i32
+    L.w4a16_w8a8_smooth.argtypes = [vp, i32, i64, vp, i64, i64, i32, vp, vp]
+    L.w4a16_w8a8_quantize_weight.restype = i32
+    L.w4a16_w8a8_quantize_weight.argtypes = [vp, i64, i64, vp, vp, vp, vp]
+    L.w4a16_w8a8_quantize_act.restype = i32
+    L.w4a16_w8a8_quantize_act.argtypes = [vp, i32, i64, i64, vp, vp, vp, vp]
+    L.w4a16_w8a8_linear.restype = i32
+    L.w4a16_w8a8_linear.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, i32, vp]
     L.w4a16_gptq_quantize.restype = i32
     L.w4a16_gptq_quantize.argtypes = [vp, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp]
     _lib = L

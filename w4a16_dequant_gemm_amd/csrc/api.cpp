@@ -257,6 +257,55 @@ int w4a16_awq_scale(const void* X, int dtype, int64_t M, int64_t K, const float*
                                               static_cast<hipStream_t>(stream)));
 }
 
+int w4a16_w8a8_smooth(const void* X, int dtype, int64_t n_samples, const float* W, int64_t N,
+                      int64_t K, int alpha_quarters, float* s, void* stream) {
+    if (!X || !W || !s) return W4A16_ERR_NULL;
+    if (dtype != W4A16_F16 && dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
+    if (n_samples < 1 || N < 1 || K < 1 || n_samples > kMaxDim || N > kMaxDim || K > kMaxDim ||
+        n_samples * K > (int64_t(1) << 40) || N * K > (int64_t(1) << 40) || alpha_quarters < 0 ||
+        alpha_quarters > 4)
+        return W4A16_ERR_SHAPE;
+    if (!aligned(X, 2) || !aligned(W, 4) || !aligned(s, 4)) return W4A16_ERR_ALIGN;
+    return hip_status(w4a16::launch_w8a8_smooth(X, dtype, (int)n_samples, W, (int)N, (int)K,
+                                                alpha_quarters, s, static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_w8a8_quantize_weight(const float* W, int64_t N, int64_t K, const float* s,
+                               int8_t* qweight, float* wscale, void* stream) {
+    if (!W || !s || !qweight || !wscale) return W4A16_ERR_NULL;
+    if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim || N * K > (int64_t(1) << 40))
+        return W4A16_ERR_SHAPE;
+    if (!aligned(W, 4) || !aligned(s, 4) || !aligned(wscale, 4)) return W4A16_ERR_ALIGN;
+    return hip_status(w4a16::launch_w8a8_quant_weight(W, (int)N, (int)K, s, qweight, wscale,
+                                                      static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_w8a8_quantize_act(const void* X, int dtype, int64_t M, int64_t K, const float* s,
+                            int8_t* qx, float* xscale, void* stream) {
+    if (!X || !s || !qx || !xscale) return W4A16_ERR_NULL;
+    if (dtype != W4A16_F16 && dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
+    if (M < 1 || K < 1 || M > kMaxDim || K > kMaxDim || M * K > (int64_t(1) << 40))
+        return W4A16_ERR_SHAPE;
+    if (!aligned(X, 2) || !aligned(s, 4) || !aligned(xscale, 4)) return W4A16_ERR_ALIGN;
+    return hip_status(w4a16::launch_w8a8_quant_act(X, dtype, (int)M, (int)K, s, qx, xscale,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_w8a8_linear(const int8_t* qx, const float* xscale, int64_t M, int64_t N, int64_t K,
+                      const int8_t* qweight, const float* wscale, void* Y, int dtype,
+                      void* stream) {
+    if (!qx || !xscale || !qweight || !wscale || !Y) return W4A16_ERR_NULL;
+    if (dtype != W4A16_F16 && dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
+    if (M < 1 || N < 1 || K < 1 || K % 128 != 0 || M * K >= (int64_t(1) << 31) ||
+        N * K >= (int64_t(1) << 31) || M * N > (int64_t(1) << 42) || K > 16777216)
+        return W4A16_ERR_SHAPE;
+    if (!aligned(qx, 16) || !aligned(qweight, 16) || !aligned(xscale, 4) || !aligned(wscale, 4) ||
+        !aligned(Y, 2))
+        return W4A16_ERR_ALIGN;
+    return hip_status(w4a16::launch_w8a8_linear(qx, xscale, (int)M, (int)N, (int)K, qweight, wscale,
+                                                Y, dtype, static_cast<hipStream_t>(stream)));
+}
+
 int w4a16_select_path(int64_t M, int64_t N, int64_t K, int64_t group_size, int dtype) {
     // Fake, aligned, non-null pointers: only shapes are examined.
     alignas(16) static const unsigned char dummy[16] = {0};

@@ -39,6 +39,16 @@ hipError_t launch_prefill(const LinearArgs& a, hipStream_t s);
 hipError_t launch_gptq_hessian(const void* X, int dtype, int n, int K, double* H, bool accumulate,
                                hipStream_t s);
 hipError_t launch_gptq_factor(double* H, int K, double damp, double* U, hipStream_t s);
+// W8A8 + SmoothQuant (w8a8.hip)
+hipError_t launch_w8a8_smooth(const void* X, int dtype, int n, const float* W, int N, int K, int a,
+                              float* s, hipStream_t st);
+hipError_t launch_w8a8_quant_weight(const float* W, int N, int K, const float* s, int8_t* q,
+                                    float* sw, hipStream_t st);
+hipError_t launch_w8a8_quant_act(const void* X, int dtype, int M, int K, const float* s, int8_t* q,
+                                 float* sx, hipStream_t st);
+hipError_t launch_w8a8_linear(const int8_t* qx, const float* sx, int M, int N, int K,
+                              const int8_t* qw, const float* sw, void* Y, int dtype, hipStream_t st);
+
 // AWQ (awq.hip)
 long long awq_workspace_doubles(long long N, long long K, long long n);
 hipError_t launch_awq_stats(const void* X, int dtype, int n, int K, float* xmean, hipStream_t s);
