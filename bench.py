@@ -463,7 +463,46 @@ def run_extras(layers, copies, W4, synth, torch, np):
     out["prefill_m4096_fp16_g128"] = pre
     out["gptq_4096x4096_g128"] = run_gptq(W4, synth, torch)
     out["awq_4096x4096_g128"] = run_awq(W4, synth, torch)
+    out["w8a8_m4096"] = run_w8a8(W4, synth, torch)
     return out
+
+
+INT8_PEAK_TOPS = 5000.0              # MI355X dense int8 MFMA
+
+
+def run_w8a8(W4, synth, torch, M=4096):
+    """W8A8 + SmoothQuant at M = 4096 on the two prefill shapes: the INT8 product (roofline:
+    int8 MFMA peak, 2 M N K ops) and the per-token activation quantization (HBM: 3 M K bytes
+    read + written)."""
+    res = {}
+    for (K, N) in [(4096, 11008), (11008, 4096)]:
+        X = synth.calibration_device(M, K, synth.FP16, 6000 + K, outlier_frac=0.01, outlier_mult=20.0)
+        W = synth.weights_device(N, K, 0.02, 6001 + K)
+        s = W4.w8a8_smooth(X, W, 2)
+        qw, sw = W4.w8a8_quantize_weight(W, s)
+        qx, sx = W4.w8a8_quantize_act(X, s)
+        Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        for _ in range(3):
+            W4.w8a8_linear(qx, sx, qw, sw, out=Y)
+        ms = time_loop(lambda i: W4.w8a8_linear(qx, sx, qw, sw, out=Y), 20, torch)
+        tops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        ms_q = time_loop(lambda i: W4.w8a8_quantize_act(X, s), 20, torch, graph=False)
+        entry = {"gemm_us": round(ms * 1e3, 1), "TOPS": round(tops, 1), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
+                 "quant_act_us": round(ms_q * 1e3, 1),
+                 "quant_act_GBps": round(3.0 * M * K / (ms_q * 1e-3) / 1e9, 1)}
+        try:   # context: the library int8 GEMM behind torch._int_mm, if this build routes it
+            a = qx
+            b = qw.t()
+            for _ in range(2):
+                torch._int_mm(a, b)
+            ms_t = time_loop(lambda i: torch._int_mm(a, b), 10, torch, graph=False)
+            entry["torch_int_mm_TOPS"] = round(2.0 * M * N * K / (ms_t * 1e-3) / 1e12, 1)
+        except Exception as e:       # noqa: BLE001 - comparator only
+            entry["torch_int_mm_TOPS"] = None
+        res[f"K{K}_N{N}"] = entry
+        log(f"  w8a8 M={M} K={K} N={N}: {entry}")
+        del X, W, qw, sw, qx, sx, Y, s
+    return res
 
 
 def run_awq(W4, synth, torch, n=512, K=4096, N=4096, reps=3):

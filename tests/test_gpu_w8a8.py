@@ -43,9 +43,10 @@ def test_smooth_factors(dtype, a):
 
 
 @pytest.mark.parametrize("dtype", [FP16, BF16])
-def test_quantize_operands(dtype):
-    X = calibration(77, 640, dtype, seed=3, outlier_frac=0.02, outlier_mult=40.0)
-    W = weights(130, 640, 0.02, seed=4)
+@pytest.mark.parametrize("K", [640, 200, 11008, 16384])     # vectorized and scalar row kernels
+def test_quantize_operands(dtype, K):
+    X = calibration(77, K, dtype, seed=3, outlier_frac=0.02, outlier_mult=40.0)
+    W = weights(130, K, 0.02, seed=4)
     s = Q.smooth_factors(X, dtype, W, 2)
     st = torch.from_numpy(s).cuda()
     qw, sw = W4.w8a8_quantize_weight(torch.from_numpy(W).cuda(), st)

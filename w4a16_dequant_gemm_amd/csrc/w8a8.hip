@@ -80,6 +80,68 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
     if (tid == 0) scale[row] = sc;
 }
 
+// Vectorized variant for K % 8 == 0 and K <= 8 * 256 * CH: thread t holds chunks t + 256 c
+// (8 consecutive values each) in registers between the max and the code pass; same
+// arithmetic as quant_rows_kernel.
+template <int DT, bool WEIGHT, int CH>
+__global__ __launch_bounds__(256) void quant_rows_vec_kernel(const void* __restrict__ src, int K,
+                                                             const float* __restrict__ s, int8_t* __restrict__ q,
+                                                             float* __restrict__ scale) {
+    __shared__ float red[256];
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int nch = K >> 3;
+    float v[CH][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int ch = tid + 256 * c;
+        if (ch < nch) {
+            const float4 s0 = *reinterpret_cast<const float4*>(s + 8 * ch);
+            const float4 s1 = *reinterpret_cast<const float4*>(s + 8 * ch + 4);
+            const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+            if constexpr (WEIGHT) {
+                const float* p = static_cast<const float*>(src) + (long long)row * K + 8 * ch;
+                const float4 a = *reinterpret_cast<const float4*>(p);
+                const float4 b = *reinterpret_cast<const float4*>(p + 4);
+                const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[c][i] = x[i] * sv[i];
+            } else {
+                const u32x4 r = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + (long long)row * K + 8 * ch);
+                const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[c][i] = in2f<DT>((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) / sv[i];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
+        }
+    }
+    red[tid] = amax;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+        __syncthreads();
+    }
+    float sc = red[0] / 127.0f;
+    if (sc == 0.0f) sc = 1.0f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int ch = tid + 256 * c;
+        if (ch < nch) {
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float cq = fminf(fmaxf(__builtin_rintf(v[c][i] / sc), -128.0f), 127.0f);
+                const uint32_t b = (uint32_t)(int)cq & 0xFFu;
+                if (i < 4) lo |= b << (8 * i); else hi |= b << (8 * (i - 4));
+            }
+            *reinterpret_cast<uint2*>(q + (long long)row * K + 8 * ch) = make_uint2(lo, hi);
+        }
+    }
+    if (tid == 0) scale[row] = sc;
+}
+
 constexpr int I_BM = 256, I_BN = 256, I_BK = 128;      // bytes of K per step
 constexpr int kGemmLds = 4 * I_BM * 8 * 16;            // A and B, two buffers each: 128 KB
 
@@ -224,19 +286,36 @@ hipError_t launch_w8a8_smooth(const void* X, int dtype, int n, const float* W, i
     return hipGetLastError();
 }
 
-hipError_t launch_w8a8_quant_weight(const float* W, int N, int K, const float* s, int8_t* q, float* sw, hipStream_t st) {
-    hipLaunchKernelGGL((quant_rows_kernel<DT_F16, true>), dim3(N), dim3(256), 0, st, static_cast<const void*>(W), K, s,
-                       q, sw);
+namespace {
+
+// vectorized rows when every pointer and row is 16-byte aligned and a row fits 8 chunks per
+// thread; the scalar kernel otherwise (same arithmetic)
+template <int DT, bool WEIGHT>
+hipError_t quant_rows(const void* src, int R, int K, const float* s, int8_t* q, float* scale, hipStream_t st) {
+    const bool vec = K % 16 == 0 && K <= 8 * 256 * 8 && (reinterpret_cast<uintptr_t>(src) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(s) & 15) == 0 && (reinterpret_cast<uintptr_t>(q) & 7) == 0;
+    if (!vec) {
+        hipLaunchKernelGGL((quant_rows_kernel<DT, WEIGHT>), dim3(R), dim3(256), 0, st, src, K, s, q, scale);
+    } else if (K <= 8 * 256 * 2) {
+        hipLaunchKernelGGL((quant_rows_vec_kernel<DT, WEIGHT, 2>), dim3(R), dim3(256), 0, st, src, K, s, q, scale);
+    } else if (K <= 8 * 256 * 4) {
+        hipLaunchKernelGGL((quant_rows_vec_kernel<DT, WEIGHT, 4>), dim3(R), dim3(256), 0, st, src, K, s, q, scale);
+    } else {
+        hipLaunchKernelGGL((quant_rows_vec_kernel<DT, WEIGHT, 8>), dim3(R), dim3(256), 0, st, src, K, s, q, scale);
+    }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_w8a8_quant_weight(const float* W, int N, int K, const float* s, int8_t* q, float* sw, hipStream_t st) {
+    return quant_rows<DT_F16, true>(W, N, K, s, q, sw, st);
 }
 
 hipError_t launch_w8a8_quant_act(const void* X, int dtype, int M, int K, const float* s, int8_t* q, float* sx,
                                  hipStream_t st) {
-    if (dtype == DT_F16)
-        hipLaunchKernelGGL((quant_rows_kernel<DT_F16, false>), dim3(M), dim3(256), 0, st, X, K, s, q, sx);
-    else
-        hipLaunchKernelGGL((quant_rows_kernel<DT_BF16, false>), dim3(M), dim3(256), 0, st, X, K, s, q, sx);
-    return hipGetLastError();
+    return dtype == DT_F16 ? quant_rows<DT_F16, false>(X, M, K, s, q, sx, st)
+                           : quant_rows<DT_BF16, false>(X, M, K, s, q, sx, st);
 }
 
 hipError_t launch_w8a8_linear(const int8_t* qx, const float* sx, int M, int N, int K, const int8_t* qw,
