@@ -35,9 +35,12 @@ What it computes (sources are the five pages on W4A16 quantization):
   INT8 activations and the integer product with a float epilogue (page 2, section 三;
   page 4, section 六; page 1 on per-token dynamic quantization).
 
+* KV-cache quantization (``kv.py``): per-token KV8 / KV4 and the decode attention that
+  reads the quantized cache (page 3, section 六 KV Cache 量化; page 1 on W4A16 + KV INT8).
+
 Readings where the pages are silent (tie rule, clamping, which scale feeds the
 zero point, nibble order, symmetric storage) are listed in the docstrings of
-``quant.py``, ``linear.py``, ``gptq.py``, ``awq.py`` and ``w8a8.py``.
+``quant.py``, ``linear.py``, ``gptq.py``, ``awq.py``, ``w8a8.py`` and ``kv.py``.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against hand-worked vectors, closed forms, exact rational arithmetic or an
