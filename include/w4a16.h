@@ -278,6 +278,45 @@ int w4a16_w8a8_linear(const int8_t* qx, const float* xscale, int64_t M, int64_t 
                       const int8_t* qweight, const float* wscale, void* Y, int dtype,
                       void* stream);
 
+/*
+ * KV-cache quantization and the decode attention that reads the quantized cache.  Page
+ * "量化实战深入（GPTQ / AWQ / SmoothQuant / KV 量化）", 六 KV Cache 量化 (KV8 / KV4, keys and
+ * values quantized separately, per token); page "Quantization & Acceleration: 解释 W8A8 与 W4A16
+ * 的差异与取舍", 深度剖析 ③ (W4A16 + KV INT8).  One scale (KV4: and zero point) per (head,
+ * token) row of D values.  KV8: s = fp16(max|x| / 127) (1.0 if 0), int8 codes
+ * clamp(rint(x / s), -127, 127); KV4: the asymmetric RTN of w4a16_quantize_pack with g = D,
+ * nibbles packed as in qweight.  Cache layout [H, Tmax, D] (codes: int8, or int32 words of 8
+ * nibbles), scales / zeros [H, Tmax] fp16.  D is 64 or 128.
+ */
+
+/*
+ * w4a16_kv_quantize -- quantize x [H, T, D] (fp16/bf16, 16-byte aligned) into codes
+ * (int8 [H, T, D] or int32 [H, T, D/8], 8-byte aligned), scales and, for bits == 4, zeros
+ * ([H, T] fp16).  Rows are independent: quantizing new tokens of a cache is a call on their
+ * rows (with the cache's row stride equal to T of that call's layout).
+ */
+int w4a16_kv_quantize(const void* x, int dtype, int64_t H, int64_t T, int64_t D, int bits,
+                      void* codes, uint16_t* scales, uint16_t* zeros, void* stream);
+
+/* fp32 elements of the w4a16_kv_attention_decode workspace (host only), or a negative status. */
+int64_t w4a16_kv_attention_workspace(int64_t Hq, int64_t T, int64_t D);
+
+/*
+ * w4a16_kv_attention_decode -- out[h] = softmax(q[h] . K_t / sqrt(D)) V over the first T of
+ * Tmax cached tokens of kv head h / (Hq / Hkv) (grouped-query attention when Hq > Hkv).
+ *   q    [Hq, D] fp16/bf16; out [Hq, D] same dtype.
+ *   kcodes, vcodes / kscales, vscales / kzeros, vzeros: the caches of w4a16_kv_quantize with
+ *        H = Hkv and T = Tmax (zeros only for bits == 4; 16-byte aligned codes).
+ *   work w4a16_kv_attention_workspace(Hq, T, D) fp32 elements.
+ * Scores and softmax in fp32 (max-subtracted), split over tokens and merged; output rounded
+ * once.
+ */
+int w4a16_kv_attention_decode(const void* q, int dtype, int64_t Hq, int64_t Hkv, int64_t T,
+                              int64_t Tmax, int64_t D, int bits, const void* kcodes,
+                              const uint16_t* kscales, const uint16_t* kzeros, const void* vcodes,
+                              const uint16_t* vscales, const uint16_t* vzeros, float* work,
+                              void* out, void* stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* w4a16_strerror(int status);
 

@@ -39,7 +39,9 @@ def test_header_declares_the_boundary():
                      "w4a16_abi_version", "w4a16_gptq_hessian", "w4a16_gptq_factor",
                      "w4a16_gptq_quantize", "w4a16_awq_workspace", "w4a16_awq_stats",
                      "w4a16_awq_search", "w4a16_awq_scale", "w4a16_w8a8_smooth",
-                     "w4a16_w8a8_quantize_weight", "w4a16_w8a8_quantize_act", "w4a16_w8a8_linear"):
+                     "w4a16_w8a8_quantize_weight", "w4a16_w8a8_quantize_act", "w4a16_w8a8_linear",
+                     "w4a16_kv_quantize", "w4a16_kv_attention_workspace",
+                     "w4a16_kv_attention_decode"):
         assert required in names
 
 
@@ -192,3 +194,21 @@ def test_w8a8_rejects_invalid_arguments(lib):
     assert lin(M=1 << 24, K=1 << 8) == L.ERR_SHAPE   # M * K >= 2^31
     assert lin(qw=C + 8) == L.ERR_ALIGN
     assert lin(dt=4) == L.ERR_DTYPE
+
+
+def test_kv_rejects_invalid_arguments(lib):
+    assert lib.w4a16_kv_attention_workspace(32, 4096, 128) > 0
+    assert lib.w4a16_kv_attention_workspace(32, 4096, 96) == L.ERR_SHAPE
+    assert lib.w4a16_kv_quantize(None, 0, 2, 8, 128, 8, B, C, None, None) == L.ERR_NULL
+    assert lib.w4a16_kv_quantize(A, 0, 2, 8, 128, 4, B, C, None, None) == L.ERR_NULL   # KV4 needs zeros
+    assert lib.w4a16_kv_quantize(A, 0, 2, 8, 128, 6, B, C, D, None) == L.ERR_SCHEME
+    assert lib.w4a16_kv_quantize(A, 0, 2, 8, 96, 8, B, C, None, None) == L.ERR_SHAPE
+    assert lib.w4a16_kv_quantize(A + 8, 0, 2, 8, 128, 8, B, C, None, None) == L.ERR_ALIGN
+    att = lambda **kw: lib.w4a16_kv_attention_decode(A, kw.get("dt", 0), kw.get("Hq", 8), kw.get("Hkv", 4),
+                                                     kw.get("T", 16), kw.get("Tmax", 32), 128, kw.get("bits", 8),
+                                                     B, C, None, B + 0x10000, C + 0x1000, None, D, D + 0x10000,
+                                                     None)
+    assert att(Hkv=3) == L.ERR_SHAPE             # Hq % Hkv != 0
+    assert att(T=40) == L.ERR_SHAPE              # T > Tmax
+    assert att(bits=4) == L.ERR_NULL             # KV4 needs zeros
+    assert att(dt=7) == L.ERR_DTYPE

@@ -17,6 +17,8 @@ the library's HIP kernels; there is no CPU or PyTorch fallback.
     activation side of the rescaling.
 ``w8a8_smooth`` / ``w8a8_quantize_weight`` / ``w8a8_quantize_act`` / ``w8a8_linear``
     W8A8 with SmoothQuant on the INT8 matrix cores.
+``kv_quantize(x, bits)`` / ``kv_attention_decode(q, cache, T)``
+    per-token KV8 / KV4 cache quantization and the decode attention over the quantized cache.
 """
 
 from __future__ import annotations
@@ -31,7 +33,7 @@ __all__ = [
     "PATH_NAMES", "W4A16Error", "quantize_pack", "linear", "dequantize", "select_path",
     "abi_version", "lib", "gptq_hessian", "gptq_factor", "gptq_quantize", "awq_stats",
     "awq_search", "awq_scale", "w8a8_smooth", "w8a8_quantize_weight", "w8a8_quantize_act",
-    "w8a8_linear",
+    "w8a8_linear", "kv_quantize", "kv_attention_decode",
 ]
 
 
@@ -315,4 +317,48 @@ def w8a8_linear(qx: torch.Tensor, sx: torch.Tensor, qw: torch.Tensor, sw: torch.
     dt = _dtype_code(out)
     check(lib().w4a16_w8a8_linear(qx.data_ptr(), sx.data_ptr(), M, N, K, qw.data_ptr(), sw.data_ptr(),
                                   out.data_ptr(), dt, _stream()), "w4a16_w8a8_linear")
+    return out
+
+
+def kv_quantize(x: torch.Tensor, bits: int = 8):
+    """Quantize ``x [H, T, D]`` (fp16/bf16) into ``(codes, scales, zeros)``: codes int8
+    ``[H, T, D]`` (KV8) or int32 ``[H, T, D/8]`` (KV4), scales / zeros fp16 ``[H, T]`` (zeros
+    None for KV8)."""
+    dt = _dtype_code(x)
+    _need(x, "x", x.dtype, 3)
+    H, T, D = x.shape
+    if bits == 8:
+        codes = torch.empty((H, T, D), dtype=torch.int8, device=x.device)
+        zeros = None
+    else:
+        codes = torch.empty((H, T, D // 8), dtype=torch.int32, device=x.device)
+        zeros = torch.empty((H, T), dtype=torch.float16, device=x.device)
+    scales = torch.empty((H, T), dtype=torch.float16, device=x.device)
+    check(lib().w4a16_kv_quantize(x.data_ptr(), dt, H, T, D, bits, codes.data_ptr(), scales.data_ptr(),
+                                  zeros.data_ptr() if zeros is not None else None, _stream()),
+          "w4a16_kv_quantize")
+    return codes, scales, zeros
+
+
+def kv_attention_decode(q: torch.Tensor, kcache, vcache, T: int, bits: int = 8,
+                        out: torch.Tensor | None = None) -> torch.Tensor:
+    """``softmax(q K^T / sqrt(D)) V`` over the first ``T`` tokens of quantized caches
+    ``(codes, scales, zeros)`` of shape ``[Hkv, Tmax, ...]``; ``q [Hq, D]``."""
+    dt = _dtype_code(q)
+    _need(q, "q", q.dtype, 2)
+    Hq, D = q.shape
+    kc, ks, kz = kcache
+    vc, vs, vz = vcache
+    Hkv, Tmax = ks.shape
+    L = lib()
+    need = L.w4a16_kv_attention_workspace(Hq, T, D)
+    if need < 0:
+        raise W4A16Error(int(need), "w4a16_kv_attention_workspace")
+    work = torch.empty(need, dtype=torch.float32, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    check(L.w4a16_kv_attention_decode(q.data_ptr(), dt, Hq, Hkv, T, Tmax, D, bits, kc.data_ptr(), ks.data_ptr(),
+                                      ptr(kz), vc.data_ptr(), vs.data_ptr(), ptr(vz), work.data_ptr(),
+                                      out.data_ptr(), _stream()), "w4a16_kv_attention_decode")
     return out

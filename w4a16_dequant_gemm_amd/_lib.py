@@ -76,6 +76,13 @@ def lib() -> ctypes.CDLL:
     L.w4a16_w8a8_quantize_act.argtypes = [vp, i32, i64, i64, vp, vp, vp, vp]
     L.w4a16_w8a8_linear.restype = i32
     L.w4a16_w8a8_linear.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, i32, vp]
+    L.w4a16_kv_attention_workspace.restype = i64
+    L.w4a16_kv_attention_workspace.argtypes = [i64, i64, i64]
+    L.w4a16_kv_quantize.restype = i32
+    L.w4a16_kv_quantize.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, vp, vp]
+    L.w4a16_kv_attention_decode.restype = i32
+    L.w4a16_kv_attention_decode.argtypes = [vp, i32, i64, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp,
+                                            vp, vp, vp]
     L.w4a16_gptq_quantize.restype = i32
     L.w4a16_gptq_quantize.argtypes = [vp, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp]
     _lib = L

@@ -306,6 +306,44 @@ int w4a16_w8a8_linear(const int8_t* qx, const float* xscale, int64_t M, int64_t 
                                                 Y, dtype, static_cast<hipStream_t>(stream)));
 }
 
+int64_t w4a16_kv_attention_workspace(int64_t Hq, int64_t T, int64_t D) {
+    if (Hq < 1 || T < 1 || (D != 64 && D != 128)) return W4A16_ERR_SHAPE;
+    return w4a16::kv_attention_workspace_floats(Hq, T, D);
+}
+
+int w4a16_kv_quantize(const void* x, int dtype, int64_t H, int64_t T, int64_t D, int bits,
+                      void* codes, uint16_t* scales, uint16_t* zeros, void* stream) {
+    if (!x || !codes || !scales || (bits == 4 && !zeros)) return W4A16_ERR_NULL;
+    if (dtype != W4A16_F16 && dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
+    if (bits != 8 && bits != 4) return W4A16_ERR_SCHEME;
+    if (H < 1 || T < 1 || (D != 64 && D != 128) || H * T > (int64_t(1) << 33)) return W4A16_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(scales, 2) || (zeros && !aligned(zeros, 2)))
+        return W4A16_ERR_ALIGN;
+    return hip_status(w4a16::launch_kv_quantize(x, dtype, H * T, (int)D, bits, codes, scales, zeros,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_kv_attention_decode(const void* q, int dtype, int64_t Hq, int64_t Hkv, int64_t T,
+                              int64_t Tmax, int64_t D, int bits, const void* kcodes,
+                              const uint16_t* kscales, const uint16_t* kzeros, const void* vcodes,
+                              const uint16_t* vscales, const uint16_t* vzeros, float* work,
+                              void* out, void* stream) {
+    if (!q || !kcodes || !kscales || !vcodes || !vscales || !work || !out) return W4A16_ERR_NULL;
+    if (bits == 4 && (!kzeros || !vzeros)) return W4A16_ERR_NULL;
+    if (dtype != W4A16_F16 && dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
+    if (bits != 8 && bits != 4) return W4A16_ERR_SCHEME;
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Hq > 65535 || T < 1 || T > Tmax ||
+        (D != 64 && D != 128) || Hkv * Tmax > (int64_t(1) << 33) || Tmax > kMaxDim)
+        return W4A16_ERR_SHAPE;
+    if (!aligned(q, 2) || !aligned(kcodes, 16) || !aligned(vcodes, 16) || !aligned(kscales, 2) ||
+        !aligned(vscales, 2) || (kzeros && !aligned(kzeros, 2)) || (vzeros && !aligned(vzeros, 2)) ||
+        !aligned(work, 4) || !aligned(out, 2))
+        return W4A16_ERR_ALIGN;
+    return hip_status(w4a16::launch_kv_attention(q, dtype, (int)Hq, (int)Hkv, (int)T, (int)Tmax, (int)D,
+                                                 bits, kcodes, kscales, kzeros, vcodes, vscales,
+                                                 vzeros, work, out, static_cast<hipStream_t>(stream)));
+}
+
 int w4a16_select_path(int64_t M, int64_t N, int64_t K, int64_t group_size, int dtype) {
     // Fake, aligned, non-null pointers: only shapes are examined.
     alignas(16) static const unsigned char dummy[16] = {0};
