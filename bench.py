@@ -464,7 +464,47 @@ def run_extras(layers, copies, W4, synth, torch, np):
     out["gptq_4096x4096_g128"] = run_gptq(W4, synth, torch)
     out["awq_4096x4096_g128"] = run_awq(W4, synth, torch)
     out["w8a8_m4096"] = run_w8a8(W4, synth, torch)
+    out["kv_decode_attention_h32_d128_t4096"] = run_kv(W4, synth, torch)
     return out
+
+
+def run_kv(W4, synth, torch, H=32, D=128, T=4096, layers=32):
+    """Decode attention of a 32-head, head-dim-128 model over a 4096-token quantized cache,
+    one query per head, across 32 layers (a different cache each, 0.5-1.1 GB in all, so no
+    layer's cache stays in the last-level cache).  Roofline: HBM, algorithmic bytes = the
+    codes and per-token parameters of K and V plus q and the output.  The per-token
+    quantization of a whole 4096-token cache is timed beside it (bytes: fp16 in, codes and
+    parameters out)."""
+    res = {}
+    q = synth.activations_device(H, D, synth.FP16, 7000)
+    out = torch.empty_like(q)
+    work = torch.empty(W4.kv_attention_workspace(H, T, D), dtype=torch.float32, device="cuda")
+    for bits in (8, 4):
+        caches = []
+        for l in range(layers):
+            k = synth.activations_device(H * T, D, synth.FP16, 7100 + 2 * l).view(H, T, D)
+            v = synth.activations_device(H * T, D, synth.FP16, 7101 + 2 * l).view(H, T, D)
+            caches.append((W4.kv_quantize(k, bits), W4.kv_quantize(v, bits)))
+            del v
+        row = D * bits // 8 + (2 if bits == 8 else 4)
+        nbytes = layers * (2 * H * T * row + 2 * 2 * H * D)
+
+        def step(i, bits=bits, caches=caches):
+            for kc, vc in caches:
+                W4.kv_attention_decode(q, kc, vc, T, bits, out=out, work=work)
+        for i in range(3):
+            step(i)
+        ms = time_loop(step, 20, torch)
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        ms_q = time_loop(lambda i, k=k, bits=bits: W4.kv_quantize(k, bits), 20, torch, graph=False)
+        qbytes = H * T * (2 * D + row)
+        entry = {"attention_us_per_layer": round(ms * 1e3 / layers, 2), "attention_GBps": round(gbps, 1),
+                 "frac_hbm_peak": round(gbps / HBM_PEAK_GBS, 4),
+                 "quantize_us": round(ms_q * 1e3, 1), "quantize_GBps": round(qbytes / (ms_q * 1e-3) / 1e9, 1)}
+        res[f"kv{bits}"] = entry
+        log(f"  kv{bits} decode attention H={H} D={D} T={T}: {entry}")
+        del caches, k
+    return res
 
 
 INT8_PEAK_TOPS = 5000.0              # MI355X dense int8 MFMA

@@ -304,12 +304,15 @@ int64_t w4a16_kv_attention_workspace(int64_t Hq, int64_t T, int64_t D);
 /*
  * w4a16_kv_attention_decode -- out[h] = softmax(q[h] . K_t / sqrt(D)) V over the first T of
  * Tmax cached tokens of kv head h / (Hq / Hkv) (grouped-query attention when Hq > Hkv).
- *   q    [Hq, D] fp16/bf16; out [Hq, D] same dtype.
+ *   q    [Hq, D] fp16/bf16, 16-byte aligned; out [Hq, D] same dtype.
  *   kcodes, vcodes / kscales, vscales / kzeros, vzeros: the caches of w4a16_kv_quantize with
- *        H = Hkv and T = Tmax (zeros only for bits == 4; 16-byte aligned codes).
- *   work w4a16_kv_attention_workspace(Hq, T, D) fp32 elements.
- * Scores and softmax in fp32 (max-subtracted), split over tokens and merged; output rounded
- * once.
+ *        H = Hkv and T = Tmax <= 2^24 (zeros only for bits == 4; 16-byte aligned codes).
+ *   work w4a16_kv_attention_workspace(Hq, T, D) fp32 elements (scratch, contents undefined
+ *        after the call; calls that overlap on one work buffer race).
+ * Scores and softmax in fp32 (max-subtracted, base-2 exponentials with q prescaled by
+ * log2(e) / sqrt(D)), each split of tokens reduced with an online softmax, the splits merged
+ * by a second launch; the output is rounded once.  The cache is read once per group of up to
+ * 4 (KV8) or 2 (KV4) query heads that share a kv head.
  */
 int w4a16_kv_attention_decode(const void* q, int dtype, int64_t Hq, int64_t Hkv, int64_t T,
                               int64_t Tmax, int64_t D, int bits, const void* kcodes,

@@ -340,10 +340,19 @@ def kv_quantize(x: torch.Tensor, bits: int = 8):
     return codes, scales, zeros
 
 
+def kv_attention_workspace(Hq: int, T: int, D: int) -> int:
+    """fp32 elements of the scratch buffer that :func:`kv_attention_decode` needs."""
+    need = lib().w4a16_kv_attention_workspace(Hq, T, D)
+    if need < 0:
+        raise W4A16Error(int(need), "w4a16_kv_attention_workspace")
+    return int(need)
+
+
 def kv_attention_decode(q: torch.Tensor, kcache, vcache, T: int, bits: int = 8,
-                        out: torch.Tensor | None = None) -> torch.Tensor:
+                        out: torch.Tensor | None = None, work: torch.Tensor | None = None) -> torch.Tensor:
     """``softmax(q K^T / sqrt(D)) V`` over the first ``T`` tokens of quantized caches
-    ``(codes, scales, zeros)`` of shape ``[Hkv, Tmax, ...]``; ``q [Hq, D]``."""
+    ``(codes, scales, zeros)`` of shape ``[Hkv, Tmax, ...]``; ``q [Hq, D]``.  ``work`` is an
+    optional fp32 device buffer of at least :func:`kv_attention_workspace` elements."""
     dt = _dtype_code(q)
     _need(q, "q", q.dtype, 2)
     Hq, D = q.shape
@@ -351,10 +360,11 @@ def kv_attention_decode(q: torch.Tensor, kcache, vcache, T: int, bits: int = 8,
     vc, vs, vz = vcache
     Hkv, Tmax = ks.shape
     L = lib()
-    need = L.w4a16_kv_attention_workspace(Hq, T, D)
-    if need < 0:
-        raise W4A16Error(int(need), "w4a16_kv_attention_workspace")
-    work = torch.empty(need, dtype=torch.float32, device=q.device)
+    need = kv_attention_workspace(Hq, T, D)
+    if work is None:
+        work = torch.empty(need, dtype=torch.float32, device=q.device)
+    elif work.dtype != torch.float32 or not work.is_cuda or work.numel() < need:
+        raise ValueError(f"work must be a float32 device tensor of at least {need} elements")
     if out is None:
         out = torch.empty_like(q)
     ptr = lambda t: t.data_ptr() if t is not None else None

@@ -333,9 +333,9 @@ int w4a16_kv_attention_decode(const void* q, int dtype, int64_t Hq, int64_t Hkv,
     if (dtype != W4A16_F16 && dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
     if (bits != 8 && bits != 4) return W4A16_ERR_SCHEME;
     if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Hq > 65535 || T < 1 || T > Tmax ||
-        (D != 64 && D != 128) || Hkv * Tmax > (int64_t(1) << 33) || Tmax > kMaxDim)
+        (D != 64 && D != 128) || Hkv * Tmax > (int64_t(1) << 33) || Tmax > (int64_t(1) << 24))
         return W4A16_ERR_SHAPE;
-    if (!aligned(q, 2) || !aligned(kcodes, 16) || !aligned(vcodes, 16) || !aligned(kscales, 2) ||
+    if (!aligned(q, 16) || !aligned(kcodes, 16) || !aligned(vcodes, 16) || !aligned(kscales, 2) ||
         !aligned(vscales, 2) || (kzeros && !aligned(kzeros, 2)) || (vzeros && !aligned(vzeros, 2)) ||
         !aligned(work, 4) || !aligned(out, 2))
         return W4A16_ERR_ALIGN;

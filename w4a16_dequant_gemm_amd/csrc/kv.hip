@@ -10,11 +10,11 @@
 //
 // Decode attention, out[h] = softmax(q_h K^T / sqrt(D)) V over the first T tokens of kv head
 // h / (Hq / Hkv), in two launches (split over tokens, then a merge):
-//   split kernel, block (split, h), 256 threads: each thread scores whole tokens (its key row
-//   read with 16-byte loads, codes converted in registers, q in registers), the block takes
-//   its max and the exponentials, then every wave accumulates p_t * value row for a quarter
-//   of the tokens with one lane per pair of dimensions (a value row is one coalesced read);
-//   the partial (max, sum, unnormalized output) goes to the workspace;
+//   split kernel, block (split, group of query heads), 256 threads: a cached row is read by a
+//   few consecutive lanes with one 16-byte load each, so a wave load covers 8-32 whole rows
+//   (1-2 KB contiguous); scores are reduced across those lanes with DPP, and every lane keeps
+//   an online softmax (running max, sum, output segment) over the rows it reads; the slots and
+//   the waves are combined at the end into the split's (max, sum, unnormalized output);
 //   merge kernel: rescales the splits to the common max and normalizes.
 // Dequantization happens in registers only; the cache is read once.
 #include "common.h"
@@ -25,7 +25,16 @@ namespace w4a16 {
 namespace {
 
 constexpr int kKvThreads = 256;
-constexpr int kKvChunkMax = 2048;       // tokens per split (LDS scores)
+// Token splits per head: about kKvBlocks split blocks over all heads, at least kKvMinRows rows
+// each (so at most kKvBlocks splits of one head).
+#ifndef W4A16_KV_MIN_ROWS
+#define W4A16_KV_MIN_ROWS 256
+#endif
+#ifndef W4A16_KV_LOADS
+#define W4A16_KV_LOADS 4
+#endif
+constexpr int kKvBlocks = 2048;
+constexpr int kKvMinRows = W4A16_KV_MIN_ROWS;
 
 // Quantize rows of D values: lane owns 8 consecutive values; D / 8 lanes per row.
 template <int DT, int BITS, int D>
@@ -99,160 +108,340 @@ __device__ __forceinline__ void codes8(uint32_t a, uint32_t b, float c[8]) {
     }
 }
 
-template <int DT, int BITS, int D>
+// Geometry of the split kernel: a cached row of RB bytes is read by LPR consecutive lanes with
+// one 16-byte load each (EPL codes per lane), so one wave load covers RPW whole rows, and a
+// wave takes U such loads of K (and of V) per iteration.
+template <int BITS, int D>
+struct KvGeom {
+    static constexpr int RB = BITS == 8 ? D : D / 2;
+    static constexpr int LPR = RB / 16;
+    static constexpr int RPW = 64 / LPR;
+    static constexpr int EPL = D / LPR;
+    static constexpr int U = W4A16_KV_LOADS;
+    static constexpr int ROWS_IT = RPW * U;
+};
+
+// Sum over the LPR (2, 4 or 8) consecutive lanes of a row group; every lane of the group gets
+// the same bits (each step adds the same two operands in both lanes of a pair).
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+    v += dpp_mov<0xB1>(v);                          // quad_perm [1,0,3,2]
+    if constexpr (LPR >= 4) v += dpp_mov<0x4E>(v);  // quad_perm [2,3,0,1]
+    if constexpr (LPR >= 8) v += dpp_mov<0x141>(v); // row_half_mirror
+    return v;
+}
+
+// The 16 (KV8) or 32 (KV4) codes of a 16-byte load, lowest address first, as floats, one
+// byte-to-float conversion each.  KV8 codes come out offset by +128 (the sign bit flipped, so
+// every byte is unsigned); the caller removes the offset with one term per row.
+template <int BITS>
+__device__ __forceinline__ void codes16(const u32x4& w, float* c) {
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if constexpr (BITS == 8) {
+            const uint32_t u = ww[k] ^ 0x80808080u;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) c[4 * k + i] = (float)((u >> (8 * i)) & 0xFFu);
+        } else {
+            uint32_t lo = ww[k] & 0x0F0F0F0Fu;                // codes 0, 2, 4, 6
+            uint32_t hi = (ww[k] >> 4) & 0x0F0F0F0Fu;         // codes 1, 3, 5, 7
+            // opaque to the optimizer, so each byte below stays one byte-to-float conversion
+            // instead of being refolded into a bit-field extract plus a conversion
+            asm volatile("" : "+v"(lo), "+v"(hi));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                c[8 * k + 2 * i] = (float)((lo >> (8 * i)) & 0xFFu);
+                c[8 * k + 2 * i + 1] = (float)((hi >> (8 * i)) & 0xFFu);
+            }
+        }
+    }
+}
+
+// One block = one token split x GQ query heads that share a kv head.  Lane (slot, seg) reads
+// segment seg of row slot of every wave load and keeps, per query head, its own running max m,
+// sum l and unnormalized output segment (online softmax over the rows of its slot); scores are
+// in the base-2 domain (q is prescaled by log2(e) / sqrt(D)).  At the end the slots and the
+// four waves are combined and the block's (m, l, o[D]) goes to the workspace.
+template <int DT, int BITS, int D, int GQ>
 __global__ __launch_bounds__(kKvThreads) void kv_attn_split_kernel(
     const uint16_t* __restrict__ q, int Hq, int Hkv, int T, int Tmax, int chunk,
     const void* __restrict__ kc, const uint16_t* __restrict__ ks, const uint16_t* __restrict__ kz,
     const void* __restrict__ vc, const uint16_t* __restrict__ vs, const uint16_t* __restrict__ vz,
     float* __restrict__ part) {
-    constexpr int RB = BITS == 8 ? D : D / 2;          // bytes per cached row
-    __shared__ float sc[kKvChunkMax];
-    __shared__ float red[kKvThreads];
-    __shared__ float acc_w[4][D];
+    using G = KvGeom<BITS, D>;
+    constexpr int RB = G::RB, LPR = G::LPR, RPW = G::RPW, EPL = G::EPL, U = G::U;
+    constexpr int NW = kKvThreads / 64;
+    __shared__ float pacc[GQ][NW][D];
+    __shared__ float pm[GQ][NW], pl[GQ][NW];
     const int split = blockIdx.x;
-    const int h = blockIdx.y;
     const int nsplit = gridDim.x;
-    const int kvh = h / (Hq / Hkv);
+    const int h0 = blockIdx.y * GQ;
+    const int kvh = h0 / (Hq / Hkv);
     const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int seg = lane % LPR, slot = lane / LPR;
     const int t0 = split * chunk;
     const int t1 = min(T, t0 + chunk);
-    const int n = max(0, t1 - t0);
     const long long rowbase = (long long)kvh * Tmax;
-    // q in registers (fp32) and its sum (for the KV4 zero point)
-    float qv[D];
+    const float NEG = -__builtin_inff();
+
+    // uniform per-head bases and 32-bit per-lane offsets (Tmax * RB < 2^32)
+    const unsigned char* kb = static_cast<const unsigned char*>(kc) + rowbase * RB;
+    const unsigned char* vb = static_cast<const unsigned char*>(vc) + rowbase * RB;
+    const uint16_t* ksb = ks + rowbase;
+    const uint16_t* vsb = vs + rowbase;
+    const uint16_t* kzb = BITS == 4 ? kz + rowbase : nullptr;
+    const uint16_t* vzb = BITS == 4 ? vz + rowbase : nullptr;
+    constexpr int STRIDE = NW * G::ROWS_IT;
+
+    // The loads of one wave iteration (rows base + u RPW + slot); rows past the split are
+    // clamped to its last row (always in the cache) and masked out of the softmax.
+    struct Raw {
+        u32x4 kw[U], vw[U];
+        uint16_t ks[U], vs[U], kz[U], vz[U];
+    };
+    auto issue = [&](int base, Raw& R) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) qv[d] = in2f<DT>(q[(long long)h * D + d]);
-    float qsum = 0.0f;
-    if constexpr (BITS == 4) {
-#pragma unroll
-        for (int d = 0; d < D; ++d) qsum += qv[d];
-    }
-    const float rsd = 1.0f / sqrtf((float)D);
-    // 1. scores of this split, one thread per token
-    float mloc = -__builtin_inff();
-    for (int i = tid; i < n; i += kKvThreads) {
-        const long long row = rowbase + t0 + i;
-        const unsigned char* kr = static_cast<const unsigned char*>(kc) + row * RB;
-        float dot = 0.0f;
-#pragma unroll
-        for (int p = 0; p < RB / 16; ++p) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(kr + 16 * p);
-            float c[8];
-            if constexpr (BITS == 8) {
-                codes8<8>(w.x, w.y, c);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) dot = fmaf(qv[16 * p + e], c[e], dot);
-                codes8<8>(w.z, w.w, c);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) dot = fmaf(qv[16 * p + 8 + e], c[e], dot);
-            } else {
-                const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    codes8<4>(ww[k], 0u, c);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) dot = fmaf(qv[32 * p + 8 * k + e], c[e], dot);
-                }
+        for (int u = 0; u < U; ++u) {
+            const int r = base + u * RPW + slot;
+            const uint32_t row = (uint32_t)(r < t1 ? r : t1 - 1);
+            const uint32_t off = row * (uint32_t)RB + 16u * (uint32_t)seg;
+            R.kw[u] = *reinterpret_cast<const u32x4*>(kb + off);
+            R.vw[u] = *reinterpret_cast<const u32x4*>(vb + off);
+            R.ks[u] = ksb[row];
+            R.vs[u] = vsb[row];
+            if constexpr (BITS == 4) {
+                R.kz[u] = kzb[row];
+                R.vz[u] = vzb[row];
             }
         }
-        const float s = h2f(ks[row]);
-        float score;
-        if constexpr (BITS == 8) score = dot * s * rsd;
-        else score = (dot - h2f(kz[row]) * qsum) * s * rsd;
-        sc[i] = score;
-        mloc = fmaxf(mloc, score);
-    }
-    red[tid] = mloc;
-    __syncthreads();
-    for (int w = kKvThreads / 2; w > 0; w >>= 1) {
-        if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-        __syncthreads();
-    }
-    const float m = red[0];
-    __syncthreads();
-    float lsum = 0.0f;
-    for (int i = tid; i < n; i += kKvThreads) {
-        const float p = expf(sc[i] - m);
-        sc[i] = p;
-        lsum += p;
-    }
-    red[tid] = lsum;
-    __syncthreads();
-    for (int w = kKvThreads / 2; w > 0; w >>= 1) {
-        if (tid < w) red[tid] += red[tid + w];
-        __syncthreads();
-    }
-    const float l = red[0];
-    // 2. p V: wave w takes tokens w, w + 4, ...; lane owns dimensions 2 lane, 2 lane + 1 (D = 128)
-    //    or lane (D = 64)
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
-    constexpr int DPL = D / 64;                      // dimensions per lane
-    float acc[DPL];
+    };
+
+    // the query's loads, then the first iteration's, are issued before either is waited on
+    const int base0 = t0 + wave * G::ROWS_IT;
+    u32x4 qraw[GQ][EPL / 8];
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) acc[j] = 0.0f;
-    for (int i = wave; i < n; i += 4) {
-        const long long row = rowbase + t0 + i;
-        const float ps = sc[i] * h2f(vs[row]);
-        const unsigned char* vr = static_cast<const unsigned char*>(vc) + row * RB;
-        if constexpr (BITS == 8) {
-            if constexpr (DPL == 2) {
-                const uint32_t two = *reinterpret_cast<const uint16_t*>(vr + 2 * lane);
-                acc[0] = fmaf(ps, (float)(int)(signed char)two, acc[0]);
-                acc[1] = fmaf(ps, (float)(int)(signed char)(two >> 8), acc[1]);
-            } else {
-                acc[0] = fmaf(ps, (float)(int)(signed char)vr[lane], acc[0]);
+    for (int g = 0; g < GQ; ++g)
+#pragma unroll
+        for (int p = 0; p < EPL / 8; ++p)
+            qraw[g][p] = *reinterpret_cast<const u32x4*>(q + (long long)(h0 + g) * D + seg * EPL + 8 * p);
+    Raw A;
+    issue(base0, A);      // a wave with no rows reads the split's last row and masks it
+    __builtin_amdgcn_sched_barrier(0);
+
+    // this lane's segment of each query head, prescaled; its segment sum (code offset term)
+    const float qscale = 1.4426950408889634f / sqrtf((float)D);
+    float qv[GQ][EPL], qseg[GQ];
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) {
+#pragma unroll
+        for (int p = 0; p < EPL / 8; ++p) {
+            const uint32_t ww[4] = {qraw[g][p].x, qraw[g][p].y, qraw[g][p].z, qraw[g][p].w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qv[g][8 * p + i] = in2f<DT>((ww[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) * qscale;
+        }
+        qseg[g] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qseg[g] += qv[g][e];
+    }
+    float m[GQ], l[GQ], acc[GQ][EPL], zoff[GQ];
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) {
+        m[g] = NEG;
+        l[g] = 0.0f;
+        zoff[g] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
+    }
+
+    // online-softmax update with the rows of one iteration
+    auto consume = [&](int base, const Raw& R, auto first) {
+        float sc[GQ][U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool ok = base + u * RPW + slot < t1;
+            const float ksc = h2f(R.ks[u]);
+            float c[EPL];
+            codes16<BITS>(R.kw[u], c);
+#pragma unroll
+            for (int g = 0; g < GQ; ++g) {
+                float d = 0.0f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) d = fmaf(qv[g][e], c[e], d);
+                d = fmaf(BITS == 4 ? -h2f(R.kz[u]) : -128.0f, qseg[g], d);
+                d = group_sum<LPR>(d);
+                sc[g][u] = ok ? d * ksc : NEG;
             }
-        } else {
-            const float z = h2f(vz[row]);
-            if constexpr (DPL == 2) {
-                const uint32_t b = vr[lane];
-                acc[0] = fmaf(ps, (float)(b & 0xFu) - z, acc[0]);
-                acc[1] = fmaf(ps, (float)(b >> 4) - z, acc[1]);
+        }
+        float pv[GQ][U];
+#pragma unroll
+        for (int g = 0; g < GQ; ++g) {
+            float mt = sc[g][0];
+#pragma unroll
+            for (int u = 1; u < U; ++u) mt = fmaxf(mt, sc[g][u]);
+            const float mn = fmaxf(m[g], mt);
+            const bool any = mn != NEG;
+            const float corr = any ? exp2f(m[g] - mn) : 1.0f;
+            float ps = 0.0f;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float p = any ? exp2f(sc[g][u] - mn) : 0.0f;
+                ps += p;
+                pv[g][u] = p * h2f(R.vs[u]);
+            }
+            m[g] = mn;
+            if constexpr (decltype(first)::value) {     // nothing accumulated yet
+                l[g] = ps;
             } else {
-                const uint32_t b = vr[lane >> 1];
-                acc[0] = fmaf(ps, (float)((b >> (4 * (lane & 1))) & 0xFu) - z, acc[0]);
+                l[g] = fmaf(l[g], corr, ps);
+                zoff[g] *= corr;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[g][e] *= corr;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float c[EPL];
+            codes16<BITS>(R.vw[u], c);
+#pragma unroll
+            for (int g = 0; g < GQ; ++g) {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(pv[g][u], c[e], acc[g][e]);
+                zoff[g] = fmaf(pv[g][u], BITS == 4 ? h2f(R.vz[u]) : 128.0f, zoff[g]);
+            }
+        }
+    };
+
+    // (a consume whose rows are all masked changes nothing)
+    consume(base0, A, std::true_type{});
+    for (int base = base0 + STRIDE; base < t1; base += STRIDE) {
+        issue(base, A);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(base, A, std::false_type{});
+    }
+
+    // combine the slots of the wave (lanes with the same segment), then the waves
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) {
+        float M = m[g];
+#pragma unroll
+        for (int off = LPR; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+        const float f = m[g] == NEG ? 0.0f : exp2f(m[g] - M);
+        float lw = l[g] * f;
+#pragma unroll
+        for (int off = LPR; off < 64; off <<= 1) lw += __shfl_xor(lw, off, 64);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            float a = (acc[g][e] - zoff[g]) * f;
+#pragma unroll
+            for (int off = LPR; off < 64; off <<= 1) a += __shfl_xor(a, off, 64);
+            acc[g][e] = a;
+        }
+        if (slot == 0) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) pacc[g][wave][seg * EPL + e] = acc[g][e];
+            if (seg == 0) {
+                pm[g][wave] = M;
+                pl[g][wave] = lw;
             }
         }
     }
-#pragma unroll
-    for (int j = 0; j < DPL; ++j) acc_w[wave][DPL * lane + j] = acc[j];
     __syncthreads();
-    float* out = part + ((long long)h * nsplit + split) * (D + 2);
-    for (int d = tid; d < D; d += kKvThreads) out[2 + d] = acc_w[0][d] + acc_w[1][d] + acc_w[2][d] + acc_w[3][d];
-    if (tid == 0) {
-        out[0] = n > 0 ? m : -__builtin_inff();
-        out[1] = l;
+    for (int idx = tid; idx < GQ * D; idx += kKvThreads) {
+        const int g = idx / D, d = idx % D;
+        float M = pm[g][0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) M = fmaxf(M, pm[g][w]);
+        float o = 0.0f, lt = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float f = pm[g][w] == NEG ? 0.0f : exp2f(pm[g][w] - M);
+            o = fmaf(pacc[g][w][d], f, o);
+            lt = fmaf(pl[g][w], f, lt);
+        }
+        float* out = part + ((long long)(h0 + g) * nsplit + split) * (D + 2);
+        out[2 + d] = o;
+        if (d == 0) {
+            out[0] = M;
+            out[1] = lt;
+        }
     }
 }
 
+// One block per query head.  Thread (phase, d) folds output dimension d of splits phase,
+// phase + PH, ... into a running (max, sum, output), eight splits per step with all their loads
+// independent (a head with up to 8 PH splits takes one memory round trip); the PH phases are
+// then combined through LDS.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void kv_attn_merge_kernel(const float* __restrict__ part, int nsplit,
                                                             uint16_t* __restrict__ out) {
+    constexpr int PH = 256 / D;
+    constexpr int S = 8;
+    __shared__ float sm[PH][D], sl[PH][D], so[PH][D];
     const int h = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int d = tid % D, ph = tid / D;
+    const float NEG = -__builtin_inff();
     const float* p = part + (long long)h * nsplit * (D + 2);
-    float m = -__builtin_inff();
-    for (int j = 0; j < nsplit; ++j) m = fmaxf(m, p[j * (D + 2)]);
-    float l = 0.0f;
-    for (int j = 0; j < nsplit; ++j) {
-        const float mj = p[j * (D + 2)];
-        if (mj != -__builtin_inff()) l += p[j * (D + 2) + 1] * expf(mj - m);
-    }
-    for (int d = threadIdx.x; d < D; d += 256) {
-        float o = 0.0f;
-        for (int j = 0; j < nsplit; ++j) {
-            const float mj = p[j * (D + 2)];
-            if (mj != -__builtin_inff()) o += p[j * (D + 2) + 2 + d] * expf(mj - m);
+    float M = NEG, L = 0.0f, O = 0.0f;
+    for (int j0 = ph; j0 < nsplit; j0 += S * PH) {
+        float mj[S], lj[S], oj[S];
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+            const int j = j0 + i * PH;
+            const long long at = (long long)(j < nsplit ? j : j0) * (D + 2);
+            mj[i] = p[at];
+            lj[i] = p[at + 1];
+            oj[i] = p[at + 2 + d];
+            if (j >= nsplit) mj[i] = NEG;
         }
-        out[(long long)h * D + d] = f2out<DT>(o / l);
+        float mn = M;
+#pragma unroll
+        for (int i = 0; i < S; ++i) mn = fmaxf(mn, mj[i]);
+        if (mn == NEG) continue;
+        const float c = exp2f(M - mn);
+        L *= c;
+        O *= c;
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+            const float w = mj[i] == NEG ? 0.0f : exp2f(mj[i] - mn);
+            L = fmaf(lj[i], w, L);
+            O = fmaf(oj[i], w, O);
+        }
+        M = mn;
+    }
+    sm[ph][d] = M;
+    sl[ph][d] = L;
+    so[ph][d] = O;
+    __syncthreads();
+    if (tid < D) {
+        float mx = sm[0][tid];
+#pragma unroll
+        for (int k = 1; k < PH; ++k) mx = fmaxf(mx, sm[k][tid]);
+        float lt = 0.0f, ot = 0.0f;
+#pragma unroll
+        for (int k = 0; k < PH; ++k) {
+            const float w = sm[k][tid] == NEG ? 0.0f : exp2f(sm[k][tid] - mx);
+            lt = fmaf(sl[k][tid], w, lt);
+            ot = fmaf(so[k][tid], w, ot);
+        }
+        out[(long long)h * D + tid] = f2out<DT>(ot / lt);
     }
 }
 
 int kv_splits(int Hq, int T) {
-    int ns = (1024 + Hq - 1) / Hq;                     // about four blocks per CU in all
-    ns = min(ns, (T + 63) / 64);                        // at least 64 tokens per split
-    ns = max(ns, (T + kKvChunkMax - 1) / kKvChunkMax);  // at most kKvChunkMax per split
+    int ns = (kKvBlocks + Hq - 1) / Hq;
+    ns = min(ns, (T + kKvMinRows - 1) / kKvMinRows);
     return max(ns, 1);
+}
+
+// query heads per block: those of one kv head, up to 4 (KV8) or 2 (KV4) to bound registers
+template <int BITS>
+int kv_group(int Hq, int Hkv) {
+    const int grp = Hq / Hkv;
+    if (BITS == 8 && grp % 4 == 0) return 4;
+    return grp % 2 == 0 ? 2 : 1;
 }
 
 template <int DT, int BITS, int D>
@@ -261,8 +450,17 @@ hipError_t kv_attn(const void* q, int Hq, int Hkv, int T, int Tmax, const void* 
                    void* out, hipStream_t st) {
     const int ns = kv_splits(Hq, T);
     const int chunk = (T + ns - 1) / ns;
-    hipLaunchKernelGGL((kv_attn_split_kernel<DT, BITS, D>), dim3(ns, Hq), dim3(kKvThreads), 0, st,
-                       static_cast<const uint16_t*>(q), Hq, Hkv, T, Tmax, chunk, kc, ks, kz, vc, vs, vz, work);
+    const int gq = kv_group<BITS>(Hq, Hkv);
+    const auto qp = static_cast<const uint16_t*>(q);
+    if (gq == 4)
+        hipLaunchKernelGGL((kv_attn_split_kernel<DT, BITS, D, (BITS == 8 ? 4 : 1)>), dim3(ns, Hq / 4),
+                           dim3(kKvThreads), 0, st, qp, Hq, Hkv, T, Tmax, chunk, kc, ks, kz, vc, vs, vz, work);
+    else if (gq == 2)
+        hipLaunchKernelGGL((kv_attn_split_kernel<DT, BITS, D, 2>), dim3(ns, Hq / 2), dim3(kKvThreads), 0, st, qp,
+                           Hq, Hkv, T, Tmax, chunk, kc, ks, kz, vc, vs, vz, work);
+    else
+        hipLaunchKernelGGL((kv_attn_split_kernel<DT, BITS, D, 1>), dim3(ns, Hq), dim3(kKvThreads), 0, st, qp, Hq,
+                           Hkv, T, Tmax, chunk, kc, ks, kz, vc, vs, vz, work);
     hipLaunchKernelGGL((kv_attn_merge_kernel<DT, D>), dim3(Hq), dim3(256), 0, st, work, ns,
                        static_cast<uint16_t*>(out));
     return hipGetLastError();
