@@ -465,7 +465,69 @@ def run_extras(layers, copies, W4, synth, torch, np):
     out["awq_4096x4096_g128"] = run_awq(W4, synth, torch)
     out["w8a8_m4096"] = run_w8a8(W4, synth, torch)
     out["kv_decode_attention_h32_d128_t4096"] = run_kv(W4, synth, torch)
+    out["full_stack_7b_32_layers"] = run_stack(W4, synth, torch)
     return out
+
+
+def run_stack(W4, synth, torch):
+    """The full decode step of a 32-layer 7B-shaped stack: 224 linears (q, k, v, o, gate, up,
+    down per layer), about 3.5 GB of packed weights, bf16 activations, launched back to back on
+    one stream (graph-captured); g = 128 at M = 1 and M = 8, and the per-channel variant
+    (g = K) at M = 1.  Bytes: every linear's packed weights and metadata."""
+    res = {}
+    for per_channel in (False, True):
+        layers = []
+        for c in synth.stack_cases(1, per_channel):
+            W = synth.weights_device(c.N, c.K, c.w_sigma, synth.seeds(c.config, c.layer)[0])
+            qw, s, z = W4.quantize_pack(W, c.g, c.scheme)
+            del W
+            layers.append((c, qw, s, z))
+        nbytes = sum(weight_bytes(c.N, c.K, c.g) for c, *_ in layers)
+        for M in ((1, 8) if not per_channel else (1,)):
+            xs = {K: synth.activations_device(M, K, synth.BF16, 8000 + K + M) for K in (4096, 11008)}
+            ys = [torch.empty((M, c.N), dtype=torch.bfloat16, device="cuda") for c, *_ in layers]
+
+            def step(i, xs=xs, ys=ys, layers=layers):
+                for (c, qw, s, z), y in zip(layers, ys):
+                    W4.linear(xs[c.K], qw, s, z, c.g, out=y)
+            for i in range(2):
+                step(i)
+            ms = time_loop(step, 5, torch)
+            gbps = nbytes / (ms * 1e-3) / 1e9
+            key = f"{'per_channel' if per_channel else 'g128'}_M{M}"
+            res[key] = {"ms_per_step": round(ms, 3), "GBps": round(gbps, 1),
+                        "frac_hbm_peak": round(gbps / HBM_PEAK_GBS, 4), "weight_GB": round(nbytes / 1e9, 3)}
+            log(f"  full stack {key}: {res[key]}")
+            del ys, xs
+        del layers
+        torch.cuda.empty_cache()
+    # context: the same step with q, k, v and gate, up concatenated along N (one launch each,
+    # the usual serving layout; the same kernels at N = 12288 and N = 22016), g = 128, M = 1
+    fused = [(4096, 12288), (4096, 4096), (4096, 22016), (11008, 4096)]
+    layers = []
+    for layer in range(32):
+        for j, (K, N) in enumerate(fused):
+            W = synth.weights_device(N, K, 0.02, 9000 + 4 * layer + j)
+            layers.append((K, N) + tuple(W4.quantize_pack(W, GROUP, W4.ASYM)))
+            del W
+    nbytes = sum(weight_bytes(N, K, GROUP) for K, N, *_ in layers)
+    xs = {K: synth.activations_device(1, K, synth.BF16, 8100 + K) for K in (4096, 11008)}
+    ys = [torch.empty((1, N), dtype=torch.bfloat16, device="cuda") for _, N, *_ in layers]
+
+    def step_fused(i):
+        for (K, N, qw, s, z), y in zip(layers, ys):
+            W4.linear(xs[K], qw, s, z, GROUP, out=y)
+    for i in range(2):
+        step_fused(i)
+    ms = time_loop(step_fused, 5, torch)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    res["g128_M1_fused_qkv_gateup"] = {"ms_per_step": round(ms, 3), "GBps": round(gbps, 1),
+                                       "frac_hbm_peak": round(gbps / HBM_PEAK_GBS, 4),
+                                       "weight_GB": round(nbytes / 1e9, 3)}
+    log(f"  full stack fused q/k/v and gate/up, M=1: {res['g128_M1_fused_qkv_gateup']}")
+    del layers, ys
+    torch.cuda.empty_cache()
+    return res
 
 
 def run_kv(W4, synth, torch, H=32, D=128, T=4096, layers=32):
