@@ -37,9 +37,9 @@ GROUP = 128
 
 
 # Kernel instantiation serving each layer at M = 1 (fp16, g = 128), as rocprofv3 names it.
-KERNEL_NAMES = {(4096, 4096): "gemv_stream_kernel<0, 1, 2, 2, 8, 0>",
-                (4096, 11008): "gemv_stream_kernel<0, 1, 2, 2, 8, 2>",
-                (11008, 4096): "gemv_stream_kernel<0, 1, 6, 2, 8, 0>"}
+KERNEL_NAMES = {(4096, 4096): "gemv_stream_kernel<0, 1, 2, 1, 8, 0>",
+                (4096, 11008): "gemv_stream_kernel<0, 1, 2, 2, 8, 0>",
+                (11008, 4096): "gemv_stream_kernel<0, 1, 6, 1, 8, 0>"}
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "w4a16_dequant_gemm_amd", "csrc", f)
                   for f in ("gemv.hip", "common.h")]

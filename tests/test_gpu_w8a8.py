@@ -33,10 +33,14 @@ def _f32bits(t) -> np.ndarray:
     return (t.cpu().numpy() if isinstance(t, torch.Tensor) else t).astype(np.float32).view(np.uint32)
 
 
-@pytest.mark.parametrize("dtype,a", [(FP16, 2), (BF16, 1), (FP16, 4), (FP16, 0)])
-def test_smooth_factors(dtype, a):
-    X = calibration(200, 320, dtype, seed=a + 1, outlier_frac=0.02, outlier_mult=40.0)
-    W = weights(96, 320, 0.02, seed=a + 2)
+# K % 4 == 0 takes the 64-channel tile kernel (ragged last tile at 4100, rows not a
+# multiple of the 512-row stride); K = 322 the one-thread-per-channel kernel
+@pytest.mark.parametrize("dtype,a,n,N,K", [(FP16, 2, 200, 96, 320), (BF16, 1, 200, 96, 320), (FP16, 4, 200, 96, 320),
+                                           (FP16, 0, 200, 96, 320), (FP16, 2, 90, 50, 322),
+                                           (BF16, 2, 1000, 700, 4100), (FP16, 3, 3, 1, 64)])
+def test_smooth_factors(dtype, a, n, N, K):
+    X = calibration(n, K, dtype, seed=a + 1, outlier_frac=0.02, outlier_mult=40.0)
+    W = weights(N, K, 0.02, seed=a + 2)
     W[:, 7] = 0.0
     s = W4.w8a8_smooth(x_to_torch(X, dtype), torch.from_numpy(W).cuda(), a)
     np.testing.assert_array_equal(_f32bits(s), _f32bits(Q.smooth_factors(X, dtype, W, a)))

@@ -630,7 +630,16 @@ constexpr int lds_rb(int M, int CPL) { return M * CPL >= 4 ? 1 : 2; }
 constexpr int lds_max_cpl(int M) {
     return M == 1 ? 6 : (M == 2 ? 4 : (M == 3 ? 3 : (M == 4 ? 2 : 0)));
 }
-constexpr int kStreamWaves = 8;       // waves per block: two per SIMD
+#ifndef W4A16_STREAM_WAVES
+#define W4A16_STREAM_WAVES 8
+#endif
+#ifndef W4A16_ONE_ROW_BLOCKS
+#define W4A16_ONE_ROW_BLOCKS 512
+#endif
+#ifndef W4A16_TWO_ROW_BLOCKS
+#define W4A16_TWO_ROW_BLOCKS 768
+#endif
+constexpr int kStreamWaves = W4A16_STREAM_WAVES;       // waves per block: two per SIMD
 
 struct LdsCfg {
     int cpl = 0;
@@ -639,8 +648,13 @@ struct LdsCfg {
     int lds = 0;               // dynamic LDS bytes
 };
 
-// One block per CU (256) when N allows, each owning ceil(N / 256) rows.  The block's
-// activations, chunk sums and (scale, zero) words must fit the LDS budget.
+// Rows per block: one row per wave while that takes at most kOneRowBlocks blocks (two per
+// CU), else two rows per wave while that takes at most kTwoRowBlocks (three per CU), so the
+// wave loads its rows at once; larger N: one block per CU (256), each owning ceil(N / 256)
+// rows streamed in batches.  The block's activations, chunk sums and (scale, zero) words
+// must fit the LDS budget.
+constexpr int kOneRowBlocks = W4A16_ONE_ROW_BLOCKS;
+constexpr int kTwoRowBlocks = W4A16_TWO_ROW_BLOCKS;
 LdsCfg pick_lds(int M, int N, int K, int G) {
     LdsCfg c;
     if (M < 1 || M > 4) return c;
@@ -648,8 +662,11 @@ LdsCfg pick_lds(int M, int N, int K, int G) {
     if (cpl > lds_max_cpl(M)) return c;
     // 32-bit buffer offsets: the packed weights must stay below 2 GiB
     if ((long long)N * (K / 2) >= (1LL << 31)) return c;
-    const int want = 256;
-    const int rpb = (N + want - 1) / want;
+    int rpb = (N + 255) / 256;
+    if ((N + kStreamWaves - 1) / kStreamWaves <= kOneRowBlocks)
+        rpb = kStreamWaves;
+    else if ((N + 2 * kStreamWaves - 1) / (2 * kStreamWaves) <= kTwoRowBlocks)
+        rpb = 2 * kStreamWaves;
     const long long pieces = ((long long)rpb * G + 7) / 8 + 1;      // 16-byte staging pieces
     if (pieces > (long long)kSzPiecesPerThread * 64 * kStreamWaves) return c;
     const long long lds = sz_lds_offset(M, cpl) + 64 * pieces;       // 8 float pairs per piece

@@ -51,6 +51,70 @@ __global__ __launch_bounds__(256) void smooth_kernel(const uint16_t* __restrict_
     s[k] = (xm == 0.0f || wm == 0.0f) ? 1.0f : v;
 }
 
+// The same factors for K % 4 == 0 with 8-byte aligned X and 16-byte aligned W rows: a block
+// owns 64 channels; thread (row group rg, column group cg) reads 4 channels of rows rg,
+// rg + 64, ... with 8 rows' loads in flight (rows past the end re-read the last row: max is
+// idempotent), then the 64 row groups are folded through LDS.  Same values as smooth_kernel
+// (a maximum does not depend on its order).
+template <int DT>
+__global__ __launch_bounds__(1024) void smooth_tile_kernel(const uint16_t* __restrict__ X, int n,
+                                                           const float* __restrict__ W, int N, int K, int a,
+                                                           float* __restrict__ s) {
+    constexpr int U = 8;
+    __shared__ float red[2][64][65];
+    const int tid = threadIdx.x;
+    const int cg = tid & 15, rg = tid >> 4;
+    const int k0 = blockIdx.x * 64 + 4 * cg;
+    const int kk = k0 < K ? k0 : 0;
+    float xm[4] = {0.0f, 0.0f, 0.0f, 0.0f}, wm[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = rg; t < n; t += 64 * U) {
+        uint2 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = *reinterpret_cast<const uint2*>(X + (long long)min(t + 64 * u, n - 1) * K + kk);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            xm[0] = fmaxf(xm[0], fabsf(in2f<DT>(v[u].x & 0xFFFFu)));
+            xm[1] = fmaxf(xm[1], fabsf(in2f<DT>(v[u].x >> 16)));
+            xm[2] = fmaxf(xm[2], fabsf(in2f<DT>(v[u].y & 0xFFFFu)));
+            xm[3] = fmaxf(xm[3], fabsf(in2f<DT>(v[u].y >> 16)));
+        }
+    }
+    for (int r = rg; r < N; r += 64 * U) {
+        float4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = *reinterpret_cast<const float4*>(W + (long long)min(r + 64 * u, N - 1) * K + kk);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            wm[0] = fmaxf(wm[0], fabsf(v[u].x));
+            wm[1] = fmaxf(wm[1], fabsf(v[u].y));
+            wm[2] = fmaxf(wm[2], fabsf(v[u].z));
+            wm[3] = fmaxf(wm[3], fabsf(v[u].w));
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        red[0][rg][4 * cg + j] = xm[j];
+        red[1][rg][4 * cg + j] = wm[j];
+    }
+    __syncthreads();
+    if (tid < 64) {
+        const int k = blockIdx.x * 64 + tid;
+        float x = 0.0f, w = 0.0f;
+        for (int g = 0; g < 64; ++g) {
+            x = fmaxf(x, red[0][g][tid]);
+            w = fmaxf(w, red[1][g][tid]);
+        }
+        if (k < K) {
+            const float num = pow_quarters(x, a);
+            const float den = pow_quarters(w, 4 - a);
+            const float v = num / (den == 0.0f ? 1.0f : den);
+            s[k] = (x == 0.0f || w == 0.0f) ? 1.0f : v;
+        }
+    }
+}
+
 // Row-wise symmetric INT8: v = w * s_j (WEIGHT) or x / s_j; one workgroup per row.
 template <int DT, bool WEIGHT>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ src, int K,
@@ -278,11 +342,20 @@ __global__ __launch_bounds__(256, 1) void w8a8_gemm_kernel(const int8_t* __restr
 
 hipError_t launch_w8a8_smooth(const void* X, int dtype, int n, const float* W, int N, int K, int a, float* s,
                               hipStream_t st) {
+    const auto x = static_cast<const uint16_t*>(X);
+    if (K % 4 == 0 && (reinterpret_cast<uintptr_t>(X) & 7) == 0 && (reinterpret_cast<uintptr_t>(W) & 15) == 0) {
+        const dim3 grid((K + 63) / 64);
+        if (dtype == DT_F16)
+            hipLaunchKernelGGL(smooth_tile_kernel<DT_F16>, grid, dim3(1024), 0, st, x, n, W, N, K, a, s);
+        else
+            hipLaunchKernelGGL(smooth_tile_kernel<DT_BF16>, grid, dim3(1024), 0, st, x, n, W, N, K, a, s);
+        return hipGetLastError();
+    }
     const dim3 grid((K + 255) / 256);
     if (dtype == DT_F16)
-        hipLaunchKernelGGL(smooth_kernel<DT_F16>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(X), n, W, N, K, a, s);
+        hipLaunchKernelGGL(smooth_kernel<DT_F16>, grid, dim3(256), 0, st, x, n, W, N, K, a, s);
     else
-        hipLaunchKernelGGL(smooth_kernel<DT_BF16>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(X), n, W, N, K, a, s);
+        hipLaunchKernelGGL(smooth_kernel<DT_BF16>, grid, dim3(256), 0, st, x, n, W, N, K, a, s);
     return hipGetLastError();
 }
 
