@@ -179,7 +179,62 @@ def cpu_baseline(layers, w_host, xs_host, y_gpu, budget_s, np, torch):
             "host_cpus": os.cpu_count(), "kind": "oracle",
             "sample": f"{steps} oracle step(s) of the same M=1 workload (3 layers, fp64 "
                       f"dequantize + BLAS matmul), {el:.1f} s",
-            "parity_vs_gpu": parity}
+            "parity_vs_gpu": parity,
+            "other_rows": cpu_baseline_rows(oracle, np)}
+
+
+def cpu_baseline_rows(oracle, np):
+    """The oracle of each further method on a bounded sample of its workload (a few seconds
+    each on the host cores), in the unit its GPU leg reports: GPTQ and AWQ in fp64
+    TFLOP/s of their algorithmic flops, W8A8 in TOP/s of the integer product, KV decode
+    attention in GB/s of the quantized cache."""
+    import synth
+    from oracle import awq, gptq, kv, w8a8
+    out = {}
+    # GPTQ, one 1024 x 1024 layer from 512 calibration rows
+    n, K, N = 512, 1024, 1024
+    X = synth.calibration(n, K, synth.FP16, 11)
+    W = synth.weights(N, K, 0.02, 12)
+    t0 = time.perf_counter()
+    U = gptq.inverse_cholesky_upper(gptq.damp_hessian(gptq.hessian(X, synth.FP16), 0.01))
+    t1 = time.perf_counter()
+    gptq.gptq_quantize(W, U, GROUP, oracle.ASYM)
+    t2 = time.perf_counter()
+    out["gptq"] = {"sample": f"K=N={K}, n={n}", "hessian_factor_s": round(t1 - t0, 3),
+                   "quantize_s": round(t2 - t1, 3),
+                   "quantize_fp64_TFLOPs": round(N * K * (K - 1) / (t2 - t1) / 1e12, 5)}
+    # AWQ, one 1024 x 1024 layer from 256 calibration rows
+    n = 256
+    X = synth.calibration(n, K, synth.FP16, 13, outlier_frac=0.01, outlier_mult=20.0)
+    t0 = time.perf_counter()
+    awq.awq_search(W, X, synth.FP16, awq.channel_mean_abs(X, synth.FP16), GROUP, oracle.ASYM)
+    t1 = time.perf_counter()
+    out["awq"] = {"sample": f"K=N={K}, n={n}", "search_s": round(t1 - t0, 3),
+                  "search_fp64_TFLOPs": round(9 * 2.0 * n * N * K / (t1 - t0) / 1e12, 5)}
+    # W8A8 with SmoothQuant, M = 128, K = N = 1024
+    M = 128
+    X = synth.calibration(M, K, synth.FP16, 14, outlier_frac=0.01, outlier_mult=20.0)
+    s = w8a8.smooth_factors(X, synth.FP16, W, 2)
+    qw, sw = w8a8.quantize_weight(W, s)
+    qx, sx = w8a8.quantize_act(X, synth.FP16, s)
+    t0 = time.perf_counter()
+    w8a8.linear_int8(qx, sx, qw, sw, synth.FP16)
+    t1 = time.perf_counter()
+    out["w8a8"] = {"sample": f"M={M}, K=N={K}", "product_s": round(t1 - t0, 3),
+                   "TOPS": round(2.0 * M * N * K / (t1 - t0) / 1e12, 5)}
+    # KV8 decode attention, 32 heads, D = 128, 2048 cached tokens
+    H, D, T = 32, 128, 2048
+    k = synth.activations(H * T, D, synth.FP16, 15).reshape(H, T, D)
+    v = synth.activations(H * T, D, synth.FP16, 16).reshape(H, T, D)
+    q = synth.activations(H, D, synth.FP16, 17)
+    Kd = kv.dequant_kv8(*kv.quantize_kv8(k, synth.FP16))
+    Vd = kv.dequant_kv8(*kv.quantize_kv8(v, synth.FP16))
+    t0 = time.perf_counter()
+    kv.attention_decode(q, synth.FP16, Kd, Vd, T)
+    t1 = time.perf_counter()
+    out["kv8_attention"] = {"sample": f"H={H}, D={D}, T={T}", "s": round(t1 - t0, 4),
+                            "GBps": round(2 * H * T * (D + 2) / (t1 - t0) / 1e9, 3)}
+    return out
 
 
 def traffic_run(K: int, N: int, W4, synth, torch, np):
