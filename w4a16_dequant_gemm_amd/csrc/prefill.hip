@@ -26,6 +26,7 @@
 //     in units of 2^-24; bf16: s' = s, c = 128 + z.
 #include "common.h"
 #include "launch.h"
+#include "tile.h"
 
 namespace w4a16 {
 
@@ -415,15 +416,10 @@ __global__ __launch_bounds__(256, 1) void prefill_f16_wide_kernel(
     const int wave = tid >> 6;
     const int l32 = lane & 31;
     const int h = lane >> 5;
-    const int tiles_n = (N + W_BN - 1) / W_BN;
-    const int tiles = ((M + W_BM - 1) / W_BM) * tiles_n;
-    // XCD-aware renumbering: hardware block b runs on XCD b % 8; the blocks of XCD x take
-    // tiles x * per_xcd + rank (the grid is padded to 8 * per_xcd)
-    const int per_xcd = (tiles + 7) / 8;
-    const int tile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (tile >= tiles) return;
-    const int m0 = (tile / tiles_n) * W_BM;
-    const int n0 = (tile % tiles_n) * W_BN;
+    int mt, nt;
+    if (!xcd_tile(blockIdx.x, (M + W_BM - 1) / W_BM, (N + W_BN - 1) / W_BN, mt, nt)) return;
+    const int m0 = mt * W_BM;
+    const int n0 = nt * W_BN;
     const int nsteps = K / W_BK;
 
     // Buffer loads: per-lane 32-bit offsets fixed for the whole K loop, the step's offset

@@ -21,6 +21,7 @@
 // CU; tiles assigned XCD-major.
 #include "common.h"
 #include "launch.h"
+#include "tile.h"
 
 namespace w4a16 {
 
@@ -223,13 +224,10 @@ __global__ __launch_bounds__(256, 1) void w8a8_gemm_kernel(const int8_t* __restr
     const int l32 = lane & 31;
     const int h = lane >> 5;
     const int wm = wave >> 1, wn = wave & 1;
-    const int tiles_n = (N + I_BN - 1) / I_BN;
-    const int tiles = ((M + I_BM - 1) / I_BM) * tiles_n;
-    const int per_xcd = (tiles + 7) / 8;
-    const int tile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (tile >= tiles) return;
-    const int m0 = (tile / tiles_n) * I_BM;
-    const int n0 = (tile % tiles_n) * I_BN;
+    int mt, nt;
+    if (!xcd_tile(blockIdx.x, (M + I_BM - 1) / I_BM, (N + I_BN - 1) / I_BN, mt, nt)) return;
+    const int m0 = mt * I_BM;
+    const int n0 = nt * I_BN;
     const int nsteps = K / I_BK;
 
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(qx), 0, 0x7FFFFFFF, 0x00020000);
