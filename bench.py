@@ -621,6 +621,48 @@ def run_kv(W4, synth, torch, H=32, D=128, T=4096, layers=32):
         res[f"kv{bits}"] = entry
         log(f"  kv{bits} decode attention H={H} D={D} T={T}: {entry}")
         del caches, k
+    res["batch16"] = run_kv_batch(W4, synth, torch, H=H, D=D)
+    return res
+
+
+def run_kv_batch(W4, synth, torch, B=16, H=32, D=128, Tmax=4096, layers=4):
+    """Decode attention for a batch of 16 sequences in one call (the serving case the cache
+    quantization is for), lengths drawn uniformly from [1024, 4096] (seeded), 4 layers'
+    caches in rotation (1.4-2.2 GB).  Bytes: each sequence's codes and per-token parameters
+    over its own length, plus q and the output."""
+    import numpy as np
+    lens = np.random.default_rng(7300).integers(1024, Tmax + 1, size=B).astype(np.int32)
+    lt = torch.from_numpy(lens).cuda()
+    q = synth.activations_device(B * H, D, synth.FP16, 7301).view(B, H, D)
+    out = torch.empty_like(q)
+    work = torch.empty(W4.kv_attention_batch_workspace(B, H, Tmax, D), dtype=torch.float32, device="cuda")
+    res = {"lengths": [int(x) for x in lens]}
+    for bits in (8, 4):
+        caches = []
+        for l in range(layers):
+            pair = []
+            for j in range(2):
+                x = synth.activations_device(B * H * Tmax, D, synth.FP16, 7400 + 2 * l + j).view(B * H, Tmax, D)
+                c, s, z = W4.kv_quantize(x, bits)
+                del x
+                pair.append((c.view(B, H, Tmax, -1), s.view(B, H, Tmax), None if z is None else z.view(B, H, Tmax)))
+            caches.append(pair)
+        row = D * bits // 8 + (2 if bits == 8 else 4)
+        nbytes = layers * (2 * H * int(lens.sum()) * row + 2 * 2 * B * H * D)
+
+        def step(i, bits=bits, caches=caches):
+            for kc, vc in caches:
+                W4.kv_attention_decode_batch(q, kc, vc, lt, bits, out=out, work=work)
+        for i in range(3):
+            step(i)
+        ms = time_loop(step, 10, torch)
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        entry = {"us_per_layer": round(ms * 1e3 / layers, 2), "GBps": round(gbps, 1),
+                 "frac_hbm_peak": round(gbps / HBM_PEAK_GBS, 4), "cache_MB_per_layer": round(nbytes / layers / 1e6, 1)}
+        res[f"kv{bits}"] = entry
+        log(f"  kv{bits} decode attention, batch of {B} (T 1024-4096), H={H} D={D}: {entry}")
+        del caches
+        torch.cuda.empty_cache()
     return res
 
 

@@ -320,6 +320,28 @@ int w4a16_kv_attention_decode(const void* q, int dtype, int64_t Hq, int64_t Hkv,
                               const uint16_t* vscales, const uint16_t* vzeros, float* work,
                               void* out, void* stream);
 
+/* fp32 elements of the w4a16_kv_attention_decode_batch workspace (host only), or a negative
+ * status. */
+int64_t w4a16_kv_attention_batch_workspace(int64_t B, int64_t Hq, int64_t Tmax, int64_t D);
+
+/*
+ * w4a16_kv_attention_decode_batch -- decode attention for a batch of B sequences, each over its
+ * own quantized cache, in one pair of launches: out[b][h] = softmax(q[b][h] . K_bt / sqrt(D)) V_b
+ * over the first lengths[b] tokens of sequence b, kv head h / (Hq / Hkv).  The serving case the
+ * cache quantization is for: more concurrent sequences in the same memory (page
+ * "量化实战深入（GPTQ / AWQ / SmoothQuant / KV 量化）", 六 KV Cache 量化).
+ *   q        [B, Hq, D] fp16/bf16, 16-byte aligned; out [B, Hq, D] same dtype.
+ *   lengths  device int32 [B]; each value is clamped into [1, Tmax] on the device.
+ *   caches   w4a16_kv_quantize output with H = B * Hkv and T = Tmax ([B, Hkv, Tmax, ...]).
+ *   work     w4a16_kv_attention_batch_workspace(B, Hq, Tmax, D) fp32 elements (scratch).
+ * Same arithmetic as w4a16_kv_attention_decode; B <= 65535, Tmax <= 2^24.
+ */
+int w4a16_kv_attention_decode_batch(const void* q, int dtype, int64_t B, int64_t Hq, int64_t Hkv,
+                                    const int32_t* lengths, int64_t Tmax, int64_t D, int bits,
+                                    const void* kcodes, const uint16_t* kscales, const uint16_t* kzeros,
+                                    const void* vcodes, const uint16_t* vscales, const uint16_t* vzeros,
+                                    float* work, void* out, void* stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* w4a16_strerror(int status);
 

@@ -41,7 +41,8 @@ def test_header_declares_the_boundary():
                      "w4a16_awq_search", "w4a16_awq_scale", "w4a16_w8a8_smooth",
                      "w4a16_w8a8_quantize_weight", "w4a16_w8a8_quantize_act", "w4a16_w8a8_linear",
                      "w4a16_kv_quantize", "w4a16_kv_attention_workspace",
-                     "w4a16_kv_attention_decode"):
+                     "w4a16_kv_attention_decode", "w4a16_kv_attention_batch_workspace",
+                     "w4a16_kv_attention_decode_batch"):
         assert required in names
 
 
@@ -212,3 +213,22 @@ def test_kv_rejects_invalid_arguments(lib):
     assert att(T=40) == L.ERR_SHAPE              # T > Tmax
     assert att(bits=4) == L.ERR_NULL             # KV4 needs zeros
     assert att(dt=7) == L.ERR_DTYPE
+
+
+def test_kv_batch_rejects_invalid_arguments(lib):
+    assert lib.w4a16_kv_attention_batch_workspace(16, 32, 4096, 128) > 0
+    assert lib.w4a16_kv_attention_batch_workspace(0, 32, 4096, 128) == L.ERR_SHAPE
+    assert lib.w4a16_kv_attention_batch_workspace(16, 32, 1 << 25, 128) == L.ERR_SHAPE
+    att = lambda **kw: lib.w4a16_kv_attention_decode_batch(
+        kw.get("q", A), kw.get("dt", 0), kw.get("B", 2), kw.get("Hq", 8), kw.get("Hkv", 4), kw.get("lens", C + 0x2000),
+        kw.get("Tmax", 32), 128, kw.get("bits", 8), B, C, None, B + 0x10000, C + 0x1000, None, D, D + 0x10000, None)
+    assert att(lens=None) == L.ERR_NULL
+    assert att(bits=4) == L.ERR_NULL             # KV4 needs zeros
+    assert att(dt=7) == L.ERR_DTYPE
+    assert att(bits=5) == L.ERR_SCHEME
+    assert att(B=0) == L.ERR_SHAPE
+    assert att(B=70000) == L.ERR_SHAPE
+    assert att(Hkv=3) == L.ERR_SHAPE             # Hq % Hkv != 0
+    assert att(Tmax=1 << 25) == L.ERR_SHAPE
+    assert att(q=A + 8) == L.ERR_ALIGN           # q must be 16-byte aligned
+    assert att(lens=C + 0x2002) == L.ERR_ALIGN

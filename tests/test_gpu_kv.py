@@ -1,7 +1,8 @@
 """GPU parity of the KV-cache entry points against the CPU oracle, through the C ABI.
 
 * quantization: KV8 / KV4 codes and fp16 scales (and zeros) bit-exact;
-* decode attention over the quantized caches: the output dtype tolerance (relative
+* decode attention over the quantized caches (one sequence, and a batch of sequences with
+  their own lengths): the output dtype tolerance (relative
   Frobenius <= 1e-3, max |d| <= 1e-2 max |ref|) against the fp64 oracle over the oracle's own
   quantized caches, with one token (closed form: the value row), grouped heads, ragged T
   inside a larger cache, long contexts that need several splits, and the 7B-like decode.
@@ -83,3 +84,40 @@ def test_attention_decode(Hq, Hkv, T, Tmax, D, bits, dtype):
         grp = Hq // Hkv
         row = np.stack([Vd[h // grp, 0] for h in range(Hq)])
         assert_close(y_to_f64(out), row, "single token")
+
+
+# Batched decode: B sequences with their own lengths in one call, against the single-sequence
+# oracle per sequence.  Lengths 0 and > Tmax exercise the documented clamp into [1, Tmax].
+BATCH_CASES = [(5, 8, 2, 300, 128, 8, FP16, [300, 1, 77, 256, 129]),
+               (3, 32, 8, 1024, 128, 4, BF16, [1024, 513, 2]),
+               (4, 4, 4, 200, 64, 8, BF16, [0, 200, 999, 64]),
+               (16, 32, 32, 2048, 128, 8, FP16, [2048 - 97 * i for i in range(16)])]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Tmax,D,bits,dtype,lens", BATCH_CASES)
+def test_attention_decode_batch(B, Hq, Hkv, Tmax, D, bits, dtype, lens):
+    k = _cache_host(B * Hkv, Tmax, D, dtype, seed=B + Tmax)
+    v = _cache_host(B * Hkv, Tmax, D, dtype, seed=B + Tmax + 1, outliers=False)
+    q = activations(B * Hq, D, dtype, seed=Tmax + B)
+    kc = W4.kv_quantize(_to_dev(k, dtype), bits)
+    vc = W4.kv_quantize(_to_dev(v, dtype), bits)
+
+    def batched(c):
+        codes, s, z = c
+        return (codes.view(B, Hkv, Tmax, -1), s.view(B, Hkv, Tmax), None if z is None else z.view(B, Hkv, Tmax))
+    lt = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    qd = x_to_torch(q, dtype).view(B, Hq, D)
+    out = W4.kv_attention_decode_batch(qd, batched(kc), batched(vc), lt, bits)
+    torch.cuda.synchronize()
+    if bits == 8:
+        Kd = KV.dequant_kv8(*KV.quantize_kv8(k, dtype))
+        Vd = KV.dequant_kv8(*KV.quantize_kv8(v, dtype))
+    else:
+        Kd = KV.dequant_kv4(*KV.quantize_kv4(k, dtype))
+        Vd = KV.dequant_kv4(*KV.quantize_kv4(v, dtype))
+    got = y_to_f64(out.view(B * Hq, D)).reshape(B, Hq, D)
+    for b in range(B):
+        T = min(max(lens[b], 1), Tmax)
+        ref = KV.attention_decode(q[b * Hq:(b + 1) * Hq], dtype, Kd[b * Hkv:(b + 1) * Hkv],
+                                  Vd[b * Hkv:(b + 1) * Hkv], T)
+        assert_close(got[b], ref_to_f64(ref, dtype), f"batch seq {b} T={T}")

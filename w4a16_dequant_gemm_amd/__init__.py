@@ -348,6 +348,44 @@ def kv_attention_workspace(Hq: int, T: int, D: int) -> int:
     return int(need)
 
 
+def kv_attention_batch_workspace(B: int, Hq: int, Tmax: int, D: int) -> int:
+    """fp32 elements of the scratch buffer that :func:`kv_attention_decode_batch` needs."""
+    need = lib().w4a16_kv_attention_batch_workspace(B, Hq, Tmax, D)
+    if need < 0:
+        raise W4A16Error(int(need), "w4a16_kv_attention_batch_workspace")
+    return int(need)
+
+
+def kv_attention_decode_batch(q: torch.Tensor, kcache, vcache, lengths: torch.Tensor, bits: int = 8,
+                              out: torch.Tensor | None = None, work: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode attention for ``B`` sequences in one call: ``q [B, Hq, D]``, caches
+    ``(codes, scales, zeros)`` of shape ``[B, Hkv, Tmax, ...]`` (scales ``[B, Hkv, Tmax]``),
+    ``lengths`` int32 ``[B]`` on the device."""
+    dt = _dtype_code(q)
+    _need(q, "q", q.dtype, 3)
+    _need(lengths, "lengths", torch.int32, 1)
+    B, Hq, D = q.shape
+    kc, ks, kz = kcache
+    vc, vs, vz = vcache
+    if ks.dim() != 3 or ks.shape[0] != B or lengths.shape[0] != B:
+        raise ValueError("caches must be [B, Hkv, Tmax, ...] and lengths [B]")
+    _, Hkv, Tmax = ks.shape
+    L = lib()
+    need = kv_attention_batch_workspace(B, Hq, Tmax, D)
+    if work is None:
+        work = torch.empty(need, dtype=torch.float32, device=q.device)
+    elif work.dtype != torch.float32 or not work.is_cuda or work.numel() < need:
+        raise ValueError(f"work must be a float32 device tensor of at least {need} elements")
+    if out is None:
+        out = torch.empty_like(q)
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    check(L.w4a16_kv_attention_decode_batch(q.data_ptr(), dt, B, Hq, Hkv, lengths.data_ptr(), Tmax, D, bits,
+                                            kc.data_ptr(), ks.data_ptr(), ptr(kz), vc.data_ptr(), vs.data_ptr(),
+                                            ptr(vz), work.data_ptr(), out.data_ptr(), _stream()),
+          "w4a16_kv_attention_decode_batch")
+    return out
+
+
 def kv_attention_decode(q: torch.Tensor, kcache, vcache, T: int, bits: int = 8,
                         out: torch.Tensor | None = None, work: torch.Tensor | None = None) -> torch.Tensor:
     """``softmax(q K^T / sqrt(D)) V`` over the first ``T`` tokens of quantized caches

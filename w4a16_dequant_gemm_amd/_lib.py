@@ -83,6 +83,11 @@ def lib() -> ctypes.CDLL:
     L.w4a16_kv_attention_decode.restype = i32
     L.w4a16_kv_attention_decode.argtypes = [vp, i32, i64, i64, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp,
                                             vp, vp, vp]
+    L.w4a16_kv_attention_batch_workspace.restype = i64
+    L.w4a16_kv_attention_batch_workspace.argtypes = [i64, i64, i64, i64]
+    L.w4a16_kv_attention_decode_batch.restype = i32
+    L.w4a16_kv_attention_decode_batch.argtypes = [vp, i32, i64, i64, i64, vp, i64, i64, i32, vp, vp, vp, vp,
+                                                  vp, vp, vp, vp, vp]
     L.w4a16_gptq_quantize.restype = i32
     L.w4a16_gptq_quantize.argtypes = [vp, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp]
     _lib = L

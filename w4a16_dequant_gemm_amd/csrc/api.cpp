@@ -307,8 +307,15 @@ int w4a16_w8a8_linear(const int8_t* qx, const float* xscale, int64_t M, int64_t 
 }
 
 int64_t w4a16_kv_attention_workspace(int64_t Hq, int64_t T, int64_t D) {
-    if (Hq < 1 || T < 1 || (D != 64 && D != 128)) return W4A16_ERR_SHAPE;
-    return w4a16::kv_attention_workspace_floats(Hq, T, D);
+    if (Hq < 1 || T < 1 || (D != 64 && D != 128) || Hq > 65535 || T > (int64_t(1) << 24)) return W4A16_ERR_SHAPE;
+    return w4a16::kv_attention_workspace_floats(1, Hq, T, D);
+}
+
+int64_t w4a16_kv_attention_batch_workspace(int64_t B, int64_t Hq, int64_t Tmax, int64_t D) {
+    if (B < 1 || Hq < 1 || Tmax < 1 || (D != 64 && D != 128) || B > 65535 || Hq > 65535 ||
+        B * Hq > (int64_t(1) << 24) || Tmax > (int64_t(1) << 24))
+        return W4A16_ERR_SHAPE;
+    return w4a16::kv_attention_workspace_floats(B, Hq, Tmax, D);
 }
 
 int w4a16_kv_quantize(const void* x, int dtype, int64_t H, int64_t T, int64_t D, int bits,
@@ -339,9 +346,30 @@ int w4a16_kv_attention_decode(const void* q, int dtype, int64_t Hq, int64_t Hkv,
         !aligned(vscales, 2) || (kzeros && !aligned(kzeros, 2)) || (vzeros && !aligned(vzeros, 2)) ||
         !aligned(work, 4) || !aligned(out, 2))
         return W4A16_ERR_ALIGN;
-    return hip_status(w4a16::launch_kv_attention(q, dtype, (int)Hq, (int)Hkv, (int)T, (int)Tmax, (int)D,
-                                                 bits, kcodes, kscales, kzeros, vcodes, vscales,
+    return hip_status(w4a16::launch_kv_attention(q, dtype, 1, (int)Hq, (int)Hkv, (int)T, nullptr, (int)Tmax,
+                                                 (int)D, bits, kcodes, kscales, kzeros, vcodes, vscales,
                                                  vzeros, work, out, static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_kv_attention_decode_batch(const void* q, int dtype, int64_t B, int64_t Hq, int64_t Hkv,
+                                    const int32_t* lengths, int64_t Tmax, int64_t D, int bits,
+                                    const void* kcodes, const uint16_t* kscales, const uint16_t* kzeros,
+                                    const void* vcodes, const uint16_t* vscales, const uint16_t* vzeros,
+                                    float* work, void* out, void* stream) {
+    if (!q || !lengths || !kcodes || !kscales || !vcodes || !vscales || !work || !out) return W4A16_ERR_NULL;
+    if (bits == 4 && (!kzeros || !vzeros)) return W4A16_ERR_NULL;
+    if (dtype != W4A16_F16 && dtype != W4A16_BF16) return W4A16_ERR_DTYPE;
+    if (bits != 8 && bits != 4) return W4A16_ERR_SCHEME;
+    if (B < 1 || B > 65535 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Hq > 65535 || B * Hq > (int64_t(1) << 24) ||
+        Tmax < 1 || Tmax > (int64_t(1) << 24) || (D != 64 && D != 128) || B * Hkv * Tmax > (int64_t(1) << 33))
+        return W4A16_ERR_SHAPE;
+    if (!aligned(q, 16) || !aligned(lengths, 4) || !aligned(kcodes, 16) || !aligned(vcodes, 16) ||
+        !aligned(kscales, 2) || !aligned(vscales, 2) || (kzeros && !aligned(kzeros, 2)) ||
+        (vzeros && !aligned(vzeros, 2)) || !aligned(work, 4) || !aligned(out, 2))
+        return W4A16_ERR_ALIGN;
+    return hip_status(w4a16::launch_kv_attention(q, dtype, (int)B, (int)Hq, (int)Hkv, (int)Tmax, lengths,
+                                                 (int)Tmax, (int)D, bits, kcodes, kscales, kzeros, vcodes,
+                                                 vscales, vzeros, work, out, static_cast<hipStream_t>(stream)));
 }
 
 int w4a16_select_path(int64_t M, int64_t N, int64_t K, int64_t group_size, int dtype) {

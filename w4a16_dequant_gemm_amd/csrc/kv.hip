@@ -165,7 +165,7 @@ __device__ __forceinline__ void codes16(const u32x4& w, float* c) {
 // four waves are combined and the block's (m, l, o[D]) goes to the workspace.
 template <int DT, int BITS, int D, int GQ>
 __global__ __launch_bounds__(kKvThreads) void kv_attn_split_kernel(
-    const uint16_t* __restrict__ q, int Hq, int Hkv, int T, int Tmax, int chunk,
+    const uint16_t* __restrict__ q, int Hq, int Hkv, int T, const int* __restrict__ lens, int Tmax, int chunk,
     const void* __restrict__ kc, const uint16_t* __restrict__ ks, const uint16_t* __restrict__ kz,
     const void* __restrict__ vc, const uint16_t* __restrict__ vs, const uint16_t* __restrict__ vz,
     float* __restrict__ part) {
@@ -178,12 +178,16 @@ __global__ __launch_bounds__(kKvThreads) void kv_attn_split_kernel(
     const int nsplit = gridDim.x;
     const int h0 = blockIdx.y * GQ;
     const int kvh = h0 / (Hq / Hkv);
+    // sequence b of the batch: its length (clamped into [1, Tmax]) and its heads
+    const int b = blockIdx.z;
+    if (lens) T = min(max(lens[b], 1), Tmax);
+    const long long hq0 = (long long)b * Hq + h0;       // first query head of the block, batch-wide
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int seg = lane % LPR, slot = lane / LPR;
     const int t0 = split * chunk;
     const int t1 = min(T, t0 + chunk);
-    const long long rowbase = (long long)kvh * Tmax;
+    const long long rowbase = ((long long)b * Hkv + kvh) * Tmax;
     const float NEG = -__builtin_inff();
 
     // uniform per-head bases and 32-bit per-lane offsets (Tmax * RB < 2^32)
@@ -225,7 +229,7 @@ __global__ __launch_bounds__(kKvThreads) void kv_attn_split_kernel(
     for (int g = 0; g < GQ; ++g)
 #pragma unroll
         for (int p = 0; p < EPL / 8; ++p)
-            qraw[g][p] = *reinterpret_cast<const u32x4*>(q + (long long)(h0 + g) * D + seg * EPL + 8 * p);
+            qraw[g][p] = *reinterpret_cast<const u32x4*>(q + (hq0 + g) * D + seg * EPL + 8 * p);
     Raw A;
     issue(base0, A);      // a wave with no rows reads the split's last row and masks it
     __builtin_amdgcn_sched_barrier(0);
@@ -360,7 +364,7 @@ __global__ __launch_bounds__(kKvThreads) void kv_attn_split_kernel(
             o = fmaf(pacc[g][w][d], f, o);
             lt = fmaf(pl[g][w], f, lt);
         }
-        float* out = part + ((long long)(h0 + g) * nsplit + split) * (D + 2);
+        float* out = part + ((hq0 + g) * nsplit + split) * (D + 2);
         out[2 + d] = o;
         if (d == 0) {
             out[0] = M;
@@ -379,7 +383,7 @@ __global__ __launch_bounds__(256) void kv_attn_merge_kernel(const float* __restr
     constexpr int PH = 256 / D;
     constexpr int S = 8;
     __shared__ float sm[PH][D], sl[PH][D], so[PH][D];
-    const int h = blockIdx.x;
+    const long long h = blockIdx.x;                     // batch-wide query head
     const int tid = threadIdx.x;
     const int d = tid % D, ph = tid / D;
     const float NEG = -__builtin_inff();
@@ -444,24 +448,27 @@ int kv_group(int Hq, int Hkv) {
     return grp % 2 == 0 ? 2 : 1;
 }
 
+// B sequences; `lens` (device, B entries) gives each sequence's length, or NULL: every
+// sequence has T tokens.  Splits are sized on the longest span (T, or Tmax with lens).
 template <int DT, int BITS, int D>
-hipError_t kv_attn(const void* q, int Hq, int Hkv, int T, int Tmax, const void* kc, const uint16_t* ks,
-                   const uint16_t* kz, const void* vc, const uint16_t* vs, const uint16_t* vz, float* work,
-                   void* out, hipStream_t st) {
-    const int ns = kv_splits(Hq, T);
-    const int chunk = (T + ns - 1) / ns;
+hipError_t kv_attn(const void* q, int B, int Hq, int Hkv, int T, const int* lens, int Tmax, const void* kc,
+                   const uint16_t* ks, const uint16_t* kz, const void* vc, const uint16_t* vs, const uint16_t* vz,
+                   float* work, void* out, hipStream_t st) {
+    const int span = lens ? Tmax : T;
+    const int ns = kv_splits(B * Hq, span);
+    const int chunk = (span + ns - 1) / ns;
     const int gq = kv_group<BITS>(Hq, Hkv);
     const auto qp = static_cast<const uint16_t*>(q);
     if (gq == 4)
-        hipLaunchKernelGGL((kv_attn_split_kernel<DT, BITS, D, (BITS == 8 ? 4 : 1)>), dim3(ns, Hq / 4),
-                           dim3(kKvThreads), 0, st, qp, Hq, Hkv, T, Tmax, chunk, kc, ks, kz, vc, vs, vz, work);
+        hipLaunchKernelGGL((kv_attn_split_kernel<DT, BITS, D, (BITS == 8 ? 4 : 1)>), dim3(ns, Hq / 4, B),
+                           dim3(kKvThreads), 0, st, qp, Hq, Hkv, T, lens, Tmax, chunk, kc, ks, kz, vc, vs, vz, work);
     else if (gq == 2)
-        hipLaunchKernelGGL((kv_attn_split_kernel<DT, BITS, D, 2>), dim3(ns, Hq / 2), dim3(kKvThreads), 0, st, qp,
-                           Hq, Hkv, T, Tmax, chunk, kc, ks, kz, vc, vs, vz, work);
+        hipLaunchKernelGGL((kv_attn_split_kernel<DT, BITS, D, 2>), dim3(ns, Hq / 2, B), dim3(kKvThreads), 0, st,
+                           qp, Hq, Hkv, T, lens, Tmax, chunk, kc, ks, kz, vc, vs, vz, work);
     else
-        hipLaunchKernelGGL((kv_attn_split_kernel<DT, BITS, D, 1>), dim3(ns, Hq), dim3(kKvThreads), 0, st, qp, Hq,
-                           Hkv, T, Tmax, chunk, kc, ks, kz, vc, vs, vz, work);
-    hipLaunchKernelGGL((kv_attn_merge_kernel<DT, D>), dim3(Hq), dim3(256), 0, st, work, ns,
+        hipLaunchKernelGGL((kv_attn_split_kernel<DT, BITS, D, 1>), dim3(ns, Hq, B), dim3(kKvThreads), 0, st, qp,
+                           Hq, Hkv, T, lens, Tmax, chunk, kc, ks, kz, vc, vs, vz, work);
+    hipLaunchKernelGGL((kv_attn_merge_kernel<DT, D>), dim3(B * Hq), dim3(256), 0, st, work, ns,
                        static_cast<uint16_t*>(out));
     return hipGetLastError();
 }
@@ -481,8 +488,8 @@ hipError_t kv_quant(const void* x, long long rows, int D, void* codes, uint16_t*
 
 }  // namespace
 
-long long kv_attention_workspace_floats(long long Hq, long long T, long long D) {
-    return Hq * kv_splits((int)Hq, (int)T) * (D + 2);
+long long kv_attention_workspace_floats(long long B, long long Hq, long long T, long long D) {
+    return B * Hq * kv_splits((int)(B * Hq), (int)T) * (D + 2);
 }
 
 hipError_t launch_kv_quantize(const void* x, int dtype, long long rows, int D, int bits, void* codes,
@@ -494,12 +501,13 @@ hipError_t launch_kv_quantize(const void* x, int dtype, long long rows, int D, i
                      : kv_quant<DT_BF16, 4>(x, rows, D, codes, scales, zeros, st);
 }
 
-hipError_t launch_kv_attention(const void* q, int dtype, int Hq, int Hkv, int T, int Tmax, int D, int bits,
-                               const void* kc, const uint16_t* ks, const uint16_t* kz, const void* vc,
-                               const uint16_t* vs, const uint16_t* vz, float* work, void* out, hipStream_t st) {
+hipError_t launch_kv_attention(const void* q, int dtype, int B, int Hq, int Hkv, int T, const int* lens, int Tmax,
+                               int D, int bits, const void* kc, const uint16_t* ks, const uint16_t* kz,
+                               const void* vc, const uint16_t* vs, const uint16_t* vz, float* work, void* out,
+                               hipStream_t st) {
 #define W4A16_KV_CASE(DTV, BV, DV)                                                                          \
     if (dtype == DTV && bits == BV && D == DV)                                                              \
-        return kv_attn<DTV, BV, DV>(q, Hq, Hkv, T, Tmax, kc, ks, kz, vc, vs, vz, work, out, st);
+        return kv_attn<DTV, BV, DV>(q, B, Hq, Hkv, T, lens, Tmax, kc, ks, kz, vc, vs, vz, work, out, st);
     W4A16_KV_CASE(DT_F16, 8, 64)
     W4A16_KV_CASE(DT_F16, 8, 128)
     W4A16_KV_CASE(DT_F16, 4, 64)

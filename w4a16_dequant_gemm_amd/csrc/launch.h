@@ -50,13 +50,15 @@ hipError_t launch_w8a8_linear(const int8_t* qx, const float* sx, int M, int N, i
                               const int8_t* qw, const float* sw, void* Y, int dtype, hipStream_t st);
 
 // KV cache (kv.hip)
-long long kv_attention_workspace_floats(long long Hq, long long T, long long D);
+long long kv_attention_workspace_floats(long long B, long long Hq, long long T, long long D);
 hipError_t launch_kv_quantize(const void* x, int dtype, long long rows, int D, int bits, void* codes,
                               uint16_t* scales, uint16_t* zeros, hipStream_t st);
-hipError_t launch_kv_attention(const void* q, int dtype, int Hq, int Hkv, int T, int Tmax, int D,
-                               int bits, const void* kc, const uint16_t* ks, const uint16_t* kz,
-                               const void* vc, const uint16_t* vs, const uint16_t* vz, float* work,
-                               void* out, hipStream_t st);
+// B sequences of Hq query heads; lens (device, B entries, clamped into [1, Tmax]) or NULL
+// for a common length T.
+hipError_t launch_kv_attention(const void* q, int dtype, int B, int Hq, int Hkv, int T, const int* lens,
+                               int Tmax, int D, int bits, const void* kc, const uint16_t* ks,
+                               const uint16_t* kz, const void* vc, const uint16_t* vs, const uint16_t* vz,
+                               float* work, void* out, hipStream_t st);
 
 // AWQ (awq.hip)
 long long awq_workspace_doubles(long long N, long long K, long long n);
