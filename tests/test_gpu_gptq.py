@@ -52,7 +52,10 @@ def test_hessian(n, K, dtype):
 def test_factor(K, damp):
     X = calibration(max(2 * K, 256), K, FP16, seed=K)
     Href = G.damp_hessian(G.hessian(X, FP16), damp)
-    H = torch.from_numpy(np.tril(G.hessian(X, FP16))).cuda()      # only the lower triangle is read
+    # only the lower triangle is read: NaN above the diagonal must not reach U
+    Hl = np.tril(G.hessian(X, FP16))
+    Hl[np.triu_indices(K, 1)] = np.nan
+    H = torch.from_numpy(Hl).cuda()
     U = W4.gptq_factor(H, damp).cpu().numpy()
     ref = G.inverse_cholesky_upper(Href)
     assert np.all(np.tril(U, -1) == 0.0)

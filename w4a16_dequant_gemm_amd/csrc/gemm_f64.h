@@ -18,9 +18,11 @@ __device__ __forceinline__ double ld_elem(const void* p, long long i) {
 
 // C = beta * C + alpha * A B with A(m, k) = A[m sam + k sak], B(k, n) = B[k sbk + n sbn],
 // C(m, n) = C[m scm + n scn].  MODE bit 0: only tiles touching the lower triangle
-// (m >= n) are computed; bit 1: B is lower triangular (B(k, n) = 0 for k < n), so the
-// contraction of a tile starts at its first column; bit 2: A is lower triangular
-// (A(m, k) = 0 for k > m), so it ends after the tile's last row.  beta == 0 never reads C.
+// (m >= n) are computed; bit 1: B is lower triangular (B(k, n) = 0 for k < n): the
+// contraction of a tile starts at its first column and the strictly upper entries are read
+// as zeros whatever memory holds there; bit 2: A is lower triangular (A(m, k) = 0 for
+// k > m): it ends after the tile's last row, strictly upper entries read as zeros.
+// beta == 0 never reads C.
 template <int AT, int BT, int MODE>
 __global__ __launch_bounds__(256) void gemm_f64_kernel(int M, int N, int K, double alpha,
                                                        const void* __restrict__ A, long long sam,
@@ -52,11 +54,13 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(int M, int N, int K, doub
             int m, k;
             if (a_krow) { m = e >> 4; k = e & 15; } else { k = e >> 6; m = e & 63; }
             const int gm = m0 + m, gk = k0 + k;
-            As[k][m] = (gm < M && gk < K) ? ld_elem<AT>(A, (long long)gm * sam + (long long)gk * sak) : 0.0;
+            As[k][m] = (gm < M && gk < K && (!(MODE & 4) || gk <= gm))
+                           ? ld_elem<AT>(A, (long long)gm * sam + (long long)gk * sak) : 0.0;
             int n, kb;
             if (b_ncol) { kb = e >> 6; n = e & 63; } else { n = e >> 4; kb = e & 15; }
             const int gn = n0 + n, gkb = k0 + kb;
-            Bs[kb][n] = (gn < N && gkb < K) ? ld_elem<BT>(B, (long long)gkb * sbk + (long long)gn * sbn) : 0.0;
+            Bs[kb][n] = (gn < N && gkb < K && (!(MODE & 2) || gkb >= gn))
+                            ? ld_elem<BT>(B, (long long)gkb * sbk + (long long)gn * sbn) : 0.0;
         }
         __syncthreads();
 #pragma unroll
