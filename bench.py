@@ -175,11 +175,31 @@ def cpu_baseline(layers, w_host, xs_host, y_gpu, budget_s, np, torch):
         mx.append(float(np.abs(y - r).max() / np.abs(r).max()))
     parity = {"packing_bit_exact_sampled_rows": packing_ok, "rel_fro": fro, "max_rel": mx,
               "ok": packing_ok and max(fro) <= 1e-3 and max(mx) <= 1e-2}
+    # one host thread on the single 4096 x 4096 layer, and the 32-layer stack extrapolated
+    # from one 7-linear layer (q, k, v, o 4096 -> 4096; gate, up 4096 -> 11008; down 11008 -> 4096)
+    one_thread = None
+    try:
+        from threadpoolctl import threadpool_limits
+        qw, s, z, nb = host[0]
+        with threadpool_limits(1):
+            t1 = time.perf_counter()
+            oracle.linear_ref(xs_host[0], 0, qw, s, z, GROUP)
+            one_thread = nb / (time.perf_counter() - t1) / 1e9
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        pass
+    by_shape = {(L.K, L.N): h for L, h in zip(layers, host)}
+    t1 = time.perf_counter()
+    for K, N in [(4096, 4096)] * 4 + [(4096, 11008)] * 2 + [(11008, 4096)]:
+        qw, s, z, _ = by_shape[(K, N)]
+        oracle.linear_ref(xs_host[0] if K == 4096 else xs_host[2], 0, qw, s, z, GROUP)
+    layer_s = time.perf_counter() - t1
     return {"value": total_bytes / el / 1e9, "unit": "GB/s", "cores": int(threads),
             "host_cpus": os.cpu_count(), "kind": "oracle",
             "sample": f"{steps} oracle step(s) of the same M=1 workload (3 layers, fp64 "
                       f"dequantize + BLAS matmul), {el:.1f} s",
             "parity_vs_gpu": parity,
+            "one_thread_GBps_4096x4096": None if one_thread is None else round(one_thread, 4),
+            "stack_32_layers_s_extrapolated": round(32 * layer_s, 2),
             "other_rows": cpu_baseline_rows(oracle, np)}
 
 
@@ -422,6 +442,7 @@ def main():
 
     extras = {"per_layer_m1": per_layer}
     if not args.no_extras:
+        extras["comparators"] = run_comparators(W4, synth, torch, ms)
         extras.update(run_extras(layers, copies, W4, synth, torch, np))
 
     cpu = None
@@ -448,6 +469,70 @@ def main():
         "extras": extras,
     }
     print(json.dumps(line), flush=True)
+
+
+def run_comparators(W4, synth, torch, w4_step_ms):
+    """Context for the M = 1 step and the M = 4096 prefill: (1) the same three layers as
+    dense fp16 weights through torch.matmul (hipBLASLt), rotating >= 1 GiB of weight copies,
+    and the W4A16 step's speedup over it; (2) the unfused path the fused kernels replace:
+    dequantize to fp32, cast to fp16, then torch.matmul, at M = 1 and M = 4096; (3) the launch
+    gap: back-to-back one-element kernels in a graph, the floor under any short launch."""
+    res = {}
+    Xs = {K: synth.activations_device(1, K, synth.FP16, 9100 + K) for K in (4096, 11008)}
+    per_copy = sum(2 * N * K for K, N in SHAPES)
+    ncopy = max(2, -(-(1 << 30) // per_copy))
+    Wd = [[torch.randn(N, K, dtype=torch.float16, device="cuda") for K, N in SHAPES] for _ in range(ncopy)]
+    Ys = [torch.empty((1, N), dtype=torch.float16, device="cuda") for _, N in SHAPES]
+
+    def dense(i):
+        for (K, N), W, Y in zip(SHAPES, Wd[i % ncopy], Ys):
+            torch.matmul(Xs[K], W.t(), out=Y)
+    for i in range(3):
+        dense(i)
+    ms = time_loop(dense, 50, torch)
+    res["dense_fp16_m1_step"] = {"us": round(ms * 1e3, 2), "GBps_fp16_weights": round(per_copy / (ms * 1e-3) / 1e9, 1),
+                                 "w4a16_speedup": round(ms / w4_step_ms, 3)}
+    log(f"  dense fp16 M=1 step (torch.matmul): {res['dense_fp16_m1_step']}")
+    del Wd
+    torch.cuda.empty_cache()
+    # unfused: dequantize (fp32) -> fp16 -> matmul
+    packed = []
+    for K, N in SHAPES:
+        W = synth.weights_device(N, K, 0.02, 9200 + K + N)
+        packed.append((K, N) + tuple(W4.quantize_pack(W, GROUP, W4.ASYM)))
+        del W
+
+    def unfused(i):
+        for (K, N, qw, s, z), Y in zip(packed, Ys):
+            torch.matmul(Xs[K], W4.dequantize(qw, s, z, GROUP).half().t(), out=Y)
+    for i in range(2):
+        unfused(i)
+    ms_u = time_loop(unfused, 10, torch, graph=False)
+    res["unfused_dequant_then_matmul_m1_step"] = {"us": round(ms_u * 1e3, 1), "fused_speedup": round(ms_u / w4_step_ms, 2)}
+    log(f"  unfused dequantize + matmul, M=1 step: {res['unfused_dequant_then_matmul_m1_step']}")
+    pf = {}
+    for K, N, qw, s, z in packed[1:]:
+        X = synth.activations_device(4096, K, synth.FP16, 9300 + K)
+        Y = torch.empty((4096, N), dtype=torch.float16, device="cuda")
+        f_fused = lambda i: W4.linear(X, qw, s, z, GROUP, out=Y)
+        f_unf = lambda i: torch.matmul(X, W4.dequantize(qw, s, z, GROUP).half().t(), out=Y)
+        for f in (f_fused, f_unf):
+            f(0)
+        t_f = time_loop(f_fused, 5, torch, graph=False)
+        t_u = time_loop(f_unf, 5, torch, graph=False)
+        pf[f"K{K}_N{N}"] = {"fused_us": round(t_f * 1e3, 1), "unfused_us": round(t_u * 1e3, 1),
+                            "fused_speedup": round(t_u / t_f, 2)}
+        del X, Y
+    res["prefill_m4096_fused_vs_unfused"] = pf
+    log(f"  prefill M=4096 fused vs unfused: {pf}")
+    del packed
+    torch.cuda.empty_cache()
+    # launch gap
+    one = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ms_l = time_loop(lambda i: one.add_(1.0), 200, torch)
+    res["launch_gap_us"] = round(ms_l * 1e3, 3)
+    log(f"  back-to-back one-element kernels: {res['launch_gap_us']} us each")
+    return res
 
 
 def run_extras(layers, copies, W4, synth, torch, np):
