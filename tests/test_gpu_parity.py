@@ -112,7 +112,10 @@ def _run_linear(M, N, K, g, scheme, dtype, path, seed, zeros_none=False, x_outli
 GEMV_CASES = [(1, 64, 256, 32), (2, 130, 512, 128), (3, 77, 1024, 1024), (4, 256, 4096, 128),
               (1, 300, 11008, 128), (5, 100, 2048, 64), (8, 64, 4096, 128), (1, 33, 28672, 128),
               (2, 50, 11008, 11008), (7, 16, 1024, 256), (1, 1, 32, 32),
-              (1, 9477, 4096, 128), (2, 5000, 2048, 64), (4, 3000, 1024, 1024), (3, 2600, 6144, 128)]
+              (1, 9477, 4096, 128), (2, 5000, 2048, 64), (4, 3000, 1024, 1024), (3, 2600, 6144, 128),
+              # grid-sizing boundaries of the streaming kernel: one row per wave up to N = 4096,
+              # two rows up to N = 12288 (768 blocks), one persistent block per CU beyond
+              (1, 4097, 1024, 128), (2, 12288, 256, 64), (1, 12289, 512, 128), (1, 4096, 12288, 128)]
 SKINNY_CASES = [(1, 64, 128, 128), (5, 100, 1024, 128), (16, 256, 4096, 128), (17, 77, 2048, 256),
                 (32, 300, 11008, 128), (31, 129, 1024, 1024), (8, 4096, 4096, 128), (2, 50, 11008, 11008),
                 (12, 1000, 28672, 128),
