@@ -235,19 +235,37 @@ __global__ __launch_bounds__(kKvThreads) void kv_attn_split_kernel(
     __builtin_amdgcn_sched_barrier(0);
 
     // this lane's segment of each query head, prescaled; its segment sum (code offset term)
+    // fp16 queries score with v_dot2 on exact 16-bit codes (KV8: 1024 + (c + 128) from one
+    // byte permute per pair; KV4: subnormal codes u 2^-24, half of them x16, from masks), with
+    // q kept as loaded (pairs in the codes' order) and scaled after the dot product; bf16
+    // queries take q prescaled in fp32 and one conversion and multiply-add per code.
+    constexpr bool DOT = DT == DT_F16;
     const float qscale = 1.4426950408889634f / sqrtf((float)D);
-    float qv[GQ][EPL], qseg[GQ];
+    float qv[GQ][DOT ? 1 : EPL], qseg[GQ];
+    uint32_t qp[GQ][DOT ? EPL / 2 : 1];
 #pragma unroll
     for (int g = 0; g < GQ; ++g) {
+        qseg[g] = 0.0f;
 #pragma unroll
         for (int p = 0; p < EPL / 8; ++p) {
             const uint32_t ww[4] = {qraw[g][p].x, qraw[g][p].y, qraw[g][p].z, qraw[g][p].w};
+            if constexpr (DOT) {
+                if constexpr (BITS == 8) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) qv[g][8 * p + i] = in2f<DT>((ww[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) * qscale;
+                    for (int i = 0; i < 4; ++i) qp[g][4 * p + i] = ww[i];
+                } else {
+                    permute_x8(ww[0], ww[1], ww[2], ww[3], &qp[g][4 * p]);
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) qseg[g] += h2f((ww[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    qv[g][8 * p + i] = in2f<DT>((ww[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) * qscale;
+                    qseg[g] += qv[g][8 * p + i];
+                }
+            }
         }
-        qseg[g] = 0.0f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) qseg[g] += qv[g][e];
     }
     float m[GQ], l[GQ], acc[GQ][EPL], zoff[GQ];
 #pragma unroll
@@ -265,17 +283,59 @@ __global__ __launch_bounds__(kKvThreads) void kv_attn_split_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const bool ok = base + u * RPW + slot < t1;
-            const float ksc = h2f(R.ks[u]);
-            float c[EPL];
-            codes16<BITS>(R.kw[u], c);
+            if constexpr (DOT) {
+                const float kq = h2f(R.ks[u]) * qscale;
+                const uint32_t ww[4] = {R.kw[u].x, R.kw[u].y, R.kw[u].z, R.kw[u].w};
+                if constexpr (BITS == 8) {
+                    uint32_t h16[8];
 #pragma unroll
-            for (int g = 0; g < GQ; ++g) {
-                float d = 0.0f;
+                    for (int k = 0; k < 4; ++k) {
+                        const uint32_t b = ww[k] ^ 0x80808080u;            // c + 128 per byte
+                        h16[2 * k] = perm(0x64646464u, b, 0x04010400u);    // (1024 + b0, 1024 + b1)
+                        h16[2 * k + 1] = perm(0x64646464u, b, 0x04030402u);
+                    }
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) d = fmaf(qv[g][e], c[e], d);
-                d = fmaf(BITS == 4 ? -h2f(R.kz[u]) : -128.0f, qseg[g], d);
-                d = group_sum<LPR>(d);
-                sc[g][u] = ok ? d * ksc : NEG;
+                    for (int g = 0; g < GQ; ++g) {
+                        float d = 0.0f;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) d = dot2<DT_F16>(qp[g][i], h16[i], d);
+                        d = fmaf(-1152.0f, qseg[g], d);
+                        d = group_sum<LPR>(d);
+                        sc[g][u] = ok ? d * kq : NEG;
+                    }
+                } else {
+                    uint32_t cd[4][4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) unpack_mask_f16(ww[k], cd[k]);
+#pragma unroll
+                    for (int g = 0; g < GQ; ++g) {
+                        float pa = 0.0f, pb = 0.0f;
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            pa = dot2<DT_F16>(qp[g][4 * k + 0], cd[k][0], pa);
+                            pb = dot2<DT_F16>(qp[g][4 * k + 1], cd[k][1], pb);
+                            pa = dot2<DT_F16>(qp[g][4 * k + 2], cd[k][2], pa);
+                            pb = dot2<DT_F16>(qp[g][4 * k + 3], cd[k][3], pb);
+                        }
+                        float d = fmaf(pb, 0.0625f, pa) * 16777216.0f;     // sum q u
+                        d = fmaf(-h2f(R.kz[u]), qseg[g], d);
+                        d = group_sum<LPR>(d);
+                        sc[g][u] = ok ? d * kq : NEG;
+                    }
+                }
+            } else {
+                const float ksc = h2f(R.ks[u]);
+                float c[EPL];
+                codes16<BITS>(R.kw[u], c);
+#pragma unroll
+                for (int g = 0; g < GQ; ++g) {
+                    float d = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) d = fmaf(qv[g][e], c[e], d);
+                    d = fmaf(BITS == 4 ? -h2f(R.kz[u]) : -128.0f, qseg[g], d);
+                    d = group_sum<LPR>(d);
+                    sc[g][u] = ok ? d * ksc : NEG;
+                }
             }
         }
         float pv[GQ][U];
