@@ -9,14 +9,16 @@
 // [Hkv, Tmax, D] (a head's tokens contiguous), scales / zeros [Hkv, Tmax] fp16.
 //
 // Decode attention, out[h] = softmax(q_h K^T / sqrt(D)) V over the first T tokens of kv head
-// h / (Hq / Hkv), in two launches (split over tokens, then a merge):
-//   split kernel, block (split, group of query heads), 256 threads: a cached row is read by a
-//   few consecutive lanes with one 16-byte load each, so a wave load covers 8-32 whole rows
-//   (1-2 KB contiguous); scores are reduced across those lanes with DPP, and every lane keeps
-//   an online softmax (running max, sum, output segment) over the rows it reads; the slots and
-//   the waves are combined at the end into the split's (max, sum, unnormalized output);
+// h / (Hq / Hkv), for one sequence or a batch of sequences with their own lengths (caches
+// [B, Hkv, Tmax, D]), in two launches (split over tokens, then a merge):
+//   split kernel, block (split, group of query heads, sequence), 256 threads: a cached row is
+//   read by a few consecutive lanes with one 16-byte load each, so a wave load covers 8-32
+//   whole rows (1-2 KB contiguous); scores (v_dot2 on exact 16-bit codes for fp16 queries)
+//   are reduced across those lanes with DPP, and every lane keeps an online softmax (running
+//   max, sum, output segment) over the rows it reads; the slots and the waves are combined at
+//   the end into the split's (max, sum, unnormalized output);
 //   merge kernel: rescales the splits to the common max and normalizes.
-// Dequantization happens in registers only; the cache is read once.
+// Dequantization happens in registers only; the cache is read once per group of query heads.
 #include "common.h"
 #include "launch.h"
 
