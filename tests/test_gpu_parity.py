@@ -325,3 +325,28 @@ FULL = [c for c in config_cases(1)] + \
 @pytest.mark.parametrize("case", FULL, ids=lambda c: c.name)
 def test_full_size_sampled(case):
     _full_size(case, m_rows=64)
+
+
+# ------------------------------------------------------- beyond 32-bit offsets
+@pytest.mark.parametrize("M", [1, 8, 300])
+def test_packed_weights_over_2gib(M):
+    """Packed weights of 2.15 GB (past every 32-bit byte offset): the dispatcher must route to
+    kernels with 64-bit addressing.  Random packed words, scales and zero points (no fp32
+    weight matrix of 17 GB is needed); sampled output columns against the oracle."""
+    N, K, g = 65600, 65536, 128
+    G = K // g
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(77 + M)
+    qw = torch.randint(-2 ** 31, 2 ** 31, (N, K // 8), dtype=torch.int32, device="cuda", generator=gen)
+    sc = (torch.rand((N, G), device="cuda", generator=gen) * 0.02 + 0.001).half()
+    z = torch.randint(0, 16, (N, G), device="cuda", generator=gen).half()
+    X = activations(M, K, FP16, seed=M + 5)
+    Y = W4.linear(x_to_torch(X, FP16), qw, sc, z, g)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(M)
+    ns = np.unique(np.concatenate([[0, N - 1, N // 2], rng.choice(N, 21, replace=False)]))
+    idx = torch.from_numpy(ns).cuda()
+    ref = oracle.linear_ref(X, FP16, qw[idx].cpu().numpy(), sc[idx].cpu().numpy(), z[idx].cpu().numpy(), g)
+    assert_close(y_to_f64(Y[:, idx]), ref_to_f64(ref, FP16), f"2 GiB+ weights M={M}")
+    del qw, sc, z, Y
+    torch.cuda.empty_cache()

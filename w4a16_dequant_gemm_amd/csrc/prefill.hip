@@ -591,7 +591,11 @@ bool prefill_supports(const LinearArgs& a) {
 
 hipError_t launch_prefill(const LinearArgs& a, hipStream_t st) {
     const int hz = a.zeros ? 1 : 0;
-    if (a.dtype == DT_F16 && a.K % (2 * W_BK) == 0) {
+    // the wide kernel addresses X, the packed weights and the group metadata with 32-bit
+    // buffer offsets; larger operands take the 64-bit addressed kernel
+    const bool offsets32 = (long long)a.M * a.K * 2 < (1LL << 31) && (long long)a.N * (a.K / 2) < (1LL << 31) &&
+                           (long long)a.N * a.G * 2 < (1LL << 31);
+    if (a.dtype == DT_F16 && a.K % (2 * W_BK) == 0 && offsets32) {
         const int tiles = ((a.M + W_BM - 1) / W_BM) * ((a.N + W_BN - 1) / W_BN);
         const int grid = 8 * ((tiles + 7) / 8);
         if (hz)
