@@ -25,7 +25,7 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
     const float* __restrict__ W, int N, int K, int g, int G, int seg, int words_per_lane,
     uint32_t* __restrict__ qw, uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros) {
     const int lane = threadIdx.x & 63;
-    const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const long long wave = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     const int gpw = 64 / seg;                      // groups served by one wave
     const int slot = lane / seg;
     const int gl = lane % seg;
