@@ -281,6 +281,50 @@ def traffic_run(K: int, N: int, W4, synth, torch, np):
     log(f"traffic run done: K={K} N={N}, {copies} weight copies, copy {COPY_MIB} MiB x5")
 
 
+def profile_run(name: str, W4, synth, torch):
+    """A short fixed workload for counter and trace runs of one further kernel family:
+    `prefill` (M = 4096 on both prefill shapes, 5 launches each), `w8a8` (the INT8 product at
+    M = 4096, both shapes, 5 launches each), `kv_batch` (batched KV8 and KV4 decode attention,
+    16 sequences, 2 layers' caches, 2 launches each), `decode_m16` (M = 16 on the 7B shapes
+    over 20 rotating weight copies, 20 launches each)."""
+    if name == "prefill":
+        for K, N in [(4096, 11008), (11008, 4096)]:
+            W = synth.weights_device(N, K, 0.02, 3000 + K)
+            qw, s, z = W4.quantize_pack(W, GROUP, W4.ASYM)
+            del W
+            X = synth.activations_device(4096, K, synth.FP16, 3001 + K)
+            Y = torch.empty((4096, N), dtype=torch.float16, device="cuda")
+            for _ in range(5):
+                W4.linear(X, qw, s, z, GROUP, out=Y)
+    elif name == "w8a8":
+        for K, N in [(4096, 11008), (11008, 4096)]:
+            X = synth.calibration_device(4096, K, synth.FP16, 6000 + K, outlier_frac=0.01, outlier_mult=20.0)
+            W = synth.weights_device(N, K, 0.02, 6001 + K)
+            s = W4.w8a8_smooth(X, W, 2)
+            qw, sw = W4.w8a8_quantize_weight(W, s)
+            qx, sx = W4.w8a8_quantize_act(X, s)
+            Y = torch.empty((4096, N), dtype=torch.float16, device="cuda")
+            for _ in range(5):
+                W4.w8a8_linear(qx, sx, qw, sw, out=Y)
+    elif name == "kv_batch":
+        run_kv_batch(W4, synth, torch, layers=2, timed=False)
+    elif name == "decode_m16":
+        for K, N in SHAPES:
+            W = synth.weights_device(N, K, 0.02, 1000 + K + N)
+            qw, s, z = W4.quantize_pack(W, GROUP, W4.ASYM)
+            del W
+            cs = [(qw.clone(), s.clone(), z.clone()) for _ in range(20)]
+            X = synth.activations_device(16, K, synth.FP16, 7)
+            Y = torch.empty((16, N), dtype=torch.float16, device="cuda")
+            for i in range(20):
+                W4.linear(X, *cs[i], GROUP, out=Y)
+            del cs
+    else:
+        raise SystemExit(f"unknown profile workload {name}")
+    torch.cuda.synchronize()
+    log(f"profile run done: {name}")
+
+
 def _counter_means(run_dir: str, counter: str):
     """Mean per-dispatch value of `counter` for each kernel name in a rocprofv3 csv run."""
     import csv
@@ -340,6 +384,8 @@ def main():
     ap.add_argument("--traffic-commands", nargs="*", default=[],
                     help="the profiler command lines, recorded in the traffic file")
     ap.add_argument("--traffic-out", default=None, help="output path of --traffic-parse")
+    ap.add_argument("--profile-run", choices=["prefill", "w8a8", "kv_batch", "decode_m16"],
+                    help="a short fixed workload of one kernel family, for counter runs")
     args = ap.parse_args()
     if args.traffic_parse:
         f, w, K, N = args.traffic_parse
@@ -362,6 +408,9 @@ def main():
     torch.cuda.set_device(0)
     if args.traffic_run:
         traffic_run(args.traffic_run[0], args.traffic_run[1], W4, synth, torch, np)
+        return
+    if args.profile_run:
+        profile_run(args.profile_run, W4, synth, torch)
         return
     step_bytes = sum(weight_bytes(N, K, GROUP) for K, N in SHAPES)
     copies = max(2, int(np.ceil(args.rotate_gib * 2**30 / step_bytes)))
@@ -710,7 +759,7 @@ def run_kv(W4, synth, torch, H=32, D=128, T=4096, layers=32):
     return res
 
 
-def run_kv_batch(W4, synth, torch, B=16, H=32, D=128, Tmax=4096, layers=4):
+def run_kv_batch(W4, synth, torch, B=16, H=32, D=128, Tmax=4096, layers=4, timed=True):
     """Decode attention for a batch of 16 sequences in one call (the serving case the cache
     quantization is for), lengths drawn uniformly from [1024, 4096] (seeded), 4 layers'
     caches in rotation (1.4-2.2 GB).  Bytes: each sequence's codes and per-token parameters
@@ -738,8 +787,11 @@ def run_kv_batch(W4, synth, torch, B=16, H=32, D=128, Tmax=4096, layers=4):
         def step(i, bits=bits, caches=caches):
             for kc, vc in caches:
                 W4.kv_attention_decode_batch(q, kc, vc, lt, bits, out=out, work=work)
-        for i in range(3):
+        for i in range(3 if timed else 2):
             step(i)
+        if not timed:
+            del caches
+            continue
         ms = time_loop(step, 10, torch)
         gbps = nbytes / (ms * 1e-3) / 1e9
         entry = {"us_per_layer": round(ms * 1e3 / layers, 2), "GBps": round(gbps, 1),
