@@ -13,7 +13,7 @@ the bytes the method must move (4 bits + 32/g bits per weight).  Also reported: 
 M sweep 1..16, prefill TFLOP/s at M = 4096, the roofline of the dominant kernel and the
 CPU oracle timed on the host (reported baseline, not a target).
 
-Prints ONE JSON line.  ``--gpus N`` with N > 1 is refused: this build runs on one GPU.
+Prints ONE JSON line.  ``--gpus N`` with N > 1 is refused: the path runs on one GPU.
 """
 
 from __future__ import annotations
@@ -826,7 +826,7 @@ def run_w8a8(W4, synth, torch, M=4096):
         entry = {"gemm_us": round(ms * 1e3, 1), "TOPS": round(tops, 1), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
                  "quant_act_us": round(ms_q * 1e3, 1),
                  "quant_act_GBps": round(3.0 * M * K / (ms_q * 1e-3) / 1e9, 1)}
-        try:   # context: the library int8 GEMM behind torch._int_mm, if this build routes it
+        try:   # context: the library int8 GEMM behind torch._int_mm, where the installed torch has one
             a = qx
             b = qw.t()
             for _ in range(2):

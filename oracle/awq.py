@@ -14,7 +14,7 @@ SmoothQuant / KV 量化）", 4.2):
   layer has the smallest output error on the calibration data (5.2);
 * the quantizer itself is the plain group-wise RTN of ``quant.py`` (5.3).
 
-Readings where the pages leave a step open or contradict themselves (listed in the design doc):
+Readings where the pages leave a step open or contradict themselves:
 
 * A1 candidates: ``s(a) = r ** (a / 4)`` for ``a = -4 .. 4`` (nine points, ``a = 0`` is plain
   RTN), ``r_i = xc_i / sqrt(max xc * min xc)`` with ``xc_i = max(x_i, 1e-6 * max x)``.  The

@@ -16,7 +16,7 @@ Method (restated from page "æ¨ç†ä¼˜åŒ–ä¸­â€œç”¨ç²¾åº¦æ¢æ€§èƒ½â€œçš„æ ¸å¿ƒæŠ€æ
 * group-wise scales and zero points (one per ``g`` columns of a row, 4.4) are those of
   the RTN quantizer (``quant.py``).
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
 
 * G1 ``Hinv`` in step 2c is the inverse Hessian of the columns not yet quantized: after
   column ``i`` is fixed it is removed from the problem (``Hinv`` loses row and column

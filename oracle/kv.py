@@ -14,7 +14,7 @@ Method (restated from the pages):
 * the consumer is decode attention: one new query per head against the cached keys and
   values, ``softmax(q K^T / sqrt(D)) V``.
 
-Readings (listed in DESIGN.md):
+Readings:
 
 * KV1 granularity: one scale (and for KV4 one zero point) per (head, token) row of ``D``
   values ("per token"); layout ``[H, T, D]`` (each head's tokens contiguous).

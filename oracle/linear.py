@@ -11,7 +11,7 @@ Weight-only é‡åŒ–; page "å¤§æ¨¡å‹æ¨ç†ä¸­ Weight-onlyã€W8A8 å’Œ FP8 é‡åŒ–æœ
 å–èˆï¼Ÿ", æ€§èƒ½å–å†³äº kernel).  The product is therefore exactly (up to summation
 order) ``Y = X W_hat^T`` with ``W_hat`` from :func:`oracle.quant.dequantize`.
 
-Readings (listed in DESIGN.md):
+Readings:
 
 * L-a the output dtype equals the activation dtype; accumulation is wide and
   the result is rounded once, round-to-nearest-even, to that dtype.

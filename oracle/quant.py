@@ -20,7 +20,7 @@ Method (restated from the pages):
   usual choice, giving 4 + 32/128 = 4.25 bits per weight; ``g = K`` is the
   per-channel case -- page 4, §3.4 量化粒度; page 3, §二 granularity table.
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
 
 * R1 orientation: ``W`` is ``[N = d_out, K = d_in]``; groups run along K.
 * R2 ``round`` is round-half-to-even (``np.rint``), the IEEE default.

@@ -16,7 +16,7 @@ Method (restated from the pages):
   ``s = max|x| / 127``, codes in [-128, 127] (3.3, 2.2); activations one symmetric scale
   per token (3.4 per-token).
 
-Readings (listed in DESIGN.md):
+Readings:
 
 * Q8-1 orientation: ``W [N, K]`` with input channels along K, so ``s W`` scales column j of
   ``W`` by ``s_j`` and ``X / s`` divides activation column j (the pages' ``diag(s)^-1 x``).
