@@ -315,11 +315,11 @@ def _full_size(case: Case, n_rows: int = 48, m_rows: int | None = None):
     assert_close(y, ref_to_f64(ref, case.dtype), case.name)
 
 
-FULL = [c for c in config_cases(1)] + \
-       [c for c in config_cases(2) if c.M in (1, 4, 16)] + \
-       [c for c in config_cases(3) if c.M in (1, 16)] + \
-       [c for c in config_cases(4) if (c.M, c.K, c.g, c.scheme) in
-        [(4096, 4096, 128, ASYM), (256, 11008, 64, SYM), (1024, 4096, 64, ASYM)]]
+# every case of the single-layer workloads: the 7B-like decode sweep (M = 1..16), the
+# 70B-like decode shapes with outlier channels and weights (bf16), and the prefill grid
+# (M = 256 / 1024 / 4096, g = 64 / 128, symmetric and asymmetric), each checked before the
+# benchmark times it
+FULL = [c for cfg in (1, 2, 3, 4) for c in config_cases(cfg)]
 
 
 @pytest.mark.parametrize("case", FULL, ids=lambda c: c.name)
