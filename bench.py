@@ -194,7 +194,9 @@ def cpu_baseline(layers, w_host, xs_host, y_gpu, budget_s, np, torch):
         oracle.linear_ref(xs_host[0] if K == 4096 else xs_host[2], 0, qw, s, z, GROUP)
     layer_s = time.perf_counter() - t1
     return {"value": total_bytes / el / 1e9, "unit": "GB/s", "cores": int(threads),
-            "host_cpus": os.cpu_count(), "kind": "oracle",
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "blas_env": {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS")},
+            "kind": "oracle",
             "sample": f"{steps} oracle step(s) of the same M=1 workload (3 layers, fp64 "
                       f"dequantize + BLAS matmul), {el:.1f} s",
             "parity_vs_gpu": parity,
