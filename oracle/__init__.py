@@ -38,9 +38,13 @@ What it computes (sources are the five pages on W4A16 quantization):
 * KV-cache quantization (``kv.py``): per-token KV8 / KV4 and the decode attention that
   reads the quantized cache (page 3, section 六 KV Cache 量化; page 1 on W4A16 + KV INT8).
 
+* W8A16 (``w8a16.py``): the same group-wise weight-only layer with 8-bit codes, four per
+  32-bit word (page 4, section 3.3 prints the 8-bit asymmetric divisor 255; page 2, section
+  二 and page 1 on INT8 weight-only quantization).
+
 Readings where the pages are silent (tie rule, clamping, which scale feeds the
 zero point, nibble order, symmetric storage) are listed in the docstrings of
-``quant.py``, ``linear.py``, ``gptq.py``, ``awq.py``, ``w8a8.py`` and ``kv.py``.
+``quant.py``, ``linear.py``, ``gptq.py``, ``awq.py``, ``w8a8.py``, ``kv.py`` and ``w8a16.py``.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against hand-worked vectors, closed forms, exact rational arithmetic or an
