@@ -342,6 +342,52 @@ int w4a16_kv_attention_decode_batch(const void* q, int dtype, int64_t B, int64_t
                                     const void* vcodes, const uint16_t* vscales, const uint16_t* vzeros,
                                     float* work, void* out, void* stream);
 
+/* ------------------------------------------------------------------------------------
+ * W8A16: the same weight-only layer with 8-bit codes, four per 32-bit word (byte k % 4 of
+ * word k / 4 is element k) and the same fp16 scale and zero point per group (page
+ * "大模型推理中 Weight-only、W8A8 和 FP8 量化有什么区别？如何选型？", 二, INT8 / INT4 weight-only
+ * with 16-bit activations; page "推理优化中“用精度换性能“的核心技术：量化", 3.3, the 8-bit
+ * asymmetric divisor 255).  Shapes, group sizes, alignment and status codes follow the 4-bit
+ * calls; qweight is [N, K/4] int32.
+ */
+
+/*
+ * w4a16_w8a16_quantize_pack -- group-wise round-to-nearest INT8 quantization and packing.
+ *   W        [N, K] fp32, device, 16-byte aligned.
+ *   qweight  out [N, K/4] int32, device, 16-byte aligned.
+ *   scales   out [N, K/g] fp16 bits; zeros out [N, K/g] fp16 bits, or NULL for the symmetric
+ *            scheme (the implicit zero point is then 128).
+ * Arithmetic per group (IEEE fp32, round-to-nearest-even, this order):
+ *   asymmetric: s32 = (max - min) / 255; s = fp16(s32), or 1.0 if that is 0;
+ *               z = rint(-min / s) + 0.0; u = clamp(rint(x / s) + z, 0, 255);
+ *   symmetric:  s32 = max|x| / 127; s as above; u = clamp(rint(x / s), -128, 127) + 128; z = 128.
+ * Bit-identical to that arithmetic; preconditions as for w4a16_quantize_pack.
+ */
+int w4a16_w8a16_quantize_pack(const float* W, int64_t N, int64_t K, int64_t group_size, int scheme,
+                              int32_t* qweight, uint16_t* scales, uint16_t* zeros, void* stream);
+
+/*
+ * w4a16_w8a16_linear -- Y[M, N] = X[M, K] . W_hat[N, K]^T, W_hat[n, k] = s (u - z) from the
+ * 8-bit codes, dequantized inside the kernel (the codes enter the products exactly and the
+ * group's s and z are applied to the fp32 partial sums); fp32 accumulation, Y rounded once to
+ * the activation dtype.  Arguments as for w4a16_linear with qweight [N, K/4]; zeros NULL means
+ * all zero points 128; any integer zero point |z| <= 2048.  Kernels: a weight-streaming GEMV
+ * for M <= 4 (when M * K * 2.25 bytes of staged activations fit 64 KB and N * K < 2^31), else
+ * the tiled MFMA GEMM, which needs K and g to be multiples of 64 (W4A16_ERR_PATH otherwise).
+ */
+int w4a16_w8a16_linear(const void* X, int dtype, int64_t M, int64_t N, int64_t K, int64_t group_size,
+                       const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros, void* Y,
+                       void* stream);
+
+/* w4a16_w8a16_linear with an explicit kernel: W4A16_PATH_AUTO, W4A16_PATH_GEMV or
+ * W4A16_PATH_PREFILL (W4A16_ERR_PATH when that kernel cannot take the problem). */
+int w4a16_w8a16_linear_ex(const void* X, int dtype, int64_t M, int64_t N, int64_t K, int64_t group_size,
+                          const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros, void* Y,
+                          int path, void* stream);
+
+/* The kernel w4a16_w8a16_linear would take (host only; a negative status for invalid shapes). */
+int w4a16_w8a16_select_path(int64_t M, int64_t N, int64_t K, int64_t group_size, int dtype);
+
 /* Human-readable text for a status code (static storage). */
 const char* w4a16_strerror(int status);
 

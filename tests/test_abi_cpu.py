@@ -42,7 +42,8 @@ def test_header_declares_the_boundary():
                      "w4a16_w8a8_quantize_weight", "w4a16_w8a8_quantize_act", "w4a16_w8a8_linear",
                      "w4a16_kv_quantize", "w4a16_kv_attention_workspace",
                      "w4a16_kv_attention_decode", "w4a16_kv_attention_batch_workspace",
-                     "w4a16_kv_attention_decode_batch"):
+                     "w4a16_kv_attention_decode_batch", "w4a16_w8a16_quantize_pack",
+                     "w4a16_w8a16_linear", "w4a16_w8a16_linear_ex", "w4a16_w8a16_select_path"):
         assert required in names
 
 
@@ -232,3 +233,56 @@ def test_kv_batch_rejects_invalid_arguments(lib):
     assert att(Tmax=1 << 25) == L.ERR_SHAPE
     assert att(q=A + 8) == L.ERR_ALIGN           # q must be 16-byte aligned
     assert att(lens=C + 0x2002) == L.ERR_ALIGN
+
+
+# --------------------------------------------------------------------------- W8A16
+def _lin8(lib, X=A, dtype=0, M=1, N=64, K=128, g=128, qw=B, s=C, z=D, Y=A + 4096, path=0):
+    return lib.w4a16_w8a16_linear_ex(X, dtype, M, N, K, g, qw, s, z, Y, path, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), L.ERR_NULL),
+    (dict(qw=None), L.ERR_NULL),
+    (dict(s=None), L.ERR_NULL),
+    (dict(Y=None), L.ERR_NULL),
+    (dict(dtype=2), L.ERR_DTYPE),
+    (dict(M=0), L.ERR_SHAPE),
+    (dict(K=48, g=48), L.ERR_SHAPE),
+    (dict(K=192, g=48), L.ERR_GROUP),
+    (dict(X=MIS), L.ERR_ALIGN),
+    (dict(qw=B + 8), L.ERR_ALIGN),
+    (dict(z=D + 1), L.ERR_ALIGN),
+    (dict(M=5, path=L.PATH_GEMV), L.ERR_PATH),                     # the 8-bit GEMV takes M <= 4
+    (dict(M=5, K=128, g=32), L.ERR_PATH),                           # M > 4 needs g % 64 == 0
+    (dict(K=96, g=32, path=L.PATH_PREFILL), L.ERR_PATH),            # the GEMM needs K % 64 == 0
+    (dict(path=L.PATH_SKINNY), L.ERR_PATH),                         # no skinny kernel for 8 bits
+    (dict(path=17), L.ERR_PATH),
+])
+def test_w8a16_linear_rejects_invalid_arguments(lib, kw, status):
+    assert _lin8(lib, **kw) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 64, 128, 128, 0, B, C, D), L.ERR_NULL),
+    ((A, 64, 128, 128, 5, B, C, D), L.ERR_SCHEME),
+    ((A, 64, 128, 128, 0, B, C, None), L.ERR_NULL),
+    ((A, 64, 100, 100, 0, B, C, D), L.ERR_SHAPE),
+    ((A, 64, 128, 96, 0, B, C, D), L.ERR_GROUP),
+    ((MIS, 64, 128, 128, 0, B, C, D), L.ERR_ALIGN),
+    ((A, 64, 128, 128, 1, B + 4, C, None), L.ERR_ALIGN),
+])
+def test_w8a16_quantize_pack_rejects_invalid_arguments(lib, args, status):
+    assert lib.w4a16_w8a16_quantize_pack(*args, None) == status
+
+
+@pytest.mark.parametrize("M,N,K,g,dtype,path", [
+    (1, 4096, 4096, 128, 0, L.PATH_GEMV),
+    (4, 11008, 4096, 128, 1, L.PATH_GEMV),
+    (4, 4096, 11008, 128, 0, L.PATH_PREFILL),      # 4 x 11008 activations exceed the GEMV's LDS
+    (1, 8192, 28672, 128, 1, L.PATH_GEMV),
+    (5, 4096, 4096, 128, 0, L.PATH_PREFILL),
+    (4096, 11008, 4096, 64, 0, L.PATH_PREFILL),
+    (2, 4096, 4096, 32, 0, L.PATH_GEMV),           # g = 32: GEMV only
+])
+def test_w8a16_dispatcher_choices(lib, M, N, K, g, dtype, path):
+    assert lib.w4a16_w8a16_select_path(M, N, K, g, dtype) == path

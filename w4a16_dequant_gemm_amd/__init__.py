@@ -31,6 +31,7 @@ from ._lib import (ASYM, BF16, F16, OK, PATH_AUTO, PATH_GEMV, PATH_NAMES, PATH_P
 __all__ = [
     "ASYM", "SYM", "F16", "BF16", "PATH_AUTO", "PATH_GEMV", "PATH_SKINNY", "PATH_PREFILL",
     "PATH_NAMES", "W4A16Error", "quantize_pack", "linear", "dequantize", "select_path",
+    "w8a16_quantize_pack", "w8a16_linear", "w8a16_select_path",
     "abi_version", "lib", "gptq_hessian", "gptq_factor", "gptq_quantize", "awq_stats",
     "awq_search", "awq_scale", "w8a8_smooth", "w8a8_quantize_weight", "w8a8_quantize_act",
     "w8a8_linear", "kv_quantize", "kv_attention_decode",
@@ -125,6 +126,66 @@ def linear(X: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zeros, 
                                scales.data_ptr(), zeros.data_ptr() if zeros is not None else None,
                                out.data_ptr(), path, _stream())
     check(st, "w4a16_linear")
+    return out
+
+
+def w8a16_quantize_pack(W: torch.Tensor, group_size: int = 128, scheme: int = ASYM,
+                        write_zeros: bool = True):
+    """8-bit codes: quantize fp32 ``W [N, K]`` on the GPU.  Returns ``(qweight int32 [N, K/4],
+    scales fp16 [N, K/g], zeros fp16 [N, K/g] or None)``; ``zeros`` is None only for the
+    symmetric scheme with ``write_zeros=False`` (implicit zero point 128)."""
+    _need(W, "W", torch.float32, 2)
+    N, K = W.shape
+    if K % 4 or group_size <= 0 or K % group_size:
+        raise ValueError("K must be a multiple of 4 and of group_size")
+    G = K // group_size
+    qweight = torch.empty((N, K // 4), dtype=torch.int32, device=W.device)
+    scales = torch.empty((N, G), dtype=torch.float16, device=W.device)
+    zeros = None
+    if scheme == ASYM or write_zeros:
+        zeros = torch.empty((N, G), dtype=torch.float16, device=W.device)
+    st = lib().w4a16_w8a16_quantize_pack(W.data_ptr(), N, K, group_size, scheme, qweight.data_ptr(),
+                                         scales.data_ptr(), zeros.data_ptr() if zeros is not None else None,
+                                         _stream())
+    check(st, "w4a16_w8a16_quantize_pack")
+    return qweight, scales, zeros
+
+
+def w8a16_select_path(M: int, N: int, K: int, group_size: int, dtype: int = F16) -> int:
+    """Kernel the 8-bit dispatcher picks (host only): ``PATH_GEMV`` or ``PATH_PREFILL``."""
+    p = lib().w4a16_w8a16_select_path(M, N, K, group_size, dtype)
+    if p < 0:
+        raise W4A16Error(p, "w8a16_select_path")
+    return p
+
+
+def w8a16_linear(X: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zeros, group_size: int,
+                 path: int = PATH_AUTO, out: torch.Tensor | None = None) -> torch.Tensor:
+    """``Y [M, N] = X [M, K] . dequant(qweight)^T`` with 8-bit codes ``qweight int32 [N, K/4]``."""
+    dt = _dtype_code(X)
+    _need(X, "X", X.dtype, 2)
+    _need(qweight, "qweight", torch.int32, 2)
+    _need(scales, "scales", torch.float16, 2)
+    if zeros is not None:
+        _need(zeros, "zeros", torch.float16, 2)
+    M, K = X.shape
+    N = qweight.shape[0]
+    if qweight.shape[1] * 4 != K:
+        raise ValueError("qweight must be [N, K/4]")
+    if group_size <= 0 or K % group_size or tuple(scales.shape) != (N, K // group_size):
+        raise ValueError("scales must be [N, K/group_size]")
+    if zeros is not None and zeros.shape != scales.shape:
+        raise ValueError("zeros must match scales")
+    if out is None:
+        out = torch.empty((M, N), dtype=X.dtype, device=X.device)
+    else:
+        _need(out, "out", X.dtype, 2)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out must be [M, N]")
+    st = lib().w4a16_w8a16_linear_ex(X.data_ptr(), dt, M, N, K, group_size, qweight.data_ptr(),
+                                     scales.data_ptr(), zeros.data_ptr() if zeros is not None else None,
+                                     out.data_ptr(), path, _stream())
+    check(st, "w4a16_w8a16_linear")
     return out
 
 

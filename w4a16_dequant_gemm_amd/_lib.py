@@ -53,6 +53,14 @@ def lib() -> ctypes.CDLL:
     L.w4a16_linear_ex.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, vp, vp, i32, vp]
     L.w4a16_select_path.restype = i32
     L.w4a16_select_path.argtypes = [i64, i64, i64, i64, i32]
+    L.w4a16_w8a16_quantize_pack.restype = i32
+    L.w4a16_w8a16_quantize_pack.argtypes = [vp, i64, i64, i64, i32, vp, vp, vp, vp]
+    L.w4a16_w8a16_linear.restype = i32
+    L.w4a16_w8a16_linear.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, vp, vp, vp]
+    L.w4a16_w8a16_linear_ex.restype = i32
+    L.w4a16_w8a16_linear_ex.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, vp, vp, i32, vp]
+    L.w4a16_w8a16_select_path.restype = i32
+    L.w4a16_w8a16_select_path.argtypes = [i64, i64, i64, i64, i32]
     L.w4a16_dequantize.restype = i32
     L.w4a16_dequantize.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp]
     L.w4a16_gptq_hessian.restype = i32

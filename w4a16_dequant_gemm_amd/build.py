@@ -13,7 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw4a16.so")
-SOURCES = ["api.cpp", "quantize.hip", "gemv.hip", "skinny.hip", "decode.hip", "prefill.hip", "gptq.hip", "awq.hip", "w8a8.hip", "kv.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemv.hip", "skinny.hip", "decode.hip", "prefill.hip", "gptq.hip", "awq.hip", "w8a8.hip", "kv.hip", "w8a16.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -405,4 +405,72 @@ int w4a16_linear(const void* X, int dtype, int64_t M, int64_t N, int64_t K, int6
                            W4A16_PATH_AUTO, stream);
 }
 
+// ----------------------------------------------------------------- W8A16 (8-bit codes)
+
+int w4a16_w8a16_quantize_pack(const float* W, int64_t N, int64_t K, int64_t group_size, int scheme,
+                              int32_t* qweight, uint16_t* scales, uint16_t* zeros, void* stream) {
+    if (!W || !qweight || !scales) return W4A16_ERR_NULL;
+    if (scheme != W4A16_ASYM_RTN && scheme != W4A16_SYM_ABSMAX) return W4A16_ERR_SCHEME;
+    if (scheme == W4A16_ASYM_RTN && !zeros) return W4A16_ERR_NULL;
+    int G = 0, gshift = 0;
+    const int st = check_shape_group(N, K, group_size, &G, &gshift);
+    if (st != W4A16_OK) return st;
+    if (!aligned(W, 16) || !aligned(qweight, 16) || !aligned(scales, 2) || (zeros && !aligned(zeros, 2)))
+        return W4A16_ERR_ALIGN;
+    return hip_status(w4a16::launch_quantize_pack8(W, (int)N, (int)K, (int)group_size, scheme,
+                                                   reinterpret_cast<uint32_t*>(qweight), scales, zeros,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+// W8A16 dispatch: the weight-streaming GEMV for up to 4 activation rows when their staged
+// copy fits its LDS budget and the packed weights are below 2 GiB, else the tiled MFMA GEMM
+// (K and g multiples of 64).
+int choose_path8(const LinearArgs& a) {
+    if (w4a16::gemv8_supports(a)) return W4A16_PATH_GEMV;
+    if (w4a16::prefill8_supports(a)) return W4A16_PATH_PREFILL;
+    return -1;
+}
+}  // namespace
+
+int w4a16_w8a16_select_path(int64_t M, int64_t N, int64_t K, int64_t group_size, int dtype) {
+    alignas(16) static const unsigned char dummy[16] = {0};
+    LinearArgs a;
+    const int st = validate_linear(dummy, dtype, M, N, K, group_size, reinterpret_cast<const int32_t*>(dummy),
+                                   reinterpret_cast<const uint16_t*>(dummy), nullptr,
+                                   const_cast<unsigned char*>(dummy), &a);
+    if (st != W4A16_OK) return st;
+    const int p = choose_path8(a);
+    return p < 0 ? W4A16_ERR_PATH : p;
+}
+
+int w4a16_w8a16_linear_ex(const void* X, int dtype, int64_t M, int64_t N, int64_t K, int64_t group_size,
+                          const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros, void* Y,
+                          int path, void* stream) {
+    LinearArgs a;
+    const int st = validate_linear(X, dtype, M, N, K, group_size, qweight, scales, zeros, Y, &a);
+    if (st != W4A16_OK) return st;
+    if (path == W4A16_PATH_AUTO) {
+        path = choose_path8(a);
+        if (path < 0) return W4A16_ERR_PATH;
+    }
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (path == W4A16_PATH_GEMV) {
+        if (!w4a16::gemv8_supports(a)) return W4A16_ERR_PATH;
+        return hip_status(w4a16::launch_gemv8(a, s));
+    }
+    if (path == W4A16_PATH_PREFILL) {
+        if (!w4a16::prefill8_supports(a)) return W4A16_ERR_PATH;
+        return hip_status(w4a16::launch_prefill8(a, s));
+    }
+    return W4A16_ERR_PATH;
+}
+
+int w4a16_w8a16_linear(const void* X, int dtype, int64_t M, int64_t N, int64_t K, int64_t group_size,
+                       const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros, void* Y,
+                       void* stream) {
+    return w4a16_w8a16_linear_ex(X, dtype, M, N, K, group_size, qweight, scales, zeros, Y, W4A16_PATH_AUTO,
+                                 stream);
+}
+
 }  // extern "C"

@@ -34,6 +34,13 @@ hipError_t launch_gemv(const LinearArgs& a, hipStream_t s);
 hipError_t launch_skinny(const LinearArgs& a, hipStream_t s);
 hipError_t launch_decode(const LinearArgs& a, hipStream_t s);
 hipError_t launch_prefill(const LinearArgs& a, hipStream_t s);
+// W8A16 (8-bit codes, four per word): quantize-pack, the decode GEMV and the tiled MFMA GEMM
+hipError_t launch_quantize_pack8(const float* W, int N, int K, int g, int scheme, uint32_t* qw,
+                                 uint16_t* scales, uint16_t* zeros, hipStream_t s);
+bool gemv8_supports(const LinearArgs& a);
+hipError_t launch_gemv8(const LinearArgs& a, hipStream_t s);
+bool prefill8_supports(const LinearArgs& a);
+hipError_t launch_prefill8(const LinearArgs& a, hipStream_t s);
 
 // GPTQ (gptq.hip)
 hipError_t launch_gptq_hessian(const void* X, int dtype, int n, int K, double* H, bool accumulate,

@@ -27,6 +27,7 @@
 #include "common.h"
 #include "launch.h"
 #include "tile.h"
+#include "w8.h"
 
 namespace w4a16 {
 
@@ -56,7 +57,12 @@ struct Mfma<DT_BF16> {
     }
 };
 
-template <int DT>
+// BITS = 8 (W8A16): 8-bit codes, four per word; lane (n, h) loads the 32 bytes holding columns
+// k0 + 32h .. + 31 (two 16-byte loads), MFMA kk takes words 2kk and 2kk + 1 (columns
+// k0 + 32h + 8kk .. + 7) in natural order, the activation tile is staged unpermuted, and the
+// codes enter the MFMA exactly (fp16 subnormals u * 2^-24, or bf16 u), so c = z for both
+// dtypes (the implicit symmetric zero point is 128).
+template <int DT, int BITS = 4>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restrict__ X,
                                                          const uint32_t* __restrict__ qw,
                                                          const uint16_t* __restrict__ scales,
@@ -80,7 +86,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restr
     const int tn = blockIdx.x % tiles_n;
     const int m0 = tm * BM;
     const int n0 = tn * BN;
-    const int KW = K >> 3;
+    const int KW = BITS == 4 ? K >> 3 : K >> 2;      // words per weight row
     const int nsteps = K / BK;
 
     // Staging role: thread t loads row t/2, columns 32*(t%2) .. +31 of the tile.
@@ -109,8 +115,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restr
         float part = 0.0f;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            uint32_t o[4];
-            permute_x8_byte(xreg[b].x, xreg[b].y, xreg[b].z, xreg[b].w, o);
+            uint32_t o[4] = {xreg[b].x, xreg[b].y, xreg[b].z, xreg[b].w};
+            if constexpr (BITS == 4) permute_x8_byte(xreg[b].x, xreg[b].y, xreg[b].z, xreg[b].w, o);
             *reinterpret_cast<u32x4*>(dst + 8 * b) = u32x4{o[0], o[1], o[2], o[3]};
             part += (pair_sum<DT>(xreg[b].x) + pair_sum<DT>(xreg[b].y)) +
                     (pair_sum<DT>(xreg[b].z) + pair_sum<DT>(xreg[b].w));
@@ -125,12 +131,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restr
         }
     };
 
-    u32x4 wreg[2];
+    constexpr int WL = BITS == 4 ? 1 : 2;            // 16-byte weight loads per row and step
+    u32x4 wreg[2][WL];
     auto load_w = [&](int step) {
 #pragma unroll
         for (int ns = 0; ns < 2; ++ns)
-            wreg[ns] = *reinterpret_cast<const u32x4*>(qw + (size_t)wrow[ns] * KW +
-                                                       (size_t)step * (BK / 8) + 4 * h);
+#pragma unroll
+            for (int i = 0; i < WL; ++i)
+                wreg[ns][i] = *reinterpret_cast<const u32x4*>(qw + (size_t)wrow[ns] * KW +
+                                                              (size_t)step * (BK * BITS / 32) + 4 * (WL * h + i));
     };
 
     f32x16 acc[2][2], accg[2][2];
@@ -158,9 +167,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restr
             for (int ns = 0; ns < 2; ++ns) {
                 const float sv = h2f(scales[(size_t)wrow[ns] * G + grp]);
                 const float zr = h2f(zsrc[(size_t)wrow[ns] * G + grp]);
-                const float zv = has_zeros ? zr : 8.0f;
+                const float zv = has_zeros ? zr : (BITS == 4 ? 8.0f : 128.0f);
                 gs[ns] = DT == DT_F16 ? sv * 16777216.0f : sv;     // fp16: fold 2^24 (exact)
-                gc[ns] = DT == DT_F16 ? zv : 128.0f + zv;
+                gc[ns] = (DT == DT_F16 || BITS == 8) ? zv : 128.0f + zv;
             }
         }
         // Dequantize this step's weights into B operands.
@@ -168,7 +177,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restr
 #pragma unroll
         for (int ns = 0; ns < 2; ++ns) {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) unpack_byte<DT == DT_F16 ? 0u : 0x43u>(wreg[ns][kk], bop[ns][kk]);
+            for (int kk = 0; kk < 4; ++kk) {
+                if constexpr (BITS == 4) {
+                    unpack_byte<DT == DT_F16 ? 0u : 0x43u>(wreg[ns][0][kk], bop[ns][kk]);
+                } else {
+                    codes8<DT>(wreg[ns][kk >> 1][2 * (kk & 1)], &bop[ns][kk][0]);
+                    codes8<DT>(wreg[ns][kk >> 1][2 * (kk & 1) + 1], &bop[ns][kk][2]);
+                }
+            }
         }
         // Prefetch the next step.
         if (step + 1 < nsteps) {
@@ -620,6 +636,26 @@ hipError_t launch_prefill(const LinearArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(prefill_kernel<DT_BF16>, dim3(tiles), dim3(256), 0, st,
                        static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, hz,
                        static_cast<uint16_t*>(a.Y), a.M, a.N, a.K, a.G, spg);
+    return hipGetLastError();
+}
+
+// W8A16: the 128 x 128 tiled kernel with 8-bit codes, either dtype.
+bool prefill8_supports(const LinearArgs& a) { return a.K % BK == 0 && a.g % BK == 0; }
+
+hipError_t launch_prefill8(const LinearArgs& a, hipStream_t st) {
+    if (!prefill8_supports(a)) return hipErrorInvalidValue;
+    const int hz = a.zeros ? 1 : 0;
+    const long long tiles = (long long)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+    if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const int spg = a.g / BK;
+    if (a.dtype == DT_F16)
+        hipLaunchKernelGGL((prefill_kernel<DT_F16, 8>), dim3((unsigned)tiles), dim3(256), 0, st,
+                           static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, hz,
+                           static_cast<uint16_t*>(a.Y), a.M, a.N, a.K, a.G, spg);
+    else
+        hipLaunchKernelGGL((prefill_kernel<DT_BF16, 8>), dim3((unsigned)tiles), dim3(256), 0, st,
+                           static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, hz,
+                           static_cast<uint16_t*>(a.Y), a.M, a.N, a.K, a.G, spg);
     return hipGetLastError();
 }
 

@@ -123,6 +123,102 @@ hipError_t launch_quantize_pack(const float* W, int N, int K, int g, int gshift,
     return hipGetLastError();
 }
 
+// 8-bit codes (W8A16): the same group-wise RTN with the 8-bit ranges of page
+// "推理优化中“用精度换性能“的核心技术：量化", section 3.3 (asymmetric s = (max - min)/255,
+// z = rint(-min/s), codes [0, 255]; symmetric s = max|x|/127, codes [-128, 127] stored as
+// q + 128), the same fp32 operation order and fp16 scale rounding as the 4-bit kernel.  A
+// lane owns whole output words of 4 bytes; byte k % 4 of word k / 4 is element k.
+template <int SCHEME>
+__device__ __forceinline__ void rtn8_params(float mn, float mx, _Float16& sh, float& s, float& z) {
+    const float s32 = (SCHEME == 0) ? (mx - mn) / 255.0f : mx / 127.0f;
+    sh = (_Float16)s32;
+    s = (float)sh;
+    if (s == 0.0f) { s = 1.0f; sh = (_Float16)1.0f; }
+    z = (SCHEME == 0) ? (__builtin_rintf((-mn) / s) + 0.0f) : 128.0f;
+}
+
+template <int SCHEME>
+__device__ __forceinline__ uint32_t rtn8_code(float x, float s, float z) {
+    float q;
+    if (SCHEME == 0) {
+        q = fminf(fmaxf(__builtin_rintf(x / s) + z, 0.0f), 255.0f);
+    } else {
+        q = fminf(fmaxf(__builtin_rintf(x / s), -128.0f), 127.0f) + 128.0f;
+    }
+    return (uint32_t)(int)q;
+}
+
+template <int SCHEME>
+__global__ __launch_bounds__(256) void quantize_pack8_kernel(
+    const float* __restrict__ W, int N, int K, int g, int G, int seg, int words_per_lane,
+    uint32_t* __restrict__ qw, uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros) {
+    const int lane = threadIdx.x & 63;
+    const long long wave = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int gpw = 64 / seg;
+    const int slot = lane / seg;
+    const int gl = lane % seg;
+    const long long gid = (long long)wave * gpw + slot;
+    const long long total = (long long)N * G;
+    const bool active_group = gid < total;
+    const int n = active_group ? (int)(gid / G) : 0;
+    const int j = active_group ? (int)(gid % G) : 0;
+    const int wcount = g >> 2;                     // 4-code words in the group
+    const float* row = W + (size_t)n * K + (size_t)j * g;
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+    for (int it = 0; it < words_per_lane; ++it) {
+        const int w = gl + it * seg;
+        if (active_group && w < wcount) {
+            const float4 a = *reinterpret_cast<const float4*>(row + 4 * w);
+            if (SCHEME == 0) {
+                mn = fminf(mn, fminf(fminf(a.x, a.y), fminf(a.z, a.w)));
+                mx = fmaxf(mx, fmaxf(fmaxf(a.x, a.y), fmaxf(a.z, a.w)));
+            } else {
+                mx = fmaxf(mx, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+            }
+        }
+    }
+    for (int off = seg >> 1; off > 0; off >>= 1) {
+        mn = fminf(mn, __shfl_xor(mn, off, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    }
+    if (!active_group) return;
+    _Float16 sh;
+    float s, z;
+    rtn8_params<SCHEME>(mn, mx, sh, s, z);
+    for (int it = 0; it < words_per_lane; ++it) {
+        const int w = gl + it * seg;
+        if (w < wcount) {
+            const float4 a = *reinterpret_cast<const float4*>(row + 4 * w);
+            const uint32_t word = rtn8_code<SCHEME>(a.x, s, z) | (rtn8_code<SCHEME>(a.y, s, z) << 8) |
+                                  (rtn8_code<SCHEME>(a.z, s, z) << 16) | (rtn8_code<SCHEME>(a.w, s, z) << 24);
+            qw[(size_t)n * (K >> 2) + (size_t)j * (g >> 2) + w] = word;
+        }
+    }
+    if (gl == 0) {
+        scales[(size_t)n * G + j] = __builtin_bit_cast(uint16_t, sh);
+        if (zeros) zeros[(size_t)n * G + j] = __builtin_bit_cast(uint16_t, (_Float16)z);
+    }
+}
+
+hipError_t launch_quantize_pack8(const float* W, int N, int K, int g, int scheme, uint32_t* qw,
+                                 uint16_t* scales, uint16_t* zeros, hipStream_t st) {
+    const int G = K / g;
+    const int wcount = g / 4;
+    const bool pow2 = (wcount & (wcount - 1)) == 0;
+    const int seg = (pow2 && wcount <= 64) ? wcount : 64;
+    const int words_per_lane = (wcount + seg - 1) / seg;
+    const long long groups = (long long)N * G;
+    const long long waves = (groups + (64 / seg) - 1) / (64 / seg);
+    const long long blocks = (waves + 3) / 4;
+    if (scheme == 0)
+        hipLaunchKernelGGL(quantize_pack8_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, st, W, N, K, g, G,
+                           seg, words_per_lane, qw, scales, zeros);
+    else
+        hipLaunchKernelGGL(quantize_pack8_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, st, W, N, K, g, G,
+                           seg, words_per_lane, qw, scales, zeros);
+    return hipGetLastError();
+}
+
 hipError_t launch_dequantize(const uint32_t* qw, const uint16_t* scales, const uint16_t* zeros,
                              int N, int K, int g, int gshift, float* out, hipStream_t st) {
     const long long words = (long long)N * (K / 8);
