@@ -256,6 +256,17 @@ def cpu_baseline_rows(oracle, np):
     t1 = time.perf_counter()
     out["kv8_attention"] = {"sample": f"H={H}, D={D}, T={T}", "s": round(t1 - t0, 4),
                             "GBps": round(2 * H * T * (D + 2) / (t1 - t0) / 1e9, 3)}
+    # W8A16 linear, M = 1 on one 4096 x 4096 layer (8-bit codes, g = 128)
+    from oracle import w8a16
+    W = synth.weights(4096, 4096, 0.02, 18)
+    codes, sc, z = w8a16.quantize8(W, GROUP, w8a16.ASYM)
+    q = w8a16.pack8(codes)
+    X = synth.activations(1, 4096, synth.FP16, 19)
+    t0 = time.perf_counter()
+    w8a16.linear8_ref(X, synth.FP16, q, sc, z, GROUP)
+    t1 = time.perf_counter()
+    out["w8a16_linear"] = {"sample": "M=1, K=N=4096, g=128", "s": round(t1 - t0, 4),
+                           "GBps": round((4096 * 4096 + 4 * 4096 * 4096 // GROUP) / (t1 - t0) / 1e9, 3)}
     return out
 
 
@@ -288,7 +299,8 @@ def profile_run(name: str, W4, synth, torch):
     `prefill` (M = 4096 on both prefill shapes, 5 launches each), `w8a8` (the INT8 product at
     M = 4096, both shapes, 5 launches each), `kv_batch` (batched KV8 and KV4 decode attention,
     16 sequences, 2 layers' caches, 2 launches each), `decode_m16` (M = 16 on the 7B shapes
-    over 20 rotating weight copies, 20 launches each)."""
+    over 20 rotating weight copies, 20 launches each), `w8a16` (8-bit codes: M = 1 on the 7B
+    shapes over 10 rotating copies, 20 launches each, and the M = 4096 prefill, 5 each)."""
     if name == "prefill":
         for K, N in [(4096, 11008), (11008, 4096)]:
             W = synth.weights_device(N, K, 0.02, 3000 + K)
@@ -310,6 +322,27 @@ def profile_run(name: str, W4, synth, torch):
                 W4.w8a8_linear(qx, sx, qw, sw, out=Y)
     elif name == "kv_batch":
         run_kv_batch(W4, synth, torch, layers=2, timed=False)
+    elif name == "w8a16":
+        # 8-bit codes: M = 1 on the 7B shapes over 10 rotating copies (20 launches each), and
+        # the prefill at M = 4096 on both shapes (5 launches each)
+        for K, N in SHAPES:
+            W = synth.weights_device(N, K, 0.02, 9000 + K + N)
+            q = W4.w8a16_quantize_pack(W, GROUP, W4.ASYM)
+            del W
+            cs = [tuple(t.clone() for t in q) for _ in range(10)]
+            X = synth.activations_device(1, K, synth.FP16, 9)
+            Y = torch.empty((1, N), dtype=torch.float16, device="cuda")
+            for i in range(20):
+                W4.w8a16_linear(X, *cs[i % 10], GROUP, out=Y)
+            del cs
+        for K, N in [(4096, 11008), (11008, 4096)]:
+            W = synth.weights_device(N, K, 0.02, 9200 + K)
+            q = W4.w8a16_quantize_pack(W, GROUP, W4.ASYM)
+            del W
+            X = synth.activations_device(4096, K, synth.FP16, 9201 + K)
+            Y = torch.empty((4096, N), dtype=torch.float16, device="cuda")
+            for _ in range(5):
+                W4.w8a16_linear(X, *q, GROUP, out=Y)
     elif name == "decode_m16":
         for K, N in SHAPES:
             W = synth.weights_device(N, K, 0.02, 1000 + K + N)
@@ -386,7 +419,7 @@ def main():
     ap.add_argument("--traffic-commands", nargs="*", default=[],
                     help="the profiler command lines, recorded in the traffic file")
     ap.add_argument("--traffic-out", default=None, help="output path of --traffic-parse")
-    ap.add_argument("--profile-run", choices=["prefill", "w8a8", "kv_batch", "decode_m16"],
+    ap.add_argument("--profile-run", choices=["prefill", "w8a8", "kv_batch", "decode_m16", "w8a16"],
                     help="a short fixed workload of one kernel family, for counter runs")
     args = ap.parse_args()
     if args.traffic_parse:
@@ -657,7 +690,58 @@ def run_extras(layers, copies, W4, synth, torch, np):
     out["w8a8_m4096"] = run_w8a8(W4, synth, torch)
     out["kv_decode_attention_h32_d128_t4096"] = run_kv(W4, synth, torch)
     out["full_stack_7b_32_layers"] = run_stack(W4, synth, torch)
+    out["w8a16_g128"] = run_w8a16(W4, synth, torch)
     return out
+
+
+def run_w8a16(W4, synth, torch):
+    """W8A16 (8-bit codes, g = 128 asym, fp16): the M = 1 step on the three 7B-like layers
+    (graph-captured, rotating >= 1 GiB of weight copies; bytes = N K + 4 N K / g per layer)
+    and each layer at M = 4, and the prefill at M = 4096 on both shapes (TFLOP/s)."""
+    res = {}
+    shapes = SHAPES
+    per_copy = sum(N * K + 4 * N * K // GROUP for K, N in shapes)
+    copies = max(2, int(-(-2**30 // per_copy)))
+    layers = []
+    for i, (K, N) in enumerate(shapes):
+        W = synth.weights_device(N, K, 0.02, 9000 + i)
+        q = W4.w8a16_quantize_pack(W, GROUP, W4.ASYM)
+        del W
+        layers.append((K, N, [q] + [tuple(t.clone() for t in q) for _ in range(copies - 1)]))
+    for M in (1, 4):
+        xs = {K: synth.activations_device(M, K, synth.FP16, 9100 + K + M) for K in (4096, 11008)}
+        ys = [torch.empty((M, N), dtype=torch.float16, device="cuda") for K, N, _ in layers]
+
+        def step(i, xs=xs, ys=ys):
+            for (K, N, cs), y in zip(layers, ys):
+                qw, sc, z = cs[i % copies]
+                W4.w8a16_linear(xs[K], qw, sc, z, GROUP, out=y)
+        for i in range(3):
+            step(i)
+        ms = time_loop(step, 50, torch)
+        gbps = per_copy / (ms * 1e-3) / 1e9
+        res[f"step_M{M}"] = {"us": round(ms * 1e3, 2), "GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBS, 4),
+                             "paths": [W4.PATH_NAMES[W4.w8a16_select_path(M, N, K, GROUP)] for K, N, _ in layers]}
+        log(f"  w8a16 step M={M}: {res[f'step_M{M}']}")
+    del layers
+    torch.cuda.empty_cache()
+    pre = {}
+    for (K, N) in [(4096, 11008), (11008, 4096)]:
+        W = synth.weights_device(N, K, 0.02, 9200 + K)
+        qw, sc, z = W4.w8a16_quantize_pack(W, GROUP, W4.ASYM)
+        del W
+        X = synth.activations_device(4096, K, synth.FP16, 9201 + K)
+        Y = torch.empty((4096, N), dtype=torch.float16, device="cuda")
+        for _ in range(3):
+            W4.w8a16_linear(X, qw, sc, z, GROUP, out=Y)
+        ms = time_loop(lambda i: W4.w8a16_linear(X, qw, sc, z, GROUP, out=Y), 10, torch)
+        tf = 2.0 * 4096 * N * K / (ms * 1e-3) / 1e12
+        pre[f"K{K}_N{N}"] = {"TFLOPs": round(tf, 1), "us": round(ms * 1e3, 1),
+                             "frac_mfma_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+        log(f"  w8a16 prefill M=4096 K={K} N={N}: {pre[f'K{K}_N{N}']}")
+        del qw, sc, z, X, Y
+    res["prefill_m4096"] = pre
+    return res
 
 
 def run_stack(W4, synth, torch):

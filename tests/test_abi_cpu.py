@@ -278,7 +278,7 @@ def test_w8a16_quantize_pack_rejects_invalid_arguments(lib, args, status):
 @pytest.mark.parametrize("M,N,K,g,dtype,path", [
     (1, 4096, 4096, 128, 0, L.PATH_GEMV),
     (4, 11008, 4096, 128, 1, L.PATH_GEMV),
-    (4, 4096, 11008, 128, 0, L.PATH_PREFILL),      # 4 x 11008 activations exceed the GEMV's LDS
+    (4, 4096, 11008, 128, 0, L.PATH_GEMV),         # activations staged in K slices
     (1, 8192, 28672, 128, 1, L.PATH_GEMV),
     (5, 4096, 4096, 128, 0, L.PATH_PREFILL),
     (4096, 11008, 4096, 64, 0, L.PATH_PREFILL),

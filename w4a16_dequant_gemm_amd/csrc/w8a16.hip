@@ -6,11 +6,11 @@
 //
 // Y[m, n] = sum_g s[n, g] (sum_{k in g} x[m, k] u[n, k] - z[n, g] sum_{k in g} x[m, k]).
 //
-// Mapping: blocks of 8 waves; each wave owns one output row at a time (rows strided over the
-// grid) and its lanes stream the row in 16-byte loads (a 1 KB contiguous run per wave
-// instruction), lane l taking the 16-column chunks l, l + 64, ...; eight loads in flight per
-// lane.  The block stages its activations in LDS once, in natural order, with the 16-column
-// chunk sums.  Codes: fp16 activations take the code bytes as subnormal halves u * 2^-24 (one
+// Mapping: blocks of 8 waves; each wave owns one output row and its lanes stream the row in
+// 16-byte loads (a 1 KB contiguous run per wave instruction), lane l taking the 16-column
+// chunks l, l + 64, ... of each slice; eight loads in flight per lane.  The block stages its
+// activations in LDS in natural order with the 16-column chunk sums, the whole row of K at
+// once while M rows fit 64 KB, else in K slices of a multiple of 1024 columns.  Codes: fp16 activations take the code bytes as subnormal halves u * 2^-24 (one
 // byte permute per pair, exact) and v_dot2; bf16 activations take each code as an exact bf16
 // (the high half of its fp32 conversion) and v_dot2.  Per chunk the group factors fold the
 // dot product and the chunk's activation sum: fp16 s' = s * 2^24, c = -z * s' (products and
@@ -37,63 +37,70 @@ template <int DT, int M>
 __global__ __launch_bounds__(kW8Threads) void gemv8_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ zeros, int has_zeros, uint16_t* __restrict__ Y, int N, int K, int G,
-    int gshift) {
+    int gshift, int KS) {
     extern __shared__ __attribute__((aligned(16))) uint32_t lds8[];
-    const int C = K >> 4;                                  // 16-column chunks per row
-    u32x4* xs = reinterpret_cast<u32x4*>(lds8);             // [M][K / 8] pieces of 8 columns
-    float* csum = reinterpret_cast<float*>(lds8 + (size_t)M * (K >> 1));   // [M][C]
+    const int CS = KS >> 4;                                // 16-column chunks per slice
+    const int KPS = KS >> 3;                               // 8-column pieces per slice row (even)
+    u32x4* xs = reinterpret_cast<u32x4*>(lds8);             // [M][KS / 8] pieces of 8 columns
+    float* csum = reinterpret_cast<float*>(lds8 + (size_t)M * (KS >> 1));   // [M][CS]
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-    // 1. Stage the activations (natural order) and the chunk sums; every thread runs every
-    //    round, so the pair exchange and the barrier are reached uniformly.
-    const int KP = K >> 3;                                 // 8-column pieces per row (even)
-    const int pieces = M * KP;
-    const uint32_t one2 = DT == DT_F16 ? 0x3C003C00u : 0x3F803F80u;
-    for (int p0 = 0; p0 < pieces; p0 += kW8Threads) {
-        const int p = p0 + tid;
-        const bool ok = p < pieces;
-        const int m = ok ? p / KP : 0;
-        const int c8 = ok ? p % KP : 0;
-        const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(X + (size_t)m * K + 8 * (size_t)c8)
-                           : u32x4{0u, 0u, 0u, 0u};
-        if (ok) xs[p] = v;
-        float sum = dot2<DT>(v.x, one2, 0.0f);
-        sum = dot2<DT>(v.y, one2, sum);
-        sum = dot2<DT>(v.z, one2, sum);
-        sum = dot2<DT>(v.w, one2, sum);
-        sum += __shfl_xor(sum, 1, 64);                    // pieces 2c and 2c + 1 form chunk c
-        if (ok && (p & 1) == 0) csum[p >> 1] = DT == DT_F16 ? sum * 5.9604644775390625e-8f : sum;
-    }
-    __syncthreads();
-
-    // 2. Rows.  A lane's chunks past the row's end re-read the row's last chunk (valid memory,
-    //    result unused); the descriptor covers exactly the N * K bytes of packed weights, which
-    //    the launcher keeps below 2 GiB.
+    // one output row per wave; a wave past the last row still stages and meets the barriers
+    const int row = blockIdx.x * kW8Waves + wave;
+    const bool live = row < N;
+    const int rrow = live ? row : N - 1;
     const __amdgpu_buffer_rsrc_t rw =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(qw), 0, N * K, 0x00020000);
     const uint16_t* zsrc = has_zeros ? zeros : scales;
-    const int CPL = (C + 63) >> 6;
-    for (int row = blockIdx.x * kW8Waves + wave; row < N; row += gridDim.x * kW8Waves) {
-        float acc[M];
+    const uint32_t one2 = DT == DT_F16 ? 0x3C003C00u : 0x3F803F80u;
+    float acc[M];
 #pragma unroll
-        for (int m = 0; m < M; ++m) acc[m] = 0.0f;
-        for (int cb = 0; cb < CPL; cb += kW8Unroll) {
+    for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+
+    for (int k0 = 0; k0 < K; k0 += KS) {
+        const int ks = min(KS, K - k0);                    // columns in this slice (multiple of 32)
+        const int kp = ks >> 3;
+        // 1. Stage the slice's activations (natural order) and 16-column chunk sums; every
+        //    thread runs every round, so the pair exchange and the barriers are uniform.
+        if (k0 > 0) __syncthreads();                       // the previous slice is consumed
+        const int pieces = M * kp;
+        for (int p0 = 0; p0 < pieces; p0 += kW8Threads) {
+            const int p = p0 + tid;
+            const bool ok = p < pieces;
+            const int m = ok ? p / kp : 0;
+            const int c8 = ok ? p % kp : 0;
+            const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(X + (size_t)m * K + k0 + 8 * (size_t)c8)
+                               : u32x4{0u, 0u, 0u, 0u};
+            if (ok) xs[m * KPS + c8] = v;
+            float sum = dot2<DT>(v.x, one2, 0.0f);
+            sum = dot2<DT>(v.y, one2, sum);
+            sum = dot2<DT>(v.z, one2, sum);
+            sum = dot2<DT>(v.w, one2, sum);
+            sum += __shfl_xor(sum, 1, 64);                // pieces 2c and 2c + 1 form chunk c
+            if (ok && (c8 & 1) == 0) csum[m * CS + (c8 >> 1)] = DT == DT_F16 ? sum * 5.9604644775390625e-8f : sum;
+        }
+        __syncthreads();
+
+        // 2. The row's chunks of this slice.  Chunks past the slice re-read its last chunk
+        //    (valid memory, result unused).
+        const int cs = ks >> 4;
+        const int cpl = (cs + 63) >> 6;
+        for (int cb = 0; cb < cpl; cb += kW8Unroll) {
             u32x4 w[kW8Unroll];
             uint16_t sb[kW8Unroll], zb[kW8Unroll];
 #pragma unroll
             for (int u = 0; u < kW8Unroll; ++u) {
-                const int c = min(lane + 64 * (cb + u), C - 1);
-                w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, row * K + 16 * c, 0, 2 /* nt */);
-                const int grp = (16 * c) >> gshift;
-                sb[u] = scales[(size_t)row * G + grp];
-                zb[u] = zsrc[(size_t)row * G + grp];
+                const int c = min(lane + 64 * (cb + u), cs - 1);
+                w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, rrow * K + k0 + 16 * c, 0, 2 /* nt */);
+                const int grp = (k0 + 16 * c) >> gshift;
+                sb[u] = scales[(size_t)rrow * G + grp];
+                zb[u] = zsrc[(size_t)rrow * G + grp];
             }
 #pragma unroll
             for (int u = 0; u < kW8Unroll; ++u) {
                 const int c = lane + 64 * (cb + u);
-                if (c < C) {
+                if (c < cs) {
                     const float sv = h2f(sb[u]);
                     const float zv = has_zeros ? h2f(zb[u]) : 128.0f;
                     const float sp = DT == DT_F16 ? sv * 16777216.0f : sv;
@@ -105,8 +112,8 @@ __global__ __launch_bounds__(kW8Threads) void gemv8_kernel(
                     codes8<DT>(w[u].w, &cd[6]);
 #pragma unroll
                     for (int m = 0; m < M; ++m) {
-                        const u32x4 a0 = xs[(size_t)m * KP + 2 * c];
-                        const u32x4 a1 = xs[(size_t)m * KP + 2 * c + 1];
+                        const u32x4 a0 = xs[m * KPS + 2 * c];
+                        const u32x4 a1 = xs[m * KPS + 2 * c + 1];
                         float pd = dot2<DT>(a0.x, cd[0], 0.0f);
                         pd = dot2<DT>(a0.y, cd[1], pd);
                         pd = dot2<DT>(a0.z, cd[2], pd);
@@ -115,27 +122,36 @@ __global__ __launch_bounds__(kW8Threads) void gemv8_kernel(
                         pd = dot2<DT>(a1.y, cd[5], pd);
                         pd = dot2<DT>(a1.z, cd[6], pd);
                         pd = dot2<DT>(a1.w, cd[7], pd);
-                        acc[m] = fmaf(cz, csum[m * C + c], fmaf(sp, pd, acc[m]));
+                        acc[m] = fmaf(cz, csum[m * CS + c], fmaf(sp, pd, acc[m]));
                     }
                 }
             }
         }
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            const float v = wave_sum(acc[m]);
-            if (lane == 0) Y[(size_t)m * N + row] = f2out<DT>(v);
-        }
     }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const float v = wave_sum(acc[m]);
+        if (live && lane == 0) Y[(size_t)m * N + row] = f2out<DT>(v);
+    }
+}
+
+// Slice width: the whole row while M rows of activations and their chunk sums fit the LDS
+// budget, else the largest multiple of 1024 columns that does.
+int w8_slice(int M, int K) {
+    if (w8_lds_bytes(M, K) <= kW8LdsBudget) return K;
+    int ks = (int)((4LL * kW8LdsBudget) / (9LL * M)) / 1024 * 1024;    // 2.25 bytes per column and row
+    while (ks > 1024 && w8_lds_bytes(M, ks) > kW8LdsBudget) ks -= 1024;
+    return ks;
 }
 
 template <int DT, int M>
 hipError_t run_gemv8(const LinearArgs& a, hipStream_t st) {
-    const long long lds = w8_lds_bytes(M, a.K);
-    const long long want = (a.N + kW8Waves - 1) / kW8Waves;
-    const int blocks = (int)(want < 8192 ? want : 8192);
-    hipLaunchKernelGGL((gemv8_kernel<DT, M>), dim3(blocks), dim3(kW8Threads), (size_t)lds, st,
+    const int ks = w8_slice(M, a.K);
+    const long long lds = w8_lds_bytes(M, ks);
+    const long long blocks = (a.N + kW8Waves - 1) / kW8Waves;
+    hipLaunchKernelGGL((gemv8_kernel<DT, M>), dim3((unsigned)blocks), dim3(kW8Threads), (size_t)lds, st,
                        static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, a.zeros ? 1 : 0,
-                       static_cast<uint16_t*>(a.Y), a.N, a.K, a.G, a.gshift);
+                       static_cast<uint16_t*>(a.Y), a.N, a.K, a.G, a.gshift, ks);
     return hipGetLastError();
 }
 
@@ -153,8 +169,7 @@ hipError_t run_gemv8_dt(const LinearArgs& a, hipStream_t st) {
 }  // namespace
 
 bool gemv8_supports(const LinearArgs& a) {
-    return a.M >= 1 && a.M <= kW8MaxM && w8_lds_bytes(a.M, a.K) <= kW8LdsBudget &&
-           (long long)a.N * a.K < (1LL << 31) - 64;
+    return a.M >= 1 && a.M <= kW8MaxM && (long long)a.N * a.K < (1LL << 31) - 64;
 }
 
 hipError_t launch_gemv8(const LinearArgs& a, hipStream_t st) {
