@@ -420,7 +420,11 @@ __global__ __launch_bounds__(256, 2) void prefill_f16_kernel(
 //     held in that XCD's L2).
 constexpr int W_BM = 256, W_BN = 256, W_BK = 64;     // K % 128 == 0: steps in pairs
 
-template <bool HZ>
+// BITS = 8 (W8A16): lane (n, h) loads the 32 bytes of columns 32h .. 32h + 31 (two 16-byte
+// loads) and MFMA j takes words 2j and 2j + 1 (one byte permute per pair instead of the nibble
+// masks; the 1536-bias construction is exact for |u - z| < 512, the implicit symmetric zero
+// point is 128).
+template <bool HZ, int BITS = 4>
 __global__ __launch_bounds__(256, 1) void prefill_f16_wide_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros,
@@ -464,7 +468,7 @@ __global__ __launch_bounds__(256, 1) void prefill_f16_wide_kernel(
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns) {
         const int wrow = min(n0 + 64 * wave + 32 * ns + l32, N - 1);
-        woff[ns] = wrow * (K / 2) + 16 * h;
+        woff[ns] = wrow * (BITS == 4 ? K / 2 : K) + (BITS == 4 ? 16 : 32) * h;
         szoff[ns] = wrow * G * 2;
     }
     auto load_a = [&](int buf, int step) {
@@ -474,15 +478,18 @@ __global__ __launch_bounds__(256, 1) void prefill_f16_wide_kernel(
                 rx, (__attribute__((address_space(3))) void*)&As[buf][(8 * wave + j) * 64], 16,
                 xoff[j], step * W_BK * 2, 0, 0);
     };
+    constexpr int WL = BITS == 4 ? 1 : 2;        // 16-byte weight loads per row and step
     struct WStage {
-        u32x4 w[2];
+        u32x4 w[2][WL];
         uint16_t s[2], z[2];
     };
     auto load_w = [&](WStage& st, int step) {
         const int grp2 = group_of(step * W_BK + 32 * h, gshift) * 2;
 #pragma unroll
         for (int ns = 0; ns < 2; ++ns) {
-            st.w[ns] = __builtin_amdgcn_raw_buffer_load_b128(rw, woff[ns], step * (W_BK / 2), 0);
+#pragma unroll
+            for (int i = 0; i < WL; ++i)
+                st.w[ns][i] = __builtin_amdgcn_raw_buffer_load_b128(rw, woff[ns] + 16 * i, step * (W_BK / 8 * BITS), 0);
             st.s[ns] = __builtin_amdgcn_raw_buffer_load_b16(rs, szoff[ns] + grp2, 0, 0);
             st.z[ns] = __builtin_amdgcn_raw_buffer_load_b16(rz, szoff[ns] + grp2, 0, 0);
         }
@@ -492,16 +499,27 @@ __global__ __launch_bounds__(256, 1) void prefill_f16_wide_kernel(
         const f16x2 bias = {(_Float16)1536.0f, (_Float16)1536.0f};
 #pragma unroll
         for (int ns = 0; ns < 2; ++ns) {
-            const float z = HZ ? h2f(st.z[ns]) : 8.0f;
+            const float z = HZ ? h2f(st.z[ns]) : (BITS == 4 ? 8.0f : 128.0f);
             const uint32_t zb = (uint32_t)(0x6600 - (int)z) & 0xFFFFu;
             const u16x2 zbias = __builtin_bit_cast(u16x2, zb | (zb << 16));
             const f16x2 sv = __builtin_bit_cast(f16x2, (uint32_t)st.s[ns] | ((uint32_t)st.s[ns] << 16));
-            const uint32_t w = st.w[ns][j];
-            const uint32_t t0 = w & 0x0F0F0F0Fu;          // u0 u2 u4 u6 (as bytes)
-            const uint32_t t1 = (w >> 4) & 0x0F0F0F0Fu;   // u1 u3 u5 u7
+            uint32_t t0, t1;
+            if constexpr (BITS == 4) {
+                const uint32_t w = st.w[ns][0][j];
+                t0 = w & 0x0F0F0F0Fu;                     // u0 u2 u4 u6 (as bytes)
+                t1 = (w >> 4) & 0x0F0F0F0Fu;              // u1 u3 u5 u7
+            } else {
+                t0 = st.w[ns][j >> 1][2 * (j & 1)];       // bytes u0 u1 u2 u3
+                t1 = st.w[ns][j >> 1][2 * (j & 1) + 1];   // bytes u4 u5 u6 u7
+            }
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                const uint32_t uu = perm(t1, t0, 0x0C040C00u + 0x00010001u * p);
+                uint32_t uu;                               // (u_2p, u_2p+1) as 16-bit integers
+                if constexpr (BITS == 4)
+                    uu = perm(t1, t0, 0x0C040C00u + 0x00010001u * p);
+                else
+                    uu = p < 2 ? perm(0u, t0, 0x0C010C00u + 0x00020002u * p)
+                               : perm(0u, t1, 0x0C010C00u + 0x00020002u * (p - 2));
                 const u16x2 biased = __builtin_bit_cast(u16x2, uu) + zbias;     // 1536 + u - z
                 const f16x2 code = __builtin_bit_cast(f16x2, biased) - bias;    // exact
                 b[ns][j][p] = __builtin_bit_cast(uint32_t, code * sv);          // one rounding
@@ -645,6 +663,22 @@ bool prefill8_supports(const LinearArgs& a) { return a.K % BK == 0 && a.g % BK =
 hipError_t launch_prefill8(const LinearArgs& a, hipStream_t st) {
     if (!prefill8_supports(a)) return hipErrorInvalidValue;
     const int hz = a.zeros ? 1 : 0;
+    // fp16: the 256 x 256 kernel while its 32-bit buffer offsets cover the operands
+    const bool offsets32 = (long long)a.M * a.K * 2 < (1LL << 31) && (long long)a.N * a.K < (1LL << 31) &&
+                           (long long)a.N * a.G * 2 < (1LL << 31);
+    if (a.dtype == DT_F16 && a.K % (2 * W_BK) == 0 && offsets32) {
+        const int tiles = ((a.M + W_BM - 1) / W_BM) * ((a.N + W_BN - 1) / W_BN);
+        const int grid = 8 * ((tiles + 7) / 8);
+        if (hz)
+            hipLaunchKernelGGL((prefill_f16_wide_kernel<true, 8>), dim3(grid), dim3(256), 0, st,
+                               static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros,
+                               static_cast<uint16_t*>(a.Y), a.M, a.N, a.K, a.G, a.gshift);
+        else
+            hipLaunchKernelGGL((prefill_f16_wide_kernel<false, 8>), dim3(grid), dim3(256), 0, st,
+                               static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros,
+                               static_cast<uint16_t*>(a.Y), a.M, a.N, a.K, a.G, a.gshift);
+        return hipGetLastError();
+    }
     const long long tiles = (long long)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
     const int spg = a.g / BK;
