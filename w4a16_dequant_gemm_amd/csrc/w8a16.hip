@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kW8Threads) void gemv8_kernel(
     extern __shared__ __attribute__((aligned(16))) uint32_t lds8[];
     const int CS = KS >> 4;                                // 16-column chunks per slice
     const int KPS = KS >> 3;                               // 8-column pieces per slice row (even)
-    u32x4* xs = reinterpret_cast<u32x4*>(lds8);             // [M][KS / 8] pieces of 8 columns
+    u32x4* xs = reinterpret_cast<u32x4*>(lds8);             // [M][2][KS / 16] pieces of 8 columns
     float* csum = reinterpret_cast<float*>(lds8 + (size_t)M * (KS >> 1));   // [M][CS]
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -72,7 +72,9 @@ __global__ __launch_bounds__(kW8Threads) void gemv8_kernel(
             const int c8 = ok ? p % kp : 0;
             const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(X + (size_t)m * K + k0 + 8 * (size_t)c8)
                                : u32x4{0u, 0u, 0u, 0u};
-            if (ok) xs[m * KPS + c8] = v;
+            // even pieces in the first half of the row's slots, odd ones in the second, so the
+            // lanes of a wave read consecutive 16-byte slots (no bank conflicts)
+            if (ok) xs[m * KPS + (c8 & 1) * (KPS >> 1) + (c8 >> 1)] = v;
             float sum = dot2<DT>(v.x, one2, 0.0f);
             sum = dot2<DT>(v.y, one2, sum);
             sum = dot2<DT>(v.z, one2, sum);
@@ -112,8 +114,8 @@ __global__ __launch_bounds__(kW8Threads) void gemv8_kernel(
                     codes8<DT>(w[u].w, &cd[6]);
 #pragma unroll
                     for (int m = 0; m < M; ++m) {
-                        const u32x4 a0 = xs[m * KPS + 2 * c];
-                        const u32x4 a1 = xs[m * KPS + 2 * c + 1];
+                        const u32x4 a0 = xs[m * KPS + c];
+                        const u32x4 a1 = xs[m * KPS + (KPS >> 1) + c];
                         float pd = dot2<DT>(a0.x, cd[0], 0.0f);
                         pd = dot2<DT>(a0.y, cd[1], pd);
                         pd = dot2<DT>(a0.z, cd[2], pd);
