@@ -372,8 +372,8 @@ int w4a16_w8a16_quantize_pack(const float* W, int64_t N, int64_t K, int64_t grou
  * group's s and z are applied to the fp32 partial sums); fp32 accumulation, Y rounded once to
  * the activation dtype.  Arguments as for w4a16_linear with qweight [N, K/4]; zeros NULL means
  * all zero points 128; any integer zero point |z| <= 2048.  Kernels: a weight-streaming GEMV
- * for M <= 4 (when M * K * 2.25 bytes of staged activations fit 64 KB and N * K < 2^31), else
- * the tiled MFMA GEMM, which needs K and g to be multiples of 64 (W4A16_ERR_PATH otherwise).
+ * for M <= 16 (when N * K < 2^31), else the tiled MFMA GEMM, which needs K and g to be
+ * multiples of 64 (W4A16_ERR_PATH otherwise).
  */
 int w4a16_w8a16_linear(const void* X, int dtype, int64_t M, int64_t N, int64_t K, int64_t group_size,
                        const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros, void* Y,

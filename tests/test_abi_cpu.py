@@ -252,8 +252,8 @@ def _lin8(lib, X=A, dtype=0, M=1, N=64, K=128, g=128, qw=B, s=C, z=D, Y=A + 4096
     (dict(X=MIS), L.ERR_ALIGN),
     (dict(qw=B + 8), L.ERR_ALIGN),
     (dict(z=D + 1), L.ERR_ALIGN),
-    (dict(M=5, path=L.PATH_GEMV), L.ERR_PATH),                     # the 8-bit GEMV takes M <= 4
-    (dict(M=5, K=128, g=32), L.ERR_PATH),                           # M > 4 needs g % 64 == 0
+    (dict(M=17, path=L.PATH_GEMV), L.ERR_PATH),                    # the 8-bit GEMV takes M <= 16
+    (dict(M=17, K=128, g=32), L.ERR_PATH),                          # M > 16 needs g % 64 == 0
     (dict(K=96, g=32, path=L.PATH_PREFILL), L.ERR_PATH),            # the GEMM needs K % 64 == 0
     (dict(path=L.PATH_SKINNY), L.ERR_PATH),                         # no skinny kernel for 8 bits
     (dict(path=17), L.ERR_PATH),
@@ -280,7 +280,8 @@ def test_w8a16_quantize_pack_rejects_invalid_arguments(lib, args, status):
     (4, 11008, 4096, 128, 1, L.PATH_GEMV),
     (4, 4096, 11008, 128, 0, L.PATH_GEMV),         # activations staged in K slices
     (1, 8192, 28672, 128, 1, L.PATH_GEMV),
-    (5, 4096, 4096, 128, 0, L.PATH_PREFILL),
+    (16, 4096, 4096, 128, 0, L.PATH_GEMV),
+    (17, 4096, 4096, 128, 0, L.PATH_PREFILL),
     (4096, 11008, 4096, 64, 0, L.PATH_PREFILL),
     (2, 4096, 4096, 32, 0, L.PATH_GEMV),           # g = 32: GEMV only
 ])

@@ -2,7 +2,7 @@
 
 * quantize-pack: 8-bit codes (as packed words), fp16 scales and zeros bit-exact, both
   schemes, group sizes 32 .. K, outlier weights;
-* linear: both kernels (the weight-streaming GEMV for M <= 4, the tiled MFMA GEMM) against
+* linear: both kernels (the weight-streaming GEMV for M <= 16, the tiled MFMA GEMM) against
   the fp64 oracle within the output bar (relative Frobenius <= 1e-3, max |d| <= 1e-2 max
   |ref|), fp16 and bf16 activations, ragged N and M, per-channel groups, symmetric with and
   without stored zero points, both kernels forced on the same problems;
@@ -72,7 +72,9 @@ GEMV_CASES = [(1, 4096, 4096, 128), (2, 300, 1024, 32), (3, 1000, 2048, 64), (4,
               (1, 8, 32, 32),
               # activations staged in K slices (M rows of K do not fit 64 KB): several slices, a
               # ragged last slice, per-channel groups spanning slices
-              (4, 300, 11008, 128), (3, 70, 20480, 256), (1, 33, 32768, 32768), (2, 1000, 15360, 64)]
+              (4, 300, 11008, 128), (3, 70, 20480, 256), (1, 33, 32768, 32768), (2, 1000, 15360, 64),
+              # up to 16 activation rows (several K slices from M = 8 on)
+              (8, 500, 4096, 128), (16, 257, 4096, 64), (13, 130, 11008, 11008)]
 PREFILL_CASES = [(5, 4096, 1024, 128), (64, 300, 2048, 64), (300, 1000, 1024, 128), (129, 257, 4096, 4096),
                  (4, 4096, 11008, 128), (1, 64, 128, 64), (512, 128, 640, 128)]
 

@@ -161,7 +161,8 @@ def w8a16_select_path(M: int, N: int, K: int, group_size: int, dtype: int = F16)
 
 def w8a16_linear(X: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zeros, group_size: int,
                  path: int = PATH_AUTO, out: torch.Tensor | None = None) -> torch.Tensor:
-    """``Y [M, N] = X [M, K] . dequant(qweight)^T`` with 8-bit codes ``qweight int32 [N, K/4]``."""
+    """``Y [M, N] = X [M, K] . dequant(qweight)^T`` with 8-bit codes ``qweight int32 [N, K/4]``
+    (the weight-streaming GEMV for M <= 16, the tiled MFMA GEMM above)."""
     dt = _dtype_code(X)
     _need(X, "X", X.dtype, 2)
     _need(qweight, "qweight", torch.int32, 2)

@@ -27,7 +27,7 @@ constexpr int kW8Waves = 8;
 constexpr int kW8Threads = 64 * kW8Waves;
 constexpr int kW8Unroll = 8;                // 16-byte weight loads in flight per lane
 constexpr int kW8LdsBudget = 65536;         // staged activations and chunk sums
-constexpr int kW8MaxM = 4;
+constexpr int kW8MaxM = 16;
 
 __host__ __device__ constexpr long long w8_lds_bytes(int M, int K) {
     return (long long)M * K * 2 + (long long)M * (K / 16) * 4;
@@ -164,6 +164,18 @@ hipError_t run_gemv8_dt(const LinearArgs& a, hipStream_t st) {
         case 2: return run_gemv8<DT, 2>(a, st);
         case 3: return run_gemv8<DT, 3>(a, st);
         case 4: return run_gemv8<DT, 4>(a, st);
+        case 5: return run_gemv8<DT, 5>(a, st);
+        case 6: return run_gemv8<DT, 6>(a, st);
+        case 7: return run_gemv8<DT, 7>(a, st);
+        case 8: return run_gemv8<DT, 8>(a, st);
+        case 9: return run_gemv8<DT, 9>(a, st);
+        case 10: return run_gemv8<DT, 10>(a, st);
+        case 11: return run_gemv8<DT, 11>(a, st);
+        case 12: return run_gemv8<DT, 12>(a, st);
+        case 13: return run_gemv8<DT, 13>(a, st);
+        case 14: return run_gemv8<DT, 14>(a, st);
+        case 15: return run_gemv8<DT, 15>(a, st);
+        case 16: return run_gemv8<DT, 16>(a, st);
     }
     return hipErrorInvalidValue;
 }
