@@ -123,6 +123,12 @@ def test_dequantize_rejects_invalid_arguments(lib):
     (4096, 11008, 4096, 128, 0, L.PATH_PREFILL),
     (1024, 4096, 11008, 64, 0, L.PATH_PREFILL),
     (1, 4096, 11008, 11008, 1, L.PATH_GEMV),          # per-channel
+    # 32 < M <= 512: the K-split skinny kernel where the tiled GEMM would have few tiles
+    (256, 4096, 11008, 128, 0, L.PATH_SKINNY),        # K = 11008, N = 4096: 16 tiles of 256 x 256
+    (256, 11008, 4096, 128, 0, L.PATH_PREFILL),       # K = 4096: the K loop is short
+    (64, 11008, 4096, 128, 1, L.PATH_SKINNY),
+    (512, 4096, 11008, 128, 1, L.PATH_PREFILL),
+    (128, 4096, 11008, 64, 0, L.PATH_PREFILL),        # g = 64: the skinny kernel needs g % 128 == 0
 ])
 def test_dispatcher_choices(lib, M, N, K, g, dtype, path):
     assert lib.w4a16_select_path(M, N, K, g, dtype) == path

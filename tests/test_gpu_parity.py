@@ -126,7 +126,11 @@ SKINNY_CASES = [(1, 64, 128, 128), (5, 100, 1024, 128), (16, 256, 4096, 128), (1
                 # 5 <= M <= 16: activations streamed next to the weights (1..4 tiles per block)
                 (5, 4100, 2048, 128), (16, 12300, 512, 128), (9, 8200, 1024, 256), (13, 33, 11008, 128),
                 (16, 4096, 11008, 128), (7, 3000, 8192, 8192), (11, 1, 256, 128), (16, 17, 4352, 128),
-                (4, 4096, 11008, 128), (3, 300, 28672, 128)]
+                (4, 4096, 11008, 128), (3, 300, 28672, 128),
+                # 32 < M <= 512: the grid also runs over 32-row chunks of M (ragged last chunk,
+                # 64 weight rows per block in fp16), K split over the waves
+                (33, 300, 1024, 128), (100, 257, 2048, 128), (256, 1000, 4096, 256), (512, 64, 1024, 1024),
+                (130, 4096, 11008, 128)]
 PREFILL_CASES = [(1, 64, 64, 64), (17, 200, 192, 64), (130, 129, 256, 128), (256, 384, 1024, 128),
                  (300, 256, 4096, 4096), (64, 128, 11008, 128), (129, 1, 128, 64)]
 # fp16 prefill also takes K % 64 == 32 and g == 32 (bf16 prefill needs multiples of 64)

@@ -8,6 +8,7 @@
 // "大模型推理中 Weight-only、W8A8 和 FP8 量化有什么区别？如何选型？", sections 二 and 五).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "../../include/w4a16.h"
@@ -80,6 +81,24 @@ int validate_linear(const void* X, int dtype, int64_t M, int64_t N, int64_t K, i
 // M-based dispatch: the weight-streaming GEMV while the dot2 work per weight stays
 // within the VALU budget of the HBM stream, the skinny MFMA kernel for small batches,
 // the tiled MFMA GEMM once the problem is compute-bound.
+// Between 32 and 512 activation rows the tiled GEMM has few tiles (256 x 256 tiles in fp16,
+// 128 x 128 in bf16) and each CU runs one of them through the whole K loop, while the skinny
+// kernel splits K over the 8 waves of every block and covers the GPU.  Estimated times
+// (microseconds, fitted to MI355X measurements of both kernels on the 7B-like prefill shapes
+// for M = 33 .. 512): skinny ~ max(40, c * M * N * K) with c = 1.05e-8 (fp16) or 1.45e-8
+// (bf16); tiled ~ (1.45 or 1.3) * (K / 64) * ceil(tiles / slots), slots = 256 CUs (fp16)
+// or 512 (bf16, two blocks per CU).
+bool skinny_beats_tiled(const LinearArgs& a) {
+    const bool f16 = a.dtype == W4A16_F16;
+    const double macs = (double)a.M * a.N * a.K;
+    const double t_skinny = std::max(40.0, (f16 ? 1.05e-8 : 1.45e-8) * macs);
+    const long long bm = f16 ? 256 : 128;
+    const long long tiles = ((a.M + bm - 1) / bm) * ((a.N + bm - 1) / bm);
+    const long long slots = f16 ? 256 : 512;
+    const double t_tiled = (f16 ? 1.45 : 1.3) * (a.K / 64.0) * (double)((tiles + slots - 1) / slots);
+    return t_skinny < t_tiled;
+}
+
 int choose_path(const LinearArgs& a) {
     // measured on MI355X: the v_dot2 GEMV leads for one row and for two rows of short K
     // (K <= 4096), the MFMA decode kernels (skinny path, 1 <= M <= 16) from there on
@@ -87,6 +106,8 @@ int choose_path(const LinearArgs& a) {
     if (a.M <= 16 && w4a16::decode_supports(a)) return W4A16_PATH_SKINNY;
     if (a.M <= 4 && w4a16::gemv_supports(a)) return W4A16_PATH_GEMV;
     if (a.M <= 32 && w4a16::skinny_supports(a)) return W4A16_PATH_SKINNY;
+    if (w4a16::skinny_supports(a) && w4a16::prefill_supports(a) && skinny_beats_tiled(a))
+        return W4A16_PATH_SKINNY;
     if (w4a16::prefill_supports(a)) return W4A16_PATH_PREFILL;
     if (w4a16::gemv_supports(a)) return W4A16_PATH_GEMV;
     if (w4a16::skinny_supports(a)) return W4A16_PATH_SKINNY;

@@ -1,4 +1,4 @@
-// Small-batch W4A16 kernel on CDNA4 matrix cores (MFMA 16x16x32), 1 <= M <= 32.
+// Small-batch W4A16 kernel on CDNA4 matrix cores (MFMA 16x16x32), 1 <= M <= 512.
 //
 // Decode batches are still bound by the weight stream (page "推理优化中“用精度换性能“的核心
 // 技术：量化", section 一), but a VALU dot product costs one instruction per two weights
@@ -7,9 +7,11 @@
 // instruction and the VALU only unpacks codes (dequantization in registers, page
 // "大模型推理中 Weight-only、W8A8 和 FP8 量化有什么区别？如何选型？", section 二).
 //
-// Work split.  A block of W waves owns NB row-blocks of 16 output rows and all of K; wave
-// w takes the k-blocks (128 columns each) w*KS .. w*KS + KS - 1 and streams them with two
-// k-blocks in flight.  Partial 16x16 tiles are summed across the waves in LDS.
+// Work split.  A block of W waves owns NB row-blocks of 16 output rows, up to 32 activation
+// rows (a second grid dimension runs over 32-row chunks of M) and all of K; wave w takes the
+// k-blocks (128 columns each) w*KS .. w*KS + KS - 1 and streams them with two k-blocks in
+// flight.  Partial 16x16 tiles are summed across the waves in LDS: the K split needs no
+// buffer outside the block and no atomics, so results do not depend on scheduling.
 //
 // MFMA operands (lane l: n = l % 16, q = l / 16).
 //   B (weights, 32 k x 16 n): lane (n, q) loads 16 bytes = 32 columns 32q .. 32q+31 of
@@ -160,6 +162,7 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(
     const int KB = K >> 7;
     const int KW = K >> 3;
     const int row0 = blockIdx.x * (16 * NB);
+    const int m0 = blockIdx.y * (16 * MT);              // this block's activation rows
 
     SkinnySrc src;
     src.x = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X), 0, M * K * 2, 0x00020000);
@@ -176,7 +179,7 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(
     int va[MT], vw[NB], vs[NB];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const int m = mt * 16 + n16;
+        const int m = m0 + mt * 16 + n16;
         va[mt] = m < M ? (m * K + 32 * q) * 2 : 0x7FFFFFF0;
     }
 #pragma unroll
@@ -226,7 +229,7 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(
         if (n < N) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int m = mt * 16 + 4 * (l >> 4) + r;
+                const int m = m0 + mt * 16 + 4 * (l >> 4) + r;
                 if (m < M) Y[(size_t)m * N + n] = f2out<DT>(v[r]);
             }
         }
@@ -234,24 +237,32 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(
 }
 
 struct SkinnyCfg {
-    int nb = 0, mt = 0, ks = 0, blocks = 0;
+    int nb = 0, mt = 0, ks = 0, blocks = 0, mblocks = 1;
 };
+
+#ifndef W4A16_SKINNY_MAX_M
+#define W4A16_SKINNY_MAX_M 512
+#endif
+constexpr int kSkinnyMaxM = W4A16_SKINNY_MAX_M;
 
 SkinnyCfg pick_skinny(const LinearArgs& a) {
     SkinnyCfg c;
-    c.mt = (a.M + 15) / 16;
-    // share activation fragments across two row-blocks when they are many (the LDS
-    // reduction buffer, W x NB x MT x 1 KB, stays within 32 KB)
-    c.nb = a.M > 8 ? 2 : 1;
+    c.mt = a.M > 32 ? 2 : (a.M + 15) / 16;
+    // share activation fragments across two row-blocks when they are many, four past 32
+    // activation rows (the grid then also runs over 32-row chunks of M, and each chunk's
+    // activations are re-read once per 64 weight rows; the LDS reduction buffer,
+    // W x NB x MT x 1 KB, stays within 64 KB)
+    c.nb = a.M > 32 ? (a.dtype == DT_F16 ? 4 : 2) : (a.M > 8 ? 2 : 1);   // bf16 x4 would spill
     const int KB = a.K / 128;
     c.ks = (KB + kSkinnyWaves - 1) / kSkinnyWaves;
     c.blocks = (a.N + 16 * c.nb - 1) / (16 * c.nb);
+    c.mblocks = (a.M + 16 * c.mt - 1) / (16 * c.mt);
     return c;
 }
 
 template <int DT, int NB, int MT>
 hipError_t run(const LinearArgs& a, const SkinnyCfg& c, hipStream_t st) {
-    hipLaunchKernelGGL((skinny_kernel<DT, NB, MT, kSkinnyWaves>), dim3(c.blocks),
+    hipLaunchKernelGGL((skinny_kernel<DT, NB, MT, kSkinnyWaves>), dim3(c.blocks, c.mblocks),
                        dim3(64 * kSkinnyWaves), 0, st, static_cast<const uint16_t*>(a.X), a.qw,
                        a.scales, a.zeros, a.zeros ? 1 : 0, static_cast<uint16_t*>(a.Y), a.M, a.N,
                        a.K, a.G, a.gshift, c.ks);
@@ -263,13 +274,15 @@ hipError_t run_dt(const LinearArgs& a, const SkinnyCfg& c, hipStream_t st) {
     if (c.nb == 1 && c.mt == 1) return run<DT, 1, 1>(a, c, st);
     if (c.nb == 2 && c.mt == 1) return run<DT, 2, 1>(a, c, st);
     if (c.nb == 2 && c.mt == 2) return run<DT, 2, 2>(a, c, st);
+    if constexpr (DT == DT_F16)
+        if (c.nb == 4 && c.mt == 2) return run<DT, 4, 2>(a, c, st);
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 bool skinny_supports(const LinearArgs& a) {
-    if (a.M < 1 || a.M > 32) return false;
+    if (a.M < 1 || a.M > kSkinnyMaxM) return false;
     if (a.K % 128 != 0) return false;
     if (a.g % 128 != 0) return false;             // g == K qualifies when K % 128 == 0
     // 32-bit buffer offsets
