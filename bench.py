@@ -683,6 +683,16 @@ def run_extras(layers, copies, W4, synth, torch, np):
                              "frac_mfma_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
                              "dense_fp16_torch_TFLOPs": round(tf_d, 1)}
         log(f"  prefill M=4096 K={K} N={N}: {tf:.1f} TFLOP/s (dense fp16 torch.matmul {tf_d:.1f})")
+        # the rest of the crossover sweep (M = 256, 1024), auto-dispatched, with the kernel it took
+        for Ms in (256, 1024):
+            Xs, Ys = X[:Ms], Y[:Ms]
+            for _ in range(3):
+                W4.linear(Xs, qw, s, z, GROUP, out=Ys)
+            ms_s = time_loop(lambda i: W4.linear(Xs, qw, s, z, GROUP, out=Ys), 10, torch)
+            tf_s = 2.0 * Ms * N * K / (ms_s * 1e-3) / 1e12
+            pre[f"K{K}_N{N}"][f"M{Ms}"] = {"TFLOPs": round(tf_s, 1), "us": round(ms_s * 1e3, 1),
+                                           "path": W4.PATH_NAMES[W4.select_path(Ms, N, K, GROUP)]}
+            log(f"  prefill M={Ms} K={K} N={N}: {pre[f'K{K}_N{N}'][f'M{Ms}']}")
         del qw, s, z, X, Y, Wd
     out["prefill_m4096_fp16_g128"] = pre
     out["gptq_4096x4096_g128"] = run_gptq(W4, synth, torch)
