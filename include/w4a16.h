@@ -70,7 +70,7 @@ typedef enum {
 typedef enum {
     W4A16_PATH_AUTO = 0,    /* dispatcher chooses from (M, N, K, g)                 */
     W4A16_PATH_GEMV = 1,    /* weight-streaming dot2 kernel, any supported g, M<=8  */
-    W4A16_PATH_SKINNY = 2,  /* weight-streaming MFMA kernel, M <= 32, g % 128 == 0  */
+    W4A16_PATH_SKINNY = 2,  /* K-split MFMA kernel, M <= 512, g % 128 == 0         */
     W4A16_PATH_PREFILL = 3  /* LDS-tiled MFMA GEMM; bf16 needs g % 64 == 0, K % 64 == 0 */
 } w4a16_path;
 
