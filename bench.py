@@ -692,6 +692,16 @@ def run_extras(layers, copies, W4, synth, torch, np):
             tf_s = 2.0 * Ms * N * K / (ms_s * 1e-3) / 1e12
             pre[f"K{K}_N{N}"][f"M{Ms}"] = {"TFLOPs": round(tf_s, 1), "us": round(ms_s * 1e3, 1),
                                            "path": W4.PATH_NAMES[W4.select_path(Ms, N, K, GROUP)]}
+            need = W4.linear_workspace(Ms, N, K, GROUP)
+            if need > 0:   # the workspace form: K split over the idle CUs
+                work = torch.empty((need + 3) // 4, dtype=torch.float32, device="cuda")
+                for _ in range(3):
+                    W4.linear_ws(Xs, qw, s, z, GROUP, work=work, out=Ys)
+                ms_w = time_loop(lambda i: W4.linear_ws(Xs, qw, s, z, GROUP, work=work, out=Ys), 10, torch)
+                pre[f"K{K}_N{N}"][f"M{Ms}"]["split_k_workspace"] = {
+                    "us": round(ms_w * 1e3, 1), "TFLOPs": round(2.0 * Ms * N * K / (ms_w * 1e-3) / 1e12, 1),
+                    "workspace_MB": round(need / 2**20, 1)}
+                del work
             log(f"  prefill M={Ms} K={K} N={N}: {pre[f'K{K}_N{N}'][f'M{Ms}']}")
         del qw, s, z, X, Y, Wd
     out["prefill_m4096_fp16_g128"] = pre

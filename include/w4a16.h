@@ -342,6 +342,29 @@ int w4a16_kv_attention_decode_batch(const void* q, int dtype, int64_t B, int64_t
                                     const void* vcodes, const uint16_t* vscales, const uint16_t* vzeros,
                                     float* work, void* out, void* stream);
 
+/*
+ * w4a16_linear_workspace -- bytes of fp32 workspace that w4a16_linear_ws can use for this
+ * problem (0: it would not split K and behaves as w4a16_linear); a negative status for invalid
+ * arguments.  Host only.
+ */
+int64_t w4a16_linear_workspace(int64_t M, int64_t N, int64_t K, int64_t group_size, int dtype);
+
+/*
+ * w4a16_linear_ws -- w4a16_linear with a caller workspace for the prefill regime's tile-starved
+ * shapes (fp16, M > 32, K % 128 == 0, fewer than 128 tiles of 256 x 256): the 256 x 256 kernel
+ * then splits K over the otherwise idle CUs, writes fp32 partial tiles to `work` and a second
+ * kernel sums them in split order and rounds once, so the result is deterministic (the same
+ * dequantized weights and products as w4a16_linear, summed in a different order).  The compute
+ * regime the pages assign to prefill (page "Quantization & Acceleration: 解释 W8A8 与 W4A16 的
+ * 差异与取舍", prefill compute-bound).
+ *   work        device fp32, 16-byte aligned, at least w4a16_linear_workspace(...) bytes
+ *               (scratch, overwritten); NULL or smaller: the call is w4a16_linear.
+ *   work_bytes  its size in bytes.  Other arguments as for w4a16_linear.
+ */
+int w4a16_linear_ws(const void* X, int dtype, int64_t M, int64_t N, int64_t K, int64_t group_size,
+                    const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros, void* Y, float* work,
+                    int64_t work_bytes, void* stream);
+
 /* ------------------------------------------------------------------------------------
  * W8A16: the same weight-only layer with 8-bit codes, four per 32-bit word (byte k % 4 of
  * word k / 4 is element k) and the same fp16 scale and zero point per group (page

@@ -293,3 +293,17 @@ def test_w8a16_quantize_pack_rejects_invalid_arguments(lib, args, status):
 ])
 def test_w8a16_dispatcher_choices(lib, M, N, K, g, dtype, path):
     assert lib.w4a16_w8a16_select_path(M, N, K, g, dtype) == path
+
+
+def test_linear_workspace_sizes(lib):
+    assert lib.w4a16_linear_workspace(16, 4096, 4096, 128, 0) == 0         # decode: no split
+    assert lib.w4a16_linear_workspace(4096, 4096, 11008, 128, 0) == 0      # enough tiles
+    assert lib.w4a16_linear_workspace(256, 4096, 11008, 128, 1) == 0       # bf16: no split
+    n = lib.w4a16_linear_workspace(256, 4096, 11008, 128, 0)
+    assert n > 0 and n % (256 * 4096 * 4) == 0                              # S fp32 partial planes
+    assert lib.w4a16_linear_workspace(256, 4096, 100, 100, 0) == L.ERR_SHAPE
+
+
+def test_linear_ws_rejects_invalid_arguments(lib):
+    assert lib.w4a16_linear_ws(None, 0, 256, 64, 128, 128, B, C, D, A, A, 0, None) == L.ERR_NULL
+    assert lib.w4a16_linear_ws(A, 0, 256, 64, 128, 128, B, C, D, A + 4096, A + 4, 1 << 20, None) == L.ERR_ALIGN

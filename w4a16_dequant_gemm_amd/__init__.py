@@ -31,7 +31,7 @@ from ._lib import (ASYM, BF16, F16, OK, PATH_AUTO, PATH_GEMV, PATH_NAMES, PATH_P
 __all__ = [
     "ASYM", "SYM", "F16", "BF16", "PATH_AUTO", "PATH_GEMV", "PATH_SKINNY", "PATH_PREFILL",
     "PATH_NAMES", "W4A16Error", "quantize_pack", "linear", "dequantize", "select_path",
-    "w8a16_quantize_pack", "w8a16_linear", "w8a16_select_path",
+    "w8a16_quantize_pack", "w8a16_linear", "w8a16_select_path", "linear_workspace", "linear_ws",
     "abi_version", "lib", "gptq_hessian", "gptq_factor", "gptq_quantize", "awq_stats",
     "awq_search", "awq_scale", "w8a8_smooth", "w8a8_quantize_weight", "w8a8_quantize_act",
     "w8a8_linear", "kv_quantize", "kv_attention_decode",
@@ -126,6 +126,41 @@ def linear(X: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zeros, 
                                scales.data_ptr(), zeros.data_ptr() if zeros is not None else None,
                                out.data_ptr(), path, _stream())
     check(st, "w4a16_linear")
+    return out
+
+
+def linear_workspace(M: int, N: int, K: int, group_size: int, dtype: int = F16) -> int:
+    """Bytes of fp32 workspace :func:`linear_ws` can use (0: it behaves as :func:`linear`)."""
+    need = lib().w4a16_linear_workspace(M, N, K, group_size, dtype)
+    if need < 0:
+        raise W4A16Error(int(need), "w4a16_linear_workspace")
+    return int(need)
+
+
+def linear_ws(X: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zeros, group_size: int,
+              work: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """:func:`linear` with a workspace for the tile-starved prefill shapes (split K, partial
+    tiles summed in fixed order).  ``work``: float32 device tensor (allocated here if None)."""
+    dt = _dtype_code(X)
+    _need(X, "X", X.dtype, 2)
+    _need(qweight, "qweight", torch.int32, 2)
+    _need(scales, "scales", torch.float16, 2)
+    M, K = X.shape
+    N = qweight.shape[0]
+    if qweight.shape[1] * 8 != K or tuple(scales.shape) != (N, K // group_size):
+        raise ValueError("qweight must be [N, K/8] and scales [N, K/group_size]")
+    need = linear_workspace(M, N, K, group_size, dt)
+    if work is None and need > 0:
+        work = torch.empty((need + 3) // 4, dtype=torch.float32, device=X.device)
+    if work is not None and (work.dtype != torch.float32 or not work.is_cuda):
+        raise ValueError("work must be a float32 device tensor")
+    if out is None:
+        out = torch.empty((M, N), dtype=X.dtype, device=X.device)
+    st = lib().w4a16_linear_ws(X.data_ptr(), dt, M, N, K, group_size, qweight.data_ptr(), scales.data_ptr(),
+                               zeros.data_ptr() if zeros is not None else None, out.data_ptr(),
+                               work.data_ptr() if work is not None else None,
+                               work.numel() * 4 if work is not None else 0, _stream())
+    check(st, "w4a16_linear_ws")
     return out
 
 

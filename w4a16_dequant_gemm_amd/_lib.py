@@ -53,6 +53,10 @@ def lib() -> ctypes.CDLL:
     L.w4a16_linear_ex.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, vp, vp, i32, vp]
     L.w4a16_select_path.restype = i32
     L.w4a16_select_path.argtypes = [i64, i64, i64, i64, i32]
+    L.w4a16_linear_workspace.restype = i64
+    L.w4a16_linear_workspace.argtypes = [i64, i64, i64, i64, i32]
+    L.w4a16_linear_ws.restype = i32
+    L.w4a16_linear_ws.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, i64, vp]
     L.w4a16_w8a16_quantize_pack.restype = i32
     L.w4a16_w8a16_quantize_pack.argtypes = [vp, i64, i64, i64, i32, vp, vp, vp, vp]
     L.w4a16_w8a16_linear.restype = i32

@@ -426,6 +426,29 @@ int w4a16_linear(const void* X, int dtype, int64_t M, int64_t N, int64_t K, int6
                            W4A16_PATH_AUTO, stream);
 }
 
+int64_t w4a16_linear_workspace(int64_t M, int64_t N, int64_t K, int64_t group_size, int dtype) {
+    alignas(16) static const unsigned char dummy[16] = {0};
+    LinearArgs a;
+    const int st = validate_linear(dummy, dtype, M, N, K, group_size, reinterpret_cast<const int32_t*>(dummy),
+                                   reinterpret_cast<const uint16_t*>(dummy), nullptr,
+                                   const_cast<unsigned char*>(dummy), &a);
+    if (st != W4A16_OK) return st;
+    return w4a16::prefill_splitk_bytes(a);
+}
+
+int w4a16_linear_ws(const void* X, int dtype, int64_t M, int64_t N, int64_t K, int64_t group_size,
+                    const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros, void* Y, float* work,
+                    int64_t work_bytes, void* stream) {
+    LinearArgs a;
+    const int st = validate_linear(X, dtype, M, N, K, group_size, qweight, scales, zeros, Y, &a);
+    if (st != W4A16_OK) return st;
+    if (work && !aligned(work, 16)) return W4A16_ERR_ALIGN;
+    const long long need = w4a16::prefill_splitk_bytes(a);
+    if (need > 0 && work && work_bytes >= need && w4a16::prefill_supports(a))
+        return hip_status(w4a16::launch_prefill_splitk(a, work, static_cast<hipStream_t>(stream)));
+    return w4a16_linear_ex(X, dtype, M, N, K, group_size, qweight, scales, zeros, Y, W4A16_PATH_AUTO, stream);
+}
+
 // ----------------------------------------------------------------- W8A16 (8-bit codes)
 
 int w4a16_w8a16_quantize_pack(const float* W, int64_t N, int64_t K, int64_t group_size, int scheme,

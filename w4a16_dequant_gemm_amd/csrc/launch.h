@@ -34,6 +34,10 @@ hipError_t launch_gemv(const LinearArgs& a, hipStream_t s);
 hipError_t launch_skinny(const LinearArgs& a, hipStream_t s);
 hipError_t launch_decode(const LinearArgs& a, hipStream_t s);
 hipError_t launch_prefill(const LinearArgs& a, hipStream_t s);
+// split-K mode of the fp16 256 x 256 prefill kernel (caller workspace of fp32 partial tiles)
+int prefill_splitk_splits(const LinearArgs& a);
+long long prefill_splitk_bytes(const LinearArgs& a);
+hipError_t launch_prefill_splitk(const LinearArgs& a, float* work, hipStream_t s);
 // W8A16 (8-bit codes, four per word): quantize-pack, the decode GEMV and the tiled MFMA GEMM
 hipError_t launch_quantize_pack8(const float* W, int N, int K, int g, int scheme, uint32_t* qw,
                                  uint16_t* scales, uint16_t* zeros, hipStream_t s);

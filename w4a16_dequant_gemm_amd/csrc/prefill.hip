@@ -424,11 +424,15 @@ constexpr int W_BM = 256, W_BN = 256, W_BK = 64;     // K % 128 == 0: steps in p
 // loads) and MFMA j takes words 2j and 2j + 1 (one byte permute per pair instead of the nibble
 // masks; the 1536-bias construction is exact for |u - z| < 512, the implicit symmetric zero
 // point is 128).
-template <bool HZ, int BITS = 4>
+// Split K (part != NULL): block (x, y) runs k-steps [y * spl, (y + 1) * spl) of its tile and
+// stores the fp32 partial tile to part[y][M][N]; splitk_reduce_kernel sums the partials in
+// split order.  Without a split, spl = K / 64, grid y = 1 and the tile goes to Y.
+template <bool HZ, int BITS = 4, bool SPLIT = false>
 __global__ __launch_bounds__(256, 1) void prefill_f16_wide_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros,
-    uint16_t* __restrict__ Y, int M, int N, int K, int G, int gshift) {
+    uint16_t* __restrict__ Y, int M, int N, int K, int G, int gshift,
+    float* __restrict__ part = nullptr, int spl = 0) {
     __shared__ __attribute__((aligned(16))) u32x4 As[2][W_BM * 8];     // 2 x 32 KB
 
     const int tid = threadIdx.x;
@@ -441,6 +445,11 @@ __global__ __launch_bounds__(256, 1) void prefill_f16_wide_kernel(
     const int m0 = mt * W_BM;
     const int n0 = nt * W_BN;
     const int nsteps = K / W_BK;
+    const int sb = SPLIT ? blockIdx.y * spl : 0;          // this block's k-steps [sb, se), even count
+    const int se = SPLIT ? min(nsteps, sb + spl) : nsteps;
+    if constexpr (SPLIT) {
+        if (sb >= se) return;                             // never planned (every split has steps)
+    }
 
     // Buffer loads: per-lane 32-bit offsets fixed for the whole K loop, the step's offset
     // as the wave-uniform soffset.  Rows past M / N are clamped (loaded, never stored).
@@ -581,21 +590,21 @@ __global__ __launch_bounds__(256, 1) void prefill_f16_wide_kernel(
     // the last step re-read it (harmless, unused).
     WStage p0, p1;
     uint32_t b0[2][4][4], b1[2][4][4];
-    load_a(0, 0);
-    load_w(p0, 0);
-    load_w(p1, min(1, nsteps - 1));
+    load_a(0, sb);
+    load_w(p0, sb);
+    load_w(p1, min(sb + 1, se - 1));
 #pragma unroll
     for (int j = 0; j < 4; ++j) dequant_word(p0, j, b0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    for (int step = 0; step < nsteps; step += 2) {
-        load_a(1, min(step + 1, nsteps - 1));
-        load_w(p0, min(step + 2, nsteps - 1));
+    for (int step = sb; step < se; step += 2) {
+        load_a(1, min(step + 1, se - 1));
+        load_w(p0, min(step + 2, se - 1));
         compute(0, b0, p1, b1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        load_a(0, min(step + 2, nsteps - 1));
-        load_w(p1, min(step + 3, nsteps - 1));
+        load_a(0, min(step + 2, se - 1));
+        load_w(p1, min(step + 3, se - 1));
         compute(1, b1, p0, b0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -610,13 +619,82 @@ __global__ __launch_bounds__(256, 1) void prefill_f16_wide_kernel(
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int m = m0 + 32 * ms + 8 * (e >> 2) + 4 * h + (e & 3);
-                if (m < M) Y[(size_t)m * N + n] = f2h_bits(acc[ms][ns][e]);
+                if (m < M) {
+                    if constexpr (SPLIT)
+                        part[((size_t)blockIdx.y * M + m) * N + n] = acc[ms][ns][e];
+                    else
+                        Y[(size_t)m * N + n] = f2h_bits(acc[ms][ns][e]);
+                }
             }
         }
     }
 }
 
+// Y = fp16(sum over the S splits of part[s]), in split order (deterministic).
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S,
+                                                            long long MN, uint16_t* __restrict__ Y) {
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < MN; i += (long long)gridDim.x * 256) {
+        float v = part[i];
+        for (int sp = 1; sp < S; ++sp) v += part[(size_t)sp * MN + i];
+        Y[i] = f2h_bits(v);
+    }
+}
+
 }  // namespace
+
+// Split-K plan of the 256 x 256 fp16 kernel for a problem with fewer tiles than CUs: splits of
+// spl k-steps (even, >= 16), S = ceil(steps / spl) of them, so every split is non-empty and
+// S * tiles stays near 256.  S <= 1 means no split.
+void splitk_plan(const LinearArgs& a, int& S, int& spl) {
+    S = 1;
+    spl = a.K / W_BK;
+    if (a.dtype != DT_F16 || a.K % (2 * W_BK) != 0 || a.M <= 32) return;
+    if (!((long long)a.M * a.K * 2 < (1LL << 31) && (long long)a.N * (a.K / 2) < (1LL << 31) &&
+          (long long)a.N * a.G * 2 < (1LL << 31)))
+        return;
+    const long long tiles = (long long)((a.M + W_BM - 1) / W_BM) * ((a.N + W_BN - 1) / W_BN);
+    if (tiles >= 128) return;
+    const int nsteps = a.K / W_BK;
+    const int want = (int)(256 / tiles);
+    int l = (nsteps + want - 1) / want;
+    l = l < 16 ? 16 : l + (l & 1);
+    S = (nsteps + l - 1) / l;
+    spl = l;
+}
+
+int prefill_splitk_splits(const LinearArgs& a) {
+    int S, spl;
+    splitk_plan(a, S, spl);
+    return S;
+}
+
+long long prefill_splitk_bytes(const LinearArgs& a) {
+    const int S = prefill_splitk_splits(a);
+    return S > 1 ? (long long)S * a.M * a.N * 4 : 0;
+}
+
+hipError_t launch_prefill_splitk(const LinearArgs& a, float* work, hipStream_t st) {
+    int S, spl;
+    splitk_plan(a, S, spl);
+    if (S <= 1 || !work) return hipErrorInvalidValue;
+    const int tiles = ((a.M + W_BM - 1) / W_BM) * ((a.N + W_BN - 1) / W_BN);
+    const dim3 grid(8 * ((tiles + 7) / 8), S);
+    if (a.zeros)
+        hipLaunchKernelGGL((prefill_f16_wide_kernel<true, 4, true>), grid, dim3(256), 0, st,
+                           static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, static_cast<uint16_t*>(a.Y),
+                           a.M, a.N, a.K, a.G, a.gshift, work, spl);
+    else
+        hipLaunchKernelGGL((prefill_f16_wide_kernel<false, 4, true>), grid, dim3(256), 0, st,
+                           static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, static_cast<uint16_t*>(a.Y),
+                           a.M, a.N, a.K, a.G, a.gshift, work, spl);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long MN = (long long)a.M * a.N;
+    const long long blocks = (MN + 255) / 256;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, st,
+                       work, S, MN, static_cast<uint16_t*>(a.Y));
+    return hipGetLastError();
+}
 
 bool prefill_supports(const LinearArgs& a) {
     if (a.dtype == DT_F16) return a.K % F_BK == 0 && a.g % F_BK == 0;   // any supported g
