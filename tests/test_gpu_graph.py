@@ -1,10 +1,11 @@
 """The entry points inside a captured HIP graph: every kernel path (GEMV, MFMA decode, MFMA
-skinny, fp16 and bf16 prefill), the W8A8 product and the batched KV decode attention are
-captured once into one graph with preallocated outputs; the graph is then replayed several
-times with eager work between the replays (other launches of the same kernels, outputs
-overwritten with NaN), and after every replay each output must equal the eager launch of
-the same call bit for bit (the kernels have a fixed reduction order).  The timed loops of
-the benchmark run the same way, so this is also the check behind its numbers.
+skinny, fp16 and bf16 prefill), the split-K workspace form, the W8A8 product and the batched
+KV decode attention are captured once into one graph with preallocated outputs (the split-K
+workspace too); the graph is then replayed several times with eager work between the
+replays (other launches of the same kernels, outputs overwritten with NaN), and after every
+replay each output must equal the eager launch of the same call bit for bit (the kernels
+have a fixed reduction order).  The timed loops of the benchmark run the same way, so this
+is also the check behind its numbers.
 """
 
 from __future__ import annotations
@@ -54,6 +55,16 @@ def test_graph_replays_match_eager():
         calls.append((f"linear M={M} K={K} N={N} g={g} path={W4.PATH_NAMES[path]}",
                       lambda out, X=X, qw=qw, s=s, zz=zz, g=g, path=path: W4.linear(X, qw, s, zz, g, path=path, out=out),
                       torch.empty((M, N), dtype=TDT[dt], device="cuda")))
+    # the workspace form on a tile-starved prefill shape (split K with the fixed-order reduction)
+    Xw = activations_device(256, 4096, FP16, 7150)
+    Ww = weights_device(1024, 4096, 0.02, 7151)
+    qww, sww, zww = W4.quantize_pack(Ww, 128, W4.ASYM)
+    del Ww
+    assert W4.linear_workspace(256, 1024, 4096, 128, FP16) > 0
+    ws = torch.empty(W4.linear_workspace(256, 1024, 4096, 128, FP16) // 4, dtype=torch.float32, device="cuda")
+    calls.append(("linear_ws split K M=256 K=4096 N=1024",
+                  lambda out: W4.linear_ws(Xw, qww, sww, zww, 128, work=ws, out=out),
+                  torch.empty((256, 1024), dtype=torch.float16, device="cuda")))
     # W8A8 product
     Xc = activations_device(256, 1024, FP16, 7200)
     Wc = weights_device(512, 1024, 0.02, 7201)
