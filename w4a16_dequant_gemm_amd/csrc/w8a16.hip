@@ -6,9 +6,10 @@
 //
 // Y[m, n] = sum_g s[n, g] (sum_{k in g} x[m, k] u[n, k] - z[n, g] sum_{k in g} x[m, k]).
 //
-// Mapping: blocks of 8 waves; each wave owns one output row and its lanes stream the row in
-// 16-byte loads (a 1 KB contiguous run per wave instruction), lane l taking the 16-column
-// chunks l, l + 64, ... of each slice; eight loads in flight per lane.  The block stages its
+// Mapping: blocks of 8 waves; each wave owns one output row (two from M = 2 on, so that each
+// activation read from LDS serves both) and its lanes stream the row in 16-byte loads (a 1 KB
+// contiguous run per wave instruction), lane l taking the 16-column chunks l, l + 64, ... of
+// each slice; eight loads in flight per lane.  The block stages its
 // activations in LDS in natural order with the 16-column chunk sums, the whole row of K at
 // once while M rows fit 64 KB, else in K slices of a multiple of 1024 columns.  Codes: fp16 activations take the code bytes as subnormal halves u * 2^-24 (one
 // byte permute per pair, exact) and v_dot2; bf16 activations take each code as an exact bf16
@@ -28,17 +29,25 @@ constexpr int kW8Threads = 64 * kW8Waves;
 constexpr int kW8Unroll = 8;                // 16-byte weight loads in flight per lane
 constexpr int kW8LdsBudget = 65536;         // staged activations and chunk sums
 constexpr int kW8MaxM = 16;
+#ifndef W4A16_W8_TWO_ROW_MIN_M
+#define W4A16_W8_TWO_ROW_MIN_M 2
+#endif
+// from this many activation rows on each wave owns two weight rows, so that every activation
+// read from LDS serves both (LDS reads per weight byte grow with M and at M = 4 match the
+// CU's share of the HBM stream)
+constexpr int kW8TwoRowMinM = W4A16_W8_TWO_ROW_MIN_M;
 
 __host__ __device__ constexpr long long w8_lds_bytes(int M, int K) {
     return (long long)M * K * 2 + (long long)M * (K / 16) * 4;
 }
 
-template <int DT, int M>
+template <int DT, int M, int R>
 __global__ __launch_bounds__(kW8Threads) void gemv8_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ zeros, int has_zeros, uint16_t* __restrict__ Y, int N, int K, int G,
     int gshift, int KS) {
     extern __shared__ __attribute__((aligned(16))) uint32_t lds8[];
+    constexpr int U = kW8Unroll / R;                       // chunks per row and batch
     const int CS = KS >> 4;                                // 16-column chunks per slice
     const int KPS = KS >> 3;                               // 8-column pieces per slice row (even)
     u32x4* xs = reinterpret_cast<u32x4*>(lds8);             // [M][2][KS / 16] pieces of 8 columns
@@ -46,17 +55,21 @@ __global__ __launch_bounds__(kW8Threads) void gemv8_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // one output row per wave; a wave past the last row still stages and meets the barriers
-    const int row = blockIdx.x * kW8Waves + wave;
-    const bool live = row < N;
-    const int rrow = live ? row : N - 1;
+    // R consecutive output rows per wave; rows past the last one re-read row N - 1 (valid
+    // memory, never stored), and every wave stages and meets the barriers
+    const int row0 = (blockIdx.x * kW8Waves + wave) * R;
+    int rrow[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) rrow[r] = min(row0 + r, N - 1);
     const __amdgpu_buffer_rsrc_t rw =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(qw), 0, N * K, 0x00020000);
     const uint16_t* zsrc = has_zeros ? zeros : scales;
     const uint32_t one2 = DT == DT_F16 ? 0x3C003C00u : 0x3F803F80u;
-    float acc[M];
+    float acc[R][M];
 #pragma unroll
-    for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
     for (int k0 = 0; k0 < K; k0 += KS) {
         const int ks = min(KS, K - k0);                    // columns in this slice (multiple of 32)
@@ -84,57 +97,70 @@ __global__ __launch_bounds__(kW8Threads) void gemv8_kernel(
         }
         __syncthreads();
 
-        // 2. The row's chunks of this slice.  Chunks past the slice re-read its last chunk
-        //    (valid memory, result unused).
+        // 2. The rows' chunks of this slice.  Chunks past the slice re-read its last chunk
+        //    (valid memory, result unused).  Each activation read from LDS serves all R rows.
         const int cs = ks >> 4;
         const int cpl = (cs + 63) >> 6;
-        for (int cb = 0; cb < cpl; cb += kW8Unroll) {
-            u32x4 w[kW8Unroll];
-            uint16_t sb[kW8Unroll], zb[kW8Unroll];
+        for (int cb = 0; cb < cpl; cb += U) {
+            u32x4 w[U][R];
+            uint16_t sb[U][R], zb[U][R];
 #pragma unroll
-            for (int u = 0; u < kW8Unroll; ++u) {
+            for (int u = 0; u < U; ++u) {
                 const int c = min(lane + 64 * (cb + u), cs - 1);
-                w[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, rrow * K + k0 + 16 * c, 0, 2 /* nt */);
                 const int grp = (k0 + 16 * c) >> gshift;
-                sb[u] = scales[(size_t)rrow * G + grp];
-                zb[u] = zsrc[(size_t)rrow * G + grp];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    w[u][r] = __builtin_amdgcn_raw_buffer_load_b128(rw, rrow[r] * K + k0 + 16 * c, 0, 2 /* nt */);
+                    sb[u][r] = scales[(size_t)rrow[r] * G + grp];
+                    zb[u][r] = zsrc[(size_t)rrow[r] * G + grp];
+                }
             }
 #pragma unroll
-            for (int u = 0; u < kW8Unroll; ++u) {
+            for (int u = 0; u < U; ++u) {
                 const int c = lane + 64 * (cb + u);
                 if (c < cs) {
-                    const float sv = h2f(sb[u]);
-                    const float zv = has_zeros ? h2f(zb[u]) : 128.0f;
-                    const float sp = DT == DT_F16 ? sv * 16777216.0f : sv;
-                    const float cz = -zv * sp;
-                    uint32_t cd[8];
-                    codes8<DT>(w[u].x, &cd[0]);
-                    codes8<DT>(w[u].y, &cd[2]);
-                    codes8<DT>(w[u].z, &cd[4]);
-                    codes8<DT>(w[u].w, &cd[6]);
+                    float sp[R], cz[R];
+                    uint32_t cd[R][8];
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const float sv = h2f(sb[u][r]);
+                        const float zv = has_zeros ? h2f(zb[u][r]) : 128.0f;
+                        sp[r] = DT == DT_F16 ? sv * 16777216.0f : sv;
+                        cz[r] = -zv * sp[r];
+                        codes8<DT>(w[u][r].x, &cd[r][0]);
+                        codes8<DT>(w[u][r].y, &cd[r][2]);
+                        codes8<DT>(w[u][r].z, &cd[r][4]);
+                        codes8<DT>(w[u][r].w, &cd[r][6]);
+                    }
 #pragma unroll
                     for (int m = 0; m < M; ++m) {
                         const u32x4 a0 = xs[m * KPS + c];
                         const u32x4 a1 = xs[m * KPS + (KPS >> 1) + c];
-                        float pd = dot2<DT>(a0.x, cd[0], 0.0f);
-                        pd = dot2<DT>(a0.y, cd[1], pd);
-                        pd = dot2<DT>(a0.z, cd[2], pd);
-                        pd = dot2<DT>(a0.w, cd[3], pd);
-                        pd = dot2<DT>(a1.x, cd[4], pd);
-                        pd = dot2<DT>(a1.y, cd[5], pd);
-                        pd = dot2<DT>(a1.z, cd[6], pd);
-                        pd = dot2<DT>(a1.w, cd[7], pd);
-                        acc[m] = fmaf(cz, csum[m * CS + c], fmaf(sp, pd, acc[m]));
+                        const float cm = csum[m * CS + c];
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            float pd = dot2<DT>(a0.x, cd[r][0], 0.0f);
+                            pd = dot2<DT>(a0.y, cd[r][1], pd);
+                            pd = dot2<DT>(a0.z, cd[r][2], pd);
+                            pd = dot2<DT>(a0.w, cd[r][3], pd);
+                            pd = dot2<DT>(a1.x, cd[r][4], pd);
+                            pd = dot2<DT>(a1.y, cd[r][5], pd);
+                            pd = dot2<DT>(a1.z, cd[r][6], pd);
+                            pd = dot2<DT>(a1.w, cd[r][7], pd);
+                            acc[r][m] = fmaf(cz[r], cm, fmaf(sp[r], pd, acc[r][m]));
+                        }
                     }
                 }
             }
         }
     }
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-        const float v = wave_sum(acc[m]);
-        if (live && lane == 0) Y[(size_t)m * N + row] = f2out<DT>(v);
-    }
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const float v = wave_sum(acc[r][m]);
+            if (row0 + r < N && lane == 0) Y[(size_t)m * N + row0 + r] = f2out<DT>(v);
+        }
 }
 
 // Slice width: the whole row while M rows of activations and their chunk sums fit the LDS
@@ -150,10 +176,17 @@ template <int DT, int M>
 hipError_t run_gemv8(const LinearArgs& a, hipStream_t st) {
     const int ks = w8_slice(M, a.K);
     const long long lds = w8_lds_bytes(M, ks);
-    const long long blocks = (a.N + kW8Waves - 1) / kW8Waves;
-    hipLaunchKernelGGL((gemv8_kernel<DT, M>), dim3((unsigned)blocks), dim3(kW8Threads), (size_t)lds, st,
-                       static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, a.zeros ? 1 : 0,
-                       static_cast<uint16_t*>(a.Y), a.N, a.K, a.G, a.gshift, ks);
+    if (M >= kW8TwoRowMinM) {
+        const long long blocks = (a.N + 2 * kW8Waves - 1) / (2 * kW8Waves);
+        hipLaunchKernelGGL((gemv8_kernel<DT, M, 2>), dim3((unsigned)blocks), dim3(kW8Threads), (size_t)lds, st,
+                           static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, a.zeros ? 1 : 0,
+                           static_cast<uint16_t*>(a.Y), a.N, a.K, a.G, a.gshift, ks);
+    } else {
+        const long long blocks = (a.N + kW8Waves - 1) / kW8Waves;
+        hipLaunchKernelGGL((gemv8_kernel<DT, M, 1>), dim3((unsigned)blocks), dim3(kW8Threads), (size_t)lds, st,
+                           static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, a.zeros ? 1 : 0,
+                           static_cast<uint16_t*>(a.Y), a.N, a.K, a.G, a.gshift, ks);
+    }
     return hipGetLastError();
 }
 
