@@ -299,7 +299,7 @@ def profile_run(name: str, W4, synth, torch):
     `prefill` (M = 4096 on both prefill shapes, 5 launches each), `w8a8` (the INT8 product at
     M = 4096, both shapes, 5 launches each), `kv_batch` (batched KV8 and KV4 decode attention,
     16 sequences, 2 layers' caches, 2 launches each), `decode_m16` (M = 16 on the 7B shapes
-    over 20 rotating weight copies, 20 launches each), `w8a16` (8-bit codes: M = 1 on the 7B
+    over 20 rotating weight copies, 20 launches each), `w8a16` (8-bit codes: M = 1 and 4 on the 7B
     shapes over 10 rotating copies, 20 launches each, and the M = 4096 prefill, 5 each)."""
     if name == "prefill":
         for K, N in [(4096, 11008), (11008, 4096)]:
@@ -323,17 +323,18 @@ def profile_run(name: str, W4, synth, torch):
     elif name == "kv_batch":
         run_kv_batch(W4, synth, torch, layers=2, timed=False)
     elif name == "w8a16":
-        # 8-bit codes: M = 1 on the 7B shapes over 10 rotating copies (20 launches each), and
+        # 8-bit codes: M = 1 and 4 on the 7B shapes over 10 rotating copies (20 launches each), and
         # the prefill at M = 4096 on both shapes (5 launches each)
         for K, N in SHAPES:
             W = synth.weights_device(N, K, 0.02, 9000 + K + N)
             q = W4.w8a16_quantize_pack(W, GROUP, W4.ASYM)
             del W
             cs = [tuple(t.clone() for t in q) for _ in range(10)]
-            X = synth.activations_device(1, K, synth.FP16, 9)
-            Y = torch.empty((1, N), dtype=torch.float16, device="cuda")
-            for i in range(20):
-                W4.w8a16_linear(X, *cs[i % 10], GROUP, out=Y)
+            for M in (1, 4):      # one weight row per wave at M = 1, two at M = 4
+                X = synth.activations_device(M, K, synth.FP16, 9 + M)
+                Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+                for i in range(20):
+                    W4.w8a16_linear(X, *cs[i % 10], GROUP, out=Y)
             del cs
         for K, N in [(4096, 11008), (11008, 4096)]:
             W = synth.weights_device(N, K, 0.02, 9200 + K)
