@@ -2,9 +2,9 @@
 
 * quantize-pack: 8-bit codes (as packed words), fp16 scales and zeros bit-exact, both
   schemes, group sizes 32 .. K, outlier weights;
-* linear: both kernels (the weight-streaming GEMV for M <= 16, the tiled MFMA GEMM) against
-  the fp64 oracle within the output bar (relative Frobenius <= 1e-3, max |d| <= 1e-2 max
-  |ref|), fp16 and bf16 activations, ragged N and M, per-channel groups, symmetric with and
+* linear: both kernels (the weight-streaming GEMV for M <= 16, one weight row per wave at
+  M = 1 and two from M = 2 on; the tiled MFMA GEMM) against the fp64 oracle within the
+  output bar (relative Frobenius <= 1e-3, max |d| <= 1e-2 max |ref|), fp16 and bf16 activations, ragged N and M, per-channel groups, symmetric with and
   without stored zero points, both kernels forced on the same problems;
 * one-hot activations: each output is one dequantized weight, rounded once, bit-exact;
 * full-size layers (the 7B-like shapes at M = 1 and 4, the prefill at M = 4096), sampled.
@@ -74,7 +74,10 @@ GEMV_CASES = [(1, 4096, 4096, 128), (2, 300, 1024, 32), (3, 1000, 2048, 64), (4,
               # ragged last slice, per-channel groups spanning slices
               (4, 300, 11008, 128), (3, 70, 20480, 256), (1, 33, 32768, 32768), (2, 1000, 15360, 64),
               # up to 16 activation rows (several K slices from M = 8 on)
-              (8, 500, 4096, 128), (16, 257, 4096, 64), (13, 130, 11008, 11008)]
+              (8, 500, 4096, 128), (16, 257, 4096, 64), (13, 130, 11008, 11008),
+              # two rows per wave: odd N (the last wave's second row is past the end), odd M
+              # over several K slices
+              (15, 201, 4096, 128), (2, 1, 1024, 128), (3, 17, 2048, 32)]
 PREFILL_CASES = [(5, 4096, 1024, 128), (64, 300, 2048, 64), (300, 1000, 1024, 128), (129, 257, 4096, 4096),
                  (4, 4096, 11008, 128), (1, 64, 128, 64), (512, 128, 640, 128)]
 
