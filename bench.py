@@ -104,22 +104,29 @@ def capture(fn, iters, torch):
     return g
 
 
-def time_graph(g, iters, torch):
-    """ms per iteration of a graph that holds ``iters`` iterations."""
+REPEATS = 5       # timed replays per measurement; the median is reported
+
+
+def time_graph(g, iters, torch, repeats: int = REPEATS):
+    """ms per iteration of a graph that holds ``iters`` iterations: one warm replay, then
+    ``repeats`` replays, each bracketed by synchronize + events; the median replay."""
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     g.replay()                     # warm replay
     torch.cuda.synchronize()
-    e0.record()
-    g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / iters
+    times = []
+    for _ in range(repeats):
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / iters)
+    return sorted(times)[len(times) // 2]
 
 
-def time_loop(fn, iters, torch, graph=True):
+def time_loop(fn, iters, torch, graph=True, repeats: int = REPEATS):
     if graph:
-        return time_graph(capture(fn, iters, torch), iters, torch)
+        return time_graph(capture(fn, iters, torch), iters, torch, repeats)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -131,11 +138,35 @@ def time_loop(fn, iters, torch, graph=True):
     return e0.elapsed_time(e1) / iters   # ms per iteration
 
 
-def cpu_baseline(layers, w_host, xs_host, y_gpu, budget_s, np, torch):
+def check_samples(samples, oracle, np):
+    """The oracle on the sampled rows of every timed extra configuration: packing bit-exact
+    (codes, scales, zero points) and outputs within the bar (relative Frobenius <= 1e-3,
+    max |dY| <= 1e-2 max |Y_ref|)."""
+    out = {}
+    for smp in samples:
+        codes, s, z = oracle.quantize(smp["W"], smp["g"], smp["scheme"])
+        qw = oracle.pack(codes)
+        pk = bool(np.array_equal(qw, smp["qw"]) and np.array_equal(s.view(np.uint16), smp["s"].view(np.uint16)))
+        if smp["z"] is not None:
+            pk &= bool(np.array_equal(z.view(np.uint16), smp["z"].view(np.uint16)))
+        ref = oracle.linear_ref(smp["X"], smp["dtype"], qw, s, smp["z"] if smp["z"] is not None else z, smp["g"])
+        if smp["dtype"] == 0:
+            r, y = ref.astype(np.float64), smp["Y"].view(np.float16).astype(np.float64)
+        else:
+            r, y = oracle.bf16_bits_to_f64(ref), oracle.bf16_bits_to_f64(smp["Y"])
+        fro = float(np.linalg.norm(y - r) / np.linalg.norm(r))
+        mx = float(np.abs(y - r).max() / np.abs(r).max())
+        out[smp["name"]] = {"packing_bit_exact": pk, "rel_fro": fro, "max_rel": mx,
+                            "ok": pk and fro <= 1e-3 and mx <= 1e-2}
+    return out
+
+
+def cpu_baseline(layers, w_host, xs_host, y_gpu, budget_s, np, torch, samples=()):
     """The oracle beside the GPU path, on the host cores: quantize each layer (checked
     bit-exact against the GPU packing on sampled rows), then time the oracle's linear
     (fp64 dequantize + BLAS product) on the same M = 1 workload and check the GPU
-    outputs of the timed step against its result."""
+    outputs of the timed step against its result; then the sampled rows of every timed
+    extra configuration against the oracle."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -173,8 +204,11 @@ def cpu_baseline(layers, w_host, xs_host, y_gpu, budget_s, np, torch):
         r = r.astype(np.float64)
         fro.append(float(np.linalg.norm(y - r) / np.linalg.norm(r)))
         mx.append(float(np.abs(y - r).max() / np.abs(r).max()))
+    extra = check_samples(samples, oracle, np)
     parity = {"packing_bit_exact_sampled_rows": packing_ok, "rel_fro": fro, "max_rel": mx,
-              "ok": packing_ok and max(fro) <= 1e-3 and max(mx) <= 1e-2}
+              "extra_configs_checked": len(extra),
+              "extra_configs_failed": {k: v for k, v in extra.items() if not v["ok"]},
+              "ok": packing_ok and max(fro) <= 1e-3 and max(mx) <= 1e-2 and all(v["ok"] for v in extra.values())}
     # one host thread on the single 4096 x 4096 layer, and the 32-layer stack extrapolated
     # from one 7-linear layer (q, k, v, o 4096 -> 4096; gate, up 4096 -> 11008; down 11008 -> 4096)
     one_thread = None
@@ -300,7 +334,8 @@ def profile_run(name: str, W4, synth, torch):
     M = 4096, both shapes, 5 launches each), `kv_batch` (batched KV8 and KV4 decode attention,
     16 sequences, 2 layers' caches, 2 launches each), `decode_m16` (M = 16 on the 7B shapes
     over 20 rotating weight copies, 20 launches each), `w8a16` (8-bit codes: M = 1 and 4 on the 7B
-    shapes over 10 rotating copies, 20 launches each, and the M = 4096 prefill, 5 each)."""
+    shapes over 10 rotating copies, 20 launches each, and the M = 4096 prefill, 5 each), `c3`
+    (the 70B-like bf16 decode shapes at M = 1, 4, 16 over 4 rotating copies, 20 launches each)."""
     if name == "prefill":
         for K, N in [(4096, 11008), (11008, 4096)]:
             W = synth.weights_device(N, K, 0.02, 3000 + K)
@@ -344,6 +379,20 @@ def profile_run(name: str, W4, synth, torch):
             Y = torch.empty((4096, N), dtype=torch.float16, device="cuda")
             for _ in range(5):
                 W4.w8a16_linear(X, *q, GROUP, out=Y)
+    elif name == "c3":
+        # the 70B-like decode shapes (bf16 with outlier channels and weights), M = 1, 4, 16,
+        # over 4 rotating copies (>= 140 MB apart in HBM), 20 launches each
+        for i, (K, N) in enumerate([(8192, 8192), (8192, 28672), (28672, 8192)]):
+            W = synth.weights_device(N, K, 0.015, 1030 + i, outlier_frac=0.001, outlier_mult=20.0)
+            q = W4.quantize_pack(W, GROUP, W4.ASYM)
+            del W
+            cs = [q] + [tuple(t.clone() for t in q) for _ in range(3)]
+            for M in (1, 4, 16):
+                X = synth.activations_device(M, K, synth.BF16, 1035 + M, outlier_frac=0.01, outlier_mult=100.0)
+                Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+                for j in range(20):
+                    W4.linear(X, *cs[j % 4], GROUP, out=Y)
+            del cs, q
     elif name == "decode_m16":
         for K, N in SHAPES:
             W = synth.weights_device(N, K, 0.02, 1000 + K + N)
@@ -420,7 +469,7 @@ def main():
     ap.add_argument("--traffic-commands", nargs="*", default=[],
                     help="the profiler command lines, recorded in the traffic file")
     ap.add_argument("--traffic-out", default=None, help="output path of --traffic-parse")
-    ap.add_argument("--profile-run", choices=["prefill", "w8a8", "kv_batch", "decode_m16", "w8a16"],
+    ap.add_argument("--profile-run", choices=["prefill", "w8a8", "kv_batch", "decode_m16", "w8a16", "c3"],
                     help="a short fixed workload of one kernel family, for counter runs")
     args = ap.parse_args()
     if args.traffic_parse:
@@ -477,20 +526,17 @@ def main():
 
     for i in range(args.warmup):
         step(i)
-    # The timed region is one replay of a graph holding exactly `steps` steps, bracketed
-    # by synchronize + events; warm-up steps run eagerly and as one warm graph replay.
+    # The timed region is a replay of a graph holding exactly `steps` steps, bracketed by
+    # synchronize + events; warm-up steps run eagerly and as one warm graph replay.  The
+    # replay is timed REPEATS times and the median replay is reported.
     g_main = capture(lambda i: step(i + args.warmup), args.steps, torch)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    g_main.replay()
-    torch.cuda.synchronize()
-    e0.record()
-    g_main.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = time_graph(g_main, args.steps, torch)
     value = step_bytes / (ms * 1e-3) / 1e9
-    log(f"step: {ms * 1e3:.1f} us, {value:.1f} GB/s")
+    log(f"step: {ms * 1e3:.1f} us, {value:.1f} GB/s (median of {REPEATS} replays of {args.steps} steps)")
+    # steady state (the same step, at least 200 back-to-back launches per replay)
+    ss_steps = max(args.steps, -(-200 // len(layers)))
+    ms_ss = ms if ss_steps == args.steps else time_loop(lambda i: step(i + args.warmup), ss_steps, torch)
+    log(f"steady state: {ms_ss * 1e3:.1f} us per step over {ss_steps * len(layers)} launches")
     # the graph replays must reproduce the eager result of the last step
     last = [o.clone() for o in outs]
     step(args.warmup + args.steps - 1)
@@ -526,13 +572,14 @@ def main():
         roofline["traffic_source"] = traffic["source"]
 
     extras = {"per_layer_m1": per_layer}
+    samples = []
     if not args.no_extras:
         extras["comparators"] = run_comparators(W4, synth, torch, ms)
-        extras.update(run_extras(layers, copies, W4, synth, torch, np))
+        extras.update(run_extras(layers, copies, W4, synth, torch, np, samples))
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(layers, w_host, xs_host, last, args.cpu_budget, np, torch)
+        cpu = cpu_baseline(layers, w_host, xs_host, last, args.cpu_budget, np, torch, samples)
         log(f"cpu oracle: {cpu['value']:.3f} GB/s on {cpu['cores']} threads; "
             f"parity vs GPU: {cpu['parity_vs_gpu']}")
         if not cpu["parity_vs_gpu"]["ok"]:
@@ -548,7 +595,11 @@ def main():
         "config": {"workload": "decode M=1 on 7B-like layers (K,N) = (4096,4096), "
                                "(4096,11008), (11008,4096); g=128 asym uint4; fp16 activations",
                    "M": 1, "group_size": GROUP, "scheme": "asym", "rotating_copies": copies,
-                   "bytes_per_step": step_bytes, "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
+                   "bytes_per_step": step_bytes, "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                   "timing": f"median of {REPEATS} graph replays of the {args.steps} timed steps",
+                   "steady_state": {"launches_per_replay": ss_steps * len(layers),
+                                    "us_per_step": round(ms_ss * 1e3, 3),
+                                    "GBps": round(step_bytes / (ms_ss * 1e-3) / 1e9, 1)}},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extras": extras,
@@ -620,7 +671,7 @@ def run_comparators(W4, synth, torch, w4_step_ms):
     return res
 
 
-def run_extras(layers, copies, W4, synth, torch, np):
+def run_extras(layers, copies, W4, synth, torch, np, samples):
     out = {}
     # decode sweep M in 2..16 on the same rotating layers
     sweep = {}
@@ -662,57 +713,121 @@ def run_extras(layers, copies, W4, synth, torch, np):
             per_path[f"M{M}_{W4.PATH_NAMES[path]}"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
     log(f"  per-path GB/s: {per_path}")
     out["decode_per_path_GBps"] = per_path
-    # prefill M = 4096
-    pre = {}
-    for (K, N) in [(4096, 11008), (11008, 4096)]:
-        W = synth.weights_device(N, K, 0.02, 3000 + K)
-        qw, s, z = W4.quantize_pack(W, GROUP, W4.ASYM)
-        del W
-        X = synth.activations_device(4096, K, synth.FP16, 3001 + K)
-        Y = torch.empty((4096, N), dtype=torch.float16, device="cuda")
-        for _ in range(3):
-            W4.linear(X, qw, s, z, GROUP, out=Y)
-        ms = time_loop(lambda i: W4.linear(X, qw, s, z, GROUP, out=Y), 10, torch)
-        tf = 2.0 * 4096 * N * K / (ms * 1e-3) / 1e12
-        # context: a dense fp16 GEMM of the same shape with fp16 weights (torch / hipBLASLt)
-        Wd = torch.randn(N, K, dtype=torch.float16, device="cuda")
-        for _ in range(3):
-            torch.matmul(X, Wd.t(), out=Y)
-        ms_d = time_loop(lambda i: torch.matmul(X, Wd.t(), out=Y), 10, torch, graph=False)
-        tf_d = 2.0 * 4096 * N * K / (ms_d * 1e-3) / 1e12
-        pre[f"K{K}_N{N}"] = {"TFLOPs": round(tf, 1), "us": round(ms * 1e3, 1),
-                             "frac_mfma_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
-                             "dense_fp16_torch_TFLOPs": round(tf_d, 1)}
-        log(f"  prefill M=4096 K={K} N={N}: {tf:.1f} TFLOP/s (dense fp16 torch.matmul {tf_d:.1f})")
-        # the rest of the crossover sweep (M = 256, 1024), auto-dispatched, with the kernel it took
-        for Ms in (256, 1024):
-            Xs, Ys = X[:Ms], Y[:Ms]
-            for _ in range(3):
-                W4.linear(Xs, qw, s, z, GROUP, out=Ys)
-            ms_s = time_loop(lambda i: W4.linear(Xs, qw, s, z, GROUP, out=Ys), 10, torch)
-            tf_s = 2.0 * Ms * N * K / (ms_s * 1e-3) / 1e12
-            pre[f"K{K}_N{N}"][f"M{Ms}"] = {"TFLOPs": round(tf_s, 1), "us": round(ms_s * 1e3, 1),
-                                           "path": W4.PATH_NAMES[W4.select_path(Ms, N, K, GROUP)]}
-            need = W4.linear_workspace(Ms, N, K, GROUP)
-            if need > 0:   # the workspace form: K split over the idle CUs
-                work = torch.empty((need + 3) // 4, dtype=torch.float32, device="cuda")
-                for _ in range(3):
-                    W4.linear_ws(Xs, qw, s, z, GROUP, work=work, out=Ys)
-                ms_w = time_loop(lambda i: W4.linear_ws(Xs, qw, s, z, GROUP, work=work, out=Ys), 10, torch)
-                pre[f"K{K}_N{N}"][f"M{Ms}"]["split_k_workspace"] = {
-                    "us": round(ms_w * 1e3, 1), "TFLOPs": round(2.0 * Ms * N * K / (ms_w * 1e-3) / 1e12, 1),
-                    "workspace_MB": round(need / 2**20, 1)}
-                del work
-            log(f"  prefill M={Ms} K={K} N={N}: {pre[f'K{K}_N{N}'][f'M{Ms}']}")
-        del qw, s, z, X, Y, Wd
-    out["prefill_m4096_fp16_g128"] = pre
+    out["c3_decode_70b_bf16_outliers"] = run_c3(W4, synth, torch, np, samples)
+    out["c4_prefill_crossover_fp16"] = run_c4(W4, synth, torch, np, samples)
     out["gptq_4096x4096_g128"] = run_gptq(W4, synth, torch)
     out["awq_4096x4096_g128"] = run_awq(W4, synth, torch)
     out["w8a8_m4096"] = run_w8a8(W4, synth, torch)
     out["kv_decode_attention_h32_d128_t4096"] = run_kv(W4, synth, torch)
-    out["full_stack_7b_32_layers"] = run_stack(W4, synth, torch)
+    out["full_stack_7b_32_layers"] = run_stack(W4, synth, torch, np, samples)
     out["w8a16_g128"] = run_w8a16(W4, synth, torch)
     return out
+
+
+def parity_sample(name, case_dtype, g, scheme, Wd, qw, s, z, X, Y, torch, np, n_cols=128, m_rows=16):
+    """Sampled inputs and GPU results of a timed configuration for the oracle leg: the fp32
+    weights, packed rows, scales and zero points of ``n_cols`` output columns, ``m_rows``
+    activation rows and the matching outputs (host copies).  Nothing is computed here."""
+    N, M = qw.shape[0], X.shape[0]
+    rng = np.random.default_rng(N + M + g)
+    ns = np.unique(np.concatenate([[0, N - 1], rng.choice(N, min(n_cols, N), replace=False)]))
+    ms = np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(m_rows, M), replace=False)]))
+    ni, mi = torch.from_numpy(ns).cuda(), torch.from_numpy(ms).cuda()
+    xh = X[mi].view(torch.int16).cpu().numpy()
+    return {"name": name, "dtype": case_dtype, "g": g, "scheme": scheme,
+            "W": Wd[ni].cpu().numpy(), "qw": qw[ni].cpu().numpy(),
+            "s": s[ni].cpu().numpy(), "z": None if z is None else z[ni].cpu().numpy(),
+            "X": xh.view(np.float16) if case_dtype == 0 else xh.view(np.uint16),
+            "Y": Y[mi][:, ni].view(torch.int16).cpu().numpy().view(np.uint16)}
+
+
+def run_c3(W4, synth, torch, np, samples):
+    """The 70B-like decode shapes: M in {1, 4, 16} on (K, N) = (8192, 8192), (8192, 28672),
+    (28672, 8192), g = 128 asymmetric, bf16 activations ~ N(0, 1) with 1 % of the channels
+    x100, weights ~ N(0, 0.015) with 0.1 % of the entries x20.  Each layer rotates through
+    >= 1 GiB of weight copies; >= 200 back-to-back launches per replay (graph), median of 5
+    replays; effective weight-stream GB/s = (packed + scale/zero bytes) / launch time."""
+    res = {}
+    shapes = [(8192, 8192), (8192, 28672), (28672, 8192)]
+    for i, (K, N) in enumerate(shapes):
+        sw, sx = synth.seeds(3, i)
+        Wd = synth.weights_device(N, K, 0.015, sw, outlier_frac=0.001, outlier_mult=20.0)
+        q = W4.quantize_pack(Wd, GROUP, W4.ASYM)
+        nbytes = weight_bytes(N, K, GROUP)
+        copies = max(2, -(-2**30 // nbytes))
+        cs = [q] + [tuple(t.clone() for t in q) for _ in range(copies - 1)]
+        for M in (1, 4, 16):
+            X = synth.activations_device(M, K, synth.BF16, sx + M, outlier_frac=0.01, outlier_mult=100.0)
+            Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+            def one(j, X=X, Y=Y, cs=cs):
+                qw, sc, z = cs[j % copies]
+                W4.linear(X, qw, sc, z, GROUP, out=Y)
+            for j in range(5):
+                one(j)
+            t = time_loop(one, 200, torch)
+            gbps = nbytes / (t * 1e-3) / 1e9
+            key = f"M{M}_K{K}_N{N}"
+            res[key] = {"us": round(t * 1e3, 2), "GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBS, 4),
+                        "bytes_per_launch": nbytes, "rotating_copies": copies,
+                        "path": W4.PATH_NAMES[W4.select_path(M, N, K, GROUP, W4.BF16)]}
+            log(f"  C3 {key}: {res[key]}")
+            one(0)
+            samples.append(parity_sample(f"C3_{key}", 1, GROUP, W4.ASYM, Wd, *cs[0], X, Y, torch, np))
+        del Wd, cs, q
+        torch.cuda.empty_cache()
+    return res
+
+
+def run_c4(W4, synth, torch, np, samples):
+    """The prefill / compute-bound crossover: M in {256, 1024, 4096} on (K, N) = (4096, 11008)
+    and (11008, 4096), g in {64, 128}, symmetric absmax and asymmetric uint4, fp16
+    activations; TFLOP/s = 2 M N K / launch time (graph of 10 launches, median of 5 replays),
+    the kernel the dispatcher took, the workspace form where it splits K, and a dense fp16
+    GEMM of the same shape with fp16 weights (torch.matmul / hipBLASLt) as context."""
+    res = {}
+    for (K, N) in [(4096, 11008), (11008, 4096)]:
+        X = synth.activations_device(4096, K, synth.FP16, 3001 + K)
+        Y = torch.empty((4096, N), dtype=torch.float16, device="cuda")
+        Wd16 = torch.randn(N, K, dtype=torch.float16, device="cuda")
+        for g in (64, 128):
+            for scheme in (W4.SYM, W4.ASYM):
+                Wd = synth.weights_device(N, K, 0.02, 3000 + K + g + scheme)
+                qw, s, z = W4.quantize_pack(Wd, g, scheme)
+                sname = "asym" if scheme == W4.ASYM else "sym"
+                for M in (256, 1024, 4096):
+                    Xs, Ys = X[:M], Y[:M]
+                    for _ in range(3):
+                        W4.linear(Xs, qw, s, z, g, out=Ys)
+                    t = time_loop(lambda i: W4.linear(Xs, qw, s, z, g, out=Ys), 10, torch)
+                    tf = 2.0 * M * N * K / (t * 1e-3) / 1e12
+                    key = f"M{M}_K{K}_N{N}_g{g}_{sname}"
+                    rec = {"TFLOPs": round(tf, 1), "us": round(t * 1e3, 1),
+                           "frac_mfma_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                           "path": W4.PATH_NAMES[W4.select_path(M, N, K, g)]}
+                    need = W4.linear_workspace(M, N, K, g)
+                    if need > 0:   # the workspace form: K split over the idle CUs
+                        work = torch.empty((need + 3) // 4, dtype=torch.float32, device="cuda")
+                        for _ in range(3):
+                            W4.linear_ws(Xs, qw, s, z, g, work=work, out=Ys)
+                        tw = time_loop(lambda i: W4.linear_ws(Xs, qw, s, z, g, work=work, out=Ys), 10, torch)
+                        rec["split_k_workspace"] = {"us": round(tw * 1e3, 1),
+                                                    "TFLOPs": round(2.0 * M * N * K / (tw * 1e-3) / 1e12, 1),
+                                                    "workspace_MB": round(need / 2**20, 1)}
+                        del work
+                    if g == 128 and scheme == W4.ASYM:
+                        for _ in range(3):
+                            torch.matmul(Xs, Wd16.t(), out=Ys)
+                        td = time_loop(lambda i: torch.matmul(Xs, Wd16.t(), out=Ys), 10, torch, graph=False)
+                        rec["dense_fp16_torch_TFLOPs"] = round(2.0 * M * N * K / (td * 1e-3) / 1e12, 1)
+                    res[key] = rec
+                    log(f"  C4 {key}: {rec}")
+                    W4.linear(Xs, qw, s, z, g, out=Ys)
+                    samples.append(parity_sample(f"C4_{key}", 0, g, scheme, Wd, qw, s, z, Xs, Ys, torch, np))
+                del Wd, qw, s, z
+        del X, Y, Wd16
+        torch.cuda.empty_cache()
+    return res
 
 
 def run_w8a16(W4, synth, torch):
@@ -765,11 +880,11 @@ def run_w8a16(W4, synth, torch):
     return res
 
 
-def run_stack(W4, synth, torch):
+def run_stack(W4, synth, torch, np, samples):
     """The full decode step of a 32-layer 7B-shaped stack: 224 linears (q, k, v, o, gate, up,
     down per layer), about 3.5 GB of packed weights, bf16 activations, launched back to back on
-    one stream (graph-captured); g = 128 at M = 1 and M = 8, and the per-channel variant
-    (g = K) at M = 1.  Bytes: every linear's packed weights and metadata."""
+    one stream (graph-captured); g = 128 and the per-channel variant (g = K), each at M = 1 and
+    M = 8.  Bytes: every linear's packed weights and metadata."""
     res = {}
     for per_channel in (False, True):
         layers = []
@@ -779,7 +894,7 @@ def run_stack(W4, synth, torch):
             del W
             layers.append((c, qw, s, z))
         nbytes = sum(weight_bytes(c.N, c.K, c.g) for c, *_ in layers)
-        for M in ((1, 8) if not per_channel else (1,)):
+        for M in (1, 8):
             xs = {K: synth.activations_device(M, K, synth.BF16, 8000 + K + M) for K in (4096, 11008)}
             ys = [torch.empty((M, c.N), dtype=torch.bfloat16, device="cuda") for c, *_ in layers]
 
@@ -794,7 +909,11 @@ def run_stack(W4, synth, torch):
             res[key] = {"ms_per_step": round(ms, 3), "GBps": round(gbps, 1),
                         "frac_hbm_peak": round(gbps / HBM_PEAK_GBS, 4), "weight_GB": round(nbytes / 1e9, 3)}
             log(f"  full stack {key}: {res[key]}")
-            del ys, xs
+            c, qw, s, z = layers[-1]          # the last layer's down projection
+            step(0)
+            Wd = synth.weights_device(c.N, c.K, c.w_sigma, synth.seeds(c.config, c.layer)[0])
+            samples.append(parity_sample(f"C5_{key}_down", 1, c.g, c.scheme, Wd, qw, s, z, xs[c.K], ys[-1], torch, np))
+            del ys, xs, Wd
         del layers
         torch.cuda.empty_cache()
     # context: the same step with q, k, v and gate, up concatenated along N (one launch each,

@@ -105,10 +105,14 @@ int w4a16_quantize_pack(const float* W, int64_t N, int64_t K, int64_t group_size
  *   qweight  [N, K/8] int32, device, 16-byte aligned.
  *   scales   [N, K/g] fp16 bits, device, 2-byte aligned.
  *   zeros    [N, K/g] fp16 bits, device, 2-byte aligned, or NULL (all zero points 8).
- *            Zero points must be integers with -480 <= z <= 480 (the quantizer gives
- *            z in [0, 15] for every group whose range contains 0; larger |z| only arise
- *            for a group far narrower than its distance from 0).
+ *            Zero points must be integers with |z| <= 2048, the range w4a16_quantize_pack
+ *            emits (z is in [0, 15] for every group whose range contains 0; larger |z|
+ *            arise for a group far narrower than its distance from 0).  Every kernel path
+ *            takes the whole range: the decode kernels and the bf16 GEMM apply z to fp32
+ *            partial sums; the fp16 GEMM rounds s * (u - z) once to fp16 per weight, with
+ *            u - z exact for z >= -2033 and rounded to an even integer below.
  *   Y        out [M, N], same dtype as X, device, 2-byte aligned.
+ * Other zero points give unspecified output (never an out-of-bounds access).
  */
 int w4a16_linear(const void* X, int dtype, int64_t M, int64_t N, int64_t K, int64_t group_size,
                  const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
@@ -391,10 +395,12 @@ int w4a16_w8a16_quantize_pack(const float* W, int64_t N, int64_t K, int64_t grou
 
 /*
  * w4a16_w8a16_linear -- Y[M, N] = X[M, K] . W_hat[N, K]^T, W_hat[n, k] = s (u - z) from the
- * 8-bit codes, dequantized inside the kernel (the codes enter the products exactly and the
- * group's s and z are applied to the fp32 partial sums); fp32 accumulation, Y rounded once to
- * the activation dtype.  Arguments as for w4a16_linear with qweight [N, K/4]; zeros NULL means
- * all zero points 128; any integer zero point |z| <= 2048.  Kernels: a weight-streaming GEMV
+ * 8-bit codes, dequantized inside the kernel (the GEMV and the bf16 GEMM multiply the exact
+ * codes and apply the group's s and z to fp32 partial sums; the fp16 GEMM rounds s * (u - z)
+ * once to fp16 per weight, u - z exact for z >= -1793 and rounded to an even integer below);
+ * fp32 accumulation, Y rounded once to the activation dtype.  Arguments as for w4a16_linear
+ * with qweight [N, K/4]; zeros NULL means all zero points 128; any integer zero point
+ * |z| <= 2048 (the range w4a16_w8a16_quantize_pack emits).  Kernels: a weight-streaming GEMV
  * for M <= 16 (when N * K < 2^31), else the tiled MFMA GEMM, which needs K and g to be
  * multiples of 64 (W4A16_ERR_PATH otherwise).
  */

@@ -295,10 +295,10 @@ def test_repeat_determinism():
 
 
 # ------------------------------------------------------- full-size workloads
-def _full_size(case: Case, n_rows: int = 48, m_rows: int | None = None):
+def _full_size(case: Case, n_rows: int = 1024, m_rows: int | None = None):
     """Full-size problem: GPU quantizes and multiplies the whole layer; the oracle checks
-    sampled output rows n (bit-exact packing and Y columns) and, for large M, sampled
-    activation rows m."""
+    ``n_rows`` sampled output rows n (bit-exact packing and Y columns) and, for large M,
+    sampled activation rows m."""
     W, X = case.make()
     Wt = torch.from_numpy(W).cuda()
     qw, sc, z = W4.quantize_pack(Wt, case.g, case.scheme)
@@ -306,7 +306,7 @@ def _full_size(case: Case, n_rows: int = 48, m_rows: int | None = None):
     Y = W4.linear(x_to_torch(X, case.dtype), qw, sc, z, case.g)
     torch.cuda.synchronize()
     rng = np.random.default_rng(case.config * 1000 + case.M)
-    ns = np.unique(np.concatenate([[0, case.N - 1], rng.choice(case.N, n_rows, replace=False)]))
+    ns = np.unique(np.concatenate([[0, case.N - 1], rng.choice(case.N, min(n_rows, case.N), replace=False)]))
     ms = np.arange(case.M) if m_rows is None or case.M <= m_rows else \
         np.unique(np.concatenate([[0, case.M - 1], rng.choice(case.M, m_rows, replace=False)]))
     codes, s_ref, z_ref = oracle.quantize(W[ns], case.g, case.scheme)
@@ -322,7 +322,7 @@ def _full_size(case: Case, n_rows: int = 48, m_rows: int | None = None):
 # every case of the single-layer workloads: the 7B-like decode sweep (M = 1..16), the
 # 70B-like decode shapes with outlier channels and weights (bf16), and the prefill grid
 # (M = 256 / 1024 / 4096, g = 64 / 128, symmetric and asymmetric), each checked before the
-# benchmark times it
+# benchmark times it, on 1024 output columns (all activation rows up to M = 64, else 64)
 FULL = [c for cfg in (1, 2, 3, 4) for c in config_cases(cfg)]
 
 

@@ -69,8 +69,8 @@ def test_full_size_sampled(M, K, N):
     qw, s, z = W4.quantize_pack(torch.from_numpy(W).cuda(), g, W4.ASYM)
     Y = W4.linear_ws(x_to_torch(X, FP16), qw, s, z, g)
     torch.cuda.synchronize()
-    ns = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 48, replace=False)]))
-    ms = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 48, replace=False)]))
+    ns = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 1024, replace=False)]))
+    ms = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 64, replace=False)]))
     codes, s_ref, z_ref = oracle.quantize(W[ns], g, oracle.ASYM)
     qn = oracle.pack(codes)
     idx = torch.from_numpy(ns).cuda()

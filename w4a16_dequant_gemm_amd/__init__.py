@@ -63,6 +63,42 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"activations must be float16 or bfloat16, got {t.dtype}")
 
 
+def _check_linear(X, qweight, scales, zeros, group_size: int, codes_per_word: int):
+    """Argument checks shared by the linear calls: dtypes, 2-D contiguous GPU tensors on the
+    device of ``X``, ``qweight [N, K/codes_per_word]``, ``scales`` and ``zeros`` (if given)
+    ``[N, K/group_size]``.  Returns ``(M, K, N)``."""
+    _need(X, "X", X.dtype, 2)
+    _need(qweight, "qweight", torch.int32, 2)
+    _need(scales, "scales", torch.float16, 2)
+    if zeros is not None:
+        _need(zeros, "zeros", torch.float16, 2)
+    M, K = X.shape
+    N = qweight.shape[0]
+    if qweight.shape[1] * codes_per_word != K:
+        raise ValueError(f"qweight must be [N, K/{codes_per_word}]")
+    if group_size <= 0 or K % group_size or tuple(scales.shape) != (N, K // group_size):
+        raise ValueError("scales must be [N, K/group_size]")
+    if zeros is not None and zeros.shape != scales.shape:
+        raise ValueError("zeros must match scales")
+    for t, name in ((qweight, "qweight"), (scales, "scales"), (zeros, "zeros")):
+        if t is not None and t.device != X.device:
+            raise ValueError(f"{name} must be on the device of X")
+    return M, K, N
+
+
+def _out(out, X, M: int, N: int) -> torch.Tensor:
+    """The output tensor: allocated ``[M, N]`` in the dtype of ``X``, or a caller tensor
+    checked for dtype, shape, device and contiguity."""
+    if out is None:
+        return torch.empty((M, N), dtype=X.dtype, device=X.device)
+    _need(out, "out", X.dtype, 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out must be [M, N]")
+    if out.device != X.device:
+        raise ValueError("out must be on the device of X")
+    return out
+
+
 def abi_version() -> int:
     return lib().w4a16_abi_version()
 
@@ -103,25 +139,8 @@ def linear(X: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zeros, 
            path: int = PATH_AUTO, out: torch.Tensor | None = None) -> torch.Tensor:
     """``Y [M, N] = X [M, K] . dequant(qweight)^T`` in the dtype of ``X``."""
     dt = _dtype_code(X)
-    _need(X, "X", X.dtype, 2)
-    _need(qweight, "qweight", torch.int32, 2)
-    _need(scales, "scales", torch.float16, 2)
-    if zeros is not None:
-        _need(zeros, "zeros", torch.float16, 2)
-    M, K = X.shape
-    N = qweight.shape[0]
-    if qweight.shape[1] * 8 != K:
-        raise ValueError("qweight must be [N, K/8]")
-    if group_size <= 0 or K % group_size or tuple(scales.shape) != (N, K // group_size):
-        raise ValueError("scales must be [N, K/group_size]")
-    if zeros is not None and zeros.shape != scales.shape:
-        raise ValueError("zeros must match scales")
-    if out is None:
-        out = torch.empty((M, N), dtype=X.dtype, device=X.device)
-    else:
-        _need(out, "out", X.dtype, 2)
-        if tuple(out.shape) != (M, N):
-            raise ValueError("out must be [M, N]")
+    M, K, N = _check_linear(X, qweight, scales, zeros, group_size, 8)
+    out = _out(out, X, M, N)
     st = lib().w4a16_linear_ex(X.data_ptr(), dt, M, N, K, group_size, qweight.data_ptr(),
                                scales.data_ptr(), zeros.data_ptr() if zeros is not None else None,
                                out.data_ptr(), path, _stream())
@@ -142,20 +161,15 @@ def linear_ws(X: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zero
     """:func:`linear` with a workspace for the tile-starved prefill shapes (split K, partial
     tiles summed in fixed order).  ``work``: float32 device tensor (allocated here if None)."""
     dt = _dtype_code(X)
-    _need(X, "X", X.dtype, 2)
-    _need(qweight, "qweight", torch.int32, 2)
-    _need(scales, "scales", torch.float16, 2)
-    M, K = X.shape
-    N = qweight.shape[0]
-    if qweight.shape[1] * 8 != K or tuple(scales.shape) != (N, K // group_size):
-        raise ValueError("qweight must be [N, K/8] and scales [N, K/group_size]")
+    M, K, N = _check_linear(X, qweight, scales, zeros, group_size, 8)
     need = linear_workspace(M, N, K, group_size, dt)
     if work is None and need > 0:
         work = torch.empty((need + 3) // 4, dtype=torch.float32, device=X.device)
-    if work is not None and (work.dtype != torch.float32 or not work.is_cuda):
-        raise ValueError("work must be a float32 device tensor")
-    if out is None:
-        out = torch.empty((M, N), dtype=X.dtype, device=X.device)
+    if work is not None:
+        _need(work, "work", torch.float32, work.dim())
+        if work.device != X.device:
+            raise ValueError("work must be on the device of X")
+    out = _out(out, X, M, N)
     st = lib().w4a16_linear_ws(X.data_ptr(), dt, M, N, K, group_size, qweight.data_ptr(), scales.data_ptr(),
                                zeros.data_ptr() if zeros is not None else None, out.data_ptr(),
                                work.data_ptr() if work is not None else None,
@@ -199,25 +213,8 @@ def w8a16_linear(X: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, z
     """``Y [M, N] = X [M, K] . dequant(qweight)^T`` with 8-bit codes ``qweight int32 [N, K/4]``
     (the weight-streaming GEMV for M <= 16, the tiled MFMA GEMM above)."""
     dt = _dtype_code(X)
-    _need(X, "X", X.dtype, 2)
-    _need(qweight, "qweight", torch.int32, 2)
-    _need(scales, "scales", torch.float16, 2)
-    if zeros is not None:
-        _need(zeros, "zeros", torch.float16, 2)
-    M, K = X.shape
-    N = qweight.shape[0]
-    if qweight.shape[1] * 4 != K:
-        raise ValueError("qweight must be [N, K/4]")
-    if group_size <= 0 or K % group_size or tuple(scales.shape) != (N, K // group_size):
-        raise ValueError("scales must be [N, K/group_size]")
-    if zeros is not None and zeros.shape != scales.shape:
-        raise ValueError("zeros must match scales")
-    if out is None:
-        out = torch.empty((M, N), dtype=X.dtype, device=X.device)
-    else:
-        _need(out, "out", X.dtype, 2)
-        if tuple(out.shape) != (M, N):
-            raise ValueError("out must be [M, N]")
+    M, K, N = _check_linear(X, qweight, scales, zeros, group_size, 4)
+    out = _out(out, X, M, N)
     st = lib().w4a16_w8a16_linear_ex(X.data_ptr(), dt, M, N, K, group_size, qweight.data_ptr(),
                                      scales.data_ptr(), zeros.data_ptr() if zeros is not None else None,
                                      out.data_ptr(), path, _stream())

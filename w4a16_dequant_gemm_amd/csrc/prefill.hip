@@ -249,6 +249,33 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------------------------
+// Exact fp16 codes for the fp16 kernels that dequantize to s * (u - z) before the MFMA.
+//
+// A 16-bit integer add on fp16 bit patterns builds the fp16 value 1536 + (u - z) + D exactly
+// while that value stays in [1024, 2048), where fp16 values are the consecutive integers.
+// The shift D is a multiple of 512 picked per (row, group) so that every code u of the row's
+// group lands there: D = 512 * floor((z - c + 256) / 512), c the middle of the code range
+// (8 for 4-bit codes, 128 for 8-bit codes), gives D - z in [-256 - c, 255 - c].  Subtracting
+// 1536 + D, a multiple of 512 in [-512, 3584] and hence an fp16 value, then leaves exactly
+// u - z whenever |u - z| <= 2048: for every code when umax - 2048 <= z <= 2048 (umax = 15 or
+// 255), and the multiply by s is the only rounding.  Below that, down to z = -2048, a
+// difference u - z > 2048 rounds to an even integer first (relative error <= 2^-11).
+struct CodeWindow {
+    uint32_t add;   // pair of 16-bit integers 0x6600 - z + D
+    uint32_t sub;   // pair of fp16 values 1536 + D
+};
+
+template <int BITS>
+__device__ __forceinline__ CodeWindow code_window(float zf) {
+    const int z = (int)zf;
+    constexpr int c = BITS == 4 ? 8 : 128;
+    const int D = ((z - c + 256) >> 9) * 512;
+    const uint32_t a = (uint32_t)(0x6600 - z + D) & 0xFFFFu;
+    const uint32_t b = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(float)(1536 + D));
+    return CodeWindow{a | (a << 16), b | (b << 16)};
+}
+
+// ---------------------------------------------------------------------------------
 // fp16 kernel: dequantize once per block into LDS.
 //
 // Block tile 256 (M) x 128 (N), k-step 32, 256 threads = 4 waves in a 2 x 2 grid, wave
@@ -257,8 +284,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restr
 //     unchanged (natural column order),
 //   - loads 8 bytes = 16 codes of one weight row and writes the dequantized fp16 weights
 //     s * (u - z) to LDS: the code pair (u, u') is built as the fp16 bits of
-//     1536 + (u - z) by one packed 16-bit integer add (exact while |u - z| < 512), then
-//     1536 is subtracted (exact) and the pair is multiplied by s (one rounding),
+//     1536 + (u - z) + D by one packed 16-bit integer add (CodeWindow), then
+//     1536 + D is subtracted (exact) and the pair is multiplied by s (one rounding),
 // so every weight is dequantized exactly once per block -- the pages' "dequantize the
 // INT4 weight to FP16, then multiply" with the FP16 weight living only in LDS.  The
 // MFMAs read both operands from LDS in natural order; rows are padded by 16 bytes,
@@ -307,8 +334,10 @@ __global__ __launch_bounds__(256, 2) void prefill_f16_kernel(
         wq[0] = v.x;
         wq[1] = v.y;
     };
-    // dequantization constants of the current group: (0x6600 - z) pair and s pair
-    uint32_t zbias = 0, spair = 0;
+    // dequantization constants of the current group: the code window of its zero point
+    // and the s pair
+    CodeWindow win{0u, 0u};
+    uint32_t spair = 0;
     int cur_group = -1;
     auto store_step = [&](int buf, int step) {
         const int grp = group_of(step * F_BK, gshift);
@@ -316,14 +345,14 @@ __global__ __launch_bounds__(256, 2) void prefill_f16_kernel(
             cur_group = grp;
             const uint16_t sb = scales[(size_t)wrow * G + grp];
             const float z = has_zeros ? h2f(zsrc[(size_t)wrow * G + grp]) : 8.0f;
-            const uint32_t zb = (uint32_t)(0x6600 - (int)z) & 0xFFFFu;
-            zbias = zb | (zb << 16);
+            win = code_window<4>(z);
             spair = (uint32_t)sb | ((uint32_t)sb << 16);
         }
         uint16_t* arow = &As[buf][tid * F_LDA];
 #pragma unroll
         for (int b = 0; b < 4; ++b) *reinterpret_cast<u32x4*>(arow + 8 * b) = xa[b];
-        const f16x2 bias = {(_Float16)1536.0f, (_Float16)1536.0f};
+        const u16x2 zbias = __builtin_bit_cast(u16x2, win.add);
+        const f16x2 bias = __builtin_bit_cast(f16x2, win.sub);
         const f16x2 sv = __builtin_bit_cast(f16x2, spair);
         uint32_t d[8];
 #pragma unroll
@@ -333,11 +362,10 @@ __global__ __launch_bounds__(256, 2) void prefill_f16_kernel(
             const uint32_t t1 = (w >> 4) & 0x0F0F0F0Fu;   // u1 u3 u5 u7
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                // (u_{2p}, u_{2p+1}) as 16-bit integers, then the fp16 bits of 1536 + u - z
+                // (u_{2p}, u_{2p+1}) as 16-bit integers, then the fp16 bits of 1536 + u - z + D
                 const uint32_t uu = perm(t1, t0, 0x0C040C00u + 0x00010001u * p);
-                const uint32_t biased = __builtin_bit_cast(uint32_t,
-                    __builtin_bit_cast(u16x2, uu) + __builtin_bit_cast(u16x2, zbias));
-                const f16x2 code = __builtin_bit_cast(f16x2, biased) - bias;    // exact
+                const uint32_t biased = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, uu) + zbias);
+                const f16x2 code = __builtin_bit_cast(f16x2, biased) - bias;    // exact u - z
                 d[4 * wi + p] = __builtin_bit_cast(uint32_t, code * sv);        // one rounding
             }
         }
@@ -410,9 +438,9 @@ __global__ __launch_bounds__(256, 2) void prefill_f16_kernel(
 //   Weights: each wave dequantizes exactly the 64 weight rows it multiplies, in
 //     registers (none goes through LDS, none is dequantized twice): lane (n, h) loads the
 //     16 bytes holding columns 32 h .. 32 h + 31 of the step for each of its two rows, one
-//     step ahead, and turns word j into the fp16 B fragment of MFMA j with the 1536-bias
-//     construction (exact 1536 + u - z, exact subtraction, one rounding in the multiply
-//     by s).  MFMA j covers columns 8 j .. 8 j + 7 and 32 + 8 j .. + 7; the activation
+//     step ahead, and turns word j into the fp16 B fragment of MFMA j with the code-window
+//     construction (CodeWindow: exact 1536 + u - z + D, exact subtraction of 1536 + D, one
+//     rounding in the multiply by s).  MFMA j covers columns 8 j .. 8 j + 7 and 32 + 8 j .. + 7; the activation
 //     fragment of lane (m, h) reads the same columns.  The next step's dequantization is
 //     interleaved with this step's MFMAs.
 //   Block order: consecutive block indices run on different XCDs; blocks are renumbered
@@ -422,7 +450,7 @@ constexpr int W_BM = 256, W_BN = 256, W_BK = 64;     // K % 128 == 0: steps in p
 
 // BITS = 8 (W8A16): lane (n, h) loads the 32 bytes of columns 32h .. 32h + 31 (two 16-byte
 // loads) and MFMA j takes words 2j and 2j + 1 (one byte permute per pair instead of the nibble
-// masks; the 1536-bias construction is exact for |u - z| < 512, the implicit symmetric zero
+// masks; the code window covers the 8-bit codes the same way, the implicit symmetric zero
 // point is 128).
 // Split K (part != NULL): block (x, y) runs k-steps [y * spl, (y + 1) * spl) of its tile and
 // stores the fp32 partial tile to part[y][M][N]; splitk_reduce_kernel sums the partials in
@@ -503,14 +531,23 @@ __global__ __launch_bounds__(256, 1) void prefill_f16_wide_kernel(
             st.z[ns] = __builtin_amdgcn_raw_buffer_load_b16(rz, szoff[ns] + grp2, 0, 0);
         }
     };
+    // code windows of a stage's two rows (per row and group, see CodeWindow)
+    struct WConst {
+        CodeWindow win[2];
+    };
+    auto stage_const = [&](const WStage& st) {
+        WConst c;
+#pragma unroll
+        for (int ns = 0; ns < 2; ++ns)
+            c.win[ns] = code_window<BITS>(HZ ? h2f(st.z[ns]) : (BITS == 4 ? 8.0f : 128.0f));
+        return c;
+    };
     // word j of both rows of a stage -> the fp16 B fragments of MFMA j: b[ns][j][4]
-    auto dequant_word = [&](const WStage& st, int j, uint32_t b[2][4][4]) {
-        const f16x2 bias = {(_Float16)1536.0f, (_Float16)1536.0f};
+    auto dequant_word = [&](const WStage& st, const WConst& wc, int j, uint32_t b[2][4][4]) {
 #pragma unroll
         for (int ns = 0; ns < 2; ++ns) {
-            const float z = HZ ? h2f(st.z[ns]) : (BITS == 4 ? 8.0f : 128.0f);
-            const uint32_t zb = (uint32_t)(0x6600 - (int)z) & 0xFFFFu;
-            const u16x2 zbias = __builtin_bit_cast(u16x2, zb | (zb << 16));
+            const u16x2 zbias = __builtin_bit_cast(u16x2, wc.win[ns].add);
+            const f16x2 bias = __builtin_bit_cast(f16x2, wc.win[ns].sub);
             const f16x2 sv = __builtin_bit_cast(f16x2, (uint32_t)st.s[ns] | ((uint32_t)st.s[ns] << 16));
             uint32_t t0, t1;
             if constexpr (BITS == 4) {
@@ -529,8 +566,8 @@ __global__ __launch_bounds__(256, 1) void prefill_f16_wide_kernel(
                 else
                     uu = p < 2 ? perm(0u, t0, 0x0C010C00u + 0x00020002u * p)
                                : perm(0u, t1, 0x0C010C00u + 0x00020002u * (p - 2));
-                const u16x2 biased = __builtin_bit_cast(u16x2, uu) + zbias;     // 1536 + u - z
-                const f16x2 code = __builtin_bit_cast(f16x2, biased) - bias;    // exact
+                const u16x2 biased = __builtin_bit_cast(u16x2, uu) + zbias;     // 1536 + u - z + D
+                const f16x2 code = __builtin_bit_cast(f16x2, biased) - bias;    // exact u - z
                 b[ns][j][p] = __builtin_bit_cast(uint32_t, code * sv);          // one rounding
             }
         }
@@ -554,6 +591,7 @@ __global__ __launch_bounds__(256, 1) void prefill_f16_wide_kernel(
     // per MFMA group so the VALU work hides under the matrix instructions.
     auto compute = [&](int buf, const uint32_t bc[2][4][4], const WStage& nx, uint32_t bn[2][4][4]) {
         const u32x4* A = As[buf];
+        const WConst nc = stage_const(nx);
         u32x4 fa[8], fb[8];        // activation fragments one MFMA group ahead
 #pragma unroll
         for (int ms = 0; ms < 8; ++ms) fa[ms] = A[ms * 256 + fslot[0]];
@@ -571,7 +609,7 @@ __global__ __launch_bounds__(256, 1) void prefill_f16_wide_kernel(
 #pragma unroll
                 for (int ns = 0; ns < 2; ++ns) acc[ms][ns] = Mfma<DT_F16>::run(af, bc[ns][j], acc[ms][ns]);
             }
-            dequant_word(nx, j, bn);
+            dequant_word(nx, nc, j, bn);
             // interleave: one fragment read and a few dequant instructions per MFMA pair
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -594,7 +632,7 @@ __global__ __launch_bounds__(256, 1) void prefill_f16_wide_kernel(
     load_w(p0, sb);
     load_w(p1, min(sb + 1, se - 1));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dequant_word(p0, j, b0);
+    for (int j = 0; j < 4; ++j) dequant_word(p0, stage_const(p0), j, b0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     for (int step = sb; step < se; step += 2) {
