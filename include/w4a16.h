@@ -57,7 +57,8 @@ typedef enum {
     W4A16_ERR_DTYPE = -5,   /* unknown activation dtype                             */
     W4A16_ERR_SCHEME = -6,  /* unknown quantization scheme                          */
     W4A16_ERR_HIP = -7,     /* the HIP runtime reported an error at launch          */
-    W4A16_ERR_PATH = -8     /* a forced kernel path cannot run this problem         */
+    W4A16_ERR_PATH = -8,    /* a forced kernel path cannot run this problem         */
+    W4A16_ERR_SCRATCH = -9  /* the static scratch buffer is too small (see below)    */
 } w4a16_status;
 
 typedef enum { W4A16_F16 = 0, W4A16_BF16 = 1 } w4a16_dtype;
@@ -368,6 +369,26 @@ int64_t w4a16_linear_workspace(int64_t M, int64_t N, int64_t K, int64_t group_si
 int w4a16_linear_ws(const void* X, int dtype, int64_t M, int64_t N, int64_t K, int64_t group_size,
                     const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros, void* Y, float* work,
                     int64_t work_bytes, void* stream);
+
+/*
+ * w4a16_linear_ws_noalloc -- w4a16_linear_ws with the library's own static scratch buffer as
+ * the workspace, so the call allocates nothing and needs no caller memory beyond X, the weights
+ * and Y.  For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).
+ *   The buffer holds 64 MiB per GPU: a file-scope device array, so every GPU the library runs
+ *   on holds its own copy until the process ends.  Its address on the current device is looked
+ *   up on the first call on that device (no allocation); the stream must belong to the current
+ *   device.  The split never needs more than 64 MiB (at most 256 partial fp32 tiles of
+ *   256 x 256); a problem that would (w4a16_linear_workspace(...) > 64 MiB) returns
+ *   W4A16_ERR_SCRATCH without launching.  Problems that do not split K run as w4a16_linear.
+ *   Results are bit-identical to w4a16_linear_ws with a large enough workspace.
+ *   Every call on one GPU shares that GPU's buffer and leaves its partial tiles in it: calls
+ *   that overlap on one GPU (several streams, several host threads) race and give undefined
+ *   results; serialize them.  Other arguments and errors as for w4a16_linear.
+ */
+int w4a16_linear_ws_noalloc(const void* X, int dtype, int64_t M, int64_t N, int64_t K, int64_t group_size,
+                            const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros, void* Y,
+                            void* stream);
 
 /* ------------------------------------------------------------------------------------
  * W8A16: the same weight-only layer with 8-bit codes, four per 32-bit word (byte k % 4 of

@@ -54,7 +54,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_abi_version_and_strerror(lib):
     assert lib.w4a16_abi_version() == 1
-    for st in range(-8, 1):
+    for st in range(-9, 1):
         assert lib.w4a16_strerror(st)
     assert lib.w4a16_strerror(-99) == b"unknown status"
 
@@ -307,3 +307,29 @@ def test_linear_workspace_sizes(lib):
 def test_linear_ws_rejects_invalid_arguments(lib):
     assert lib.w4a16_linear_ws(None, 0, 256, 64, 128, 128, B, C, D, A, A, 0, None) == L.ERR_NULL
     assert lib.w4a16_linear_ws(A, 0, 256, 64, 128, 128, B, C, D, A + 4096, A + 4, 1 << 20, None) == L.ERR_ALIGN
+
+
+def test_linear_ws_noalloc_rejects_invalid_arguments(lib):
+    # host-side checks run before the scratch buffer is looked up (no GPU needed)
+    f = lib.w4a16_linear_ws_noalloc
+    assert f(None, 0, 256, 64, 128, 128, B, C, D, A, None) == L.ERR_NULL
+    assert f(A, 0, 256, 64, 128, 128, B, C, D, None, None) == L.ERR_NULL
+    assert f(A + 4, 0, 256, 64, 128, 128, B, C, D, A + 4096, None) == L.ERR_ALIGN
+    assert f(A, 3, 256, 64, 128, 128, B, C, D, A + 4096, None) == L.ERR_DTYPE
+    assert f(A, 0, 0, 64, 128, 128, B, C, D, A + 4096, None) == L.ERR_SHAPE
+    assert f(A, 0, 256, 64, 100, 100, B, C, D, A + 4096, None) == L.ERR_SHAPE
+    assert f(A, 0, 256, 64, 128, 48, B, C, D, A + 4096, None) == L.ERR_GROUP
+
+
+def test_static_scratch_covers_every_split():
+    # the no-allocation entry point's 64 MiB buffer holds the workspace of every split the
+    # planner makes (at most 256 partial fp32 tiles of 256 x 256)
+    lib = L.lib()
+    worst = 0
+    for M in (33, 100, 255, 256, 257, 511, 1024, 2047, 4096, 8192, 16384, 32512):
+        for N in (1, 255, 256, 700, 2048, 4096, 11008, 28672):
+            for K in (128, 2048, 4096, 8320, 11008, 28672):
+                need = lib.w4a16_linear_workspace(M, N, K, 128, 0)
+                assert need >= 0
+                worst = max(worst, need)
+    assert 0 < worst <= 64 * 2 ** 20

@@ -13,8 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libw4a16.so")
 
 OK = 0
-ERR_NULL, ERR_SHAPE, ERR_GROUP, ERR_ALIGN, ERR_DTYPE, ERR_SCHEME, ERR_HIP, ERR_PATH = \
-    -1, -2, -3, -4, -5, -6, -7, -8
+ERR_NULL, ERR_SHAPE, ERR_GROUP, ERR_ALIGN, ERR_DTYPE, ERR_SCHEME, ERR_HIP, ERR_PATH, ERR_SCRATCH = \
+    -1, -2, -3, -4, -5, -6, -7, -8, -9
 F16, BF16 = 0, 1
 ASYM, SYM = 0, 1
 PATH_AUTO, PATH_GEMV, PATH_SKINNY, PATH_PREFILL = 0, 1, 2, 3
@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
     L.w4a16_linear_workspace.argtypes = [i64, i64, i64, i64, i32]
     L.w4a16_linear_ws.restype = i32
     L.w4a16_linear_ws.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, i64, vp]
+    L.w4a16_linear_ws_noalloc.restype = i32
+    L.w4a16_linear_ws_noalloc.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, vp, vp, vp]
     L.w4a16_w8a16_quantize_pack.restype = i32
     L.w4a16_w8a16_quantize_pack.argtypes = [vp, i64, i64, i64, i32, vp, vp, vp, vp]
     L.w4a16_w8a16_linear.restype = i32

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw4a16.so")
 OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["api.cpp", "quantize.hip", "gemv.hip", "skinny.hip", "decode.hip", "prefill.hip", "gptq.hip",
-           "awq.hip", "w8a8.hip", "kv.hip", "w8a16.hip"]
+           "awq.hip", "w8a8.hip", "kv.hip", "w8a16.hip", "scratch.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

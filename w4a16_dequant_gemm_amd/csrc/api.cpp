@@ -153,6 +153,8 @@ const char* w4a16_strerror(int status) {
         case W4A16_ERR_SCHEME: return "unknown quantization scheme";
         case W4A16_ERR_HIP: return "HIP runtime error at launch";
         case W4A16_ERR_PATH: return "the requested kernel path does not support this problem";
+        case W4A16_ERR_SCRATCH:
+            return "the problem needs more workspace than the library's static scratch buffer (64 MiB)";
         default: return "unknown status";
     }
 }
@@ -446,6 +448,22 @@ int w4a16_linear_ws(const void* X, int dtype, int64_t M, int64_t N, int64_t K, i
     const long long need = w4a16::prefill_splitk_bytes(a);
     if (need > 0 && work && work_bytes >= need && w4a16::prefill_supports(a))
         return hip_status(w4a16::launch_prefill_splitk(a, work, static_cast<hipStream_t>(stream)));
+    return w4a16_linear_ex(X, dtype, M, N, K, group_size, qweight, scales, zeros, Y, W4A16_PATH_AUTO, stream);
+}
+
+int w4a16_linear_ws_noalloc(const void* X, int dtype, int64_t M, int64_t N, int64_t K, int64_t group_size,
+                            const int32_t* qweight, const uint16_t* scales, const uint16_t* zeros, void* Y,
+                            void* stream) {
+    LinearArgs a;
+    const int st = validate_linear(X, dtype, M, N, K, group_size, qweight, scales, zeros, Y, &a);
+    if (st != W4A16_OK) return st;
+    const long long need = w4a16::prefill_splitk_bytes(a);
+    if (need > w4a16::kScratchBytes) return W4A16_ERR_SCRATCH;
+    if (need > 0 && w4a16::prefill_supports(a)) {
+        float* work = nullptr;
+        if (w4a16::scratch_device_ptr(&work) != hipSuccess) return W4A16_ERR_HIP;
+        return hip_status(w4a16::launch_prefill_splitk(a, work, static_cast<hipStream_t>(stream)));
+    }
     return w4a16_linear_ex(X, dtype, M, N, K, group_size, qweight, scales, zeros, Y, W4A16_PATH_AUTO, stream);
 }
 

@@ -38,6 +38,10 @@ hipError_t launch_prefill(const LinearArgs& a, hipStream_t s);
 int prefill_splitk_splits(const LinearArgs& a);
 long long prefill_splitk_bytes(const LinearArgs& a);
 hipError_t launch_prefill_splitk(const LinearArgs& a, float* work, hipStream_t s);
+// the library's static per-device scratch (scratch.hip): its size, and its device address on
+// the current device (looked up once per device)
+constexpr long long kScratchBytes = 64LL << 20;
+hipError_t scratch_device_ptr(float** out);
 // W8A16 (8-bit codes, four per word): quantize-pack, the decode GEMV and the tiled MFMA GEMM
 hipError_t launch_quantize_pack8(const float* W, int N, int K, int g, int scheme, uint32_t* qw,
                                  uint16_t* scales, uint16_t* zeros, hipStream_t s);
