@@ -39,7 +39,8 @@ GROUP = 128
 # Kernel instantiation serving each layer at M = 1 (fp16, g = 128), as rocprofv3 names it.
 KERNEL_NAMES = {(4096, 4096): "gemv_stream_kernel<0, 1, 2, 1, 8, 0>",
                 (4096, 11008): "gemv_stream_kernel<0, 1, 2, 2, 8, 0>",
-                (11008, 4096): "gemv_stream_kernel<0, 1, 6, 1, 8, 0>"}
+                (11008, 4096): "gemv_stream_kernel<0, 1, 6, 1, 8, 0>",
+                "step": "gemv_group_kernel<0>"}     # the whole M = 1 step in one grouped launch
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "w4a16_dequant_gemm_amd", "csrc", f)
                   for f in ("gemv.hip", "common.h")]
@@ -59,14 +60,17 @@ def source_hash() -> str:
     return h.hexdigest()
 
 
-def traffic_file(K: int, N: int) -> str:
+def traffic_file(shape) -> str:
+    if shape == "step":
+        return os.path.join(PROFILES, "traffic_gemv_group_m1_7b_step.json")
+    K, N = shape
     return os.path.join(PROFILES, f"traffic_gemv_stream_m1_k{K}_n{N}.json")
 
 
-def traffic_record(K: int, N: int):
-    """HBM bytes per launch from the committed counter summary, if it was taken on the
-    current kernel source (else None)."""
-    path = traffic_file(K, N)
+def traffic_record(shape):
+    """HBM bytes per launch from the committed counter summary of a layer (K, N) or of the
+    grouped step ("step"), if it was taken on the current kernel source (else None)."""
+    path = traffic_file(shape)
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -304,28 +308,38 @@ def cpu_baseline_rows(oracle, np):
     return out
 
 
-def traffic_run(K: int, N: int, W4, synth, torch, np):
+def traffic_run(shape, W4, synth, torch, np):
     """Workload for the two counter passes: a plain elementwise copy (y = -x) of COPY_MIB
     MiB (calibration: known bytes read and written) five times, then 20 launches of the
-    layer's kernel at M = 1 over rotating weight copies."""
-    nbytes = weight_bytes(N, K, GROUP)
+    layer's kernel at M = 1 (shape (K, N)) or of the grouped M = 1 step ("step") over
+    rotating weight copies."""
+    shapes = SHAPES if shape == "step" else [shape]
+    nbytes = sum(weight_bytes(N, K, GROUP) for K, N in shapes)
     copies = max(2, int(np.ceil(2**30 / nbytes)))
-    L = Layer(K, N, GROUP, copies, 1000 + 10 * 2 + SHAPES.index((K, N)), W4, synth, torch)
-    del L.W
-    X = synth.activations_device(1, K, synth.FP16, 1015)
-    Y = torch.empty((1, N), dtype=torch.float16, device="cuda")
+    layers = [Layer(K, N, GROUP, copies, 1000 + 10 * 2 + SHAPES.index((K, N)), W4, synth, torch) for K, N in shapes]
+    for L in layers:
+        del L.W
+    xs = {K: synth.activations_device(1, K, synth.FP16, 1015) for K in (4096, 11008)}
+    ys = [torch.empty((1, L.N), dtype=torch.float16, device="cuda") for L in layers]
+
+    def run(i):
+        c = i % copies
+        if shape == "step":
+            W4.linear_batch([(xs[L.K], *L.copies[c], GROUP) for L in layers], outs=ys)
+        else:
+            W4.linear(xs[layers[0].K], *layers[0].copies[c], GROUP, out=ys[0])
     src = torch.ones(COPY_MIB << 19, dtype=torch.float16, device="cuda")
     dst = torch.empty_like(src)
     for i in range(3):
-        W4.linear(X, *L.copies[i % copies], GROUP, out=Y)
+        run(i)
     torch.cuda.synchronize()
     for _ in range(5):
         torch.neg(src, out=dst)          # one elementwise kernel: reads and writes COPY_MIB MiB
     torch.cuda.synchronize()
     for i in range(20):
-        W4.linear(X, *L.copies[(i + 3) % copies], GROUP, out=Y)
+        run(i + 3)
     torch.cuda.synchronize()
-    log(f"traffic run done: K={K} N={N}, {copies} weight copies, copy {COPY_MIB} MiB x5")
+    log(f"traffic run done: {shape}, {copies} weight copies, copy {COPY_MIB} MiB x5")
 
 
 def profile_run(name: str, W4, synth, torch):
@@ -425,13 +439,16 @@ def _counter_means(run_dir: str, counter: str):
     return vals
 
 
-def traffic_parse(fetch_dir: str, write_dir: str, K: int, N: int, commands, out_path=None):
+def traffic_parse(fetch_dir: str, write_dir: str, shape, commands, out_path=None):
     """Turn the FETCH_SIZE / WRITE_SIZE passes of traffic_run into HBM bytes per launch
-    of the layer's kernel, scaled by what the counters read for the known-size copy."""
-    kname = KERNEL_NAMES[(K, N)]
-    out = {"kernel": kname, "M": 1, "K": K, "N": N, "group_size": GROUP,
+    of the layer's (or the grouped step's) kernel, scaled by what the counters read for the
+    known-size copy."""
+    kname = KERNEL_NAMES[shape]
+    shapes = SHAPES if shape == "step" else [shape]
+    out = {"kernel": kname, "M": 1, "layers_KN": shapes, "group_size": GROUP,
            "source_sha256": source_hash(), "copy_bytes": COPY_MIB << 20,
-           "algorithmic_bytes_per_launch": weight_bytes(N, K, GROUP), "commands": commands}
+           "algorithmic_bytes_per_launch": sum(weight_bytes(N, K, GROUP) for K, N in shapes),
+           "commands": commands}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         vals = _counter_means(d, counter)
         kv = [v for name, vs in vals.items() if kname in name for v in vs]
@@ -446,7 +463,7 @@ def traffic_parse(fetch_dir: str, write_dir: str, K: int, N: int, commands, out_
     out["traffic_bytes_per_launch"] = round(out["fetch_kib_per_launch"] * 1024 * out["factor_fetch"] +
                                             out["write_kib_per_launch"] * 1024 * out["factor_write"])
     out["traffic_over_algorithmic"] = out["traffic_bytes_per_launch"] / out["algorithmic_bytes_per_launch"]
-    out_path = out_path or traffic_file(K, N)
+    out_path = out_path or traffic_file(shape)
     os.makedirs(os.path.dirname(out_path), exist_ok=True)
     with open(out_path, "w") as fh:
         json.dump(out, fh, indent=1)
@@ -462,9 +479,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--traffic-run", nargs=2, type=int, metavar=("K", "N"),
-                    help="counter workload: calibration copy + the layer's kernel at M = 1")
-    ap.add_argument("--traffic-parse", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "K", "N"),
+    ap.add_argument("--traffic-run", nargs="+", metavar="K N | step",
+                    help="counter workload: calibration copy + the layer's kernel at M = 1, or the "
+                         "grouped M = 1 step")
+    ap.add_argument("--traffic-parse", nargs="+", metavar="FETCH_DIR WRITE_DIR K N | step",
                     help="write profiles/traffic_*.json from the two counter passes")
     ap.add_argument("--traffic-commands", nargs="*", default=[],
                     help="the profiler command lines, recorded in the traffic file")
@@ -472,9 +490,11 @@ def main():
     ap.add_argument("--profile-run", choices=["prefill", "w8a8", "kv_batch", "decode_m16", "w8a16", "c3"],
                     help="a short fixed workload of one kernel family, for counter runs")
     args = ap.parse_args()
+    def shape_arg(v):
+        return "step" if v == ["step"] else (int(v[0]), int(v[1]))
     if args.traffic_parse:
-        f, w, K, N = args.traffic_parse
-        traffic_parse(f, w, int(K), int(N), args.traffic_commands, args.traffic_out)
+        f, w = args.traffic_parse[:2]
+        traffic_parse(f, w, shape_arg(args.traffic_parse[2:]), args.traffic_commands, args.traffic_out)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -492,7 +512,7 @@ def main():
     W4.lib()
     torch.cuda.set_device(0)
     if args.traffic_run:
-        traffic_run(args.traffic_run[0], args.traffic_run[1], W4, synth, torch, np)
+        traffic_run(shape_arg(args.traffic_run), W4, synth, torch, np)
         return
     if args.profile_run:
         profile_run(args.profile_run, W4, synth, torch)
@@ -518,7 +538,14 @@ def main():
 
     outs = [torch.empty((1, L.N), dtype=torch.float16, device="cuda") for L in layers]
 
+    # The step: the three layers are independent, so they run as one w4a16_linear_batch call,
+    # one grouped launch that streams all of their weights.  For comparison the same step with
+    # one w4a16_linear launch per layer.
     def step(i):
+        c = i % copies
+        W4.linear_batch([(xd, *L.copies[c], GROUP) for L, xd in zip(layers, xs_dev)], outs=outs)
+
+    def step_separate(i):
         c = i % copies
         for L, xd, o in zip(layers, xs_dev, outs):
             qw, s, z = L.copies[c]
@@ -533,17 +560,26 @@ def main():
     ms = time_graph(g_main, args.steps, torch)
     value = step_bytes / (ms * 1e-3) / 1e9
     log(f"step: {ms * 1e3:.1f} us, {value:.1f} GB/s (median of {REPEATS} replays of {args.steps} steps)")
-    # steady state (the same step, at least 200 back-to-back launches per replay)
-    ss_steps = max(args.steps, -(-200 // len(layers)))
-    ms_ss = ms if ss_steps == args.steps else time_loop(lambda i: step(i + args.warmup), ss_steps, torch)
-    log(f"steady state: {ms_ss * 1e3:.1f} us per step over {ss_steps * len(layers)} launches")
-    # the graph replays must reproduce the eager result of the last step
+    # the graph replays must reproduce the eager result of the last step, and the grouped
+    # launch the per-layer launches, bit for bit
     last = [o.clone() for o in outs]
     step(args.warmup + args.steps - 1)
     torch.cuda.synchronize()
     if not all(torch.equal(a, b) for a, b in zip(last, outs)):
         print(json.dumps({"metric": METRIC, "error": "graph replay differs from eager launch"}))
         sys.exit(1)
+    step_separate(args.warmup + args.steps - 1)
+    torch.cuda.synchronize()
+    if not all(torch.equal(a, b) for a, b in zip(last, outs)):
+        print(json.dumps({"metric": METRIC, "error": "grouped launch differs from per-layer launches"}))
+        sys.exit(1)
+    # steady state: the grouped step is one launch, so >= 200 steps per replay; its per-step
+    # time is the grouped kernel's average launch duration (the dominant and only kernel)
+    ss_steps = max(args.steps, 200)
+    ms_ss = time_loop(lambda i: step(i + args.warmup), ss_steps, torch)
+    log(f"steady state: {ms_ss * 1e3:.2f} us per grouped launch over {ss_steps} launches")
+    ms_sep = time_loop(lambda i: step_separate(i + args.warmup), max(args.steps, 67), torch)
+    log(f"separate launches: {ms_sep * 1e3:.1f} us per step")
 
     # per-layer launch durations (back-to-back launches of one kernel over the copies)
     per_layer = []
@@ -559,15 +595,14 @@ def main():
                           "path": W4.PATH_NAMES[W4.select_path(1, L.N, L.K, GROUP)],
                           "kernel": KERNEL_NAMES.get((L.K, L.N), "?")})
         log(f"  layer K={L.K} N={L.N}: {t * 1e3:.2f} us/launch {per_layer[-1]['GBps']:.0f} GB/s")
-    # dominant kernel: the layer with the longest launches (each layer runs one kernel)
-    dom = max(per_layer, key=lambda p: p["us"])
-    achieved = dom["bytes"] / (dom["us"] * 1e-6) / 1e9
-    traffic = traffic_record(dom["K"], dom["N"])
+    achieved = step_bytes / (ms_ss * 1e-3) / 1e9
+    traffic = traffic_record("step")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic["bytes_per_launch"] if traffic else None,
-                "kernel": f"{dom['kernel']} (M=1, K={dom['K']}, N={dom['N']})",
-                "avg_launch_us": round(dom["us"], 3), "bytes_per_launch": dom["bytes"]}
+                "kernel": f"{KERNEL_NAMES['step']} (M=1, the three layers in one launch)",
+                "avg_launch_us": round(ms_ss * 1e3, 3), "bytes_per_launch": step_bytes,
+                "launches_timed": ss_steps}
     if traffic:
         roofline["traffic_source"] = traffic["source"]
 
@@ -593,13 +628,15 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": "decode M=1 on 7B-like layers (K,N) = (4096,4096), "
-                               "(4096,11008), (11008,4096); g=128 asym uint4; fp16 activations",
+                               "(4096,11008), (11008,4096), independent; g=128 asym uint4; fp16 activations",
                    "M": 1, "group_size": GROUP, "scheme": "asym", "rotating_copies": copies,
                    "bytes_per_step": step_bytes, "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                   "launch": "one w4a16_linear_batch call per step (one grouped launch over the three layers)",
                    "timing": f"median of {REPEATS} graph replays of the {args.steps} timed steps",
-                   "steady_state": {"launches_per_replay": ss_steps * len(layers),
-                                    "us_per_step": round(ms_ss * 1e3, 3),
-                                    "GBps": round(step_bytes / (ms_ss * 1e-3) / 1e9, 1)}},
+                   "steady_state": {"launches_per_replay": ss_steps, "us_per_step": round(ms_ss * 1e3, 3),
+                                    "GBps": round(step_bytes / (ms_ss * 1e-3) / 1e9, 1)},
+                   "separate_launches": {"us_per_step": round(ms_sep * 1e3, 3),
+                                         "GBps": round(step_bytes / (ms_sep * 1e-3) / 1e9, 1)}},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extras": extras,
@@ -909,6 +946,26 @@ def run_stack(W4, synth, torch, np, samples):
             res[key] = {"ms_per_step": round(ms, 3), "GBps": round(gbps, 1),
                         "frac_hbm_peak": round(gbps / HBM_PEAK_GBS, 4), "weight_GB": round(nbytes / 1e9, 3)}
             log(f"  full stack {key}: {res[key]}")
+            if M == 1:
+                # the same step with each transformer layer's independent projections batched:
+                # w4a16_linear_batch over (q, k, v) and over (gate, up), then o and down alone
+                # (4 launches per layer instead of 7; the dependencies of a real layer kept)
+                def step_b(i, xs=xs, ys=ys, layers=layers):
+                    for l0 in range(0, len(layers), 7):
+                        grp = [(xs[c.K], qw, s, z, c.g) for c, qw, s, z in layers[l0:l0 + 7]]
+                        out = ys[l0:l0 + 7]
+                        W4.linear_batch(grp[0:3], outs=out[0:3])
+                        W4.linear(*grp[3], out=out[3])
+                        W4.linear_batch(grp[4:6], outs=out[4:6])
+                        W4.linear(*grp[6], out=out[6])
+                for i in range(2):
+                    step_b(i)
+                msb = time_loop(step_b, 5, torch)
+                gb = nbytes / (msb * 1e-3) / 1e9
+                res[key + "_batched_qkv_gateup"] = {"ms_per_step": round(msb, 3), "GBps": round(gb, 1),
+                                                    "frac_hbm_peak": round(gb / HBM_PEAK_GBS, 4),
+                                                    "launches_per_step": 128}
+                log(f"  full stack {key}, q/k/v and gate/up batched: {res[key + '_batched_qkv_gateup']}")
             c, qw, s, z = layers[-1]          # the last layer's down projection
             step(0)
             Wd = synth.weights_device(c.N, c.K, c.w_sigma, synth.seeds(c.config, c.layer)[0])

@@ -129,6 +129,36 @@ int w4a16_linear_ex(const void* X, int dtype, int64_t M, int64_t N, int64_t K,
                     const uint16_t* zeros, void* Y, int path, void* stream);
 
 /*
+ * w4a16_linear_batch -- several independent linear layers in one call, for a decode step that
+ * runs many layers on the same token (for example the q, k and v projections, or the experts
+ * of a mixture, or any set of layers whose inputs are ready).  Each item is a w4a16_linear
+ * problem with the call's activation dtype:
+ *   X        [M, K] fp16 or bf16, device, 16-byte aligned;
+ *   M, N, K, group_size, qweight, scales, zeros, Y  as for w4a16_linear.
+ * Every item is validated before anything is enqueued; the first invalid item's status is
+ * returned and nothing runs.  Items with M = 1 that the weight-streaming GEMV takes
+ * (K <= 12288, packed weights < 2 GiB) share launches of up to 16 layers, in item order: one
+ * grid streams all of their weights, so the fixed cost of a launch (dispatch, ramp-up and
+ * drain, about as long as streaming a 7B-sized layer at decode) is paid once per group.  The
+ * other items run as w4a16_linear, in item order.  Grouped outputs meet w4a16_linear's
+ * accuracy contract; they are computed with the arithmetic of its weight-streaming GEMV, in
+ * the same order, so where w4a16_linear takes that kernel for the layer (for example every
+ * 7B-shaped layer at g = 128) the two results are identical bit for bit.  Items run
+ * concurrently: no item's Y may overlap another item's inputs or output.
+ *   items    host array of `count` descriptors (read during the call only); 1 <= count <= 65536.
+ */
+typedef struct {
+    const void* X;
+    int64_t M, N, K, group_size;
+    const int32_t* qweight;
+    const uint16_t* scales;
+    const uint16_t* zeros;
+    void* Y;
+} w4a16_linear_item;
+
+int w4a16_linear_batch(const w4a16_linear_item* items, int count, int dtype, void* stream);
+
+/*
  * w4a16_select_path -- the path W4A16_PATH_AUTO would take for this problem (host only,
  * no GPU needed), or a negative status if the arguments are invalid.
  */

@@ -333,3 +333,20 @@ def test_static_scratch_covers_every_split():
                 assert need >= 0
                 worst = max(worst, need)
     assert 0 < worst <= 64 * 2 ** 20
+
+
+def test_linear_batch_rejects_invalid_arguments(lib):
+    # every item is validated before anything is enqueued (no GPU needed)
+    items = (L.LinearItem * 2)()
+    items[0] = L.LinearItem(A, 1, 64, 128, 128, B, C, D, A + 4096)
+    items[1] = L.LinearItem(A, 1, 64, 100, 100, B, C, D, A + 4096)       # K % 32 != 0
+    assert lib.w4a16_linear_batch(items, 2, 0, None) == L.ERR_SHAPE
+    items[1] = L.LinearItem(None, 1, 64, 128, 128, B, C, D, A + 4096)
+    assert lib.w4a16_linear_batch(items, 2, 0, None) == L.ERR_NULL
+    items[1] = L.LinearItem(A, 1, 64, 128, 48, B, C, D, A + 4096)        # group size
+    assert lib.w4a16_linear_batch(items, 2, 0, None) == L.ERR_GROUP
+    items[1] = L.LinearItem(A + 2, 1, 64, 128, 128, B, C, D, A + 4096)   # X alignment
+    assert lib.w4a16_linear_batch(items, 2, 0, None) == L.ERR_ALIGN
+    assert lib.w4a16_linear_batch(items, 2, 7, None) == L.ERR_DTYPE
+    assert lib.w4a16_linear_batch(None, 1, 0, None) == L.ERR_NULL
+    assert lib.w4a16_linear_batch(items, 0, 0, None) == L.ERR_SHAPE

@@ -9,6 +9,8 @@ the library's HIP kernels; there is no CPU or PyTorch fallback.
     group-wise INT4 RTN quantization of an fp32 ``[N, K]`` CUDA tensor.
 ``linear(X, qweight, scales, zeros, group_size, path=PATH_AUTO)`` -> ``Y``
     ``Y = X . dequant(qweight)^T`` for fp16/bf16 ``X [M, K]``.
+``linear_batch([(X, qweight, scales, zeros, group_size), ...])`` -> ``[Y, ...]``
+    independent layers in one call; one-row layers share grouped launches.
 ``gptq_hessian(X, H=None)`` / ``gptq_factor(H, damp)`` / ``gptq_quantize(W, U, group_size, scheme)``
     GPTQ: ``H = 2 X^T X`` (fp64, lower triangle), the upper Cholesky factor ``U`` of the
     damped inverse, and the compensated column-wise quantization in the packed format.
@@ -25,12 +27,13 @@ from __future__ import annotations
 
 import torch
 
+from . import _lib as _lib_mod
 from ._lib import (ASYM, BF16, F16, OK, PATH_AUTO, PATH_GEMV, PATH_NAMES, PATH_PREFILL,
                    PATH_SKINNY, SYM, W4A16Error, check, lib)
 
 __all__ = [
     "ASYM", "SYM", "F16", "BF16", "PATH_AUTO", "PATH_GEMV", "PATH_SKINNY", "PATH_PREFILL",
-    "PATH_NAMES", "W4A16Error", "quantize_pack", "linear", "dequantize", "select_path",
+    "PATH_NAMES", "W4A16Error", "quantize_pack", "linear", "linear_batch", "dequantize", "select_path",
     "w8a16_quantize_pack", "w8a16_linear", "w8a16_select_path", "linear_workspace", "linear_ws",
     "abi_version", "lib", "gptq_hessian", "gptq_factor", "gptq_quantize", "awq_stats",
     "awq_search", "awq_scale", "w8a8_smooth", "w8a8_quantize_weight", "w8a8_quantize_act",
@@ -146,6 +149,33 @@ def linear(X: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zeros, 
                                out.data_ptr(), path, _stream())
     check(st, "w4a16_linear")
     return out
+
+
+def linear_batch(layers, outs=None) -> list:
+    """Several independent layers in one call: ``layers`` is a sequence of
+    ``(X, qweight, scales, zeros, group_size)`` with one activation dtype; returns the outputs
+    ``Y`` (``outs``, if given, supplies them).  One-row layers share grouped launches."""
+    layers = list(layers)
+    if not layers:
+        raise ValueError("linear_batch needs at least one layer")
+    dt = _dtype_code(layers[0][0])
+    outs = list(outs) if outs is not None else [None] * len(layers)
+    if len(outs) != len(layers):
+        raise ValueError("outs must match layers")
+    items = (_lib_mod.LinearItem * len(layers))()
+    ys = []
+    for i, ((X, qweight, scales, zeros, group_size), out) in enumerate(zip(layers, outs)):
+        if _dtype_code(X) != dt:
+            raise TypeError("all layers of a batch need the same activation dtype")
+        M, K, N = _check_linear(X, qweight, scales, zeros, group_size, 8)
+        if X.device != layers[0][0].device:
+            raise ValueError("all layers of a batch must be on one device")
+        y = _out(out, X, M, N)
+        items[i] = _lib_mod.LinearItem(X.data_ptr(), M, N, K, group_size, qweight.data_ptr(), scales.data_ptr(),
+                                       zeros.data_ptr() if zeros is not None else None, y.data_ptr())
+        ys.append(y)
+    check(lib().w4a16_linear_batch(items, len(layers), dt, _stream()), "w4a16_linear_batch")
+    return ys
 
 
 def linear_workspace(M: int, N: int, K: int, group_size: int, dtype: int = F16) -> int:

@@ -20,6 +20,13 @@ ASYM, SYM = 0, 1
 PATH_AUTO, PATH_GEMV, PATH_SKINNY, PATH_PREFILL = 0, 1, 2, 3
 PATH_NAMES = {PATH_GEMV: "gemv", PATH_SKINNY: "skinny", PATH_PREFILL: "prefill"}
 
+class LinearItem(ctypes.Structure):
+    """``w4a16_linear_item`` of the C ABI."""
+    _fields_ = [("X", ctypes.c_void_p), ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("group_size", ctypes.c_int64), ("qweight", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("zeros", ctypes.c_void_p), ("Y", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -57,6 +64,8 @@ def lib() -> ctypes.CDLL:
     L.w4a16_linear_workspace.argtypes = [i64, i64, i64, i64, i32]
     L.w4a16_linear_ws.restype = i32
     L.w4a16_linear_ws.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, i64, vp]
+    L.w4a16_linear_batch.restype = i32
+    L.w4a16_linear_batch.argtypes = [ctypes.POINTER(LinearItem), i32, i32, vp]
     L.w4a16_linear_ws_noalloc.restype = i32
     L.w4a16_linear_ws_noalloc.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, vp, vp, vp]
     L.w4a16_w8a16_quantize_pack.restype = i32

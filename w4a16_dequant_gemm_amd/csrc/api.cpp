@@ -10,6 +10,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <vector>
 
 #include "../../include/w4a16.h"
 #include "launch.h"
@@ -19,6 +20,8 @@ using w4a16::LinearArgs;
 namespace {
 
 constexpr int64_t kMaxDim = 2147483647LL;
+constexpr int kMaxBatch = 65536;          // layers per w4a16_linear_batch call
+constexpr int kGroupLaunch = 16;          // one-row layers per grouped launch
 constexpr int64_t kGptqMaxK = 46340;      // K * K fp64 elements indexable in 31 bits
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -426,6 +429,48 @@ int w4a16_linear(const void* X, int dtype, int64_t M, int64_t N, int64_t K, int6
                  void* stream) {
     return w4a16_linear_ex(X, dtype, M, N, K, group_size, qweight, scales, zeros, Y,
                            W4A16_PATH_AUTO, stream);
+}
+
+int w4a16_linear_batch(const w4a16_linear_item* items, int count, int dtype, void* stream) {
+    if (!items) return W4A16_ERR_NULL;
+    if (count < 1 || count > kMaxBatch) return W4A16_ERR_SHAPE;
+    std::vector<LinearArgs> args((size_t)count);
+    std::vector<int> paths((size_t)count);
+    for (int i = 0; i < count; ++i) {
+        const w4a16_linear_item& it = items[i];
+        const int st = validate_linear(it.X, dtype, it.M, it.N, it.K, it.group_size, it.qweight, it.scales,
+                                       it.zeros, it.Y, &args[(size_t)i]);
+        if (st != W4A16_OK) return st;
+        paths[(size_t)i] = choose_path(args[(size_t)i]);
+        if (paths[(size_t)i] < 0) return W4A16_ERR_PATH;
+    }
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    // one-row layers the grouped kernel takes share launches of up to 16 layers, in item
+    // order; a group of one and every other layer run as w4a16_linear
+    std::vector<LinearArgs> group;
+    auto flush = [&]() -> int {
+        int st = W4A16_OK;
+        if (group.size() == 1)
+            st = run_linear(group[0], choose_path(group[0]), s);
+        else if (!group.empty())
+            st = hip_status(w4a16::launch_gemv_group(group.data(), (int)group.size(), s));
+        group.clear();
+        return st;
+    };
+    for (int i = 0; i < count; ++i) {
+        const LinearArgs& a = args[(size_t)i];
+        if (w4a16::gemv_group_supports(a)) {
+            group.push_back(a);
+            if ((int)group.size() == kGroupLaunch) {
+                const int st = flush();
+                if (st != W4A16_OK) return st;
+            }
+        } else {
+            const int st = run_linear(a, paths[(size_t)i], s);
+            if (st != W4A16_OK) return st;
+        }
+    }
+    return flush();
 }
 
 int64_t w4a16_linear_workspace(int64_t M, int64_t N, int64_t K, int64_t group_size, int dtype) {

@@ -348,12 +348,13 @@ __device__ __forceinline__ void store_batch(const float acc[RB][M], int row, int
 __host__ __device__ constexpr int sz_lds_offset(int M, int CPL) { return (lds_bytes(M, CPL) + 15) & ~15; }
 constexpr int kSzPiecesPerThread = 2;     // 16-byte pieces of scales (and of zeros) per thread
 
+// The work of one block of the streaming kernel (block index `blk`), shared by the plain
+// kernel and the grouped kernel (several independent layers in one launch).
 template <int DT, int M, int CPL, int RB, int W, int NB>
-__global__ __launch_bounds__(64 * W) void gemv_stream_kernel(
-    const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw,
+__device__ __forceinline__ void stream_block(
+    uint32_t* __restrict__ lds, const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int has_zeros,
-    uint16_t* __restrict__ Y, int N, int K, int G, int gshift, int rows_per_block) {
-    extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+    uint16_t* __restrict__ Y, int N, int K, int G, int gshift, int rows_per_block, int blk) {
     constexpr int CH = CPL * 64;                       // padded chunks per activation row
     constexpr int NT = 64 * W;
     constexpr int JOBS = M * CH * 4;                   // 8-column staging jobs
@@ -367,7 +368,7 @@ __global__ __launch_bounds__(64 * W) void gemv_stream_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int C = K >> 5;
     const int KW = K >> 3;
-    const int row_begin = blockIdx.x * rows_per_block;
+    const int row_begin = blk * rows_per_block;
     const int row_end = min(N, row_begin + rows_per_block);
     // NB == 0: one batch per wave holding all of its rows, an even split of the block's
     // rows (wave w: rows_w .. rows_{w+1} - 1); otherwise batches of RB rows strided by W * RB.
@@ -534,6 +535,16 @@ __global__ __launch_bounds__(64 * W) void gemv_stream_kernel(
             }
         }
     }
+}
+
+template <int DT, int M, int CPL, int RB, int W, int NB>
+__global__ __launch_bounds__(64 * W) void gemv_stream_kernel(
+    const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int has_zeros,
+    uint16_t* __restrict__ Y, int N, int K, int G, int gshift, int rows_per_block) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+    stream_block<DT, M, CPL, RB, W, NB>(lds, X, qw, scales, zeros, has_zeros, Y, N, K, G, gshift,
+                                        rows_per_block, blockIdx.x);
 }
 
 struct GemvCfg {
@@ -728,7 +739,132 @@ hipError_t run_lds(const LinearArgs& a, const LdsCfg& c, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
+// ---------------------------------------------------------------------------------
+// Grouped launch: several independent one-row layers (M = 1) in one kernel.  Each launch
+// pays a fixed cost of about 1.8 us on this GPU (dispatch behind the previous kernel, ramp
+// up, drain), which at decode is comparable to streaming a whole 7B-sized layer; one grid
+// over the layers pays it once.  Block b works for the layer whose block range holds b and
+// runs that layer's streaming block with the layer's own configuration, so every output is
+// computed exactly as by the layer's own launch (same lane-to-chunk mapping, same order of
+// sums).  Configurations: one batch per wave holding all of its rows (one or two rows per
+// wave, 8 waves per block), chunks per lane 1 .. 6 (K <= 12288); two rows per wave only for
+// up to 3 chunks per lane, which keeps the kernel's register count at that of the one-row
+// 6-chunk body.
+constexpr int kGroupMax = 16;
+
+struct GroupItem {
+    const uint16_t* X;
+    const uint32_t* qw;
+    const uint16_t* scales;
+    const uint16_t* zeros;
+    uint16_t* Y;
+    int N, K, G, gshift;
+    int rows_per_block;
+    int block_begin;       // first grid block of this layer
+    int variant;           // group_variant(CPL, RB)
+    int has_zeros;
+};
+
+struct GroupArgs {
+    GroupItem it[kGroupMax];
+    int count;
+};
+
+constexpr int group_variant(int cpl, int rb) { return cpl <= 3 ? 2 * (cpl - 1) + (rb - 1) : 6 + (cpl - 4); }
+
+template <int DT>
+__global__ __launch_bounds__(64 * kStreamWaves) void gemv_group_kernel(const GroupArgs ga) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+    const int b = blockIdx.x;
+    int i = 0;
+#pragma unroll
+    for (int j = 1; j < kGroupMax; ++j)
+        if (j < ga.count && b >= ga.it[j].block_begin) i = j;
+    const GroupItem& t = ga.it[i];
+    const int lb = b - t.block_begin;
+#define W4A16_GROUP_CASE(CPL, RB)                                                                          \
+    case group_variant(CPL, RB):                                                                        \
+        stream_block<DT, 1, CPL, RB, kStreamWaves, 0>(lds, t.X, t.qw, t.scales, t.zeros, t.has_zeros, t.Y, \
+                                                      t.N, t.K, t.G, t.gshift, t.rows_per_block, lb);     \
+        break;
+    switch (t.variant) {
+        W4A16_GROUP_CASE(1, 1)
+        W4A16_GROUP_CASE(1, 2)
+        W4A16_GROUP_CASE(2, 1)
+        W4A16_GROUP_CASE(2, 2)
+        W4A16_GROUP_CASE(3, 1)
+        W4A16_GROUP_CASE(3, 2)
+        W4A16_GROUP_CASE(4, 1)
+        W4A16_GROUP_CASE(5, 1)
+        W4A16_GROUP_CASE(6, 1)
+        default: break;
+    }
+#undef W4A16_GROUP_CASE
+}
+
+// The grouped configuration of one layer, or cpl == 0 if the grouped kernel cannot take it.
+LdsCfg pick_group(const LinearArgs& a, int* rb) {
+    LdsCfg c;
+    if (a.M != 1) return c;
+    const int cpl = (a.K / 32 + 63) / 64;
+    if (cpl > lds_max_cpl(1)) return c;
+    if ((long long)a.N * (a.K / 2) >= (1LL << 31)) return c;
+    *rb = ((a.N + kStreamWaves - 1) / kStreamWaves <= kOneRowBlocks || cpl > 3) ? 1 : 2;
+    const int rpb = *rb * kStreamWaves;
+    const long long pieces = ((long long)rpb * a.G + 7) / 8 + 1;
+    if (pieces > (long long)kSzPiecesPerThread * 64 * kStreamWaves) return c;
+    const long long lds = sz_lds_offset(1, cpl) + 64 * pieces;
+    if (lds > kLdsBudget) return c;
+    c.cpl = cpl;
+    c.rows_per_block = rpb;
+    c.blocks = (a.N + rpb - 1) / rpb;
+    c.lds = (int)lds;
+    return c;
+}
+
 }  // namespace
+
+bool gemv_group_supports(const LinearArgs& a) {
+    int rb = 0;
+    return pick_group(a, &rb).cpl > 0;
+}
+
+hipError_t launch_gemv_group(const LinearArgs* items, int count, hipStream_t st) {
+    if (count < 1 || count > kGroupMax) return hipErrorInvalidValue;
+    GroupArgs ga{};
+    ga.count = count;
+    long long blocks = 0;
+    int lds = 0;
+    for (int i = 0; i < count; ++i) {
+        const LinearArgs& a = items[i];
+        if (a.dtype != items[0].dtype) return hipErrorInvalidValue;
+        int rb = 0;
+        const LdsCfg c = pick_group(a, &rb);
+        if (c.cpl == 0) return hipErrorInvalidValue;
+        GroupItem& t = ga.it[i];
+        t.X = static_cast<const uint16_t*>(a.X);
+        t.qw = a.qw;
+        t.scales = a.scales;
+        t.zeros = a.zeros;
+        t.Y = static_cast<uint16_t*>(a.Y);
+        t.N = a.N;
+        t.K = a.K;
+        t.G = a.G;
+        t.gshift = a.gshift;
+        t.rows_per_block = c.rows_per_block;
+        t.block_begin = (int)blocks;
+        t.variant = group_variant(c.cpl, rb);
+        t.has_zeros = a.zeros ? 1 : 0;
+        blocks += c.blocks;
+        lds = lds > c.lds ? lds : c.lds;
+    }
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (items[0].dtype == DT_F16)
+        hipLaunchKernelGGL(gemv_group_kernel<DT_F16>, dim3((unsigned)blocks), dim3(64 * kStreamWaves), lds, st, ga);
+    else
+        hipLaunchKernelGGL(gemv_group_kernel<DT_BF16>, dim3((unsigned)blocks), dim3(64 * kStreamWaves), lds, st, ga);
+    return hipGetLastError();
+}
 
 bool gemv_supports(const LinearArgs& a) {
     if (a.M < 1 || a.M > kMaxM) return false;

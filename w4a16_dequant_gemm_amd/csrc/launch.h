@@ -31,6 +31,9 @@ hipError_t launch_quantize_pack(const float* W, int N, int K, int g, int gshift,
 hipError_t launch_dequantize(const uint32_t* qw, const uint16_t* scales, const uint16_t* zeros,
                              int N, int K, int g, int gshift, float* out, hipStream_t s);
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t s);
+// grouped launch of independent one-row layers (gemv.hip): at most 16 per launch, one dtype
+bool gemv_group_supports(const LinearArgs& a);
+hipError_t launch_gemv_group(const LinearArgs* items, int count, hipStream_t s);
 hipError_t launch_skinny(const LinearArgs& a, hipStream_t s);
 hipError_t launch_decode(const LinearArgs& a, hipStream_t s);
 hipError_t launch_prefill(const LinearArgs& a, hipStream_t s);
