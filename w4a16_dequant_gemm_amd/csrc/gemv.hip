@@ -19,6 +19,8 @@
 //   bf16: codes are 128 + u from byte permutes (unpack_byte<0x43>); the bias leaves with
 //     the chunk's activation sum.
 // Partial sums are reduced across the wave with DPP and across waves through LDS.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -744,13 +746,16 @@ hipError_t run_lds(const LinearArgs& a, const LdsCfg& c, hipStream_t st) {
 // pays a fixed cost of about 1.8 us on this GPU (dispatch behind the previous kernel, ramp
 // up, drain), which at decode is comparable to streaming a whole 7B-sized layer; one grid
 // over the layers pays it once.  Block b works for the layer whose block range holds b and
-// runs that layer's streaming block with the layer's own configuration, so every output is
-// computed exactly as by the layer's own launch (same lane-to-chunk mapping, same order of
-// sums).  Configurations: one batch per wave holding all of its rows (one or two rows per
-// wave, 8 waves per block), chunks per lane 1 .. 6 (K <= 12288); two rows per wave only for
-// up to 3 chunks per lane, which keeps the kernel's register count at that of the one-row
-// 6-chunk body.
+// runs the streaming block body for that layer, so every output is computed exactly as by
+// the layer's own launch (same lane-to-chunk mapping, same order of sums).  Blocks of 4
+// waves, each wave loading all of its rows at once: two rows per wave for up to 3 chunks
+// per lane (K <= 6144), one row for 4 .. 6 chunks (K <= 12288), which keeps the kernel's
+// register count at that of the one-row 6-chunk body.  Measured on the 7B-like step
+// (4096 x 4096, 4096 -> 11008, 11008 -> 4096): 8-wave blocks 14.1 us, 4-wave 14.2 us, 4-wave
+// with the long-row layer dispatched first 13.5 us, one row per wave for N <= 4096 15.0 us,
+// two rows per wave everywhere (150 VGPRs) 15.1 us.
 constexpr int kGroupMax = 16;
+constexpr int kGroupWaves = 4;        // waves per block of the grouped kernel
 
 struct GroupItem {
     const uint16_t* X;
@@ -773,7 +778,7 @@ struct GroupArgs {
 constexpr int group_variant(int cpl, int rb) { return cpl <= 3 ? 2 * (cpl - 1) + (rb - 1) : 6 + (cpl - 4); }
 
 template <int DT>
-__global__ __launch_bounds__(64 * kStreamWaves) void gemv_group_kernel(const GroupArgs ga) {
+__global__ __launch_bounds__(64 * kGroupWaves) void gemv_group_kernel(const GroupArgs ga) {
     extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
     const int b = blockIdx.x;
     int i = 0;
@@ -784,15 +789,12 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemv_group_kernel(const Gro
     const int lb = b - t.block_begin;
 #define W4A16_GROUP_CASE(CPL, RB)                                                                          \
     case group_variant(CPL, RB):                                                                        \
-        stream_block<DT, 1, CPL, RB, kStreamWaves, 0>(lds, t.X, t.qw, t.scales, t.zeros, t.has_zeros, t.Y, \
+        stream_block<DT, 1, CPL, RB, kGroupWaves, 0>(lds, t.X, t.qw, t.scales, t.zeros, t.has_zeros, t.Y, \
                                                       t.N, t.K, t.G, t.gshift, t.rows_per_block, lb);     \
         break;
     switch (t.variant) {
-        W4A16_GROUP_CASE(1, 1)
         W4A16_GROUP_CASE(1, 2)
-        W4A16_GROUP_CASE(2, 1)
         W4A16_GROUP_CASE(2, 2)
-        W4A16_GROUP_CASE(3, 1)
         W4A16_GROUP_CASE(3, 2)
         W4A16_GROUP_CASE(4, 1)
         W4A16_GROUP_CASE(5, 1)
@@ -809,10 +811,10 @@ LdsCfg pick_group(const LinearArgs& a, int* rb) {
     const int cpl = (a.K / 32 + 63) / 64;
     if (cpl > lds_max_cpl(1)) return c;
     if ((long long)a.N * (a.K / 2) >= (1LL << 31)) return c;
-    *rb = ((a.N + kStreamWaves - 1) / kStreamWaves <= kOneRowBlocks || cpl > 3) ? 1 : 2;
-    const int rpb = *rb * kStreamWaves;
+    *rb = cpl > 3 ? 1 : 2;
+    const int rpb = *rb * kGroupWaves;
     const long long pieces = ((long long)rpb * a.G + 7) / 8 + 1;
-    if (pieces > (long long)kSzPiecesPerThread * 64 * kStreamWaves) return c;
+    if (pieces > (long long)kSzPiecesPerThread * 64 * kGroupWaves) return c;
     const long long lds = sz_lds_offset(1, cpl) + 64 * pieces;
     if (lds > kLdsBudget) return c;
     c.cpl = cpl;
@@ -835,8 +837,13 @@ hipError_t launch_gemv_group(const LinearArgs* items, int count, hipStream_t st)
     ga.count = count;
     long long blocks = 0;
     int lds = 0;
-    for (int i = 0; i < count; ++i) {
-        const LinearArgs& a = items[i];
+    // blocks of the layers with the longest rows (the longest-lived blocks) are dispatched first
+    int order[kGroupMax];
+    for (int i = 0; i < count; ++i) order[i] = i;
+    std::stable_sort(order, order + count, [&](int x, int y) { return items[x].K > items[y].K; });
+    for (int oi = 0; oi < count; ++oi) {
+        const int i = oi;
+        const LinearArgs& a = items[order[oi]];
         if (a.dtype != items[0].dtype) return hipErrorInvalidValue;
         int rb = 0;
         const LdsCfg c = pick_group(a, &rb);
@@ -860,9 +867,9 @@ hipError_t launch_gemv_group(const LinearArgs* items, int count, hipStream_t st)
     }
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     if (items[0].dtype == DT_F16)
-        hipLaunchKernelGGL(gemv_group_kernel<DT_F16>, dim3((unsigned)blocks), dim3(64 * kStreamWaves), lds, st, ga);
+        hipLaunchKernelGGL(gemv_group_kernel<DT_F16>, dim3((unsigned)blocks), dim3(64 * kGroupWaves), lds, st, ga);
     else
-        hipLaunchKernelGGL(gemv_group_kernel<DT_BF16>, dim3((unsigned)blocks), dim3(64 * kStreamWaves), lds, st, ga);
+        hipLaunchKernelGGL(gemv_group_kernel<DT_BF16>, dim3((unsigned)blocks), dim3(64 * kGroupWaves), lds, st, ga);
     return hipGetLastError();
 }
 
