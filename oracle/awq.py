@@ -17,11 +17,20 @@ SmoothQuant / KV 量化）", 4.2):
 Readings where the pages leave a step open or contradict themselves:
 
 * A1 candidates: ``s(a) = r ** (a / 4)`` for ``a = -4 .. 4`` (nine points, ``a = 0`` is plain
-  RTN), ``r_i = xc_i / sqrt(max xc * min xc)`` with ``xc_i = max(x_i, 1e-6 * max x)``.  The
-  page says salient channels get ``s_i > 1`` (weights shrunk) but also that the error of
-  the quantized layer picks the scale; the grid spans both directions (``a < 0`` enlarges
-  the salient channels' weights) and the measured error decides.  Exponents are quarters so
-  the candidates come from IEEE-exact fp32 operations only (square roots, products, one
+  RTN), ``r_i = xc_i / sqrt(max xc * min xc)`` with ``xc_i = max(x_i, 1e-6 * max x)``: every
+  channel gets its own candidate value from one exponent shared by all channels (5.1 gives
+  the importance as a power of the channel's activation magnitude), and the search picks
+  the exponent whose quantized layer has the smallest output error.  5.2 also calls the
+  search per-channel; a literal independent choice per channel (each channel alone, the
+  others unscaled) is a different method, compared in the tests: the channels of a group
+  share one quantization grid, so independently chosen values combine badly and keep only
+  a small part of the error reduction (0.6-0.9 of RTN against 0.2-0.3 for the shared
+  exponent on outlier data), and its cost (an output-error evaluation per channel and
+  candidate) does not fit the page's "seconds for a 4096-channel layer".  The page says
+  salient channels get ``s_i > 1`` (weights shrunk) but also that the error of the quantized
+  layer picks the scale; the grid spans both directions (``a < 0`` enlarges the salient
+  channels' weights) and the measured error decides.  Exponents are quarters so the
+  candidates come from IEEE-exact fp32 operations only (square roots, products, one
   division), reproducible bit for bit.
 * A2 the statistic is the activation magnitude alone (the weight factor of 5.1's salience
   formula does not enter the candidate scales).

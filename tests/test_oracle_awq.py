@@ -8,7 +8,10 @@
 * a = 0 is plain RTN (codes and loss); the search returns the first minimum;
 * on calibration data with outlier channels the search beats RTN by enlarging the
   salient channels' weights (a < 0);
-* the scaled activations are rounded once (exact rational check).
+* the scaled activations are rounded once (exact rational check);
+* the reading of the search (one exponent shared by all channels, per-channel scale values)
+  against the literal per-channel search (each channel choosing alone): the two choose
+  differently, and the shared exponent reaches a far lower output error.
 """
 
 from fractions import Fraction
@@ -95,3 +98,45 @@ def test_scaled_activations_round_once():
     for k in range(3):
         exact = Fraction(float(X[0, k])) * Fraction(float(s[k]))
         assert float(got[0, k]) == F.round_fraction_to_format(exact, F.F16)
+
+
+def _per_channel_search(W, X, dtype, xm, g, scheme):
+    """The literal per-channel reading, for comparison only: each channel on its own tries the
+    nine candidate values r_i^(a/4) (every other channel unscaled) and keeps the one with the
+    smallest quantized output error (ties to the smaller |a|, then the negative a); the chosen
+    values are then applied together."""
+    K = W.shape[1]
+    S = {a: A.candidate_scales(xm, a) for a in A.GRID}
+    order = (0, -1, 1, -2, 2, -3, 3, -4, 4)
+    best = np.zeros(K, dtype=int)
+    for i in range(K):
+        losses = []
+        for a in order:
+            s = np.ones(K, np.float32)
+            s[i] = S[a][i]
+            codes, sc, z = oracle.quantize((W / s[None, :]).astype(np.float32), g, scheme)
+            losses.append(A.awq_loss(X, dtype, W, s, codes, sc, z, g))
+        best[i] = order[int(np.argmin(losses))]
+    s = np.array([S[best[i]][i] for i in range(K)], np.float32)
+    codes, sc, z = oracle.quantize((W / s[None, :]).astype(np.float32), g, scheme)
+    return best, A.awq_loss(X, dtype, W, s, codes, sc, z, g)
+
+
+@pytest.mark.parametrize("seed", [6, 8])
+def test_shared_exponent_versus_literal_per_channel_search(seed):
+    # The reading pinned here: one exponent a for all channels (the scales s_i = r_i^(a/4) are
+    # per channel, the search parameter is shared), chosen by the layer's quantized output
+    # error.  A literal per-channel search -- every channel choosing its own a with the others
+    # unscaled -- is a different method: its channels do choose different exponents, and
+    # because the channels of a group share one quantization grid, the independently chosen
+    # values combine badly; on outlier data it keeps only a small part of the error reduction.
+    X = calibration(128, 128, FP16, seed=seed, outlier_frac=0.02, outlier_mult=20.0)
+    W = weights(32, 128, 0.02, seed=seed + 1)
+    xm = A.channel_mean_abs(X, FP16)
+    best, losses, *_ = A.awq_search(W, X, FP16, xm, 32, oracle.ASYM)
+    rtn = losses[A.GRID.index(0)]
+    choices, loss_pc = _per_channel_search(W, X, FP16, xm, 32, oracle.ASYM)
+    assert len(set(choices.tolist())) > 3                    # the two readings differ
+    assert losses[best] < 0.4 * rtn                           # shared exponent: < 40 % of RTN
+    assert losses[best] < 0.6 * loss_pc                       # ... and well below the literal one
+    assert loss_pc < rtn                                      # which still beats RTN
