@@ -238,12 +238,19 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(
     const int sz_first = row_begin * G;
     const int sz_al = sz_first & ~7;
     const int sz_pieces = ((row_end - row_begin) * G + (sz_first - sz_al) + 7) >> 3;
+    // only waves that own staging pieces load them (wave-uniform): redundant prologue loads
+    // delay the weight stream
     u32x4 sv[kSzPieces], zv[kSzPieces];
 #pragma unroll
     for (int j = 0; j < kSzPieces; ++j) {
         const int off = (sz_al + 8 * min(tid + NTH * j, sz_pieces - 1)) * 2;
-        sv[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-        zv[j] = __builtin_amdgcn_raw_buffer_load_b128(rz, off, 0, 0);
+        if ((wave + W * j) * 64 < sz_pieces) {
+            sv[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+            zv[j] = __builtin_amdgcn_raw_buffer_load_b128(rz, off, 0, 0);
+        } else {
+            sv[j] = u32x4{0u, 0u, 0u, 0u};
+            zv[j] = u32x4{0u, 0u, 0u, 0u};
+        }
     }
     const int tail = min(full_end + (tid & 7), total - 1);
     const uint16_t s_tail = __builtin_amdgcn_raw_buffer_load_b16(rs_all, tail * 2, 0, 0);
@@ -457,12 +464,19 @@ __global__ __launch_bounds__(64 * W) void decode16_kernel(
     const int sz_first = row_begin * G;
     const int sz_al = sz_first & ~7;
     const int sz_pieces = ((row_end - row_begin) * G + (sz_first - sz_al) + 7) >> 3;
+    // only waves that own staging pieces load them (wave-uniform): redundant prologue loads
+    // delay the weight stream
     u32x4 sv[kSzPieces], zv[kSzPieces];
 #pragma unroll
     for (int j = 0; j < kSzPieces; ++j) {
         const int off = (sz_al + 8 * min(tid + NTH * j, sz_pieces - 1)) * 2;
-        sv[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-        zv[j] = __builtin_amdgcn_raw_buffer_load_b128(rz, off, 0, 0);
+        if ((wave + W * j) * 64 < sz_pieces) {
+            sv[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+            zv[j] = __builtin_amdgcn_raw_buffer_load_b128(rz, off, 0, 0);
+        } else {
+            sv[j] = u32x4{0u, 0u, 0u, 0u};
+            zv[j] = u32x4{0u, 0u, 0u, 0u};
+        }
     }
     const int tail = min(full_end + (tid & 7), total - 1);
     const uint16_t s_tail = __builtin_amdgcn_raw_buffer_load_b16(rs_all, tail * 2, 0, 0);

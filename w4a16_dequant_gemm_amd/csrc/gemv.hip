@@ -425,12 +425,20 @@ __device__ __forceinline__ void stream_block(
         const int c = e >> 2;
         xv[j] = reinterpret_cast<const u32x4*>(X + (size_t)m * K + ((size_t)(c < C ? c : 0) << 5))[e & 3];
     }
+    //    Only waves that own staging pieces load them (wave-uniform branches): every vector
+    //    memory instruction of the prologue delays the block's weight stream, redundant
+    //    ones included (measured: 0.4 us per 7B-like step).
     u32x4 sv[JSZ], zv[JSZ];
 #pragma unroll
     for (int j = 0; j < JSZ; ++j) {
         const int off = (sz_al + 8 * min(tid + NT * j, sz_pieces - 1)) * 2;
-        sv[j] = __builtin_amdgcn_raw_buffer_load_b128(src.s, off, 0, 0);
-        zv[j] = __builtin_amdgcn_raw_buffer_load_b128(src.z, off, 0, 0);
+        if ((wave + W * j) * 64 < sz_pieces) {
+            sv[j] = __builtin_amdgcn_raw_buffer_load_b128(src.s, off, 0, 0);
+            zv[j] = __builtin_amdgcn_raw_buffer_load_b128(src.z, off, 0, 0);
+        } else {
+            sv[j] = u32x4{0u, 0u, 0u, 0u};
+            zv[j] = u32x4{0u, 0u, 0u, 0u};
+        }
     }
     const int tail = min(full_end + (tid & 7), total - 1);
     const uint16_t st = __builtin_amdgcn_raw_buffer_load_b16(s_all, tail * 2, 0, 0);
