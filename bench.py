@@ -470,6 +470,43 @@ def traffic_parse(fetch_dir: str, write_dir: str, shape, commands, out_path=None
     print(json.dumps(out))
 
 
+def trace_summary(run_dir: str, out_path: str, header: str = ""):
+    """Per-kernel duration statistics of a rocprofv3 --kernel-trace --stats run: calls, average,
+    p10, median, p90, min, max and share of the total, from every dispatch's end - start in the
+    run's kernel_trace csv (all csv files under run_dir)."""
+    import csv
+    import glob
+    durs = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                name = row.get("Kernel_Name") or row.get("Name") or "?"
+                d = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1000.0
+                durs.setdefault(name, []).append(d)
+    if not durs:
+        raise SystemExit(f"no kernel_trace csv under {run_dir}")
+    total = sum(sum(v) for v in durs.values())
+
+    def short(n):
+        n = n.split("(")[0] if "(" in n and not n.startswith("void") else n
+        n = n.replace("w4a16::(anonymous namespace)::", "").replace("void ", "")
+        return n[:92]
+
+    def pct(v, q):
+        v = sorted(v)
+        return v[min(len(v) - 1, int(q * (len(v) - 1) + 0.5))]
+    lines = [header.rstrip("\n")] if header else []
+    lines.append(f"{'kernel':<92} {'calls':>6} {'avg_us':>8} {'p10_us':>8} {'med_us':>8} {'p90_us':>8} "
+                 f"{'min_us':>8} {'max_us':>8} {'pct':>6}")
+    for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{short(name):<92} {len(v):>6} {sum(v) / len(v):>8.2f} {pct(v, 0.1):>8.2f} "
+                     f"{pct(v, 0.5):>8.2f} {pct(v, 0.9):>8.2f} {min(v):>8.2f} {max(v):>8.2f} "
+                     f"{100 * sum(v) / total:>6.2f}")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines[:40]))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -487,9 +524,16 @@ def main():
     ap.add_argument("--traffic-commands", nargs="*", default=[],
                     help="the profiler command lines, recorded in the traffic file")
     ap.add_argument("--traffic-out", default=None, help="output path of --traffic-parse")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("RUN_DIR", "OUT"),
+                    help="per-kernel duration statistics of a rocprofv3 --kernel-trace run")
+    ap.add_argument("--trace-header", default="", help="text put above the --trace-summary table")
     ap.add_argument("--profile-run", choices=["prefill", "w8a8", "kv_batch", "decode_m16", "w8a16", "c3"],
                     help="a short fixed workload of one kernel family, for counter runs")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary[0], args.trace_summary[1], args.trace_header)
+        return
+
     def shape_arg(v):
         return "step" if v == ["step"] else (int(v[0]), int(v[1]))
     if args.traffic_parse:
