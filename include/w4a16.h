@@ -109,9 +109,9 @@ int w4a16_quantize_pack(const float* W, int64_t N, int64_t K, int64_t group_size
  *            Zero points must be integers with |z| <= 2048, the range w4a16_quantize_pack
  *            emits (z is in [0, 15] for every group whose range contains 0; larger |z|
  *            arise for a group far narrower than its distance from 0).  Every kernel path
- *            takes the whole range: the decode kernels and the bf16 GEMM apply z to fp32
- *            partial sums; the fp16 GEMM rounds s * (u - z) once to fp16 per weight, with
- *            u - z exact for z >= -2033 and rounded to an even integer below.
+ *            takes the whole range exactly: the decode kernels and the bf16 GEMM apply z to
+ *            fp32 partial sums; the fp16 GEMM rounds s * (u - z), exact in fp32, once to fp16
+ *            per weight.
  *   Y        out [M, N], same dtype as X, device, 2-byte aligned.
  * Other zero points give unspecified output (never an out-of-bounds access).
  */
@@ -447,8 +447,8 @@ int w4a16_w8a16_quantize_pack(const float* W, int64_t N, int64_t K, int64_t grou
 /*
  * w4a16_w8a16_linear -- Y[M, N] = X[M, K] . W_hat[N, K]^T, W_hat[n, k] = s (u - z) from the
  * 8-bit codes, dequantized inside the kernel (the GEMV and the bf16 GEMM multiply the exact
- * codes and apply the group's s and z to fp32 partial sums; the fp16 GEMM rounds s * (u - z)
- * once to fp16 per weight, u - z exact for z >= -1793 and rounded to an even integer below);
+ * codes and apply the group's s and z to fp32 partial sums; the fp16 GEMM rounds s * (u - z),
+ * exact in fp32, once to fp16 per weight);
  * fp32 accumulation, Y rounded once to the activation dtype.  Arguments as for w4a16_linear
  * with qweight [N, K/4]; zeros NULL means all zero points 128; any integer zero point
  * |z| <= 2048 (the range w4a16_w8a16_quantize_pack emits).  Kernels: a weight-streaming GEMV

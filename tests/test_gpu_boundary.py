@@ -4,8 +4,8 @@
   called directly through ctypes with raw device pointers, against the oracle;
 * the whole zero-point range the quantizers emit, ``|z| <= 2048``, on every kernel path of
   both code widths: random codes with zero points spread over the range (including the
-  edges of the fp16 kernels' exact code window), against the oracle's exact ``s (u - z)``;
-  one-hot activations bit-exact wherever ``u - z`` is exact in fp16;
+  points where ``u - z`` leaves the fp16 integers), against the oracle's exact ``s (u - z)``;
+  one-hot activations bit-exact everywhere;
 * the quantizers on groups far from 0 (large ``|z|``), bit-exact;
 * the binding's argument checks on the workspace form and the output tensor.
 """
@@ -76,9 +76,9 @@ def test_plain_w8a16_linear_through_c_abi(M, dtype):
 
 
 # ------------------------------------------------------- the whole zero-point range
-# zero points over [-2048, 2048]: both ends, the old 1536-bias window edges (+-480, 512), the
-# boundaries of the 512-wide shifts, and the lowest zero points at which u - z is still exact
-# in fp16 (-2033 for 4-bit codes, -1793 for 8-bit codes)
+# zero points over [-2048, 2048]: both ends, +-480 and 512 (the edges of the exact range of an
+# integer-add construction of 1536 + u - z on fp16 bits), multiples of 512 and their
+# neighbours, and -2033 / -1793, below which u - z itself leaves the fp16 integers
 Z_VALUES = [-2048, -2040, -2033, -2000, -1800, -1793, -1537, -1536, -1024, -777, -600, -513, -481,
             -480, -300, -8, 0, 7, 15, 100, 255, 300, 480, 481, 512, 513, 600, 765, 1023, 1024, 1280,
             1536, 1537, 2000, 2047, 2048]
@@ -140,11 +140,11 @@ def test_linear_whole_zero_point_range(bits, path, M, K, g, dtype):
 @pytest.mark.parametrize("dtype", [FP16, BF16])
 @pytest.mark.parametrize("bits,path,M,K,g", [c for c in WIDE_Z_CASES if c[1] != W4.PATH_GEMV or c[2] == 1])
 def test_one_hot_whole_zero_point_range(bits, path, M, K, g, dtype):
-    # one-hot rows select single weights s (u - z): every kernel rounds that product once,
-    # bit-exact against the oracle wherever u - z is an fp16 integer (z >= umax - 2048)
+    # one-hot rows select single weights s (u - z): every kernel rounds that product once
+    # (the fp16 GEMMs from an exact fp32 s (u - z)), bit-exact against the oracle over the
+    # whole zero-point range
     N = 150
-    zmin = -2033 if bits == 4 else -1793
-    qw_np, s, z = _wide_z_layer(N, K, g, bits, seed=K + bits, zmin=zmin)
+    qw_np, s, z = _wide_z_layer(N, K, g, bits, seed=K + bits)
     qw, st, zt = upload_packed(qw_np, s, z)
     ks = np.unique(np.r_[0, 1, 5, 63, 64, 100, 127, 128, 129, 511, 512, K - 65, K - 1,
                          np.random.default_rng(5).choice(K, max(M, 16) - 13, replace=False)])[:max(M, 1)]

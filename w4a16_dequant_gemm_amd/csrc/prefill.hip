@@ -249,30 +249,61 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------------------------
-// Exact fp16 codes for the fp16 kernels that dequantize to s * (u - z) before the MFMA.
+// fp16 dequantization for the fp16 kernels that multiply dequantized weights:
+// w = fp16(s * (u - z)), rounded once.
 //
-// A 16-bit integer add on fp16 bit patterns builds the fp16 value 1536 + (u - z) + D exactly
-// while that value stays in [1024, 2048), where fp16 values are the consecutive integers.
-// The shift D is a multiple of 512 picked per (row, group) so that every code u of the row's
-// group lands there: D = 512 * floor((z - c + 256) / 512), c the middle of the code range
-// (8 for 4-bit codes, 128 for 8-bit codes), gives D - z in [-256 - c, 255 - c].  Subtracting
-// 1536 + D, a multiple of 512 in [-512, 3584] and hence an fp16 value, then leaves exactly
-// u - z whenever |u - z| <= 2048: for every code when umax - 2048 <= z <= 2048 (umax = 15 or
-// 255), and the multiply by s is the only rounding.  Below that, down to z = -2048, a
-// difference u - z > 2048 rounds to an even integer first (relative error <= 2^-11).
-struct CodeWindow {
-    uint32_t add;   // pair of 16-bit integers 0x6600 - z + D
-    uint32_t sub;   // pair of fp16 values 1536 + D
-};
+// The codes are fp16 subnormals u * 2^-24 taken from the packed word by masks (exact: a
+// nibble in the low bits of an fp16 with a zero exponent field), in "mask order" (u0,u4)
+// (16u1,16u5) (u2,u6) (16u3,16u7) for 4-bit codes.  Each weight is one mixed-precision FMA,
+// fma(code, s', c) evaluated in fp32 with s' = s * 2^24 (or s * 2^20 for the x16 slots) and
+// c = -s * z, its result rounded once to fp16 into the low or high half of the output
+// register (v_fma_mixlo_f16 / v_fma_mixhi_f16, which read either half of a 32-bit source).
+// s has 11 significant bits and u - z at most 12 (|z| <= 2048), so s' * code and the sum
+// s (u - z) are exact in fp32: the single fp16 rounding is the only one, for every zero
+// point the quantizers emit.  The pair (lo, hi) picks its two codes from any halves, which
+// rebuilds natural column order without permutes.
+template <int LO_HI, int HI_HI>
+__device__ __forceinline__ uint32_t dq_pair(uint32_t src_lo, float s_lo, uint32_t src_hi, float s_hi, float c) {
+    uint32_t r;
+    if constexpr (LO_HI)
+        asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(src_lo), "v"(s_lo), "v"(c));
+    else
+        asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(src_lo), "v"(s_lo), "v"(c));
+    if constexpr (HI_HI)
+        asm("v_fma_mixhi_f16 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(r) : "v"(src_hi), "v"(s_hi), "v"(c));
+    else
+        asm("v_fma_mixhi_f16 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "+v"(r) : "v"(src_hi), "v"(s_hi), "v"(c));
+    return r;
+}
 
-template <int BITS>
-__device__ __forceinline__ CodeWindow code_window(float zf) {
-    const int z = (int)zf;
-    constexpr int c = BITS == 4 ? 8 : 128;
-    const int D = ((z - c + 256) >> 9) * 512;
-    const uint32_t a = (uint32_t)(0x6600 - z + D) & 0xFFFFu;
-    const uint32_t b = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(float)(1536 + D));
-    return CodeWindow{a | (a << 16), b | (b << 16)};
+// The fp32 constants of one (row, group): s * 2^24, s * 2^20 and -s * z (all exact).
+struct DqConst {
+    float s24, s20, c;
+};
+__device__ __forceinline__ DqConst dq_const(uint16_t s_bits, float z) {
+    const float s = h2f(s_bits);
+    return DqConst{s * 16777216.0f, s * 1048576.0f, -s * z};
+}
+
+// One packed word of 4-bit codes (8 consecutive columns) -> four fp16 pairs in natural order.
+__device__ __forceinline__ void dq_word4(uint32_t w, const DqConst& q, uint32_t out[4]) {
+    const uint32_t w8 = w >> 8;
+    const uint32_t m0 = w & 0x000F000Fu;     // u0 u4
+    const uint32_t m1 = w & 0x00F000F0u;     // 16 u1, 16 u5
+    const uint32_t m2 = w8 & 0x000F000Fu;    // u2 u6
+    const uint32_t m3 = w8 & 0x00F000F0u;    // 16 u3, 16 u7
+    out[0] = dq_pair<0, 0>(m0, q.s24, m1, q.s20, q.c);    // (u0, u1)
+    out[1] = dq_pair<0, 0>(m2, q.s24, m3, q.s20, q.c);    // (u2, u3)
+    out[2] = dq_pair<1, 1>(m0, q.s24, m1, q.s20, q.c);    // (u4, u5)
+    out[3] = dq_pair<1, 1>(m2, q.s24, m3, q.s20, q.c);    // (u6, u7)
+}
+
+// One 32-bit word of 8-bit codes (4 consecutive columns) -> two fp16 pairs in natural order.
+__device__ __forceinline__ void dq_word8(uint32_t w, const DqConst& q, uint32_t out[2]) {
+    const uint32_t p0 = perm(0u, w, 0x0C010C00u);          // (u0, u1) as subnormals
+    const uint32_t p1 = perm(0u, w, 0x0C030C02u);          // (u2, u3)
+    out[0] = dq_pair<0, 1>(p0, q.s24, p0, q.s24, q.c);
+    out[1] = dq_pair<0, 1>(p1, q.s24, p1, q.s24, q.c);
 }
 
 // ---------------------------------------------------------------------------------
@@ -283,9 +314,8 @@ __device__ __forceinline__ CodeWindow code_window(float zf) {
 //   - loads 64 bytes of one activation row (its 32 columns) and stores them to LDS
 //     unchanged (natural column order),
 //   - loads 8 bytes = 16 codes of one weight row and writes the dequantized fp16 weights
-//     s * (u - z) to LDS: the code pair (u, u') is built as the fp16 bits of
-//     1536 + (u - z) + D by one packed 16-bit integer add (CodeWindow), then
-//     1536 + D is subtracted (exact) and the pair is multiplied by s (one rounding),
+//     fp16(s * (u - z)) to LDS (dq_word4: masks and one mixed-precision FMA per weight,
+//     one rounding),
 // so every weight is dequantized exactly once per block -- the pages' "dequantize the
 // INT4 weight to FP16, then multiply" with the FP16 weight living only in LDS.  The
 // MFMAs read both operands from LDS in natural order; rows are padded by 16 bytes,
@@ -334,41 +364,21 @@ __global__ __launch_bounds__(256, 2) void prefill_f16_kernel(
         wq[0] = v.x;
         wq[1] = v.y;
     };
-    // dequantization constants of the current group: the code window of its zero point
-    // and the s pair
-    CodeWindow win{0u, 0u};
-    uint32_t spair = 0;
+    // dequantization constants of the current group
+    DqConst dq{0.0f, 0.0f, 0.0f};
     int cur_group = -1;
     auto store_step = [&](int buf, int step) {
         const int grp = group_of(step * F_BK, gshift);
         if (grp != cur_group) {
             cur_group = grp;
-            const uint16_t sb = scales[(size_t)wrow * G + grp];
-            const float z = has_zeros ? h2f(zsrc[(size_t)wrow * G + grp]) : 8.0f;
-            win = code_window<4>(z);
-            spair = (uint32_t)sb | ((uint32_t)sb << 16);
+            dq = dq_const(scales[(size_t)wrow * G + grp], has_zeros ? h2f(zsrc[(size_t)wrow * G + grp]) : 8.0f);
         }
         uint16_t* arow = &As[buf][tid * F_LDA];
 #pragma unroll
         for (int b = 0; b < 4; ++b) *reinterpret_cast<u32x4*>(arow + 8 * b) = xa[b];
-        const u16x2 zbias = __builtin_bit_cast(u16x2, win.add);
-        const f16x2 bias = __builtin_bit_cast(f16x2, win.sub);
-        const f16x2 sv = __builtin_bit_cast(f16x2, spair);
         uint32_t d[8];
-#pragma unroll
-        for (int wi = 0; wi < 2; ++wi) {
-            const uint32_t w = wq[wi];
-            const uint32_t t0 = w & 0x0F0F0F0Fu;          // u0 u2 u4 u6 (as bytes)
-            const uint32_t t1 = (w >> 4) & 0x0F0F0F0Fu;   // u1 u3 u5 u7
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                // (u_{2p}, u_{2p+1}) as 16-bit integers, then the fp16 bits of 1536 + u - z + D
-                const uint32_t uu = perm(t1, t0, 0x0C040C00u + 0x00010001u * p);
-                const uint32_t biased = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, uu) + zbias);
-                const f16x2 code = __builtin_bit_cast(f16x2, biased) - bias;    // exact u - z
-                d[4 * wi + p] = __builtin_bit_cast(uint32_t, code * sv);        // one rounding
-            }
-        }
+        dq_word4(wq[0], dq, &d[0]);
+        dq_word4(wq[1], dq, &d[4]);
         uint16_t* brow = &Bs[buf][wr * F_LDA + 16 * wh];
         *reinterpret_cast<u32x4*>(brow) = u32x4{d[0], d[1], d[2], d[3]};
         *reinterpret_cast<u32x4*>(brow + 8) = u32x4{d[4], d[5], d[6], d[7]};
@@ -438,9 +448,8 @@ __global__ __launch_bounds__(256, 2) void prefill_f16_kernel(
 //   Weights: each wave dequantizes exactly the 64 weight rows it multiplies, in
 //     registers (none goes through LDS, none is dequantized twice): lane (n, h) loads the
 //     16 bytes holding columns 32 h .. 32 h + 31 of the step for each of its two rows, one
-//     step ahead, and turns word j into the fp16 B fragment of MFMA j with the code-window
-//     construction (CodeWindow: exact 1536 + u - z + D, exact subtraction of 1536 + D, one
-//     rounding in the multiply by s).  MFMA j covers columns 8 j .. 8 j + 7 and 32 + 8 j .. + 7; the activation
+//     step ahead, and turns word j into the fp16 B fragment of MFMA j (dq_word4: one
+//     mixed-precision FMA per weight, exact in fp32, one rounding to fp16).  MFMA j covers columns 8 j .. 8 j + 7 and 32 + 8 j .. + 7; the activation
 //     fragment of lane (m, h) reads the same columns.  The next step's dequantization is
 //     interleaved with this step's MFMAs.
 //   Block order: consecutive block indices run on different XCDs; blocks are renumbered
@@ -450,8 +459,7 @@ constexpr int W_BM = 256, W_BN = 256, W_BK = 64;     // K % 128 == 0: steps in p
 
 // BITS = 8 (W8A16): lane (n, h) loads the 32 bytes of columns 32h .. 32h + 31 (two 16-byte
 // loads) and MFMA j takes words 2j and 2j + 1 (one byte permute per pair instead of the nibble
-// masks; the code window covers the 8-bit codes the same way, the implicit symmetric zero
-// point is 128).
+// masks (dq_word8), the implicit symmetric zero point is 128).
 // Split K (part != NULL): block (x, y) runs k-steps [y * spl, (y + 1) * spl) of its tile and
 // stores the fp32 partial tile to part[y][M][N]; splitk_reduce_kernel sums the partials in
 // split order.  Without a split, spl = K / 64, grid y = 1 and the tile goes to Y.
@@ -531,44 +539,26 @@ __global__ __launch_bounds__(256, 1) void prefill_f16_wide_kernel(
             st.z[ns] = __builtin_amdgcn_raw_buffer_load_b16(rz, szoff[ns] + grp2, 0, 0);
         }
     };
-    // code windows of a stage's two rows (per row and group, see CodeWindow)
+    // dequantization constants of a stage's two rows (per row and group)
     struct WConst {
-        CodeWindow win[2];
+        DqConst q[2];
     };
     auto stage_const = [&](const WStage& st) {
         WConst c;
 #pragma unroll
         for (int ns = 0; ns < 2; ++ns)
-            c.win[ns] = code_window<BITS>(HZ ? h2f(st.z[ns]) : (BITS == 4 ? 8.0f : 128.0f));
+            c.q[ns] = dq_const(st.s[ns], HZ ? h2f(st.z[ns]) : (BITS == 4 ? 8.0f : 128.0f));
         return c;
     };
     // word j of both rows of a stage -> the fp16 B fragments of MFMA j: b[ns][j][4]
     auto dequant_word = [&](const WStage& st, const WConst& wc, int j, uint32_t b[2][4][4]) {
 #pragma unroll
         for (int ns = 0; ns < 2; ++ns) {
-            const u16x2 zbias = __builtin_bit_cast(u16x2, wc.win[ns].add);
-            const f16x2 bias = __builtin_bit_cast(f16x2, wc.win[ns].sub);
-            const f16x2 sv = __builtin_bit_cast(f16x2, (uint32_t)st.s[ns] | ((uint32_t)st.s[ns] << 16));
-            uint32_t t0, t1;
             if constexpr (BITS == 4) {
-                const uint32_t w = st.w[ns][0][j];
-                t0 = w & 0x0F0F0F0Fu;                     // u0 u2 u4 u6 (as bytes)
-                t1 = (w >> 4) & 0x0F0F0F0Fu;              // u1 u3 u5 u7
+                dq_word4(st.w[ns][0][j], wc.q[ns], b[ns][j]);
             } else {
-                t0 = st.w[ns][j >> 1][2 * (j & 1)];       // bytes u0 u1 u2 u3
-                t1 = st.w[ns][j >> 1][2 * (j & 1) + 1];   // bytes u4 u5 u6 u7
-            }
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                uint32_t uu;                               // (u_2p, u_2p+1) as 16-bit integers
-                if constexpr (BITS == 4)
-                    uu = perm(t1, t0, 0x0C040C00u + 0x00010001u * p);
-                else
-                    uu = p < 2 ? perm(0u, t0, 0x0C010C00u + 0x00020002u * p)
-                               : perm(0u, t1, 0x0C010C00u + 0x00020002u * (p - 2));
-                const u16x2 biased = __builtin_bit_cast(u16x2, uu) + zbias;     // 1536 + u - z + D
-                const f16x2 code = __builtin_bit_cast(f16x2, biased) - bias;    // exact u - z
-                b[ns][j][p] = __builtin_bit_cast(uint32_t, code * sv);          // one rounding
+                dq_word8(st.w[ns][j >> 1][2 * (j & 1)], wc.q[ns], &b[ns][j][0]);       // columns 0..3
+                dq_word8(st.w[ns][j >> 1][2 * (j & 1) + 1], wc.q[ns], &b[ns][j][2]);   // columns 4..7
             }
         }
     };
