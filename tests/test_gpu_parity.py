@@ -115,7 +115,11 @@ GEMV_CASES = [(1, 64, 256, 32), (2, 130, 512, 128), (3, 77, 1024, 1024), (4, 256
               (1, 9477, 4096, 128), (2, 5000, 2048, 64), (4, 3000, 1024, 1024), (3, 2600, 6144, 128),
               # grid-sizing boundaries of the streaming kernel: one row per wave up to N = 4096,
               # two rows up to N = 12288 (768 blocks), one persistent block per CU beyond
-              (1, 4097, 1024, 128), (2, 12288, 256, 64), (1, 12289, 512, 128), (1, 4096, 12288, 128)]
+              (1, 4097, 1024, 128), (2, 12288, 256, 64), (1, 12289, 512, 128), (1, 4096, 12288, 128),
+              # one-row layers with >= 4 chunks per lane: one row per wave at any N, rows up to
+              # K = 28672 (more than 64 KB of LDS), and past the LDS budget (g = 32 at K = 28672)
+              (1, 12400, 8192, 128), (1, 70, 28672, 28672), (1, 500, 16384, 64), (1, 9, 14336, 128),
+              (1, 40, 28672, 32)]
 SKINNY_CASES = [(1, 64, 128, 128), (5, 100, 1024, 128), (16, 256, 4096, 128), (17, 77, 2048, 256),
                 (32, 300, 11008, 128), (31, 129, 1024, 1024), (8, 4096, 4096, 128), (2, 50, 11008, 11008),
                 (12, 1000, 28672, 128),
