@@ -1,7 +1,7 @@
 // Decode-regime W4A16 kernels on CDNA4 matrix cores, 1 <= M <= 16 (MFMA 16x16x32);
 // K % 256 == 0 and g % 128 == 0.  decode_kernel (M <= 4) stages the activations in LDS;
-// decode16_kernel (M <= 16; used from 5 rows, or when the activations do not fit the LDS)
-// streams them from memory next to the weights.
+// decode_ring_kernel (M <= 16; used from 5 rows, or when the activations do not fit the LDS)
+// loads them from memory next to a weight stream that goes straight into an LDS ring.
 //
 // At decode the layer streams every packed weight once per token (page
 // "推理优化中“用精度换性能“的核心技术：量化", section 一), so the kernel is built around the
@@ -41,6 +41,9 @@
 //     activation sum (staging pass, 16-lane DPP sum); fp16: s' = s * 2^24, c = z;
 //     bf16: s' = s, c = 128 + z.  (scale, zero) pairs of the block's rows are staged in
 //     LDS with coalesced loads, one 32-bit word per (row, group).
+#include <algorithm>
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -376,35 +379,93 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(
     }
 }
 
-// ---------------------------------------------------------------------------------
-// Up to 16 rows: the same weight stream, tiles and k-split, with all sixteen MFMA rows in
-// use.  The activations no longer fit the LDS (16 rows of K), so each wave loads the
-// activation fragments of its k-block pairs straight from memory (L2-resident: every
-// block reads all of X), P pairs ahead together with the weights; lane (n, q) loads row
-// n (zeros for n >= M), columns 128 kb + 32 q .. + 31 of each k-block and puts them in
-// the unpack's pair order in registers.  The k-block activation sums come from four more
-// MFMAs against a constant B operand (2^-24 in the x1 slots and 16 * 2^-24 in the x16
-// slots for fp16, 1.0 for bf16), so they land in the accumulator layout: lane (n, q)
-// element j holds row 4 q + j.
+// Activation fragments of one k-block pair in registers (ring kernel): lane (n, q) holds row
+// n, columns 128 kb + 32 q .. + 31 of each k-block of the pair.
 struct XStage {
     u32x4 x[2][4];
 };
 
-template <int DT, int T, int P, int W>
-__global__ __launch_bounds__(64 * W) void decode16_kernel(
+// ---------------------------------------------------------------------------------
+// Up to 16 rows (used from 5 rows, or when the activations do not fit decode_kernel's LDS),
+// with the weight stream in an LDS ring.  Holding the weight loads in flight in registers,
+// next to the activation fragments, caps a CU at about 32 KB of weights in flight (two waves
+// per SIMD); the HBM stream needs several times that.  Here the weights go from memory
+// straight into LDS (buffer loads with the LDS-direct form, no registers while in flight):
+// each wave owns a ring of D = T * PK
+// slots of one (tile, k-block pair) unit each, 2 KB, and refills a slot as soon as its
+// unit is in registers, so PK k-block pairs of all T tiles are in flight per wave, up to
+// 128 KB per CU.  Every slot is an LDS object of its own, so the compiler's waits on the
+// loads name exactly the slot being read (one object for all slots would make every read
+// wait for the whole ring).  The activations no longer fit the LDS (16 rows of K), so each
+// wave loads the fragments of its k-block pairs straight from memory (L2-resident: every
+// block reads all of X) into registers one pair ahead, where they serve all T tiles; lane
+// (n, q) loads row n (zeros for n >= M) and puts it in the unpack's pair order.  The
+// k-block activation sums come from four more MFMAs against a constant B operand (2^-24 in
+// the x1 slots and 16 * 2^-24 in the x16 slots for fp16, 1.0 for bf16), so they land in
+// the accumulator layout: lane (n, q) element j holds row 4 q + j.
+//
+// Unit layout in a slot: load instruction h (0, 1), lane l fetches row r = 8 h + l / 8 of
+// the tile, 16-byte piece (l % 8) ^ (r / 2 % 8) of the pair's 128 bytes, and lands in slot
+// word 64 h + l = 8 r + l % 8 (eight consecutive lanes still read one 128-byte line, only
+// in permuted order); lane (n, q) later reads piece 4 e + q of row n (k-block e of the
+// pair) from word 8 n + ((4 e + q) ^ (n / 2 % 8)), free of bank conflicts.  The MFMA
+// operands and the per-(tile, k-block) scale fold are those of decode_kernel.
+constexpr int kRingSlots = 8;
+constexpr int kRingUnit = 128;              // 16-byte words per unit (2 KB)
+__shared__ __attribute__((aligned(16))) u32x4 g_ring0[kWaves][kRingUnit];
+__shared__ __attribute__((aligned(16))) u32x4 g_ring1[kWaves][kRingUnit];
+__shared__ __attribute__((aligned(16))) u32x4 g_ring2[kWaves][kRingUnit];
+__shared__ __attribute__((aligned(16))) u32x4 g_ring3[kWaves][kRingUnit];
+__shared__ __attribute__((aligned(16))) u32x4 g_ring4[kWaves][kRingUnit];
+__shared__ __attribute__((aligned(16))) u32x4 g_ring5[kWaves][kRingUnit];
+__shared__ __attribute__((aligned(16))) u32x4 g_ring6[kWaves][kRingUnit];
+__shared__ __attribute__((aligned(16))) u32x4 g_ring7[kWaves][kRingUnit];
+
+template <int d>
+__device__ __forceinline__ u32x4* ring_slot(int wave) {
+    static_assert(d >= 0 && d < kRingSlots, "ring slot");
+    if constexpr (d == 0) return g_ring0[wave];
+    else if constexpr (d == 1) return g_ring1[wave];
+    else if constexpr (d == 2) return g_ring2[wave];
+    else if constexpr (d == 3) return g_ring3[wave];
+    else if constexpr (d == 4) return g_ring4[wave];
+    else if constexpr (d == 5) return g_ring5[wave];
+    else if constexpr (d == 6) return g_ring6[wave];
+    else return g_ring7[wave];
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// Both load instructions of one unit into ring slot d.
+template <int d>
+__device__ __forceinline__ void ring_fill(__amdgpu_buffer_rsrc_t r, int wave, const int vw[2], int kp) {
+    u32x4* s = ring_slot<d>(wave);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)s, 16, vw[0],
+                                             kp * 128, 0, 2 /* nt */);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(s + 64), 16, vw[1],
+                                             kp * 128, 0, 2 /* nt */);
+}
+
+template <int DT, int T, int PK>
+__global__ __launch_bounds__(64 * kWaves) void decode_ring_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int has_zeros,
-    uint16_t* __restrict__ Y, int M, int N, int K, int G, int gshift, int NT, int nblk, int KSP,
-    int off_wt) {
-    extern __shared__ __attribute__((aligned(16))) uint32_t dlds[];
+    uint16_t* __restrict__ Y, int M, int N, int K, int G, int gshift, int NT, int nblk, int KSP) {
+    constexpr int W = kWaves;
     constexpr int NTH = 64 * W;
-    const int KB = K >> 7;
-    unsigned char* lbase = reinterpret_cast<unsigned char*>(dlds);
+    static_assert(T * PK <= kRingSlots && T <= W, "ring configuration");
+    extern __shared__ __attribute__((aligned(16))) uint32_t dlds[];
     uint32_t* szs = dlds;                                                  // (s | z << 16) words
+    const int KB = K >> 7;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    u32x4* wt = reinterpret_cast<u32x4*>(lbase + off_wt) + wave * 128;     // 2 KB per wave
     const int n16 = lane & 15;
     const int q = lane >> 4;
 
@@ -434,21 +495,20 @@ __global__ __launch_bounds__(64 * W) void decode16_kernel(
     const __amdgpu_buffer_rsrc_t rz_all =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(zsrc), 0, total * 2, 0x00020000);
 
-    int vw[T][2], wslot[2], rslot[2];
+    // unit loads: lane -> (row 8 h + lane / 8, permuted piece); rows past N clamped
+    int vw[T][2];
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int n = min((tile0 + t) * 16 + 8 * h + (lane >> 3), N - 1);
-            vw[t][h] = n * (K >> 1) + 16 * (lane & 7);
+            const int r = 8 * h + (lane >> 3);
+            const int c = (lane & 7) ^ ((r >> 1) & 7);
+            const int n = min((tile0 + t) * 16 + r, N - 1);
+            vw[t][h] = n * (K >> 1) + 16 * c;
         }
+    int rslot[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int r = 8 * h + (lane >> 3);
-        wslot[h] = 8 * r + ((lane & 7) ^ ((r >> 1) & 7));
-        const int c = 4 * h + q;
-        rslot[h] = 8 * n16 + (c ^ ((n16 >> 1) & 7));
-    }
+    for (int e = 0; e < 2; ++e) rslot[e] = 8 * n16 + ((4 * e + q) ^ ((n16 >> 1) & 7));
     // activation fragment offset of this lane; rows >= M point past the buffer (zeros)
     const int xoff = n16 < M ? (n16 * K + 32 * q) * 2 : 0x40000000;
     auto load_x = [&](XStage& xs, int kp, bool live) {
@@ -460,57 +520,62 @@ __global__ __launch_bounds__(64 * W) void decode16_kernel(
                                                                    kp * 512, 0);
     };
 
-    // 1. (scale, zero) staging loads first, then P pairs of activations and weights
+    // 1. (scale, zero) staging loads, the first pair's activations, then the ring: pair
+    //    kp0 + p of tile t into slot p * T + t
     const int sz_first = row_begin * G;
     const int sz_al = sz_first & ~7;
     const int sz_pieces = ((row_end - row_begin) * G + (sz_first - sz_al) + 7) >> 3;
-    // only waves that own staging pieces load them (wave-uniform): redundant prologue loads
-    // delay the weight stream
+    //    Waves without staging pieces load through `none` (no memory access): a branch
+    //    around the loads would make the compiler wait for them at the join.
     u32x4 sv[kSzPieces], zv[kSzPieces];
 #pragma unroll
     for (int j = 0; j < kSzPieces; ++j) {
         const int off = (sz_al + 8 * min(tid + NTH * j, sz_pieces - 1)) * 2;
-        if ((wave + W * j) * 64 < sz_pieces) {
-            sv[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-            zv[j] = __builtin_amdgcn_raw_buffer_load_b128(rz, off, 0, 0);
-        } else {
-            sv[j] = u32x4{0u, 0u, 0u, 0u};
-            zv[j] = u32x4{0u, 0u, 0u, 0u};
-        }
+        const bool own = (wave + W * j) * 64 < sz_pieces;            // wave-uniform
+        sv[j] = __builtin_amdgcn_raw_buffer_load_b128(own ? rs : none, off, 0, 0);
+        zv[j] = __builtin_amdgcn_raw_buffer_load_b128(own ? rz : none, off, 0, 0);
     }
     const int tail = min(full_end + (tid & 7), total - 1);
     const uint16_t s_tail = __builtin_amdgcn_raw_buffer_load_b16(rs_all, tail * 2, 0, 0);
     const uint16_t z_tail = __builtin_amdgcn_raw_buffer_load_b16(rz_all, tail * 2, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    XStage xst[P];
-    Stage<T> st[P];
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-        load_x(xst[p], kp0 + p, p < np);
-        load_stage<T>(st[p], rw, none, kp0 + p, p < np, vw, ntiles);
-    }
+    XStage xr;
+    load_x(xr, kp0, np > 0);
+    static_for<0, PK>([&](auto pc) {
+        constexpr int p = decltype(pc)::value;
+        static_for<0, T>([&](auto tc) {
+            constexpr int t = decltype(tc)::value;
+            ring_fill<p * T + t>(p < np && t < ntiles ? rw : none, wave, vw[t], kp0 + p);
+        });
+    });
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. (scale | zero << 16) words; NULL zeros become 8.0 (0x4800)
+    // 2. (scale | zero << 16) words; NULL zeros become 8.0 (0x4800).  Branch-free: threads
+    //    without a piece (or tail half) write the spare words at `spare` (a store under a
+    //    branch would pull its load into the branch, behind a wait for every load).
+    const int spare = 8 * sz_pieces;                 // 12 spare words after the staged ones
 #pragma unroll
     for (int j = 0; j < kSzPieces; ++j) {
         const int p = tid + NTH * j;
         const u32x4 sw = sv[j];
         const u32x4 zw = has_zeros ? zv[j] : u32x4{0x48004800u, 0x48004800u, 0x48004800u, 0x48004800u};
-        if (p < sz_pieces && sz_al + 8 * p + 8 <= total) {
-            u32x4* dst = reinterpret_cast<u32x4*>(szs + 8 * p);
-            dst[0] = u32x4{perm(zw.x, sw.x, 0x05040100u), perm(zw.x, sw.x, 0x07060302u),
-                           perm(zw.y, sw.y, 0x05040100u), perm(zw.y, sw.y, 0x07060302u)};
-            dst[1] = u32x4{perm(zw.z, sw.z, 0x05040100u), perm(zw.z, sw.z, 0x07060302u),
-                           perm(zw.w, sw.w, 0x05040100u), perm(zw.w, sw.w, 0x07060302u)};
-        }
+        const bool ok = p < sz_pieces && sz_al + 8 * p + 8 <= total;
+        u32x4* dst = reinterpret_cast<u32x4*>(szs + (ok ? 8 * p : spare));
+        dst[0] = u32x4{perm(zw.x, sw.x, 0x05040100u), perm(zw.x, sw.x, 0x07060302u),
+                       perm(zw.y, sw.y, 0x05040100u), perm(zw.y, sw.y, 0x07060302u)};
+        dst[1] = u32x4{perm(zw.z, sw.z, 0x05040100u), perm(zw.z, sw.z, 0x07060302u),
+                       perm(zw.w, sw.w, 0x05040100u), perm(zw.w, sw.w, 0x07060302u)};
     }
     {
         const int h = full_end + tid;
-        if (tid < 8 && h < total && h >= sz_al && h < sz_al + 8 * sz_pieces)
-            szs[h - sz_al] = (uint32_t)s_tail | ((uint32_t)(has_zeros ? z_tail : (uint16_t)0x4800) << 16);
+        const bool ok = tid < 8 && h < total && h >= sz_al && h < sz_al + 8 * sz_pieces;
+        szs[ok ? h - sz_al : spare + 8] =
+            (uint32_t)s_tail | ((uint32_t)(has_zeros ? z_tail : (uint16_t)0x4800) << 16);
     }
-    __syncthreads();
+    //    Barrier on the staging stores only: __syncthreads() would also wait for the
+    //    ring's loads (they write LDS), which each wave reads only itself.
+    __builtin_amdgcn_s_waitcnt(0xC07F);               // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
 
     int szo[T];
 #pragma unroll
@@ -518,149 +583,121 @@ __global__ __launch_bounds__(64 * W) void decode16_kernel(
     f32x4 tile[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) tile[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    // constant B operand of the activation-sum MFMAs
     const uint32_t ones_lo = DT == DT_F16 ? 0x00010001u : 0x3F803F80u;
     const uint32_t ones_hi = DT == DT_F16 ? 0x00100010u : 0x3F803F80u;
     const uint32_t ones[4] = {ones_lo, ones_hi, ones_lo, ones_hi};
 
-    // One k-block pair, k-block by k-block (fewer live registers): activation fragments in
-    // pair order, their sums, then for each tile the lanes holding k-block e of the unit
-    // pass it through the transpose slots.
-    const bool my_half[2] = {(lane & 7) < 4, (lane & 7) >= 4};
-    auto compute = [&](const XStage& xs, const Stage<T>& sw, int kp) {
+    // One k-block pair (ring slots p * T ..): activations to pair order and their sums, the
+    // next pair's activations into the freed registers, then every tile's unit; REFILL
+    // issues the unit PK pairs ahead into the slot just read (unconditionally, zeros past
+    // the slice, so the compiler's load counts stay exact).  Deeper activation prefetch was
+    // measured slower (more registers, same waits).
+    auto kpair = [&](auto pc, int kp, auto refill) {
+        constexpr int p = decltype(pc)::value;
+        constexpr bool REFILL = decltype(refill)::value;
+        uint32_t a[2][4][4];
+        f32x4 S[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            uint32_t a[4][4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const u32x4 v = xs.x[e][j];
+                const u32x4 v = xr.x[e][j];
                 if constexpr (DT == DT_F16) {
-                    permute_x8(v.x, v.y, v.z, v.w, a[j]);
+                    permute_x8(v.x, v.y, v.z, v.w, a[e][j]);
                     const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-                    a[j][1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a[j][1]) * sixteenth);
-                    a[j][3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a[j][3]) * sixteenth);
+                    a[e][j][1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a[e][j][1]) * sixteenth);
+                    a[e][j][3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a[e][j][3]) * sixteenth);
                 } else {
-                    permute_x8_byte(v.x, v.y, v.z, v.w, a[j]);
+                    permute_x8_byte(v.x, v.y, v.z, v.w, a[e][j]);
                 }
             }
-            f32x4 S = mfma16<DT>(a[0], ones, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+            S[e] = mfma16<DT>(a[e][0], ones, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
-            for (int j = 1; j < 4; ++j) S = mfma16<DT>(a[j], ones, S);
-            const int grp = ((2 * kp + e) << 7) >> gshift;
-#pragma unroll
-            for (int t = 0; t < T; ++t) {
-                if (my_half[e]) {
-                    wt[wslot[0]] = sw.w[t][0];
-                    wt[wslot[1]] = sw.w[t][1];
-                }
-                __builtin_amdgcn_wave_barrier();
-                const u32x4 wb = wt[rslot[e]];
-                __builtin_amdgcn_wave_barrier();
-                uint32_t bq[4][4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if constexpr (DT == DT_F16)
-                        unpack_mask_f16(wb[j], bq[j]);
-                    else
-                        unpack_byte<0x43>(wb[j], bq[j]);
-                }
-                f32x4 acc = mfma16<DT>(a[0], bq[0], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
-#pragma unroll
-                for (int j = 1; j < 4; ++j) acc = mfma16<DT>(a[j], bq[j], acc);
-                const uint32_t sz = szs[szo[t] + grp];
-                const float s = h2f((uint16_t)(sz & 0xFFFFu));
-                const float z = h2f((uint16_t)(sz >> 16));
-                const float sp = DT == DT_F16 ? s * 16777216.0f : s;
-                const float c = DT == DT_F16 ? z : 128.0f + z;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) tile[t][j] = fmaf(sp, fmaf(-c, S[j], acc[j]), tile[t][j]);
-            }
+            for (int j = 1; j < 4; ++j) S[e] = mfma16<DT>(a[e][j], ones, S[e]);
         }
+        load_x(xr, kp + 1, kp + 1 < kp1);             // zeros past the slice
+        int grp[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) grp[e] = ((2 * kp + e) << 7) >> gshift;
+        static_for<0, T>([&](auto tc) {
+            constexpr int t = decltype(tc)::value;
+            constexpr int d = p * T + t;
+            if (t < ntiles) {                         // wave-uniform
+                const u32x4* slot = ring_slot<d>(wave);
+                u32x4 wb[2];
+                wb[0] = slot[rslot[0]];
+                wb[1] = slot[rslot[1]];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    uint32_t bq[4][4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        if constexpr (DT == DT_F16)
+                            unpack_mask_f16(wb[e][j], bq[j]);
+                        else
+                            unpack_byte<0x43>(wb[e][j], bq[j]);
+                    }
+                    f32x4 acc = mfma16<DT>(a[e][0], bq[0], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+                    for (int j = 1; j < 4; ++j) acc = mfma16<DT>(a[e][j], bq[j], acc);
+                    const uint32_t sz = szs[szo[t] + grp[e]];
+                    const float s = h2f((uint16_t)(sz & 0xFFFFu));
+                    const float z = h2f((uint16_t)(sz >> 16));
+                    const float sp = DT == DT_F16 ? s * 16777216.0f : s;
+                    const float c = DT == DT_F16 ? z : 128.0f + z;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) tile[t][j] = fmaf(sp, fmaf(-c, S[e][j], acc[j]), tile[t][j]);
+                }
+            }
+            if constexpr (REFILL)
+                ring_fill<d>(kp + PK < kp1 && t < ntiles ? rw : none, wave, vw[t], kp + PK);
+        });
     };
 
-    // 3. k-block pairs of the slice, P in flight; the last round computes what is in flight
+    // 3. Rounds of PK pairs; the main loop runs while another round follows, the last
+    //    round computes what is in flight without refills.
     int i = 0;
-    for (; i + P < np; i += P) {
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-            compute(xst[p], st[p], kp0 + i + p);
-            load_x(xst[p], kp0 + i + p + P, i + p + P < np);
-            load_stage<T>(st[p], rw, none, kp0 + i + p + P, i + p + P < np, vw, ntiles);
-        }
-    }
-#pragma unroll
-    for (int p = 0; p < P; ++p)
-        if (i + p < np) compute(xst[p], st[p], kp0 + i + p);
+    for (; i + PK < np; i += PK)
+        static_for<0, PK>([&](auto pc) { kpair(pc, kp0 + i + decltype(pc)::value, std::true_type{}); });
+    static_for<0, PK>([&](auto pc) {
+        if (i + decltype(pc)::value < np) kpair(pc, kp0 + i + decltype(pc)::value, std::false_type{});
+    });
 
-    // 4. sum the waves' partial tiles in the LDS; lane (n, q) element j is row 4 q + j
+    // 4. Sum the waves' partial tiles through the ring (all loads landed first: the main
+    //    loop's last refills past the slice are zero loads still on their way); wave t
+    //    reduces tile t; lane (n, q) element j is row 4 q + j.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    f32x4* red = reinterpret_cast<f32x4*>(lbase);
-#pragma unroll
-    for (int t = 0; t < T; ++t) red[(wave * T + t) * 64 + lane] = tile[t];
+    static_for<0, T>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        ring_slot<t / 2>(wave)[64 * (t % 2) + lane] = __builtin_bit_cast(u32x4, tile[t]);
+    });
     __syncthreads();
-    for (int idx = tid; idx < T * 64; idx += NTH) {
-        const int t = idx >> 6;
-        const int l = idx & 63;
-        f32x4 v = red[t * 64 + l];
-        for (int w = 1; w < W; ++w) {
-            const f32x4 u = red[(w * T + t) * 64 + l];
-            v[0] += u[0]; v[1] += u[1]; v[2] += u[2]; v[3] += u[3];
-        }
-        const int n = (tile0 + t) * 16 + (l & 15);
-        if (t < ntiles && n < N) {
+    static_for<0, T>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        if (wave == t && t < ntiles) {
+            f32x4 v = __builtin_bit_cast(f32x4, ring_slot<t / 2>(0)[64 * (t % 2) + lane]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int m = 4 * (l >> 4) + j;
-                if (m < M) Y[(size_t)m * N + n] = f2out<DT>(v[j]);
+            for (int w = 1; w < W; ++w) {
+                const f32x4 u = __builtin_bit_cast(f32x4, ring_slot<t / 2>(w)[64 * (t % 2) + lane]);
+                v[0] += u[0]; v[1] += u[1]; v[2] += u[2]; v[3] += u[3];
+            }
+            const int n = (tile0 + t) * 16 + n16;
+            if (n < N) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int m = 4 * q + j;
+                    if (m < M) Y[(size_t)m * N + n] = f2out<DT>(v[j]);
+                }
             }
         }
-    }
+    });
 }
 
 struct DecCfg {
-    int t = 0, p = 0, ksp = 0, nblk = 0, xreg = 0;
+    int t = 0, p = 0, ksp = 0, nblk = 0;
     int sk = 0, spare = 0, szs = 0, wt = 0, lds = 0;
 };
-
-// 5 <= M <= 16 (decode16_kernel): no activation staging; LDS = (scale, zero) words, the
-// per-wave transpose buffers, and later the partial tiles.
-DecCfg pick_decode16(const LinearArgs& a) {
-    DecCfg c;
-    if (a.M < 1 || a.M > 16 || a.K % 256 != 0 || a.g % 128 != 0) return c;
-    if ((long long)a.N * (a.K / 2) >= (1LL << 31) || (long long)a.M * a.K * 2 >= (1LL << 30)) return c;
-    if ((long long)a.N * a.G * 2 >= (1LL << 31)) return c;
-    const int NT = (a.N + 15) / 16;
-    const int KB = a.K / 128;
-    int t = (NT + 255) / 256;
-    if (t > 4) t = 4;
-    const long long pieces = ((long long)t * 16 * a.G + 7) / 8 + 1;
-    if (pieces > (long long)kSzPieces * 64 * kWaves) return c;
-    c.wt = align16((int)pieces * 32);
-    long long lds = (long long)c.wt + (long long)kWaves * 2048;
-    const long long red = (long long)kWaves * t * 1024;
-    if (red > lds) lds = red;
-    if (lds > kLdsBudget) return c;
-    c.lds = (int)lds;
-    c.t = t;
-    c.p = t == 4 ? 1 : 2;            // register budget of two waves per SIMD
-    c.ksp = (KB / 2 + kWaves - 1) / kWaves;
-    c.nblk = (NT + t - 1) / t;
-    return c;
-}
-
-DecCfg pick_decode_staged(const LinearArgs& a);
-
-// M <= 4 prefers the activation-staging kernel; when the activations do not fit its LDS
-// (long K), or M > 4, the streaming one (c.xreg).
-DecCfg pick_decode(const LinearArgs& a) {
-    if (a.M <= 4) {
-        const DecCfg c = pick_decode_staged(a);
-        if (c.t > 0) return c;
-    }
-    DecCfg c = pick_decode16(a);
-    c.xreg = 1;
-    return c;
-}
 
 DecCfg pick_decode_staged(const LinearArgs& a) {
     DecCfg c;
@@ -722,26 +759,8 @@ hipError_t run_m(const LinearArgs& a, const DecCfg& c, hipStream_t st) {
     }
 }
 
-template <int DT, int T, int P>
-hipError_t run16(const LinearArgs& a, const DecCfg& c, hipStream_t st) {
-    hipLaunchKernelGGL((decode16_kernel<DT, T, P, kWaves>), dim3(c.nblk), dim3(64 * kWaves), c.lds, st,
-                       static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, a.zeros ? 1 : 0,
-                       static_cast<uint16_t*>(a.Y), a.M, a.N, a.K, a.G, a.gshift, (a.N + 15) / 16, c.nblk,
-                       c.ksp, c.wt);
-    return hipGetLastError();
-}
-
 template <int DT>
 hipError_t run_dt(const LinearArgs& a, const DecCfg& c, hipStream_t st) {
-    if (c.xreg) {
-        switch (c.t) {
-            case 1: return run16<DT, 1, 2>(a, c, st);
-            case 2: return run16<DT, 2, 2>(a, c, st);
-            case 3: return run16<DT, 3, 2>(a, c, st);
-            case 4: return run16<DT, 4, 1>(a, c, st);
-        }
-        return hipErrorInvalidValue;
-    }
     switch (a.M) {
         case 1: return run_m<DT, 1>(a, c, st);
         case 2: return run_m<DT, 2>(a, c, st);
@@ -751,14 +770,82 @@ hipError_t run_dt(const LinearArgs& a, const DecCfg& c, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
+// The ring kernel: T tiles per block, about one block per CU (T = NT / 256, at most 8, fewer
+// when the block's (scale, zero) words would not fit); PK pairs in flight per wave, two up to
+// four tiles and one beyond (PK * T <= 8 slots).  Measured against holding the weight loads
+// in registers (16 rows; 4096 -> 4096, 4096 -> 11008, 11008 -> 4096, 8192 -> 28672,
+// 28672 -> 8192): 7.0 / 10.1 / 13.9 / 26.9 / 37.3 us against 7.3 / 11.1 / 14.1 / 34.2 /
+// 38.1 us.  Deeper rings for few tiles (four pairs) were slower.
+struct RingCfg {
+    int t = 0, pk = 0, ksp = 0, nblk = 0, lds = 0;
+};
+
+constexpr int kLdsPerCu = 160 * 1024;
+
+RingCfg pick_ring(const LinearArgs& a) {
+    RingCfg c;
+    if (a.M < 1 || a.M > 16 || a.K % 256 != 0 || a.g % 128 != 0) return c;
+    if ((long long)a.N * (a.K / 2) >= (1LL << 31) || (long long)a.M * a.K * 2 >= (1LL << 30)) return c;
+    if ((long long)a.N * a.G * 2 >= (1LL << 31)) return c;
+    const int NT = (a.N + 15) / 16;
+    const int KP = a.K / 256;
+    for (int t = std::min(kRingSlots, (NT + 255) / 256); t >= 1; --t) {
+        const int pk = t <= 4 ? 2 : 1;
+        const long long pieces = ((long long)t * 16 * a.G + 7) / 8 + 1;
+        if (pieces > (long long)kSzPieces * 64 * kWaves) continue;
+        const long long dyn = align16((int)pieces * 32 + 48);          // + spare words
+        const long long ring = (long long)t * pk * kWaves * kRingUnit * 16;
+        if (dyn + ring > kLdsPerCu) continue;
+        c.t = t;
+        c.pk = pk;
+        c.ksp = (KP + kWaves - 1) / kWaves;
+        c.nblk = (NT + t - 1) / t;
+        c.lds = (int)dyn;
+        return c;
+    }
+    return c;
+}
+
+template <int DT, int T, int PK>
+hipError_t run_ring3(const LinearArgs& a, const RingCfg& c, hipStream_t st) {
+    hipLaunchKernelGGL((decode_ring_kernel<DT, T, PK>), dim3(c.nblk), dim3(64 * kWaves), c.lds, st,
+                       static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, a.zeros ? 1 : 0,
+                       static_cast<uint16_t*>(a.Y), a.M, a.N, a.K, a.G, a.gshift, (a.N + 15) / 16, c.nblk,
+                       c.ksp);
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t run_ring(const LinearArgs& a, const RingCfg& c, hipStream_t st) {
+    switch (c.t) {
+        case 1: return run_ring3<DT, 1, 2>(a, c, st);
+        case 2: return run_ring3<DT, 2, 2>(a, c, st);
+        case 3: return run_ring3<DT, 3, 2>(a, c, st);
+        case 4: return run_ring3<DT, 4, 2>(a, c, st);
+        case 5: return run_ring3<DT, 5, 1>(a, c, st);
+        case 6: return run_ring3<DT, 6, 1>(a, c, st);
+        case 7: return run_ring3<DT, 7, 1>(a, c, st);
+        case 8: return run_ring3<DT, 8, 1>(a, c, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
 
-bool decode_supports(const LinearArgs& a) { return pick_decode(a).t > 0; }
+// M <= 4 prefers the activation-staging kernel; when the activations do not fit its LDS
+// (long K), or M > 4, the ring kernel.
+bool decode_supports(const LinearArgs& a) {
+    return (a.M <= 4 && pick_decode_staged(a).t > 0) || pick_ring(a).t > 0;
+}
 
 hipError_t launch_decode(const LinearArgs& a, hipStream_t st) {
-    const DecCfg c = pick_decode(a);
-    if (c.t == 0) return hipErrorInvalidValue;
-    return a.dtype == DT_F16 ? run_dt<DT_F16>(a, c, st) : run_dt<DT_BF16>(a, c, st);
+    if (a.M <= 4) {
+        const DecCfg c = pick_decode_staged(a);
+        if (c.t > 0) return a.dtype == DT_F16 ? run_dt<DT_F16>(a, c, st) : run_dt<DT_BF16>(a, c, st);
+    }
+    const RingCfg rc = pick_ring(a);
+    if (rc.t == 0) return hipErrorInvalidValue;
+    return a.dtype == DT_F16 ? run_ring<DT_F16>(a, rc, st) : run_ring<DT_BF16>(a, rc, st);
 }
 
 }  // namespace w4a16
