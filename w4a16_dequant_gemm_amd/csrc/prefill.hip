@@ -455,6 +455,16 @@ __global__ __launch_bounds__(256, 2) void prefill_f16_kernel(
 //   Block order: consecutive block indices run on different XCDs; blocks are renumbered
 //     so that each XCD works through consecutive tiles (a few 256-row activation panels,
 //     held in that XCD's L2).
+// Device-only builtins behind device functions: inside a lambda whose body depends on a
+// kernel template parameter, a raw builtin makes the host pass drop the kernel's launch stub.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, u32x4* dst, int voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
+}
+template <int MASK, int N>
+__device__ __forceinline__ void sched_group() {
+    __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
+}
+
 constexpr int W_BM = 256, W_BN = 256, W_BK = 64;     // K % 128 == 0: steps in pairs
 
 // BITS = 8 (W8A16): lane (n, h) loads the 32 bytes of columns 32h .. 32h + 31 (two 16-byte
@@ -463,13 +473,14 @@ constexpr int W_BM = 256, W_BN = 256, W_BK = 64;     // K % 128 == 0: steps in p
 // Split K (part != NULL): block (x, y) runs k-steps [y * spl, (y + 1) * spl) of its tile and
 // stores the fp32 partial tile to part[y][M][N]; splitk_reduce_kernel sums the partials in
 // split order.  Without a split, spl = K / 64, grid y = 1 and the tile goes to Y.
-template <bool HZ, int BITS = 4, bool SPLIT = false>
-__global__ __launch_bounds__(256, 1) void prefill_f16_wide_kernel(
+template <bool HZ, int BITS = 4, bool SPLIT = false, int MS = 8>
+__global__ __launch_bounds__(256, (MS >= 8 || BITS == 8) ? 1 : 2) void prefill_f16_wide_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros,
     uint16_t* __restrict__ Y, int M, int N, int K, int G, int gshift,
     float* __restrict__ part = nullptr, int spl = 0) {
-    __shared__ __attribute__((aligned(16))) u32x4 As[2][W_BM * 8];     // 2 x 32 KB
+    constexpr int BMk = 32 * MS;                                       // block rows
+    __shared__ __attribute__((aligned(16))) u32x4 As[2][BMk * 8];      // 2 x 32 KB at 256 rows
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -477,8 +488,8 @@ __global__ __launch_bounds__(256, 1) void prefill_f16_wide_kernel(
     const int l32 = lane & 31;
     const int h = lane >> 5;
     int mt, nt;
-    if (!xcd_tile(blockIdx.x, (M + W_BM - 1) / W_BM, (N + W_BN - 1) / W_BN, mt, nt)) return;
-    const int m0 = mt * W_BM;
+    if (!xcd_tile(blockIdx.x, (M + BMk - 1) / BMk, (N + W_BN - 1) / W_BN, mt, nt)) return;
+    const int m0 = mt * BMk;
     const int n0 = nt * W_BN;
     const int nsteps = K / W_BK;
     const int sb = SPLIT ? blockIdx.y * spl : 0;          // this block's k-steps [sb, se), even count
@@ -499,13 +510,13 @@ __global__ __launch_bounds__(256, 1) void prefill_f16_wide_kernel(
     const __amdgpu_buffer_rsrc_t rz =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(zsrc), 0, 0x7FFFFFFF, 0x00020000);
 
-    // activation staging: instruction j of wave w fills slots (8 w + j) * 64 + lane, i.e.
-    // row r = (8 w + j) * 8 + lane / 8, slot lane % 8, which holds column piece
+    // activation staging: instruction j of wave w fills slots (MS w + j) * 64 + lane, i.e.
+    // row r = (MS w + j) * 8 + lane / 8, slot lane % 8, which holds column piece
     // (lane % 8) ^ ((r / 2) % 8)
-    int xoff[8];
+    int xoff[MS];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int r = (8 * wave + j) * 8 + (lane >> 3);
+    for (int j = 0; j < MS; ++j) {
+        const int r = (MS * wave + j) * 8 + (lane >> 3);
         const int c = (lane & 7) ^ ((r >> 1) & 7);
         xoff[j] = (min(m0 + r, M - 1) * K + 8 * c) * 2;
     }
@@ -518,10 +529,7 @@ __global__ __launch_bounds__(256, 1) void prefill_f16_wide_kernel(
     }
     auto load_a = [&](int buf, int step) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rx, (__attribute__((address_space(3))) void*)&As[buf][(8 * wave + j) * 64], 16,
-                xoff[j], step * W_BK * 2, 0, 0);
+        for (int j = 0; j < MS; ++j) lds_load16(rx, &As[buf][(MS * wave + j) * 64], xoff[j], step * W_BK * 2);
     };
     constexpr int WL = BITS == 4 ? 1 : 2;        // 16-byte weight loads per row and step
     struct WStage {
@@ -563,9 +571,9 @@ __global__ __launch_bounds__(256, 1) void prefill_f16_wide_kernel(
         }
     };
 
-    f32x16 acc[8][2];
+    f32x16 acc[MS][2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < MS; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -582,19 +590,19 @@ __global__ __launch_bounds__(256, 1) void prefill_f16_wide_kernel(
     auto compute = [&](int buf, const uint32_t bc[2][4][4], const WStage& nx, uint32_t bn[2][4][4]) {
         const u32x4* A = As[buf];
         const WConst nc = stage_const(nx);
-        u32x4 fa[8], fb[8];        // activation fragments one MFMA group ahead
+        u32x4 fa[MS], fb[MS];      // activation fragments one MFMA group ahead
 #pragma unroll
-        for (int ms = 0; ms < 8; ++ms) fa[ms] = A[ms * 256 + fslot[0]];
+        for (int ms = 0; ms < MS; ++ms) fa[ms] = A[ms * 256 + fslot[0]];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             u32x4* cur = (j & 1) ? fb : fa;
             u32x4* nxt = (j & 1) ? fa : fb;
             if (j < 3) {
 #pragma unroll
-                for (int ms = 0; ms < 8; ++ms) nxt[ms] = A[ms * 256 + fslot[j + 1]];
+                for (int ms = 0; ms < MS; ++ms) nxt[ms] = A[ms * 256 + fslot[j + 1]];
             }
 #pragma unroll
-            for (int ms = 0; ms < 8; ++ms) {
+            for (int ms = 0; ms < MS; ++ms) {
                 const uint32_t af[4] = {cur[ms].x, cur[ms].y, cur[ms].z, cur[ms].w};
 #pragma unroll
                 for (int ns = 0; ns < 2; ++ns) acc[ms][ns] = Mfma<DT_F16>::run(af, bc[ns][j], acc[ms][ns]);
@@ -602,11 +610,11 @@ __global__ __launch_bounds__(256, 1) void prefill_f16_wide_kernel(
             dequant_word(nx, nc, j, bn);
             // interleave: one fragment read and a few dequant instructions per MFMA pair
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if (j < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);              // VALU
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
+            for (int i = 0; i < MS; ++i) {
+                if (j < 3) sched_group<0x100, 1>();   // DS read
+                sched_group<0x008, 1>();              // MFMA
+                sched_group<0x002, 5>();              // VALU
+                sched_group<0x008, 1>();              // MFMA
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -639,7 +647,7 @@ __global__ __launch_bounds__(256, 1) void prefill_f16_wide_kernel(
     }
 
 #pragma unroll
-    for (int ms = 0; ms < 8; ++ms) {
+    for (int ms = 0; ms < MS; ++ms) {
 #pragma unroll
         for (int ns = 0; ns < 2; ++ns) {
             const int n = n0 + 64 * wave + 32 * ns + l32;
@@ -724,6 +732,38 @@ hipError_t launch_prefill_splitk(const LinearArgs& a, float* work, hipStream_t s
     return hipGetLastError();
 }
 
+// Rows per block of the wide kernel (MS 32-row MFMA tiles): 256, halved while the grid has
+// fewer than 160 blocks and the halved tile still gives at most one block per CU (a smaller
+// tile dequantizes the same weights for fewer rows, so it only pays where CUs would idle).
+// Measured (plain call, g = 128): M = 256, 4096 -> 11008: 104.8 -> 76.8 us (64 rows);
+// M = 1024, 11008 -> 4096: 272 -> 203 us (64 rows); M = 2048, 11008 -> 4096: 282 -> 245 us
+// (128 rows); M = 1024, 4096 -> 11008 keeps 256 rows (172 blocks: 125 us, 138 us at 128).
+int wide_blocks(int M, int N, int ms) { return ((M + 32 * ms - 1) / (32 * ms)) * ((N + W_BN - 1) / W_BN); }
+int wide_ms(int M, int N) {
+    int ms = 8;
+    while (ms > 2 && (long long)wide_blocks(M, N, ms) < 160 && (long long)wide_blocks(M, N, ms / 2) <= 256) ms /= 2;
+    return ms;
+}
+
+template <bool HZ, int BITS>
+hipError_t launch_wide(const LinearArgs& a, hipStream_t st) {
+    const int ms = wide_ms(a.M, a.N);
+    const int tiles = wide_blocks(a.M, a.N, ms);
+    const dim3 grid(8 * ((tiles + 7) / 8));
+    const uint16_t* X = static_cast<const uint16_t*>(a.X);
+    uint16_t* Y = static_cast<uint16_t*>(a.Y);
+    if (ms == 8)
+        hipLaunchKernelGGL((prefill_f16_wide_kernel<HZ, BITS, false, 8>), grid, dim3(256), 0, st, X, a.qw,
+                           a.scales, a.zeros, Y, a.M, a.N, a.K, a.G, a.gshift, nullptr, 0);
+    else if (ms == 4)
+        hipLaunchKernelGGL((prefill_f16_wide_kernel<HZ, BITS, false, 4>), grid, dim3(256), 0, st, X, a.qw,
+                           a.scales, a.zeros, Y, a.M, a.N, a.K, a.G, a.gshift, nullptr, 0);
+    else
+        hipLaunchKernelGGL((prefill_f16_wide_kernel<HZ, BITS, false, 2>), grid, dim3(256), 0, st, X, a.qw,
+                           a.scales, a.zeros, Y, a.M, a.N, a.K, a.G, a.gshift, nullptr, 0);
+    return hipGetLastError();
+}
+
 bool prefill_supports(const LinearArgs& a) {
     if (a.dtype == DT_F16) return a.K % F_BK == 0 && a.g % F_BK == 0;   // any supported g
     return a.K % BK == 0 && a.g % BK == 0;
@@ -735,19 +775,8 @@ hipError_t launch_prefill(const LinearArgs& a, hipStream_t st) {
     // buffer offsets; larger operands take the 64-bit addressed kernel
     const bool offsets32 = (long long)a.M * a.K * 2 < (1LL << 31) && (long long)a.N * (a.K / 2) < (1LL << 31) &&
                            (long long)a.N * a.G * 2 < (1LL << 31);
-    if (a.dtype == DT_F16 && a.K % (2 * W_BK) == 0 && offsets32) {
-        const int tiles = ((a.M + W_BM - 1) / W_BM) * ((a.N + W_BN - 1) / W_BN);
-        const int grid = 8 * ((tiles + 7) / 8);
-        if (hz)
-            hipLaunchKernelGGL(prefill_f16_wide_kernel<true>, dim3(grid), dim3(256), 0, st,
-                               static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros,
-                               static_cast<uint16_t*>(a.Y), a.M, a.N, a.K, a.G, a.gshift);
-        else
-            hipLaunchKernelGGL(prefill_f16_wide_kernel<false>, dim3(grid), dim3(256), 0, st,
-                               static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros,
-                               static_cast<uint16_t*>(a.Y), a.M, a.N, a.K, a.G, a.gshift);
-        return hipGetLastError();
-    }
+    if (a.dtype == DT_F16 && a.K % (2 * W_BK) == 0 && offsets32)
+        return hz ? launch_wide<true, 4>(a, st) : launch_wide<false, 4>(a, st);
     if (a.dtype == DT_F16) {
         const int tiles = ((a.M + F_BM - 1) / F_BM) * ((a.N + F_BN - 1) / F_BN);
         hipLaunchKernelGGL(prefill_f16_kernel, dim3(tiles), dim3(256), 0, st,
@@ -769,22 +798,11 @@ bool prefill8_supports(const LinearArgs& a) { return a.K % BK == 0 && a.g % BK =
 hipError_t launch_prefill8(const LinearArgs& a, hipStream_t st) {
     if (!prefill8_supports(a)) return hipErrorInvalidValue;
     const int hz = a.zeros ? 1 : 0;
-    // fp16: the 256 x 256 kernel while its 32-bit buffer offsets cover the operands
+    // fp16: the wide kernel while its 32-bit buffer offsets cover the operands
     const bool offsets32 = (long long)a.M * a.K * 2 < (1LL << 31) && (long long)a.N * a.K < (1LL << 31) &&
                            (long long)a.N * a.G * 2 < (1LL << 31);
-    if (a.dtype == DT_F16 && a.K % (2 * W_BK) == 0 && offsets32) {
-        const int tiles = ((a.M + W_BM - 1) / W_BM) * ((a.N + W_BN - 1) / W_BN);
-        const int grid = 8 * ((tiles + 7) / 8);
-        if (hz)
-            hipLaunchKernelGGL((prefill_f16_wide_kernel<true, 8>), dim3(grid), dim3(256), 0, st,
-                               static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros,
-                               static_cast<uint16_t*>(a.Y), a.M, a.N, a.K, a.G, a.gshift);
-        else
-            hipLaunchKernelGGL((prefill_f16_wide_kernel<false, 8>), dim3(grid), dim3(256), 0, st,
-                               static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros,
-                               static_cast<uint16_t*>(a.Y), a.M, a.N, a.K, a.G, a.gshift);
-        return hipGetLastError();
-    }
+    if (a.dtype == DT_F16 && a.K % (2 * W_BK) == 0 && offsets32)
+        return hz ? launch_wide<true, 8>(a, st) : launch_wide<false, 8>(a, st);
     const long long tiles = (long long)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
     const int spg = a.g / BK;
