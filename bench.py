@@ -507,6 +507,62 @@ def trace_summary(run_dir: str, out_path: str, header: str = ""):
     print("\n".join(lines[:40]))
 
 
+def counter_summary(run_dirs, out_path: str, header: str = ""):
+    """Per-kernel means of the counters of one or more rocprofv3 --pmc runs (each run's
+    counter_collection csv), with derived figures: matrix-core busy share, L2 hit rate and
+    miss bytes, instructions per wave, the share of wave cycles spent waiting, LDS bank
+    conflict cycles.  Counter values are means per dispatch."""
+    import csv
+    import glob
+    sums, grid = {}, {}
+    for d in run_dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    k = r["Kernel_Name"]
+                    sums.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                    if r.get("Grid_Size"):
+                        grid[k] = r["Grid_Size"]
+    if not sums:
+        raise SystemExit(f"no counter_collection csv under {run_dirs}")
+
+    def short(n):
+        return n.replace("w4a16::(anonymous namespace)::", "").replace("void ", "").split("(unsigned")[0][:90]
+
+    lines = [header.rstrip("\n")] if header else []
+    for k in sorted(sums, key=lambda k: -max(sum(v) for v in sums[k].values())):
+        c = {n: sum(v) / len(v) for n, v in sums[k].items()}
+        lines.append(f"{short(k)}  (grid {grid.get(k, '?')} threads)")
+        lines.append("  raw: " + ", ".join(f"{n}={c[n]:.0f}" for n in sorted(c)))
+        d = []
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c and c.get("GRBM_GUI_ACTIVE"):
+            d.append(f"MFMA busy {100 * (c['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024) / (c['GRBM_GUI_ACTIVE'] / 8):.1f} %")
+        if "TCC_HIT_sum" in c and "TCC_MISS_sum" in c:
+            t = c["TCC_HIT_sum"] + c["TCC_MISS_sum"]
+            d.append(f"L2 hit rate {100 * c['TCC_HIT_sum'] / max(t, 1):.1f} %, miss bytes "
+                     f"{c['TCC_MISS_sum'] * 128 / 1e6:.1f} MB")
+        w = c.get("SQ_WAVES")
+        if w:
+            per = [f"{c[n] / w:.0f} {lab}" for n, lab in (("SQ_INSTS_VALU", "VALU"), ("SQ_INSTS_MFMA", "MFMA"),
+                                                           ("SQ_INSTS_VMEM_RD", "VMEM reads"), ("SQ_INSTS_LDS", "LDS"),
+                                                           ("SQ_INSTS_SALU", "SALU")) if n in c]
+            if per:
+                d.append("per wave: " + ", ".join(per))
+        wc = c.get("SQ_WAVE_CYCLES")
+        if wc:
+            fr = [f"{lab} {100 * c[n] / wc:.0f} %" for n, lab in (("SQ_WAIT_ANY", "any"),
+                                                                  ("SQ_WAIT_INST_ANY", "on instruction dependencies"))
+                  if n in c]
+            if fr:
+                d.append("waiting: " + ", ".join(fr))
+        if "SQ_LDS_BANK_CONFLICT" in c:
+            d.append(f"LDS bank conflict cycles {c['SQ_LDS_BANK_CONFLICT']:.0f}")
+        lines.append("  derived: " + "; ".join(d))
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines[:60]))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -527,11 +583,18 @@ def main():
     ap.add_argument("--trace-summary", nargs=2, metavar=("RUN_DIR", "OUT"),
                     help="per-kernel duration statistics of a rocprofv3 --kernel-trace run")
     ap.add_argument("--trace-header", default="", help="text put above the --trace-summary table")
+    ap.add_argument("--counter-summary", nargs="+", metavar="RUN_DIR... OUT",
+                    help="per-kernel counter means and derived figures of rocprofv3 --pmc runs")
     ap.add_argument("--profile-run", choices=["prefill", "w8a8", "kv_batch", "decode_m16", "w8a16", "c3"],
                     help="a short fixed workload of one kernel family, for counter runs")
     args = ap.parse_args()
     if args.trace_summary:
         trace_summary(args.trace_summary[0], args.trace_summary[1], args.trace_header)
+        return
+    if args.counter_summary:
+        if len(args.counter_summary) < 2:
+            raise SystemExit("--counter-summary needs at least one run directory and an output path")
+        counter_summary(args.counter_summary[:-1], args.counter_summary[-1], args.trace_header)
         return
 
     def shape_arg(v):
