@@ -470,10 +470,18 @@ def traffic_parse(fetch_dir: str, write_dir: str, shape, commands, out_path=None
     print(json.dumps(out))
 
 
+def _library_kernel(name: str) -> bool:
+    """False for the framework's own helper kernels that a profiled workload launches while it
+    sets up inputs (torch's random generators, sorts, casts): summaries leave them out."""
+    return not (name.startswith("at::") or name.startswith("void at::") or "rocprim::" in name
+                or "randperm" in name or name.startswith("(anonymous namespace)::elementwise")
+                or name.startswith("void (anonymous namespace)::elementwise"))
+
+
 def trace_summary(run_dir: str, out_path: str, header: str = ""):
     """Per-kernel duration statistics of a rocprofv3 --kernel-trace --stats run: calls, average,
     p10, median, p90, min, max and share of the total, from every dispatch's end - start in the
-    run's kernel_trace csv (all csv files under run_dir)."""
+    run's kernel_trace csv (all csv files under run_dir); torch's setup kernels left out."""
     import csv
     import glob
     durs = {}
@@ -481,6 +489,8 @@ def trace_summary(run_dir: str, out_path: str, header: str = ""):
         with open(f) as fh:
             for row in csv.DictReader(fh):
                 name = row.get("Kernel_Name") or row.get("Name") or "?"
+                if not _library_kernel(name):
+                    continue
                 d = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1000.0
                 durs.setdefault(name, []).append(d)
     if not durs:
@@ -520,6 +530,8 @@ def counter_summary(run_dirs, out_path: str, header: str = ""):
             with open(f) as fh:
                 for r in csv.DictReader(fh):
                     k = r["Kernel_Name"]
+                    if not _library_kernel(k):
+                        continue
                     sums.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
                     if r.get("Grid_Size"):
                         grid[k] = r["Grid_Size"]
