@@ -474,13 +474,20 @@ constexpr int W_BM = 256, W_BN = 256, W_BK = 64;     // K % 128 == 0: steps in p
 // stores the fp32 partial tile to part[y][M][N]; splitk_reduce_kernel sums the partials in
 // split order.  Without a split, spl = K / 64, grid y = 1 and the tile goes to Y.
 template <bool HZ, int BITS = 4, bool SPLIT = false, int MS = 8>
-__global__ __launch_bounds__(256, (MS >= 8 || BITS == 8) ? 1 : 2) void prefill_f16_wide_kernel(
+__global__ __launch_bounds__(256, (MS >= 8 || BITS == 8 || (MS == 2 && !SPLIT)) ? 1 : 2) void prefill_f16_wide_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros,
     uint16_t* __restrict__ Y, int M, int N, int K, int G, int gshift,
     float* __restrict__ part = nullptr, int spl = 0) {
     constexpr int BMk = 32 * MS;                                       // block rows
-    __shared__ __attribute__((aligned(16))) u32x4 As[2][BMk * 8];      // 2 x 32 KB at 256 rows
+    // the activation double buffer as two LDS objects, so that the compiler's wait before a
+    // fragment read covers only the loads into that buffer (one object would make every read
+    // wait for the other buffer's loads, issued for the next step)
+    __shared__ __attribute__((aligned(16))) u32x4 As0[BMk * 8];        // 32 KB at 256 rows
+    __shared__ __attribute__((aligned(16))) u32x4 As1[BMk * 8];
+    // 64-row blocks run three steps deep (below): a third activation buffer
+    constexpr bool DEEP = MS == 2 && BITS == 4 && !SPLIT;
+    __shared__ __attribute__((aligned(16))) u32x4 As2[DEEP ? BMk * 8 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -527,9 +534,9 @@ __global__ __launch_bounds__(256, (MS >= 8 || BITS == 8) ? 1 : 2) void prefill_f
         woff[ns] = wrow * (BITS == 4 ? K / 2 : K) + (BITS == 4 ? 16 : 32) * h;
         szoff[ns] = wrow * G * 2;
     }
-    auto load_a = [&](int buf, int step) {
+    auto load_a = [&](u32x4* As, int step) {
 #pragma unroll
-        for (int j = 0; j < MS; ++j) lds_load16(rx, &As[buf][(MS * wave + j) * 64], xoff[j], step * W_BK * 2);
+        for (int j = 0; j < MS; ++j) lds_load16(rx, &As[(MS * wave + j) * 64], xoff[j], step * W_BK * 2);
     };
     constexpr int WL = BITS == 4 ? 1 : 2;        // 16-byte weight loads per row and step
     struct WStage {
@@ -587,8 +594,7 @@ __global__ __launch_bounds__(256, (MS >= 8 || BITS == 8) ? 1 : 2) void prefill_f
     // One step: MFMAs on the activations in LDS buffer `buf` and the dequantized weights
     // `bc`, while the next step's packed weights `nx` are dequantized into `bn`, one word
     // per MFMA group so the VALU work hides under the matrix instructions.
-    auto compute = [&](int buf, const uint32_t bc[2][4][4], const WStage& nx, uint32_t bn[2][4][4]) {
-        const u32x4* A = As[buf];
+    auto compute = [&](const u32x4* A, const uint32_t bc[2][4][4], const WStage& nx, uint32_t bn[2][4][4]) {
         const WConst nc = stage_const(nx);
         u32x4 fa[MS], fb[MS];      // activation fragments one MFMA group ahead
 #pragma unroll
@@ -620,30 +626,82 @@ __global__ __launch_bounds__(256, (MS >= 8 || BITS == 8) ? 1 : 2) void prefill_f
         }
     };
 
-    // Pipeline: activations one step ahead (global -> LDS), packed weights one step ahead
-    // and dequantized weights one step ahead (registers).  The LDS-destination loads are
-    // complete when vmcnt drains; each step ends with that wait and a barrier.  Loads past
-    // the last step re-read it (harmless, unused).
-    WStage p0, p1;
-    uint32_t b0[2][4][4], b1[2][4][4];
-    load_a(0, sb);
-    load_w(p0, sb);
-    load_w(p1, min(sb + 1, se - 1));
+    // Pipeline: activations one step ahead (global -> LDS), packed weights two steps ahead
+    // and dequantized weights one step ahead (registers).  A step issues the next step's
+    // activation loads and the packed weights of the step after, and ends once the next
+    // activation tile is in LDS (step_end), leaving the weight loads in flight: they are needed
+    // one step later.  Loads past the last step re-read it (harmless, unused).
+    // End of a step: this wave's loads into the next activation buffer must have landed
+    // before the barrier (other waves read them after it).  A read of one of this wave's own
+    // words of that buffer makes the compiler wait for exactly those loads (it tracks the
+    // LDS-destination loads per LDS object), whatever order it gave the loads; the bare
+    // s_barrier then leaves the weight loads in flight (__syncthreads() would drain them).
+    auto step_end = [&](const u32x4* next) {
+        const u32x4 v = next[(MS * wave) * 64 + lane];
+        asm volatile("" ::"v"(v.x));
+        __builtin_amdgcn_s_barrier();
+    };
+    if constexpr (DEEP) {
+        // 64-row blocks: a k-step's matrix work (16 MFMAs per wave) is shorter than a memory
+        // round trip, so with one step of prefetch every step waited for its loads (1.2 us per
+        // step against about 0.45 us of MFMA).  Three stages: step s computes on activation
+        // buffer s % 3 and dequantized weights b[s % 3], dequantizes packed stage (s + 1) % 3,
+        // and issues the activations of step s + 2 and the packed weights of step s + 3 (into
+        // the stage step s's weights left); it ends once the activations of step s + 1 are in.
+        WStage p0, p1, p2;
+        uint32_t b0[2][4][4], b1[2][4][4], b2[2][4][4];
+        load_a(As0, sb);
+        load_a(As1, min(sb + 1, se - 1));
+        load_w(p0, sb);
+        load_w(p1, min(sb + 1, se - 1));
+        load_w(p2, min(sb + 2, se - 1));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dequant_word(p0, stage_const(p0), j, b0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    for (int step = sb; step < se; step += 2) {
-        load_a(1, min(step + 1, se - 1));
-        load_w(p0, min(step + 2, se - 1));
-        compute(0, b0, p1, b1);
+        for (int j = 0; j < 4; ++j) dequant_word(p0, stage_const(p0), j, b0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        load_a(0, min(step + 2, se - 1));
-        load_w(p1, min(step + 3, se - 1));
-        compute(1, b1, p0, b0);
+        // the loop body is one basic block: with a branch between its steps the compiler sank
+        // each weight load into the block of its use, undoing the prefetch
+        int step = sb;
+        for (; step + 3 <= se; step += 3) {
+            load_a(As2, min(step + 2, se - 1));
+            load_w(p0, min(step + 3, se - 1));
+            compute(As0, b0, p1, b1);
+            step_end(As1);
+            load_a(As0, min(step + 3, se - 1));
+            load_w(p1, min(step + 4, se - 1));
+            compute(As1, b1, p2, b2);
+            step_end(As2);
+            load_a(As1, min(step + 4, se - 1));
+            load_w(p2, min(step + 5, se - 1));
+            compute(As2, b2, p0, b0);
+            step_end(As0);
+        }
+        // the last one or two steps: their activations and weights are already in flight
+        if (step < se) {                                  // uniform
+            compute(As0, b0, p1, b1);
+            step_end(As1);
+            if (step + 1 < se) compute(As1, b1, p2, b2);
+        }
+    } else {
+        WStage p0, p1;
+        uint32_t b0[2][4][4], b1[2][4][4];
+        load_a(As0, sb);
+        load_w(p0, sb);
+        load_w(p1, min(sb + 1, se - 1));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dequant_word(p0, stage_const(p0), j, b0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+        for (int step = sb; step < se; step += 2) {
+            load_a(As1, min(step + 1, se - 1));
+            load_w(p0, min(step + 2, se - 1));
+            compute(As0, b0, p1, b1);
+            step_end(As1);
+            load_a(As0, min(step + 2, se - 1));
+            load_w(p1, min(step + 3, se - 1));
+            compute(As1, b1, p0, b0);
+            step_end(As0);
+        }
     }
 
 #pragma unroll
