@@ -665,12 +665,8 @@ constexpr int kDefaultLdsLimit = 64 * 1024;     // dynamic LDS above this must b
 #ifndef W4A16_TWO_ROW_BLOCKS
 #define W4A16_TWO_ROW_BLOCKS 768
 #endif
-#ifndef W4A16_PERSIST_BLOCKS
-#define W4A16_PERSIST_BLOCKS 256
-#endif
-#ifndef W4A16_STREAM_NB
-#define W4A16_STREAM_NB 2
-#endif
+constexpr int kPersistBlocks = 256;                    // one CU-resident block per CU
+constexpr int kStreamBatches = 2;                      // row batches in flight per wave
 constexpr int kStreamWaves = W4A16_STREAM_WAVES;       // waves per block: two per SIMD
 
 struct LdsCfg {
@@ -698,7 +694,7 @@ LdsCfg pick_lds(int M, int N, int K, int G) {
     if (cpl > lds_max_cpl(M)) return c;
     // 32-bit buffer offsets: the packed weights must stay below 2 GiB
     if ((long long)N * (K / 2) >= (1LL << 31)) return c;
-    int rpb = (N + W4A16_PERSIST_BLOCKS - 1) / W4A16_PERSIST_BLOCKS;
+    int rpb = (N + kPersistBlocks - 1) / kPersistBlocks;
     if ((M == 1 && cpl >= 4) || (N + kStreamWaves - 1) / kStreamWaves <= kOneRowBlocks)
         rpb = kStreamWaves;
     else if ((N + 2 * kStreamWaves - 1) / (2 * kStreamWaves) <= kTwoRowBlocks)
@@ -741,7 +737,7 @@ hipError_t run_one(const LinearArgs& a, const LdsCfg& c, hipStream_t st) {
         if (c.rows_per_block != kStreamWaves) return hipErrorInvalidValue;
         return run_lds4<DT, 1, CPL, 1, 0>(a, c, st);
     } else if constexpr (RB > kOneShotRows || RB * M * CPL > kOneShotLoads) {
-        return run_lds4<DT, M, CPL, lds_rb(M, CPL), W4A16_STREAM_NB>(a, c, st);
+        return run_lds4<DT, M, CPL, lds_rb(M, CPL), kStreamBatches>(a, c, st);
     } else {
         if (c.rows_per_block <= RB * kStreamWaves) return run_lds4<DT, M, CPL, RB, 0>(a, c, st);
         return run_one<DT, M, CPL, RB + 1>(a, c, st);
