@@ -119,7 +119,10 @@ def test_dequantize_rejects_invalid_arguments(lib):
     (16, 4096, 4096, 128, 0, L.PATH_SKINNY),
     (8, 4096, 11008, 128, 1, L.PATH_SKINNY),          # MFMA decode kernel, 5 <= M <= 16
     (17, 4096, 4096, 128, 0, L.PATH_SKINNY),
-    (1, 8192, 28672, 128, 1, L.PATH_GEMV),
+    (1, 8192, 28672, 128, 1, L.PATH_SKINNY),         # one row of K > 24576: the MFMA decode kernel
+    (1, 8192, 24576, 128, 1, L.PATH_GEMV),
+    (1, 28672, 8192, 128, 0, L.PATH_GEMV),
+    (1, 8192, 28672, 64, 0, L.PATH_GEMV),             # g = 64: the MFMA decode kernel needs g % 128 == 0
     (4096, 11008, 4096, 128, 0, L.PATH_PREFILL),
     (1024, 4096, 11008, 64, 0, L.PATH_PREFILL),
     (1, 4096, 11008, 11008, 1, L.PATH_GEMV),          # per-channel

@@ -104,8 +104,11 @@ bool skinny_beats_tiled(const LinearArgs& a) {
 
 int choose_path(const LinearArgs& a) {
     // measured on MI355X: the v_dot2 GEMV leads for one row and for two rows of short K
-    // (K <= 4096), the MFMA decode kernels (skinny path, 1 <= M <= 16) from there on
-    if ((a.M == 1 || (a.M == 2 && a.K <= 4096)) && w4a16::gemv_supports(a)) return W4A16_PATH_GEMV;
+    // (K <= 4096), the MFMA decode kernels (skinny path, 1 <= M <= 16) from there on; one row
+    // of K > 24576 streams faster through the MFMA decode kernel's LDS ring (N = 8192:
+    // K = 28672 23.9 against 27.2 us, K = 24576 21.8 against 20.8 us)
+    const bool long_row = a.M == 1 && a.K > 24576 && w4a16::decode_supports(a);
+    if ((a.M == 1 || (a.M == 2 && a.K <= 4096)) && !long_row && w4a16::gemv_supports(a)) return W4A16_PATH_GEMV;
     if (a.M <= 16 && w4a16::decode_supports(a)) return W4A16_PATH_SKINNY;
     if (a.M <= 4 && w4a16::gemv_supports(a)) return W4A16_PATH_GEMV;
     if (a.M <= 32 && w4a16::skinny_supports(a)) return W4A16_PATH_SKINNY;
