@@ -349,8 +349,19 @@ def profile_run(name: str, W4, synth, torch):
     16 sequences, 2 layers' caches, 2 launches each), `decode_m16` (M = 16 on the 7B shapes
     over 20 rotating weight copies, 20 launches each), `w8a16` (8-bit codes: M = 1 and 4 on the 7B
     shapes over 10 rotating copies, 20 launches each, and the M = 4096 prefill, 5 each), `c3`
-    (the 70B-like bf16 decode shapes at M = 1, 4, 16 over 4 rotating copies, 20 launches each)."""
-    if name == "prefill":
+    (the 70B-like bf16 decode shapes at M = 1, 4, 16 over 4 rotating copies, 20 launches each),
+    `crossover` (the plain prefill call at M = 256 on (4096, 11008) and at M = 1024 on
+    (11008, 4096), g = 128 asym, 5 launches each)."""
+    if name == "crossover":
+        for M, K, N in [(256, 4096, 11008), (1024, 11008, 4096)]:
+            W = synth.weights_device(N, K, 0.02, 3100 + K)
+            qw, s, z = W4.quantize_pack(W, GROUP, W4.ASYM)
+            del W
+            X = synth.activations_device(M, K, synth.FP16, 3101 + K)
+            Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+            for _ in range(5):
+                W4.linear(X, qw, s, z, GROUP, out=Y)
+    elif name == "prefill":
         for K, N in [(4096, 11008), (11008, 4096)]:
             W = synth.weights_device(N, K, 0.02, 3000 + K)
             qw, s, z = W4.quantize_pack(W, GROUP, W4.ASYM)
@@ -597,7 +608,7 @@ def main():
     ap.add_argument("--trace-header", default="", help="text put above the --trace-summary table")
     ap.add_argument("--counter-summary", nargs="+", metavar="RUN_DIR... OUT",
                     help="per-kernel counter means and derived figures of rocprofv3 --pmc runs")
-    ap.add_argument("--profile-run", choices=["prefill", "w8a8", "kv_batch", "decode_m16", "w8a16", "c3"],
+    ap.add_argument("--profile-run", choices=["prefill", "crossover", "w8a8", "kv_batch", "decode_m16", "w8a16", "c3"],
                     help="a short fixed workload of one kernel family, for counter runs")
     args = ap.parse_args()
     if args.trace_summary:

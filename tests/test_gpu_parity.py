@@ -138,7 +138,14 @@ SKINNY_CASES = [(1, 64, 128, 128), (5, 100, 1024, 128), (16, 256, 4096, 128), (1
                 (33, 300, 1024, 128), (100, 257, 2048, 128), (256, 1000, 4096, 256), (512, 64, 1024, 1024),
                 (130, 4096, 11008, 128)]
 PREFILL_CASES = [(1, 64, 64, 64), (17, 200, 192, 64), (130, 129, 256, 128), (256, 384, 1024, 128),
-                 (300, 256, 4096, 4096), (64, 128, 11008, 128), (129, 1, 128, 64)]
+                 (300, 256, 4096, 4096), (64, 128, 11008, 128), (129, 1, 128, 64),
+                 # fp16: 128-row tiles with K split over two wave groups (K % 256 == 0), ragged M and
+                 # N; then K % 256 != 0, which keeps one group
+                 (1100, 4000, 768, 128), (1100, 4096, 640, 64),
+                 # 64-row tiles, three-stage loop: 3 and 4 steps per wave group
+                 (70, 520, 384, 128), (70, 520, 512, 64),
+                 # 172 groups per row: more than the kernel stages in LDS, loaded per step instead
+                 (64, 130, 11008, 64)]
 # fp16 prefill also takes K % 64 == 32 and g == 32 (bf16 prefill needs multiples of 64)
 PREFILL_F16_CASES = [(40, 150, 96, 32), (257, 300, 160, 32), (70, 64, 96, 96), (513, 260, 2080, 32)]
 

@@ -24,6 +24,8 @@
 //     group's last step acc += s'[n] * (acc_g - c[n] * S_g[m]) with S_g the group's
 //     activation sum of row m (computed while staging), fp16: s' = s * 2^24, c = z and S_g
 //     in units of 2^-24; bf16: s' = s, c = 128 + z.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 #include "tile.h"
@@ -466,6 +468,7 @@ __device__ __forceinline__ void sched_group() {
 }
 
 constexpr int W_BM = 256, W_BN = 256, W_BK = 64;     // K % 128 == 0: steps in pairs
+constexpr int kSzlPieces = 12;           // SZL: at most 96 groups per block k-range
 
 // BITS = 8 (W8A16): lane (n, h) loads the 32 bytes of columns 32h .. 32h + 31 (two 16-byte
 // loads) and MFMA j takes words 2j and 2j + 1 (one byte permute per pair instead of the nibble
@@ -473,25 +476,44 @@ constexpr int W_BM = 256, W_BN = 256, W_BK = 64;     // K % 128 == 0: steps in p
 // Split K (part != NULL): block (x, y) runs k-steps [y * spl, (y + 1) * spl) of its tile and
 // stores the fp32 partial tile to part[y][M][N]; splitk_reduce_kernel sums the partials in
 // split order.  Without a split, spl = K / 64, grid y = 1 and the tile goes to Y.
-template <bool HZ, int BITS = 4, bool SPLIT = false, int MS = 8>
-__global__ __launch_bounds__(256, (MS >= 8 || BITS == 8 || (MS == 2 && !SPLIT)) ? 1 : 2) void prefill_f16_wide_kernel(
+//
+// KG = 2 splits K inside the block: wave w works on columns 64 (w % 4) ... of the tile over the
+// k-steps of parity w / 4 (two wave groups in lockstep, each with its own activation tiles),
+// and the second group's accumulators are added to the first's through LDS at the end, in
+// fixed order.  It doubles the waves per SIMD for tiles of 64 and 128 rows, which a grid of at
+// most one block per CU otherwise runs one wave per SIMD, without any buffer outside the block.
+// The host launches KG = 2 only with a step count the loops divide (K % 128 == 0 with 64-row
+// tiles, K % 256 == 0 with 128-row ones).
+//
+// SZL: the block's scales and zeros for its k-range sit in LDS (dynamic, gp dwords per weight
+// row, s | z << 16, gp odd so the 32 rows a wave reads per step fall in distinct banks),
+// staged once at the start by one thread per row with 16-byte loads.  Loading them per step
+// instead costs four 2-byte loads per wave and step, each touching 32 rows' cache lines: with
+// 64-row tiles that was half of the address unit's work, and the address unit, not the
+// matrix cores, set the pace.
+template <bool HZ, int BITS = 4, bool SPLIT = false, int MS = 8, int KG = 1, bool SZL = false>
+__global__ __launch_bounds__(256 * KG, (MS >= 8 || BITS == 8 || (MS == 2 && !SPLIT) || KG > 1 || SZL) ? 1 : 2) void prefill_f16_wide_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros,
     uint16_t* __restrict__ Y, int M, int N, int K, int G, int gshift,
-    float* __restrict__ part = nullptr, int spl = 0) {
+    float* __restrict__ part = nullptr, int spl = 0, int gp = 0) {
+    static_assert(KG == 1 || (KG == 2 && BITS == 4 && !SPLIT && MS <= 4), "k-groups: 4-bit, plain, <= 128 rows");
     constexpr int BMk = 32 * MS;                                       // block rows
+    constexpr int ASZ = BMk * 8;                                       // one group's tile, 16-byte slots
     // the activation double buffer as two LDS objects, so that the compiler's wait before a
     // fragment read covers only the loads into that buffer (one object would make every read
     // wait for the other buffer's loads, issued for the next step)
-    __shared__ __attribute__((aligned(16))) u32x4 As0[BMk * 8];        // 32 KB at 256 rows
-    __shared__ __attribute__((aligned(16))) u32x4 As1[BMk * 8];
+    __shared__ __attribute__((aligned(16))) u32x4 As0[KG * ASZ];       // 32 KB at 256 rows
+    __shared__ __attribute__((aligned(16))) u32x4 As1[KG * ASZ];
     // 64-row blocks run three steps deep (below): a third activation buffer
-    constexpr bool DEEP = MS == 2 && BITS == 4 && !SPLIT;
-    __shared__ __attribute__((aligned(16))) u32x4 As2[DEEP ? BMk * 8 : 1];
+    constexpr bool DEEP = MS == 2 && BITS == 4 && !SPLIT && KG == 1;
+    __shared__ __attribute__((aligned(16))) u32x4 As2[DEEP ? KG * ASZ : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = (tid >> 6) & 3;                     // column quarter of the tile
+    const int kg = KG > 1 ? tid >> 8 : 0;                 // k-step parity of this wave's group
+    const int abase = kg * ASZ;                           // this group's activation tiles
     const int l32 = lane & 31;
     const int h = lane >> 5;
     int mt, nt;
@@ -504,6 +526,14 @@ __global__ __launch_bounds__(256, (MS >= 8 || BITS == 8 || (MS == 2 && !SPLIT)) 
     if constexpr (SPLIT) {
         if (sb >= se) return;                             // never planned (every split has steps)
     }
+    // local step t of this group is k-step sb + kg + KG t; L local steps per group; a load
+    // past the group's last step re-reads that step (unused)
+    const int L = (se - sb) / KG;
+    auto gstep = [&](int t) { return sb + kg + KG * min(t, L - 1); };
+    // SZL: groups [g0, g0 + gl) of the block's k-range, staged in LDS
+    extern __shared__ __attribute__((aligned(16))) uint32_t szl[];
+    const int g0 = SZL ? (sb * W_BK) >> gshift : 0;
+    const int gl = SZL ? (((se * W_BK) - 1) >> gshift) + 1 - g0 : 0;
 
     // Buffer loads: per-lane 32-bit offsets fixed for the whole K loop, the step's offset
     // as the wave-uniform soffset.  Rows past M / N are clamped (loaded, never stored).
@@ -536,7 +566,7 @@ __global__ __launch_bounds__(256, (MS >= 8 || BITS == 8 || (MS == 2 && !SPLIT)) 
     }
     auto load_a = [&](u32x4* As, int step) {
 #pragma unroll
-        for (int j = 0; j < MS; ++j) lds_load16(rx, &As[(MS * wave + j) * 64], xoff[j], step * W_BK * 2);
+        for (int j = 0; j < MS; ++j) lds_load16(rx, &As[abase + (MS * wave + j) * 64], xoff[j], step * W_BK * 2);
     };
     constexpr int WL = BITS == 4 ? 1 : 2;        // 16-byte weight loads per row and step
     struct WStage {
@@ -544,14 +574,20 @@ __global__ __launch_bounds__(256, (MS >= 8 || BITS == 8 || (MS == 2 && !SPLIT)) 
         uint16_t s[2], z[2];
     };
     auto load_w = [&](WStage& st, int step) {
-        const int grp2 = group_of(step * W_BK + 32 * h, gshift) * 2;
+        const int grp = group_of(step * W_BK + 32 * h, gshift);
 #pragma unroll
         for (int ns = 0; ns < 2; ++ns) {
 #pragma unroll
             for (int i = 0; i < WL; ++i)
                 st.w[ns][i] = __builtin_amdgcn_raw_buffer_load_b128(rw, woff[ns] + 16 * i, step * (W_BK / 8 * BITS), 0);
-            st.s[ns] = __builtin_amdgcn_raw_buffer_load_b16(rs, szoff[ns] + grp2, 0, 0);
-            st.z[ns] = __builtin_amdgcn_raw_buffer_load_b16(rz, szoff[ns] + grp2, 0, 0);
+            if constexpr (SZL) {
+                const uint32_t v = szl[(64 * wave + 32 * ns + l32) * gp + grp - g0];
+                st.s[ns] = (uint16_t)v;
+                st.z[ns] = (uint16_t)(v >> 16);
+            } else {
+                st.s[ns] = __builtin_amdgcn_raw_buffer_load_b16(rs, szoff[ns] + grp * 2, 0, 0);
+                st.z[ns] = __builtin_amdgcn_raw_buffer_load_b16(rz, szoff[ns] + grp * 2, 0, 0);
+            }
         }
     };
     // dequantization constants of a stage's two rows (per row and group)
@@ -577,6 +613,49 @@ __global__ __launch_bounds__(256, (MS >= 8 || BITS == 8 || (MS == 2 && !SPLIT)) 
             }
         }
     };
+
+    if constexpr (SZL) {
+        // thread t < 256 stages weight row n0 + t (clamped): local groups [0, gl) of its scales
+        // and zeros, 16-byte pieces at local offsets min(8 p, gl - 8) (inside the row's range,
+        // the last one overlapping its neighbour), all loads in flight at once
+        if (tid < 256) {
+            const int row = min(n0 + tid, N - 1);
+            const int rbase = (row * G + g0) * 2;
+            uint32_t* dst = szl + tid * gp;
+            if (gl >= 8) {
+                const int P = (gl + 7) >> 3;
+                const __amdgpu_buffer_rsrc_t rnull =
+                    __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(scales), 0, 0, 0x00020000);
+                u32x4 sv[kSzlPieces], zv[kSzlPieces];
+#pragma unroll
+                for (int p = 0; p < kSzlPieces; ++p) {
+                    const int o = rbase + 2 * min(8 * p, gl - 8);
+                    sv[p] = __builtin_amdgcn_raw_buffer_load_b128(p < P ? rs : rnull, o, 0, 0);
+                    zv[p] = HZ ? __builtin_amdgcn_raw_buffer_load_b128(p < P ? rz : rnull, o, 0, 0) : u32x4{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+                for (int p = 0; p < kSzlPieces; ++p) {
+                    if (p < P) {
+                        uint32_t* d = dst + min(8 * p, gl - 8);
+                        const uint32_t sw[4] = {sv[p].x, sv[p].y, sv[p].z, sv[p].w};
+                        const uint32_t zw[4] = {zv[p].x, zv[p].y, zv[p].z, zv[p].w};
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            d[2 * j] = (sw[j] & 0xFFFFu) | (zw[j] << 16);
+                            d[2 * j + 1] = (sw[j] >> 16) | (zw[j] & 0xFFFF0000u);
+                        }
+                    }
+                }
+            } else {
+                for (int j = 0; j < gl; ++j) {
+                    const uint32_t sj = __builtin_amdgcn_raw_buffer_load_b16(rs, rbase + 2 * j, 0, 0);
+                    const uint32_t zj = HZ ? __builtin_amdgcn_raw_buffer_load_b16(rz, rbase + 2 * j, 0, 0) : 0u;
+                    dst[j] = sj | (zj << 16);
+                }
+            }
+        }
+        __syncthreads();
+    }
 
     f32x16 acc[MS][2];
 #pragma unroll
@@ -637,7 +716,7 @@ __global__ __launch_bounds__(256, (MS >= 8 || BITS == 8 || (MS == 2 && !SPLIT)) 
     // LDS-destination loads per LDS object), whatever order it gave the loads; the bare
     // s_barrier then leaves the weight loads in flight (__syncthreads() would drain them).
     auto step_end = [&](const u32x4* next) {
-        const u32x4 v = next[(MS * wave) * 64 + lane];
+        const u32x4 v = next[abase + (MS * wave) * 64 + lane];
         asm volatile("" ::"v"(v.x));
         __builtin_amdgcn_s_barrier();
     };
@@ -650,58 +729,84 @@ __global__ __launch_bounds__(256, (MS >= 8 || BITS == 8 || (MS == 2 && !SPLIT)) 
         // the stage step s's weights left); it ends once the activations of step s + 1 are in.
         WStage p0, p1, p2;
         uint32_t b0[2][4][4], b1[2][4][4], b2[2][4][4];
-        load_a(As0, sb);
-        load_a(As1, min(sb + 1, se - 1));
-        load_w(p0, sb);
-        load_w(p1, min(sb + 1, se - 1));
-        load_w(p2, min(sb + 2, se - 1));
+        load_a(As0, gstep(0));
+        load_a(As1, gstep(1));
+        load_w(p0, gstep(0));
+        load_w(p1, gstep(1));
+        load_w(p2, gstep(2));
 #pragma unroll
         for (int j = 0; j < 4; ++j) dequant_word(p0, stage_const(p0), j, b0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         // the loop body is one basic block: with a branch between its steps the compiler sank
         // each weight load into the block of its use, undoing the prefetch
-        int step = sb;
-        for (; step + 3 <= se; step += 3) {
-            load_a(As2, min(step + 2, se - 1));
-            load_w(p0, min(step + 3, se - 1));
-            compute(As0, b0, p1, b1);
+        int t = 0;
+        for (; t + 3 <= L; t += 3) {
+            load_a(As2, gstep(t + 2));
+            load_w(p0, gstep(t + 3));
+            compute(As0 + abase, b0, p1, b1);
             step_end(As1);
-            load_a(As0, min(step + 3, se - 1));
-            load_w(p1, min(step + 4, se - 1));
-            compute(As1, b1, p2, b2);
+            load_a(As0, gstep(t + 3));
+            load_w(p1, gstep(t + 4));
+            compute(As1 + abase, b1, p2, b2);
             step_end(As2);
-            load_a(As1, min(step + 4, se - 1));
-            load_w(p2, min(step + 5, se - 1));
-            compute(As2, b2, p0, b0);
+            load_a(As1, gstep(t + 4));
+            load_w(p2, gstep(t + 5));
+            compute(As2 + abase, b2, p0, b0);
             step_end(As0);
         }
         // the last one or two steps: their activations and weights are already in flight
-        if (step < se) {                                  // uniform
-            compute(As0, b0, p1, b1);
+        if (t < L) {                                      // uniform
+            compute(As0 + abase, b0, p1, b1);
             step_end(As1);
-            if (step + 1 < se) compute(As1, b1, p2, b2);
+            if (t + 1 < L) compute(As1 + abase, b1, p2, b2);
         }
     } else {
         WStage p0, p1;
         uint32_t b0[2][4][4], b1[2][4][4];
-        load_a(As0, sb);
-        load_w(p0, sb);
-        load_w(p1, min(sb + 1, se - 1));
+        load_a(As0, gstep(0));
+        load_w(p0, gstep(0));
+        load_w(p1, gstep(1));
 #pragma unroll
         for (int j = 0; j < 4; ++j) dequant_word(p0, stage_const(p0), j, b0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        for (int step = sb; step < se; step += 2) {
-            load_a(As1, min(step + 1, se - 1));
-            load_w(p0, min(step + 2, se - 1));
-            compute(As0, b0, p1, b1);
+        for (int t = 0; t < L; t += 2) {
+            load_a(As1, gstep(t + 1));
+            load_w(p0, gstep(t + 2));
+            compute(As0 + abase, b0, p1, b1);
             step_end(As1);
-            load_a(As0, min(step + 2, se - 1));
-            load_w(p1, min(step + 3, se - 1));
-            compute(As1, b1, p0, b0);
+            load_a(As0, gstep(t + 2));
+            load_w(p1, gstep(t + 3));
+            compute(As1 + abase, b1, p0, b0);
             step_end(As0);
         }
+    }
+
+    if constexpr (KG > 1) {
+        // group 1's accumulators into group 0's, one 32-row tile at a time through the activation
+        // buffers (free once every load into them has landed): 8 KB per wave and round
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        constexpr int R0 = KG * ASZ / 512;                // 8 KB regions in As0
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) {
+            __syncthreads();
+            float* red = reinterpret_cast<float*>(wave < R0 ? As0 + wave * 512 : As1 + (wave - R0) * 512);
+            if (kg == 1) {
+#pragma unroll
+                for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) red[(ns * 16 + e) * 64 + lane] = acc[ms][ns][e];
+            }
+            __syncthreads();
+            if (kg == 0) {
+#pragma unroll
+                for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[ms][ns][e] += red[(ns * 16 + e) * 64 + lane];
+            }
+        }
+        if (kg == 1) return;
     }
 
 #pragma unroll
@@ -735,6 +840,44 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 }
 
 }  // namespace
+
+constexpr int kLdsPerCu = 160 * 1024;
+
+// One launch of an instantiation of the wide kernel.  SZL kernels take 256 * gp * 4 bytes of
+// dynamic LDS next to their static activation buffers; the per-kernel limit on dynamic LDS
+// (64 KB by default) is raised on every launch.
+template <bool HZ, int BITS, bool SPLIT, int MS, int KG, bool SZL>
+hipError_t launch_wide_k(dim3 grid, const LinearArgs& a, float* part, int spl, int gp, hipStream_t st) {
+    const int dyn = SZL ? 256 * gp * 4 : 0;
+    if constexpr (SZL) {
+        const hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&prefill_f16_wide_kernel<HZ, BITS, SPLIT, MS, KG, SZL>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, dyn);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((prefill_f16_wide_kernel<HZ, BITS, SPLIT, MS, KG, SZL>), grid, dim3(256 * KG), dyn, st,
+                       static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, static_cast<uint16_t*>(a.Y),
+                       a.M, a.N, a.K, a.G, a.gshift, part, spl, gp);
+    return hipGetLastError();
+}
+
+// Row stride (dwords, odd) of the LDS-staged scales and zeros of a wide-kernel launch, or 0 when
+// they are loaded per step: the groups of a block's k-range (all of K, or the largest split)
+// must number at most 8 kSzlPieces and fit the LDS next to the activation buffers.
+int wide_szl_stride(const LinearArgs& a, int ms, int kg, bool split, int spl) {
+    const int nsteps = a.K / W_BK;
+    int gl = 0;
+    for (int sb = 0; sb < nsteps; sb += split ? spl : nsteps) {
+        const int se = split ? std::min(nsteps, sb + spl) : nsteps;
+        gl = std::max(gl, (((se * W_BK) - 1) >> a.gshift) + 1 - ((sb * W_BK) >> a.gshift));
+    }
+    const int gp = gl | 1;
+    const bool deep = ms == 2 && !split && kg == 1;
+    const int stat = kg * 4096 * ms * (deep ? 3 : 2);
+    if (gl > 8 * kSzlPieces || stat + 256 * gp * 4 > kLdsPerCu) return 0;
+    return gp;
+}
+
 
 // Split-K plan of the 256 x 256 fp16 kernel for a problem with fewer tiles than CUs: splits of
 // spl k-steps (even, >= 16), S = ceil(steps / spl) of them, so every split is non-empty and
@@ -773,15 +916,14 @@ hipError_t launch_prefill_splitk(const LinearArgs& a, float* work, hipStream_t s
     if (S <= 1 || !work) return hipErrorInvalidValue;
     const int tiles = ((a.M + W_BM - 1) / W_BM) * ((a.N + W_BN - 1) / W_BN);
     const dim3 grid(8 * ((tiles + 7) / 8), S);
+    const int gp = wide_szl_stride(a, 8, 1, true, spl);
+    hipError_t e;
     if (a.zeros)
-        hipLaunchKernelGGL((prefill_f16_wide_kernel<true, 4, true>), grid, dim3(256), 0, st,
-                           static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, static_cast<uint16_t*>(a.Y),
-                           a.M, a.N, a.K, a.G, a.gshift, work, spl);
+        e = gp > 0 ? launch_wide_k<true, 4, true, 8, 1, true>(grid, a, work, spl, gp, st)
+                   : launch_wide_k<true, 4, true, 8, 1, false>(grid, a, work, spl, 0, st);
     else
-        hipLaunchKernelGGL((prefill_f16_wide_kernel<false, 4, true>), grid, dim3(256), 0, st,
-                           static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, static_cast<uint16_t*>(a.Y),
-                           a.M, a.N, a.K, a.G, a.gshift, work, spl);
-    const hipError_t e = hipGetLastError();
+        e = gp > 0 ? launch_wide_k<false, 4, true, 8, 1, true>(grid, a, work, spl, gp, st)
+                   : launch_wide_k<false, 4, true, 8, 1, false>(grid, a, work, spl, 0, st);
     if (e != hipSuccess) return e;
     const long long MN = (long long)a.M * a.N;
     const long long blocks = (MN + 255) / 256;
@@ -803,23 +945,34 @@ int wide_ms(int M, int N) {
     return ms;
 }
 
+template <bool HZ, int BITS, int MS, int KG>
+hipError_t launch_wide_ms(dim3 grid, const LinearArgs& a, int gp, hipStream_t st) {
+    if constexpr (BITS == 4) {
+        if (gp > 0) return launch_wide_k<HZ, 4, false, MS, KG, true>(grid, a, nullptr, 0, gp, st);
+    }
+    return launch_wide_k<HZ, BITS, false, MS, KG, false>(grid, a, nullptr, 0, 0, st);
+}
+
 template <bool HZ, int BITS>
 hipError_t launch_wide(const LinearArgs& a, hipStream_t st) {
     const int ms = wide_ms(a.M, a.N);
+    // 64- and 128-row tiles (grids of at most one block per CU) split K over two wave groups
+    // when the step count allows: two waves per SIMD issue VALU work twice as fast as one.
+    // Measured (fp16, g = 128, scales and zeros in LDS): M = 256, 4096 -> 11008: 54.9 -> 49.2 us;
+    // M = 1024, 11008 -> 4096: 152.0 -> 139.1 us; M = 2048, 11008 -> 4096: 205.7 -> 196.6 us.
+    const int kg = BITS == 4 && ms <= 4 && (a.K / W_BK) % 4 == 0 ? 2 : 1;
+    const int gp = BITS == 4 ? wide_szl_stride(a, ms, kg, false, 0) : 0;
     const int tiles = wide_blocks(a.M, a.N, ms);
     const dim3 grid(8 * ((tiles + 7) / 8));
-    const uint16_t* X = static_cast<const uint16_t*>(a.X);
-    uint16_t* Y = static_cast<uint16_t*>(a.Y);
-    if (ms == 8)
-        hipLaunchKernelGGL((prefill_f16_wide_kernel<HZ, BITS, false, 8>), grid, dim3(256), 0, st, X, a.qw,
-                           a.scales, a.zeros, Y, a.M, a.N, a.K, a.G, a.gshift, nullptr, 0);
-    else if (ms == 4)
-        hipLaunchKernelGGL((prefill_f16_wide_kernel<HZ, BITS, false, 4>), grid, dim3(256), 0, st, X, a.qw,
-                           a.scales, a.zeros, Y, a.M, a.N, a.K, a.G, a.gshift, nullptr, 0);
-    else
-        hipLaunchKernelGGL((prefill_f16_wide_kernel<HZ, BITS, false, 2>), grid, dim3(256), 0, st, X, a.qw,
-                           a.scales, a.zeros, Y, a.M, a.N, a.K, a.G, a.gshift, nullptr, 0);
-    return hipGetLastError();
+    if constexpr (BITS == 4) {
+        if (kg == 2) {
+            if (ms == 4) return launch_wide_ms<HZ, 4, 4, 2>(grid, a, gp, st);
+            if (ms == 2) return launch_wide_ms<HZ, 4, 2, 2>(grid, a, gp, st);
+        }
+    }
+    if (ms == 8) return launch_wide_ms<HZ, BITS, 8, 1>(grid, a, gp, st);
+    if (ms == 4) return launch_wide_ms<HZ, BITS, 4, 1>(grid, a, gp, st);
+    return launch_wide_ms<HZ, BITS, 2, 1>(grid, a, gp, st);
 }
 
 bool prefill_supports(const LinearArgs& a) {
