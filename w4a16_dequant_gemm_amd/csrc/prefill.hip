@@ -947,9 +947,7 @@ int wide_ms(int M, int N) {
 
 template <bool HZ, int BITS, int MS, int KG>
 hipError_t launch_wide_ms(dim3 grid, const LinearArgs& a, int gp, hipStream_t st) {
-    if constexpr (BITS == 4) {
-        if (gp > 0) return launch_wide_k<HZ, 4, false, MS, KG, true>(grid, a, nullptr, 0, gp, st);
-    }
+    if (gp > 0) return launch_wide_k<HZ, BITS, false, MS, KG, true>(grid, a, nullptr, 0, gp, st);
     return launch_wide_k<HZ, BITS, false, MS, KG, false>(grid, a, nullptr, 0, 0, st);
 }
 
@@ -961,7 +959,7 @@ hipError_t launch_wide(const LinearArgs& a, hipStream_t st) {
     // Measured (fp16, g = 128, scales and zeros in LDS): M = 256, 4096 -> 11008: 54.9 -> 49.2 us;
     // M = 1024, 11008 -> 4096: 152.0 -> 139.1 us; M = 2048, 11008 -> 4096: 205.7 -> 196.6 us.
     const int kg = BITS == 4 && ms <= 4 && (a.K / W_BK) % 4 == 0 ? 2 : 1;
-    const int gp = BITS == 4 ? wide_szl_stride(a, ms, kg, false, 0) : 0;
+    const int gp = wide_szl_stride(a, ms, kg, false, 0);
     const int tiles = wide_blocks(a.M, a.N, ms);
     const dim3 grid(8 * ((tiles + 7) / 8));
     if constexpr (BITS == 4) {
