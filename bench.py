@@ -532,7 +532,8 @@ def counter_summary(run_dirs, out_path: str, header: str = ""):
     """Per-kernel means of the counters of one or more rocprofv3 --pmc runs (each run's
     counter_collection csv), with derived figures: matrix-core busy share, L2 hit rate and
     miss bytes, instructions per wave, the share of wave cycles spent waiting, LDS bank
-    conflict cycles.  Counter values are means per dispatch."""
+    conflict cycles, address-unit busy share and L1 requests to L2 per L1 access.  Counter
+    values are means per dispatch."""
     import csv
     import glob
     sums, grid = {}, {}
@@ -580,6 +581,10 @@ def counter_summary(run_dirs, out_path: str, header: str = ""):
                 d.append("waiting: " + ", ".join(fr))
         if "SQ_LDS_BANK_CONFLICT" in c:
             d.append(f"LDS bank conflict cycles {c['SQ_LDS_BANK_CONFLICT']:.0f}")
+        if "TA_BUSY_avr" in c and c.get("GRBM_GUI_ACTIVE"):
+            d.append(f"address unit (TA) busy {100 * c['TA_BUSY_avr'] / (c['GRBM_GUI_ACTIVE'] / 8):.0f} %")
+        if "TCP_TCC_READ_REQ_sum" in c and c.get("TCP_TOTAL_CACHE_ACCESSES_sum"):
+            d.append(f"L1 read requests to L2 per L1 access {c['TCP_TCC_READ_REQ_sum'] / c['TCP_TOTAL_CACHE_ACCESSES_sum']:.2f}")
         lines.append("  derived: " + "; ".join(d))
     with open(out_path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
