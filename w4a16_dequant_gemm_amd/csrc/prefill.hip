@@ -482,8 +482,8 @@ constexpr int kSzlPieces = 12;           // SZL: at most 96 groups per block k-r
 // and the second group's accumulators are added to the first's through LDS at the end, in
 // fixed order.  It doubles the waves per SIMD for tiles of 64 and 128 rows, which a grid of at
 // most one block per CU otherwise runs one wave per SIMD, without any buffer outside the block.
-// The host launches KG = 2 only with a step count the loops divide (K % 128 == 0 with 64-row
-// tiles, K % 256 == 0 with 128-row ones).
+// The host launches KG = 2 only when each group's step count is even (K % 256 == 0), which the
+// two-step loop needs; with KG = 2 the 64-row tile runs that loop, not the three-step one.
 //
 // SZL: the block's scales and zeros for its k-range sit in LDS (dynamic, gp dwords per weight
 // row, s | z << 16, gp odd so the 32 rows a wave reads per step fall in distinct banks),
@@ -505,7 +505,7 @@ __global__ __launch_bounds__(256 * KG, (MS >= 8 || BITS == 8 || (MS == 2 && !SPL
     // wait for the other buffer's loads, issued for the next step)
     __shared__ __attribute__((aligned(16))) u32x4 As0[KG * ASZ];       // 32 KB at 256 rows
     __shared__ __attribute__((aligned(16))) u32x4 As1[KG * ASZ];
-    // 64-row blocks run three steps deep (below): a third activation buffer
+    // 64-row blocks with one wave group run three steps deep (below): a third activation buffer
     constexpr bool DEEP = MS == 2 && BITS == 4 && !SPLIT && KG == 1;
     __shared__ __attribute__((aligned(16))) u32x4 As2[DEEP ? KG * ASZ : 1];
 
