@@ -184,4 +184,57 @@ __device__ __forceinline__ float pair_sum(uint32_t p) {
 // (shift = 31 makes every column group 0).
 __device__ __forceinline__ int group_of(int k, int gshift) { return (int)((uint32_t)k >> gshift); }
 
+// Scales and zeros of `rows` consecutive weight rows into LDS, groups [g0, g0 + gl) of each, as
+// (s | z << 16) dwords at a row stride of gp dwords (odd: the 16 or 32 rows a wave reads at one
+// group fall in distinct banks).  REP threads per row: thread t < REP rows stages pieces
+// t / rows, t / rows + REP, ... of row min(row0 + t % rows, N - 1), a piece being the 16 bytes
+// at local offset min(8 p, gl - 8) (inside the row's range, the last one overlapping its
+// neighbour), all of a thread's loads in flight at once (gl <= 8 kSzStagePieces); 2-byte loads
+// by one thread per row when gl < 8.  Without zeros (hz false) the high halves are 0.  The
+// caller synchronizes before reading.  Staged once per block, this replaces two 2-byte loads
+// per row set and k-step, each touching as many cache lines as the row set has rows.
+constexpr int kSzStagePieces = 12;
+template <int REP>
+__device__ __forceinline__ void stage_sz_rows(uint32_t* szl, int gp, int tid, int rows, int row0, int N,
+                                              int G, int g0, int gl, bool hz, __amdgpu_buffer_rsrc_t rs,
+                                              __amdgpu_buffer_rsrc_t rz, __amdgpu_buffer_rsrc_t rnull) {
+    constexpr int PT = (kSzStagePieces + REP - 1) / REP;          // pieces per thread
+    if (tid >= REP * rows) return;
+    const int rr = tid % rows, k = tid / rows;
+    const int row = min(row0 + rr, N - 1);
+    const int rbase = (row * G + g0) * 2;
+    uint32_t* dst = szl + rr * gp;
+    if (gl >= 8) {
+        const int P = (gl + 7) >> 3;
+        u32x4 sv[PT], zv[PT];
+#pragma unroll
+        for (int i = 0; i < PT; ++i) {
+            const int p = k + REP * i;
+            const int o = rbase + 2 * min(8 * p, gl - 8);
+            sv[i] = __builtin_amdgcn_raw_buffer_load_b128(p < P ? rs : rnull, o, 0, 0);
+            zv[i] = __builtin_amdgcn_raw_buffer_load_b128(p < P && hz ? rz : rnull, o, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < PT; ++i) {
+            const int p = k + REP * i;
+            if (p < P) {
+                uint32_t* d = dst + min(8 * p, gl - 8);
+                const uint32_t sw[4] = {sv[i].x, sv[i].y, sv[i].z, sv[i].w};
+                const uint32_t zw[4] = {zv[i].x, zv[i].y, zv[i].z, zv[i].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    d[2 * j] = (sw[j] & 0xFFFFu) | (zw[j] << 16);
+                    d[2 * j + 1] = (sw[j] >> 16) | (zw[j] & 0xFFFF0000u);
+                }
+            }
+        }
+    } else if (k == 0) {
+        for (int j = 0; j < gl; ++j) {
+            const uint32_t sj = __builtin_amdgcn_raw_buffer_load_b16(rs, rbase + 2 * j, 0, 0);
+            const uint32_t zj = hz ? __builtin_amdgcn_raw_buffer_load_b16(rz, rbase + 2 * j, 0, 0) : 0u;
+            dst[j] = sj | (zj << 16);
+        }
+    }
+}
+
 }  // namespace w4a16

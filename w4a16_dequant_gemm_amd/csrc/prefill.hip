@@ -468,7 +468,6 @@ __device__ __forceinline__ void sched_group() {
 }
 
 constexpr int W_BM = 256, W_BN = 256, W_BK = 64;     // K % 128 == 0: steps in pairs
-constexpr int kSzlPieces = 12;           // SZL: at most 96 groups per block k-range
 
 // BITS = 8 (W8A16): lane (n, h) loads the 32 bytes of columns 32h .. 32h + 31 (two 16-byte
 // loads) and MFMA j takes words 2j and 2j + 1 (one byte permute per pair instead of the nibble
@@ -615,45 +614,9 @@ __global__ __launch_bounds__(256 * KG, (MS >= 8 || BITS == 8 || (MS == 2 && !SPL
     };
 
     if constexpr (SZL) {
-        // thread t < 256 stages weight row n0 + t (clamped): local groups [0, gl) of its scales
-        // and zeros, 16-byte pieces at local offsets min(8 p, gl - 8) (inside the row's range,
-        // the last one overlapping its neighbour), all loads in flight at once
-        if (tid < 256) {
-            const int row = min(n0 + tid, N - 1);
-            const int rbase = (row * G + g0) * 2;
-            uint32_t* dst = szl + tid * gp;
-            if (gl >= 8) {
-                const int P = (gl + 7) >> 3;
-                const __amdgpu_buffer_rsrc_t rnull =
-                    __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(scales), 0, 0, 0x00020000);
-                u32x4 sv[kSzlPieces], zv[kSzlPieces];
-#pragma unroll
-                for (int p = 0; p < kSzlPieces; ++p) {
-                    const int o = rbase + 2 * min(8 * p, gl - 8);
-                    sv[p] = __builtin_amdgcn_raw_buffer_load_b128(p < P ? rs : rnull, o, 0, 0);
-                    zv[p] = HZ ? __builtin_amdgcn_raw_buffer_load_b128(p < P ? rz : rnull, o, 0, 0) : u32x4{0u, 0u, 0u, 0u};
-                }
-#pragma unroll
-                for (int p = 0; p < kSzlPieces; ++p) {
-                    if (p < P) {
-                        uint32_t* d = dst + min(8 * p, gl - 8);
-                        const uint32_t sw[4] = {sv[p].x, sv[p].y, sv[p].z, sv[p].w};
-                        const uint32_t zw[4] = {zv[p].x, zv[p].y, zv[p].z, zv[p].w};
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            d[2 * j] = (sw[j] & 0xFFFFu) | (zw[j] << 16);
-                            d[2 * j + 1] = (sw[j] >> 16) | (zw[j] & 0xFFFF0000u);
-                        }
-                    }
-                }
-            } else {
-                for (int j = 0; j < gl; ++j) {
-                    const uint32_t sj = __builtin_amdgcn_raw_buffer_load_b16(rs, rbase + 2 * j, 0, 0);
-                    const uint32_t zj = HZ ? __builtin_amdgcn_raw_buffer_load_b16(rz, rbase + 2 * j, 0, 0) : 0u;
-                    dst[j] = sj | (zj << 16);
-                }
-            }
-        }
+        const __amdgpu_buffer_rsrc_t rnull =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(scales), 0, 0, 0x00020000);
+        stage_sz_rows<KG>(szl, gp, tid, W_BN, n0, N, G, g0, gl, HZ, rs, rz, rnull);
         __syncthreads();
     }
 
@@ -863,7 +826,7 @@ hipError_t launch_wide_k(dim3 grid, const LinearArgs& a, float* part, int spl, i
 
 // Row stride (dwords, odd) of the LDS-staged scales and zeros of a wide-kernel launch, or 0 when
 // they are loaded per step: the groups of a block's k-range (all of K, or the largest split)
-// must number at most 8 kSzlPieces and fit the LDS next to the activation buffers.
+// must number at most 8 kSzStagePieces and fit the LDS next to the activation buffers.
 int wide_szl_stride(const LinearArgs& a, int ms, int kg, bool split, int spl) {
     const int nsteps = a.K / W_BK;
     int gl = 0;
@@ -874,7 +837,7 @@ int wide_szl_stride(const LinearArgs& a, int ms, int kg, bool split, int spl) {
     const int gp = gl | 1;
     const bool deep = ms == 2 && !split && kg == 1;
     const int stat = kg * 4096 * ms * (deep ? 3 : 2);
-    if (gl > 8 * kSzlPieces || stat + 256 * gp * 4 > kLdsPerCu) return 0;
+    if (gl > 8 * kSzStagePieces || stat + 256 * gp * 4 > kLdsPerCu) return 0;
     return gp;
 }
 

@@ -73,10 +73,13 @@ struct SkinnySrc {
     __amdgpu_buffer_rsrc_t x, w, s, z, none;
 };
 
-template <int NB, int MT>
+// SZL: the scales and zeros come from the block's LDS copy (row nb * 16 + n16 at stride gp)
+// instead of two 2-byte loads per row-block and k-block.
+template <int NB, int MT, bool SZL>
 __device__ __forceinline__ void load_kblock(KBlock<NB, MT>& kb, const SkinnySrc& src, int k_block,
                                             bool live, const int va[MT], const int vw[NB],
-                                            const int vs[NB], int gshift) {
+                                            const int vs[NB], int gshift, const uint32_t* szl, int gp,
+                                            int n16) {
     const __amdgpu_buffer_rsrc_t rx = live ? src.x : src.none;   // wave-uniform selects
     const __amdgpu_buffer_rsrc_t rw = live ? src.w : src.none;
     const __amdgpu_buffer_rsrc_t rs = live ? src.s : src.none;
@@ -87,8 +90,14 @@ __device__ __forceinline__ void load_kblock(KBlock<NB, MT>& kb, const SkinnySrc&
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         kb.w[nb] = __builtin_amdgcn_raw_buffer_load_b128(rw, vw[nb], ow, 2 /* nt */);
-        kb.s[nb] = __builtin_amdgcn_raw_buffer_load_b16(rs, vs[nb], og, 0);
-        kb.z[nb] = __builtin_amdgcn_raw_buffer_load_b16(rz, vs[nb], og, 0);
+        if constexpr (SZL) {
+            const uint32_t v = szl[(nb * 16 + n16) * gp + ((k_block << 7) >> gshift)];
+            kb.s[nb] = (uint16_t)v;
+            kb.z[nb] = (uint16_t)(v >> 16);
+        } else {
+            kb.s[nb] = __builtin_amdgcn_raw_buffer_load_b16(rs, vs[nb], og, 0);
+            kb.z[nb] = __builtin_amdgcn_raw_buffer_load_b16(rz, vs[nb], og, 0);
+        }
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -148,12 +157,15 @@ __device__ __forceinline__ void compute_kblock(const KBlock<NB, MT>& kb, int has
     }
 }
 
-template <int DT, int NB, int MT, int W>
+template <int DT, int NB, int MT, int W, bool SZL>
 __global__ __launch_bounds__(64 * W) void skinny_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int has_zeros,
-    uint16_t* __restrict__ Y, int M, int N, int K, int G, int gshift, int KS) {
+    uint16_t* __restrict__ Y, int M, int N, int K, int G, int gshift, int KS, int gp) {
+    // the waves' partial tiles at the end; during the k-loop (SZL) the block's scales and zeros,
+    // 16 NB rows x gp dwords (gp <= 97 fits: the buffer holds 8 MT KB per row-block)
     __shared__ f32x4 red[W][NB][MT][64];
+    uint32_t* szl = reinterpret_cast<uint32_t*>(&red[0][0][0][0]);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -195,20 +207,25 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) tile[nb][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
+    if constexpr (SZL) {
+        stage_sz_rows<4 * W / NB>(szl, gp, tid, 16 * NB, row0, N, G, 0, G, has_zeros != 0, src.s, src.z, src.none);
+        __syncthreads();
+    }
     const int kb0 = wave * KS;
     const int kb1 = min(KB, kb0 + KS);
     const int nk = kb1 > kb0 ? kb1 - kb0 : 0;
     KBlock<NB, MT> buf0, buf1;
-    load_kblock<NB, MT>(buf0, src, min(kb0, KB - 1), nk > 0, va, vw, vs, gshift);
-    load_kblock<NB, MT>(buf1, src, min(kb0 + 1, KB - 1), nk > 1, va, vw, vs, gshift);
+    load_kblock<NB, MT, SZL>(buf0, src, min(kb0, KB - 1), nk > 0, va, vw, vs, gshift, szl, gp, n16);
+    load_kblock<NB, MT, SZL>(buf1, src, min(kb0 + 1, KB - 1), nk > 1, va, vw, vs, gshift, szl, gp, n16);
     // Unconditional prefetch and compute: a k-block past the end loads zeros through
     // `none` and adds nothing (zero activations, zero sums).
     for (int i = 0; i < nk; i += 2) {
         compute_kblock<DT, NB, MT>(buf0, has_zeros, tile);
-        load_kblock<NB, MT>(buf0, src, min(kb0 + i + 2, KB - 1), i + 2 < nk, va, vw, vs, gshift);
+        load_kblock<NB, MT, SZL>(buf0, src, min(kb0 + i + 2, KB - 1), i + 2 < nk, va, vw, vs, gshift, szl, gp, n16);
         compute_kblock<DT, NB, MT>(buf1, has_zeros, tile);
-        load_kblock<NB, MT>(buf1, src, min(kb0 + i + 3, KB - 1), i + 3 < nk, va, vw, vs, gshift);
+        load_kblock<NB, MT, SZL>(buf1, src, min(kb0 + i + 3, KB - 1), i + 3 < nk, va, vw, vs, gshift, szl, gp, n16);
     }
+    if constexpr (SZL) __syncthreads();                  // every wave done with the staged words
 
     // Sum the waves' partial tiles; lane (n, q) of the tile holds rows m = 4q .. 4q+3.
 #pragma unroll
@@ -262,10 +279,20 @@ SkinnyCfg pick_skinny(const LinearArgs& a) {
 
 template <int DT, int NB, int MT>
 hipError_t run(const LinearArgs& a, const SkinnyCfg& c, hipStream_t st) {
-    hipLaunchKernelGGL((skinny_kernel<DT, NB, MT, kSkinnyWaves>), dim3(c.blocks, c.mblocks),
-                       dim3(64 * kSkinnyWaves), 0, st, static_cast<const uint16_t*>(a.X), a.qw,
-                       a.scales, a.zeros, a.zeros ? 1 : 0, static_cast<uint16_t*>(a.Y), a.M, a.N,
-                       a.K, a.G, a.gshift, c.ks);
+    // scales and zeros staged in LDS when the row's groups fit the staging (G <= 96); measured
+    // (fp16, g = 128): M = 256, 11008 -> 4096: 109.5 -> 92.4 us; M = 128, 4096 -> 4096: 24.2 ->
+    // 18.1 us; M = 32, 4096 -> 11008: 31.6 -> 25.7 us (the address unit was 75 % busy)
+    const bool szl = a.G <= 8 * kSzStagePieces;
+    if (szl)
+        hipLaunchKernelGGL((skinny_kernel<DT, NB, MT, kSkinnyWaves, true>), dim3(c.blocks, c.mblocks),
+                           dim3(64 * kSkinnyWaves), 0, st, static_cast<const uint16_t*>(a.X), a.qw,
+                           a.scales, a.zeros, a.zeros ? 1 : 0, static_cast<uint16_t*>(a.Y), a.M, a.N,
+                           a.K, a.G, a.gshift, c.ks, a.G | 1);
+    else
+        hipLaunchKernelGGL((skinny_kernel<DT, NB, MT, kSkinnyWaves, false>), dim3(c.blocks, c.mblocks),
+                           dim3(64 * kSkinnyWaves), 0, st, static_cast<const uint16_t*>(a.X), a.qw,
+                           a.scales, a.zeros, a.zeros ? 1 : 0, static_cast<uint16_t*>(a.Y), a.M, a.N,
+                           a.K, a.G, a.gshift, c.ks, 0);
     return hipGetLastError();
 }
 
