@@ -124,6 +124,14 @@ def test_dequantize_rejects_invalid_arguments(lib):
     (1, 28672, 8192, 128, 0, L.PATH_GEMV),
     (1, 8192, 28672, 64, 0, L.PATH_GEMV),             # g = 64: the MFMA decode kernel needs g % 128 == 0
     (4096, 11008, 4096, 128, 0, L.PATH_PREFILL),
+    # fp16 between 32 and 512 rows, where the measured crossover lies: 4096 -> 11008 turns tiled
+    # by M = 128, 11008 -> 4096 and 4096 -> 4096 past M = 256
+    (64, 11008, 4096, 128, 0, L.PATH_SKINNY),
+    (192, 11008, 4096, 128, 0, L.PATH_PREFILL),
+    (256, 4096, 11008, 128, 0, L.PATH_SKINNY),
+    (320, 4096, 11008, 128, 0, L.PATH_PREFILL),
+    (256, 4096, 4096, 128, 0, L.PATH_SKINNY),
+    (384, 4096, 4096, 128, 0, L.PATH_PREFILL),
     (1024, 4096, 11008, 64, 0, L.PATH_PREFILL),
     (1, 4096, 11008, 11008, 1, L.PATH_GEMV),          # per-channel
     # 32 < M <= 512: the K-split skinny kernel where the tiled GEMM would have few tiles

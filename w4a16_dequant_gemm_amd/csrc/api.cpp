@@ -84,21 +84,24 @@ int validate_linear(const void* X, int dtype, int64_t M, int64_t N, int64_t K, i
 // M-based dispatch: the weight-streaming GEMV while the dot2 work per weight stays
 // within the VALU budget of the HBM stream, the skinny MFMA kernel for small batches,
 // the tiled MFMA GEMM once the problem is compute-bound.
-// Between 32 and 512 activation rows the tiled GEMM has few tiles (256 x 256 tiles in fp16,
-// 128 x 128 in bf16) and each CU runs one of them through the whole K loop, while the skinny
-// kernel splits K over the 8 waves of every block and covers the GPU.  Estimated times
-// (microseconds, fitted to MI355X measurements of both kernels on the 7B-like prefill shapes
-// for M = 33 .. 512): skinny ~ max(40, c * M * N * K) with c = 1.05e-8 (fp16) or 1.45e-8
-// (bf16); tiled ~ (1.45 or 1.3) * (K / 64) * ceil(tiles / slots), slots = 256 CUs (fp16)
-// or 512 (bf16, two blocks per CU).
+// Between 32 and 512 activation rows the tiled GEMM has few tiles and each CU runs one of them
+// through the whole K loop, while the skinny kernel splits K over the 8 waves of every block and
+// covers the GPU.  Estimated times (microseconds, fitted to MI355X measurements of both kernels
+// on the 7B-like prefill shapes for M = 48 .. 512; fp16 picks the faster one at 26 of 27
+// measured points): fp16 skinny ~ max(3.9e-3 K, 0.9e-8 M N K), the wide tiled kernel as
+// prefill_f16_estimate_us; bf16 skinny ~ max(40, 1.45e-8 M N K), tiled ~ 1.3 (K / 64)
+// ceil(tiles / 512) with 128 x 128 tiles, two blocks per CU.
 bool skinny_beats_tiled(const LinearArgs& a) {
-    const bool f16 = a.dtype == W4A16_F16;
     const double macs = (double)a.M * a.N * a.K;
-    const double t_skinny = std::max(40.0, (f16 ? 1.05e-8 : 1.45e-8) * macs);
-    const long long bm = f16 ? 256 : 128;
-    const long long tiles = ((a.M + bm - 1) / bm) * ((a.N + bm - 1) / bm);
-    const long long slots = f16 ? 256 : 512;
-    const double t_tiled = (f16 ? 1.45 : 1.3) * (a.K / 64.0) * (double)((tiles + slots - 1) / slots);
+    if (a.dtype == W4A16_F16) {
+        const double t_tiled = w4a16::prefill_f16_estimate_us(a);
+        if (t_tiled > 0.0) return std::max(3.9e-3 * a.K, 0.9e-8 * macs) < t_tiled;
+        const long long tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
+        return std::max(40.0, 1.05e-8 * macs) < 1.45 * (a.K / 64.0) * (double)((tiles + 255) / 256);
+    }
+    const double t_skinny = std::max(40.0, 1.45e-8 * macs);
+    const long long tiles = ((a.M + 127) / 128) * ((a.N + 127) / 128);
+    const double t_tiled = 1.3 * (a.K / 64.0) * (double)((tiles + 511) / 512);
     return t_skinny < t_tiled;
 }
 

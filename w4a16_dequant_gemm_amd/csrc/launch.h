@@ -37,6 +37,9 @@ hipError_t launch_gemv_group(const LinearArgs* items, int count, hipStream_t s);
 hipError_t launch_skinny(const LinearArgs& a, hipStream_t s);
 hipError_t launch_decode(const LinearArgs& a, hipStream_t s);
 hipError_t launch_prefill(const LinearArgs& a, hipStream_t s);
+// estimated time (us) of the plain fp16 prefill launch on the 4-bit wide kernel, < 0 when another
+// kernel would run (host only; for the dispatcher)
+double prefill_f16_estimate_us(const LinearArgs& a);
 // split-K mode of the fp16 256 x 256 prefill kernel (caller workspace of fp32 partial tiles)
 int prefill_splitk_splits(const LinearArgs& a);
 long long prefill_splitk_bytes(const LinearArgs& a);

@@ -936,6 +936,21 @@ hipError_t launch_wide(const LinearArgs& a, hipStream_t st) {
     return launch_wide_ms<HZ, BITS, 2, 1>(grid, a, gp, st);
 }
 
+// Time of the plain fp16 4-bit launch: a block round costs s(rows) us per k-step, growing with
+// the block count, one round per 256 blocks.  s = 0.62 / 0.92 / 1.57 us for 64- / 128- /
+// 256-row tiles, fitted to MI355X measurements on the 7B-like prefill shapes for M = 48 .. 1024
+// (within about 10 %).
+double prefill_f16_estimate_us(const LinearArgs& a) {
+    const bool offsets32 = (long long)a.M * a.K * 2 < (1LL << 31) && (long long)a.N * (a.K / 2) < (1LL << 31) &&
+                           (long long)a.N * a.G * 2 < (1LL << 31);
+    if (a.dtype != DT_F16 || a.K % (2 * W_BK) != 0 || !offsets32) return -1.0;
+    const int ms = wide_ms(a.M, a.N);
+    const long long blocks = wide_blocks(a.M, a.N, ms);
+    const double s = ms == 2 ? 0.62 : (ms == 4 ? 0.92 : 1.57);
+    const long long rounds = (blocks + 255) / 256;
+    return s * (1.0 + (double)std::min(blocks, 256LL) / 1000.0) * (a.K / (double)W_BK) * (double)rounds;
+}
+
 bool prefill_supports(const LinearArgs& a) {
     if (a.dtype == DT_F16) return a.K % F_BK == 0 && a.g % F_BK == 0;   // any supported g
     return a.K % BK == 0 && a.g % BK == 0;
