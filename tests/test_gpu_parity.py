@@ -136,7 +136,9 @@ SKINNY_CASES = [(1, 64, 128, 128), (5, 100, 1024, 128), (16, 256, 4096, 128), (1
                 # 32 < M <= 512: the grid also runs over 32-row chunks of M (ragged last chunk,
                 # 64 weight rows per block in fp16), K split over the waves
                 (33, 300, 1024, 128), (100, 257, 2048, 128), (256, 1000, 4096, 256), (512, 64, 1024, 1024),
-                (130, 4096, 11008, 128)]
+                (130, 4096, 11008, 128),
+                # more groups per row than the skinny kernel stages in LDS (> 96): loaded per k-block
+                (24, 300, 16384, 128), (40, 130, 14336, 128)]
 PREFILL_CASES = [(1, 64, 64, 64), (17, 200, 192, 64), (130, 129, 256, 128), (256, 384, 1024, 128),
                  (300, 256, 4096, 4096), (64, 128, 11008, 128), (129, 1, 128, 64),
                  # fp16: 128-row tiles with K split over two wave groups (K % 256 == 0), ragged M and
