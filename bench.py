@@ -826,8 +826,8 @@ def run_comparators(W4, synth, torch, w4_step_ms):
         f_unf = lambda i: torch.matmul(X, W4.dequantize(qw, s, z, GROUP).half().t(), out=Y)
         for f in (f_fused, f_unf):
             f(0)
-        t_f = time_loop(f_fused, 5, torch, graph=False)
-        t_u = time_loop(f_unf, 5, torch, graph=False)
+        t_f = time_loop(f_fused, 5, torch)
+        t_u = time_loop(f_unf, 5, torch)
         pf[f"K{K}_N{N}"] = {"fused_us": round(t_f * 1e3, 1), "unfused_us": round(t_u * 1e3, 1),
                             "fused_speedup": round(t_u / t_f, 2)}
         del X, Y
@@ -857,11 +857,19 @@ def run_extras(layers, copies, W4, synth, torch, np, samples):
             for L, o in zip(layers, outs):
                 qw, s, z = L.copies[c]
                 W4.linear(xs[L.K], qw, s, z, GROUP, out=o)
+
+        def step_batch(i):
+            c = i % copies
+            W4.linear_batch([(xs[L.K], *L.copies[c], GROUP) for L in layers], outs=outs)
         for i in range(5):
             step(i)
+            step_batch(i)
         ms = time_loop(step, 50, torch)
+        ms_b = time_loop(step_batch, 50, torch)
         sweep[f"M{M}"] = {"GBps": round(nbytes / (ms * 1e-3) / 1e9, 1), "us_per_step": round(ms * 1e3, 2),
-                          "paths": [W4.PATH_NAMES[W4.select_path(M, L.N, L.K, GROUP)] for L in layers]}
+                          "paths": [W4.PATH_NAMES[W4.select_path(M, L.N, L.K, GROUP)] for L in layers],
+                          "batch_call": {"GBps": round(nbytes / (ms_b * 1e-3) / 1e9, 1),
+                                         "us_per_step": round(ms_b * 1e3, 2)}}
         log(f"  sweep M={M}: {sweep[f'M{M}']}")
     out["decode_sweep_fp16_g128"] = sweep
     # each kernel path forced, per M (same layers, same rotation)
@@ -1081,26 +1089,26 @@ def run_stack(W4, synth, torch, np, samples):
             res[key] = {"ms_per_step": round(ms, 3), "GBps": round(gbps, 1),
                         "frac_hbm_peak": round(gbps / HBM_PEAK_GBS, 4), "weight_GB": round(nbytes / 1e9, 3)}
             log(f"  full stack {key}: {res[key]}")
-            if M == 1:
-                # the same step with each transformer layer's independent projections batched:
-                # w4a16_linear_batch over (q, k, v) and over (gate, up), then o and down alone
-                # (4 launches per layer instead of 7; the dependencies of a real layer kept)
-                def step_b(i, xs=xs, ys=ys, layers=layers):
-                    for l0 in range(0, len(layers), 7):
-                        grp = [(xs[c.K], qw, s, z, c.g) for c, qw, s, z in layers[l0:l0 + 7]]
-                        out = ys[l0:l0 + 7]
-                        W4.linear_batch(grp[0:3], outs=out[0:3])
-                        W4.linear(*grp[3], out=out[3])
-                        W4.linear_batch(grp[4:6], outs=out[4:6])
-                        W4.linear(*grp[6], out=out[6])
-                for i in range(2):
-                    step_b(i)
-                msb = time_loop(step_b, 5, torch)
-                gb = nbytes / (msb * 1e-3) / 1e9
-                res[key + "_batched_qkv_gateup"] = {"ms_per_step": round(msb, 3), "GBps": round(gb, 1),
-                                                    "frac_hbm_peak": round(gb / HBM_PEAK_GBS, 4),
-                                                    "launches_per_step": 128}
-                log(f"  full stack {key}, q/k/v and gate/up batched: {res[key + '_batched_qkv_gateup']}")
+            # the same step with each transformer layer's independent projections batched:
+            # w4a16_linear_batch over (q, k, v) and over (gate, up), then o and down alone
+            # (4 launches per layer instead of 7; the dependencies of a real layer kept;
+            # M = 1: the grouped GEMV, M = 8: the grouped ring decode kernel)
+            def step_b(i, xs=xs, ys=ys, layers=layers):
+                for l0 in range(0, len(layers), 7):
+                    grp = [(xs[c.K], qw, s, z, c.g) for c, qw, s, z in layers[l0:l0 + 7]]
+                    out = ys[l0:l0 + 7]
+                    W4.linear_batch(grp[0:3], outs=out[0:3])
+                    W4.linear(*grp[3], out=out[3])
+                    W4.linear_batch(grp[4:6], outs=out[4:6])
+                    W4.linear(*grp[6], out=out[6])
+            for i in range(2):
+                step_b(i)
+            msb = time_loop(step_b, 5, torch)
+            gb = nbytes / (msb * 1e-3) / 1e9
+            res[key + "_batched_qkv_gateup"] = {"ms_per_step": round(msb, 3), "GBps": round(gb, 1),
+                                                "frac_hbm_peak": round(gb / HBM_PEAK_GBS, 4),
+                                                "launches_per_step": 128}
+            log(f"  full stack {key}, q/k/v and gate/up batched: {res[key + '_batched_qkv_gateup']}")
             c, qw, s, z = layers[-1]          # the last layer's down projection
             step(0)
             Wd = synth.weights_device(c.N, c.K, c.w_sigma, synth.seeds(c.config, c.layer)[0])

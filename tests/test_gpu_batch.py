@@ -1,5 +1,6 @@
 """GPU parity of w4a16_linear_batch, the call that runs several independent layers, with the
-one-row layers sharing grouped launches (one grid over their weights).
+one-row layers sharing grouped launches (one grid over their weights) and layers of up to 8
+rows sharing grouped launches of the ring decode kernel.
 
 * grouped outputs equal w4a16_linear's bit for bit wherever that call takes the same
   weight-streaming kernel (the grouped kernel runs each layer's block with the layer's own
@@ -8,7 +9,10 @@ one-row layers sharing grouped launches (one grid over their weights).
   one-row layers (several grouped launches), ragged and per-channel layers, symmetric
   weights without zero points, both activation dtypes;
 * a 70B-shaped one-row layer (random codes), against the oracle on sampled rows;
-* the batch captured in a HIP graph and replayed, every replay equal to the eager result.
+* the batch captured in a HIP graph and replayed, every replay equal to the eager result;
+* ring-kernel groups (2 <= M <= 8): outputs equal the single call's bit for bit where that
+  call runs the ring kernel (M >= 5), meet the oracle's bar everywhere (M <= 4 alone runs the
+  activation-staging kernel), ragged and per-channel layers, more than 16 layers, a graph.
 """
 
 from __future__ import annotations
@@ -101,6 +105,63 @@ def test_batch_graph_replay_matches_eager():
     layers = [_layer(1, N, K, 128, FP16, seed=800 + i) for i, (N, K) in
               enumerate([(4096, 4096), (11008, 4096), (4096, 11008)])]
     outs = [torch.empty((1, L["t"][1].shape[0]), dtype=torch.float16, device="cuda") for L in layers]
+    W4.linear_batch([L["t"] for L in layers], outs=outs)
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        W4.linear_batch([L["t"] for L in layers], outs=outs)
+    for _ in range(3):
+        for o in outs:
+            o.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o.view(torch.int16), e.view(torch.int16))
+
+
+# (M, N, K, g, scheme, zeros_none): layers the ring decode kernel takes in a group (M <= 8, N and K
+# <= 12288, K % 256 == 0, g % 128 == 0): the 7B-like shapes, ragged N, per-channel groups,
+# symmetric weights without zero points
+RING = [(8, 4096, 4096, 128, ASYM, False), (8, 11008, 4096, 128, ASYM, False),
+        (8, 4096, 11008, 128, ASYM, False), (5, 1000, 2048, 128, ASYM, False),
+        (7, 777, 4096, 4096, ASYM, False), (6, 300, 12288, 256, SYM, True), (4, 1040, 4096, 128, ASYM, False),
+        (3, 500, 8192, 128, ASYM, False), (2, 2000, 6144, 128, SYM, True)]
+
+
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+def test_ring_group_equals_ring_kernel_and_oracle(dtype):
+    layers = [_layer(M, N, K, g, dtype, seed=900 + i, scheme=sc, zeros_none=zn)
+              for i, (M, N, K, g, sc, zn) in enumerate(RING)]
+    assert all(W4.select_path(M, N, K, g, dtype) == W4.PATH_SKINNY for M, N, K, g, _, _ in RING if M > 2)
+    ys = W4.linear_batch([L["t"] for L in layers])
+    singles = [W4.linear(*L["t"]) for L in layers]
+    torch.cuda.synchronize()
+    for L, y, y1, shape in zip(layers, ys, singles, RING):
+        if shape[0] >= 5:          # alone, the ring kernel too
+            assert torch.equal(y.view(torch.int16), y1.view(torch.int16)), f"ring group != single {shape}"
+        ref = oracle.linear_ref(L["X"], dtype, L["qn"], L["s"], L["z"], L["g"])
+        assert_close(y_to_f64(y), ref_to_f64(ref, dtype), f"ring group {shape}")
+
+
+def test_ring_groups_of_more_than_16_layers():
+    shapes = [(3 + i % 6, 256 + 48 * i, 2048 if i % 3 else 4096, 128) for i in range(22)]    # 16 + 6
+    layers = [_layer(*sh, FP16, seed=1000 + i) for i, sh in enumerate(shapes)]
+    ys = W4.linear_batch([L["t"] for L in layers])
+    singles = [W4.linear(*L["t"]) for L in layers]
+    torch.cuda.synchronize()
+    for sh, L, y, y1 in zip(shapes, layers, ys, singles):
+        if sh[0] >= 5:
+            assert torch.equal(y.view(torch.int16), y1.view(torch.int16)), f"ring group != single {sh}"
+        ref = oracle.linear_ref(L["X"], FP16, L["qn"], L["s"], L["z"], L["g"])
+        assert_close(y_to_f64(y), ref.astype(np.float64), f"ring group item {sh}")
+
+
+def test_ring_group_graph_replay_matches_eager():
+    layers = [_layer(8, N, K, 128, FP16, seed=1100 + i) for i, (N, K) in
+              enumerate([(4096, 4096), (11008, 4096), (4096, 11008)])]
+    outs = [torch.empty((8, L["t"][1].shape[0]), dtype=torch.float16, device="cuda") for L in layers]
     W4.linear_batch([L["t"] for L in layers], outs=outs)
     torch.cuda.synchronize()
     eager = [o.clone() for o in outs]

@@ -21,7 +21,7 @@ namespace {
 
 constexpr int64_t kMaxDim = 2147483647LL;
 constexpr int kMaxBatch = 65536;          // layers per w4a16_linear_batch call
-constexpr int kGroupLaunch = 16;          // one-row layers per grouped launch
+constexpr int kGroupLaunch = 16;          // layers per grouped launch
 constexpr int64_t kGptqMaxK = 46340;      // K * K fp64 elements indexable in 31 bits
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -451,32 +451,40 @@ int w4a16_linear_batch(const w4a16_linear_item* items, int count, int dtype, voi
         if (paths[(size_t)i] < 0) return W4A16_ERR_PATH;
     }
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    // one-row layers the grouped kernel takes share launches of up to 16 layers, in item
-    // order; a group of one and every other layer run as w4a16_linear
-    std::vector<LinearArgs> group;
-    auto flush = [&]() -> int {
+    // Layers that a grouped kernel takes share launches of up to 16 layers, in item order:
+    // one-row layers (the streaming GEMV) and layers that run alone on the ring decode
+    // kernel (MFMA, up to 16 rows); a group of one and every other layer run as w4a16_linear.
+    std::vector<LinearArgs> rows1, ring;
+    auto flush = [&](std::vector<LinearArgs>& group, bool gemv) -> int {
         int st = W4A16_OK;
         if (group.size() == 1)
             st = run_linear(group[0], choose_path(group[0]), s);
         else if (!group.empty())
-            st = hip_status(w4a16::launch_gemv_group(group.data(), (int)group.size(), s));
+            st = hip_status(gemv ? w4a16::launch_gemv_group(group.data(), (int)group.size(), s)
+                                 : w4a16::launch_ring_group(group.data(), (int)group.size(), s));
         group.clear();
         return st;
     };
     for (int i = 0; i < count; ++i) {
         const LinearArgs& a = args[(size_t)i];
-        if (w4a16::gemv_group_supports(a)) {
+        const int p = paths[(size_t)i];
+        const bool g1 = w4a16::gemv_group_supports(a);
+        const bool g2 = !g1 && p == W4A16_PATH_SKINNY && w4a16::skinny_supports(a) && w4a16::ring_group_supports(a);
+        if (g1 || g2) {
+            std::vector<LinearArgs>& group = g1 ? rows1 : ring;
             group.push_back(a);
             if ((int)group.size() == kGroupLaunch) {
-                const int st = flush();
+                const int st = flush(group, g1);
                 if (st != W4A16_OK) return st;
             }
         } else {
-            const int st = run_linear(a, paths[(size_t)i], s);
+            const int st = run_linear(a, p, s);
             if (st != W4A16_OK) return st;
         }
     }
-    return flush();
+    const int st = flush(rows1, true);
+    if (st != W4A16_OK) return st;
+    return flush(ring, false);
 }
 
 int64_t w4a16_linear_workspace(int64_t M, int64_t N, int64_t K, int64_t group_size, int dtype) {

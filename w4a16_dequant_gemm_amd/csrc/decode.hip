@@ -452,11 +452,13 @@ __device__ __forceinline__ void ring_fill(__amdgpu_buffer_rsrc_t r, int wave, co
                                              kp * 128, 0, 2 /* nt */);
 }
 
+// One block of the ring kernel: block `bid` of a layer's grid of `nblk` blocks (the
+// single-layer kernel and the grouped kernel both run this body).
 template <int DT, int T, int PK>
-__global__ __launch_bounds__(64 * kWaves) void decode_ring_kernel(
+__device__ __forceinline__ void ring_block(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int has_zeros,
-    uint16_t* __restrict__ Y, int M, int N, int K, int G, int gshift, int NT, int nblk, int KSP) {
+    uint16_t* __restrict__ Y, int M, int N, int K, int G, int gshift, int NT, int nblk, int KSP, int bid) {
     constexpr int W = kWaves;
     constexpr int NTH = 64 * W;
     static_assert(T * PK <= kRingSlots && T <= W, "ring configuration");
@@ -469,8 +471,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_ring_kernel(
     const int n16 = lane & 15;
     const int q = lane >> 4;
 
-    const int tile0 = (int)(((long long)blockIdx.x * NT) / nblk);
-    const int ntiles = (int)(((long long)(blockIdx.x + 1) * NT) / nblk) - tile0;
+    const int tile0 = (int)(((long long)bid * NT) / nblk);
+    const int ntiles = (int)(((long long)(bid + 1) * NT) / nblk) - tile0;
     const int row_begin = tile0 * 16;
     const int row_end = min(N, row_begin + ntiles * 16);
     const int kp0 = wave * KSP;
@@ -694,6 +696,48 @@ __global__ __launch_bounds__(64 * kWaves) void decode_ring_kernel(
     });
 }
 
+template <int DT, int T, int PK>
+__global__ __launch_bounds__(64 * kWaves) void decode_ring_kernel(
+    const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int has_zeros,
+    uint16_t* __restrict__ Y, int M, int N, int K, int G, int gshift, int NT, int nblk, int KSP) {
+    ring_block<DT, T, PK>(X, qw, scales, zeros, has_zeros, Y, M, N, K, G, gshift, NT, nblk, KSP, blockIdx.x);
+}
+
+// Grouped launch of independent layers on the ring kernel: one grid over the layers' blocks
+// (block b works for the layer whose block range holds b), so the layers' latency chains
+// (the weight and activation round trips of a block) overlap instead of running one launch
+// after another.  A tile's arithmetic does not depend on the block that holds it, so each
+// output is bit-identical to the layer's own launch on the ring kernel.
+constexpr int kRingGroupMax = 16;
+
+struct RingGroupItem {
+    const uint16_t* X;
+    const uint32_t* qw;
+    const uint16_t* scales;
+    const uint16_t* zeros;
+    uint16_t* Y;
+    int has_zeros, M, N, K, G, gshift, NT, nblk, ksp;
+    int block_begin;       // first grid block of this layer
+};
+
+struct RingGroupArgs {
+    RingGroupItem it[kRingGroupMax];
+    int count;
+};
+
+template <int DT, int T, int PK>
+__global__ __launch_bounds__(64 * kWaves) void decode_ring_group_kernel(const RingGroupArgs ga) {
+    const int b = blockIdx.x;
+    int i = 0;
+#pragma unroll
+    for (int j = 1; j < kRingGroupMax; ++j)
+        if (j < ga.count && b >= ga.it[j].block_begin) i = j;
+    const RingGroupItem& t = ga.it[i];
+    ring_block<DT, T, PK>(t.X, t.qw, t.scales, t.zeros, t.has_zeros, t.Y, t.M, t.N, t.K, t.G, t.gshift, t.NT,
+                          t.nblk, t.ksp, b - t.block_begin);
+}
+
 struct DecCfg {
     int t = 0, p = 0, ksp = 0, nblk = 0;
     int sk = 0, spare = 0, szs = 0, wt = 0, lds = 0;
@@ -782,28 +826,39 @@ struct RingCfg {
 
 constexpr int kLdsPerCu = 160 * 1024;
 
-RingCfg pick_ring(const LinearArgs& a) {
+constexpr int ring_pk(int t) { return t <= 4 ? 2 : 1; }
+constexpr long long ring_bytes(int t) { return (long long)t * ring_pk(t) * kWaves * kRingUnit * 16; }
+
+bool ring_shape_ok(const LinearArgs& a) {
+    if (a.M < 1 || a.M > 16 || a.K % 256 != 0 || a.g % 128 != 0) return false;
+    if ((long long)a.N * (a.K / 2) >= (1LL << 31) || (long long)a.M * a.K * 2 >= (1LL << 30)) return false;
+    return (long long)a.N * a.G * 2 < (1LL << 31);
+}
+
+// The configuration with t tiles per block, or t == 0 when its staging or LDS does not fit.
+RingCfg ring_cfg(const LinearArgs& a, int t) {
     RingCfg c;
-    if (a.M < 1 || a.M > 16 || a.K % 256 != 0 || a.g % 128 != 0) return c;
-    if ((long long)a.N * (a.K / 2) >= (1LL << 31) || (long long)a.M * a.K * 2 >= (1LL << 30)) return c;
-    if ((long long)a.N * a.G * 2 >= (1LL << 31)) return c;
+    const long long pieces = ((long long)t * 16 * a.G + 7) / 8 + 1;
+    if (pieces > (long long)kSzPieces * 64 * kWaves) return c;
+    const long long dyn = align16((int)pieces * 32 + 48);              // + spare words
+    if (dyn + ring_bytes(t) > kLdsPerCu) return c;
     const int NT = (a.N + 15) / 16;
-    const int KP = a.K / 256;
-    for (int t = std::min(kRingSlots, (NT + 255) / 256); t >= 1; --t) {
-        const int pk = t <= 4 ? 2 : 1;
-        const long long pieces = ((long long)t * 16 * a.G + 7) / 8 + 1;
-        if (pieces > (long long)kSzPieces * 64 * kWaves) continue;
-        const long long dyn = align16((int)pieces * 32 + 48);          // + spare words
-        const long long ring = (long long)t * pk * kWaves * kRingUnit * 16;
-        if (dyn + ring > kLdsPerCu) continue;
-        c.t = t;
-        c.pk = pk;
-        c.ksp = (KP + kWaves - 1) / kWaves;
-        c.nblk = (NT + t - 1) / t;
-        c.lds = (int)dyn;
-        return c;
-    }
+    c.t = t;
+    c.pk = ring_pk(t);
+    c.ksp = (a.K / 256 + kWaves - 1) / kWaves;
+    c.nblk = (NT + t - 1) / t;
+    c.lds = (int)dyn;
     return c;
+}
+
+RingCfg pick_ring(const LinearArgs& a) {
+    if (!ring_shape_ok(a)) return RingCfg{};
+    const int NT = (a.N + 15) / 16;
+    for (int t = std::min(kRingSlots, (NT + 255) / 256); t >= 1; --t) {
+        const RingCfg c = ring_cfg(a, t);
+        if (c.t > 0) return c;
+    }
+    return RingCfg{};
 }
 
 template <int DT, int T, int PK>
@@ -846,6 +901,71 @@ hipError_t launch_decode(const LinearArgs& a, hipStream_t st) {
     const RingCfg rc = pick_ring(a);
     if (rc.t == 0) return hipErrorInvalidValue;
     return a.dtype == DT_F16 ? run_ring<DT_F16>(a, rc, st) : run_ring<DT_BF16>(a, rc, st);
+}
+
+namespace {
+// A layer joins a grouped launch with one tile per block: up to 8 activation rows and rows
+// and columns of at most 12288, where the blocks are small (32 KB of ring, two blocks per
+// CU), the layers' blocks overlap, and the activations re-read by the extra blocks (2 M
+// bytes per column against 8 bytes of weights per tile) stay within L2's reach.  Measured on
+// the 7B-like step (three layers, one batch call against three calls): M = 4: 23.4 -> 20.3
+// us, M = 8: 25.7 -> 23.1 us; larger layers (8192 -> 28672, 28672 -> 8192) and M = 16 were
+// slower grouped (M = 8, 70B-like step: 64.5 -> 87.6 us with one tile per block).
+RingCfg ring_group_cfg(const LinearArgs& a) {
+    if (a.M > 8 || a.N > 12288 || a.K > 12288 || pick_ring(a).t == 0) return RingCfg{};
+    return ring_cfg(a, 1);
+}
+}  // namespace
+
+bool ring_group_supports(const LinearArgs& a) { return ring_group_cfg(a).t > 0; }
+
+hipError_t launch_ring_group(const LinearArgs* items, int count, hipStream_t st) {
+    if (count < 1 || count > kRingGroupMax) return hipErrorInvalidValue;
+    // every layer of the group runs one tile per block (ring_group_cfg), each within the LDS
+    int lds = 0;
+    RingCfg cfg[kRingGroupMax];
+    for (int i = 0; i < count; ++i) {
+        if (items[i].dtype != items[0].dtype) return hipErrorInvalidValue;
+        cfg[i] = ring_group_cfg(items[i]);
+        if (cfg[i].t != 1) return hipErrorInvalidValue;
+        lds = std::max(lds, cfg[i].lds);
+    }
+    // blocks of the layers with the longest rows (the longest-lived blocks) are dispatched first
+    int order[kRingGroupMax];
+    for (int i = 0; i < count; ++i) order[i] = i;
+    std::stable_sort(order, order + count, [&](int x, int y) { return items[x].K > items[y].K; });
+    RingGroupArgs ga{};
+    ga.count = count;
+    long long blocks = 0;
+    for (int oi = 0; oi < count; ++oi) {
+        const LinearArgs& a = items[order[oi]];
+        const RingCfg& c = cfg[order[oi]];
+        RingGroupItem& t = ga.it[oi];
+        t.X = static_cast<const uint16_t*>(a.X);
+        t.qw = a.qw;
+        t.scales = a.scales;
+        t.zeros = a.zeros;
+        t.Y = static_cast<uint16_t*>(a.Y);
+        t.has_zeros = a.zeros ? 1 : 0;
+        t.M = a.M;
+        t.N = a.N;
+        t.K = a.K;
+        t.G = a.G;
+        t.gshift = a.gshift;
+        t.NT = (a.N + 15) / 16;
+        t.nblk = c.nblk;
+        t.ksp = c.ksp;
+        t.block_begin = (int)blocks;
+        blocks += c.nblk;
+    }
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (items[0].dtype == DT_F16)
+        hipLaunchKernelGGL((decode_ring_group_kernel<DT_F16, 1, ring_pk(1)>), dim3((unsigned)blocks),
+                           dim3(64 * kWaves), lds, st, ga);
+    else
+        hipLaunchKernelGGL((decode_ring_group_kernel<DT_BF16, 1, ring_pk(1)>), dim3((unsigned)blocks),
+                           dim3(64 * kWaves), lds, st, ga);
+    return hipGetLastError();
 }
 
 }  // namespace w4a16

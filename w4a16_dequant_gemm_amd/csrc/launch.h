@@ -36,6 +36,10 @@ bool gemv_group_supports(const LinearArgs& a);
 hipError_t launch_gemv_group(const LinearArgs* items, int count, hipStream_t s);
 hipError_t launch_skinny(const LinearArgs& a, hipStream_t s);
 hipError_t launch_decode(const LinearArgs& a, hipStream_t s);
+// grouped launch of independent layers that run on the ring decode kernel (decode.hip): at
+// most 16 per launch, one dtype; ring_group_supports tells whether a layer alone would run there
+bool ring_group_supports(const LinearArgs& a);
+hipError_t launch_ring_group(const LinearArgs* items, int count, hipStream_t s);
 hipError_t launch_prefill(const LinearArgs& a, hipStream_t s);
 // estimated time (us) of the plain fp16 prefill launch on the 4-bit wide kernel, < 0 when another
 // kernel would run (host only; for the dispatcher)
