@@ -146,10 +146,15 @@ PREFILL_CASES = [(1, 64, 64, 64), (17, 200, 192, 64), (130, 129, 256, 128), (256
                  (1100, 4000, 768, 128), (1100, 4096, 640, 64),
                  # 64-row tiles, three-stage loop: 3 and 4 steps per wave group
                  (70, 520, 384, 128), (70, 520, 512, 64),
-                 # 172 groups per row: more than the kernel stages in LDS, loaded per step instead
-                 (64, 130, 11008, 64)]
-# fp16 prefill also takes K % 64 == 32 and g == 32 (bf16 prefill needs multiples of 64)
-PREFILL_F16_CASES = [(40, 150, 96, 32), (257, 300, 160, 32), (70, 64, 96, 96), (513, 260, 2080, 32)]
+                 # more groups per row than one LDS staging holds (fp16: staged in phases of up to
+                 # 95 groups): 172 groups, 64-row tiles with two wave groups; 128 groups, 128-row
+                 # tiles with two wave groups; 130 groups, 64-row tiles three steps deep; g = 128
+                 # (112 groups)
+                 (64, 130, 11008, 64), (1100, 4000, 8192, 64), (200, 300, 8320, 64), (300, 260, 14336, 128)]
+# fp16 prefill also takes K % 64 == 32 and g == 32 (bf16 prefill needs multiples of 64); the last
+# case has 128 groups of 32 per row (staged in two phases)
+PREFILL_F16_CASES = [(40, 150, 96, 32), (257, 300, 160, 32), (70, 64, 96, 96), (513, 260, 2080, 32),
+                     (100, 260, 4096, 32)]
 
 
 @pytest.mark.parametrize("dtype", [FP16, BF16])

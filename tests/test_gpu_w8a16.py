@@ -79,7 +79,9 @@ GEMV_CASES = [(1, 4096, 4096, 128), (2, 300, 1024, 32), (3, 1000, 2048, 64), (4,
               # over several K slices
               (15, 201, 4096, 128), (2, 1, 1024, 128), (3, 17, 2048, 32)]
 PREFILL_CASES = [(5, 4096, 1024, 128), (64, 300, 2048, 64), (300, 1000, 1024, 128), (129, 257, 4096, 4096),
-                 (4, 4096, 11008, 128), (1, 64, 128, 64), (512, 128, 640, 128)]
+                 (4, 4096, 11008, 128), (1, 64, 128, 64), (512, 128, 640, 128),
+                 # more groups per row than one LDS staging holds (fp16: staged in phases)
+                 (200, 300, 8192, 64)]
 
 
 @pytest.mark.parametrize("dtype", [FP16, BF16])

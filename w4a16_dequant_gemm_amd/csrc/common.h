@@ -189,16 +189,16 @@ __device__ __forceinline__ int group_of(int k, int gshift) { return (int)((uint3
 // group fall in distinct banks).  REP threads per row: thread t < REP rows stages pieces
 // t / rows, t / rows + REP, ... of row min(row0 + t % rows, N - 1), a piece being the 16 bytes
 // at local offset min(8 p, gl - 8) (inside the row's range, the last one overlapping its
-// neighbour), all of a thread's loads in flight at once (gl <= 8 kSzStagePieces); 2-byte loads
+// neighbour), all of a thread's loads in flight at once (gl <= 8 PIECES); 2-byte loads
 // by one thread per row when gl < 8.  Without zeros (hz false) the high halves are 0.  The
 // caller synchronizes before reading.  Staged once per block, this replaces two 2-byte loads
 // per row set and k-step, each touching as many cache lines as the row set has rows.
 constexpr int kSzStagePieces = 12;
-template <int REP>
+template <int REP, int PIECES = kSzStagePieces>
 __device__ __forceinline__ void stage_sz_rows(uint32_t* szl, int gp, int tid, int rows, int row0, int N,
                                               int G, int g0, int gl, bool hz, __amdgpu_buffer_rsrc_t rs,
                                               __amdgpu_buffer_rsrc_t rz, __amdgpu_buffer_rsrc_t rnull) {
-    constexpr int PT = (kSzStagePieces + REP - 1) / REP;          // pieces per thread
+    constexpr int PT = (PIECES + REP - 1) / REP;                  // pieces per thread
     if (tid >= REP * rows) return;
     const int rr = tid % rows, k = tid / rows;
     const int row = min(row0 + rr, N - 1);

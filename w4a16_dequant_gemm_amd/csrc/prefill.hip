@@ -490,13 +490,14 @@ constexpr int W_BM = 256, W_BN = 256, W_BK = 64;     // K % 128 == 0: steps in p
 // instead costs four 2-byte loads per wave and step, each touching 32 rows' cache lines: with
 // 64-row tiles that was half of the address unit's work, and the address unit, not the
 // matrix cores, set the pace.
-template <bool HZ, int BITS = 4, bool SPLIT = false, int MS = 8, int KG = 1, bool SZL = false>
+template <bool HZ, int BITS = 4, bool SPLIT = false, int MS = 8, int KG = 1, bool SZL = false, bool PH = false>
 __global__ __launch_bounds__(256 * KG, (MS >= 8 || BITS == 8 || (MS == 2 && !SPLIT) || KG > 1 || SZL) ? 1 : 2) void prefill_f16_wide_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros,
     uint16_t* __restrict__ Y, int M, int N, int K, int G, int gshift,
-    float* __restrict__ part = nullptr, int spl = 0, int gp = 0) {
+    float* __restrict__ part = nullptr, int spl = 0, int gp = 0, int pst = 0) {
     static_assert(KG == 1 || (KG == 2 && BITS == 4 && !SPLIT && MS <= 4), "k-groups: 4-bit, plain, <= 128 rows");
+    static_assert(!PH || (SZL && !SPLIT), "phases: staged scales and zeros, plain launch");
     constexpr int BMk = 32 * MS;                                       // block rows
     constexpr int ASZ = BMk * 8;                                       // one group's tile, 16-byte slots
     // the activation double buffer as two LDS objects, so that the compiler's wait before a
@@ -525,14 +526,18 @@ __global__ __launch_bounds__(256 * KG, (MS >= 8 || BITS == 8 || (MS == 2 && !SPL
     if constexpr (SPLIT) {
         if (sb >= se) return;                             // never planned (every split has steps)
     }
-    // local step t of this group is k-step sb + kg + KG t; L local steps per group; a load
-    // past the group's last step re-reads that step (unused)
-    const int L = (se - sb) / KG;
-    auto gstep = [&](int t) { return sb + kg + KG * min(t, L - 1); };
-    // SZL: groups [g0, g0 + gl) of the block's k-range, staged in LDS
+    // The k-range runs in phases [pb, pe) of pst k-steps each (PH; else one phase), every phase
+    // with its own staged scales and zeros (SZL) and its own pipeline fill.  Local step t
+    // of this group is k-step pb + kg + KG t; L local steps per group and phase; a load past the
+    // group's last step re-reads that step (unused).
+    int pb = sb;
+    int pe = PH ? min(se, sb + pst) : se;
+    int L = (pe - pb) / KG;
+    auto gstep = [&](int t) { return pb + kg + KG * min(t, L - 1); };
+    // SZL: groups [g0, g0 + gl) of the phase, staged in LDS
     extern __shared__ __attribute__((aligned(16))) uint32_t szl[];
-    const int g0 = SZL ? (sb * W_BK) >> gshift : 0;
-    const int gl = SZL ? (((se * W_BK) - 1) >> gshift) + 1 - g0 : 0;
+    int g0 = SZL ? (pb * W_BK) >> gshift : 0;
+    int gl = SZL ? (((pe * W_BK) - 1) >> gshift) + 1 - g0 : 0;
 
     // Buffer loads: per-lane 32-bit offsets fixed for the whole K loop, the step's offset
     // as the wave-uniform soffset.  Rows past M / N are clamped (loaded, never stored).
@@ -613,13 +618,6 @@ __global__ __launch_bounds__(256 * KG, (MS >= 8 || BITS == 8 || (MS == 2 && !SPL
         }
     };
 
-    if constexpr (SZL) {
-        const __amdgpu_buffer_rsrc_t rnull =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(scales), 0, 0, 0x00020000);
-        stage_sz_rows<KG>(szl, gp, tid, W_BN, n0, N, G, g0, gl, HZ, rs, rz, rnull);
-        __syncthreads();
-    }
-
     f32x16 acc[MS][2];
 #pragma unroll
     for (int i = 0; i < MS; ++i)
@@ -683,6 +681,13 @@ __global__ __launch_bounds__(256 * KG, (MS >= 8 || BITS == 8 || (MS == 2 && !SPL
         asm volatile("" ::"v"(v.x));
         __builtin_amdgcn_s_barrier();
     };
+    for (;;) {                                            // phases
+    if constexpr (SZL) {
+        const __amdgpu_buffer_rsrc_t rnull =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(scales), 0, 0, 0x00020000);
+        stage_sz_rows<KG>(szl, gp, tid, W_BN, n0, N, G, g0, gl, HZ, rs, rz, rnull);
+        __syncthreads();
+    }
     if constexpr (DEEP) {
         // 64-row blocks: a k-step's matrix work (16 MFMAs per wave) is shorter than a memory
         // round trip, so with one step of prefetch every step waited for its loads (1.2 us per
@@ -744,6 +749,17 @@ __global__ __launch_bounds__(256 * KG, (MS >= 8 || BITS == 8 || (MS == 2 && !SPL
             compute(As1 + abase, b1, p0, b0);
             step_end(As0);
         }
+    }
+    if (!PH || pe >= se) break;                           // uniform
+    // next phase: every load of this one has landed (the last steps' prefetches re-read into
+    // the buffers the next fill writes) and every wave is done with its staged words
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    pb = pe;
+    pe = min(se, pb + pst);
+    L = (pe - pb) / KG;
+    g0 = (pb * W_BK) >> gshift;
+    gl = (((pe * W_BK) - 1) >> gshift) + 1 - g0;
     }
 
     if constexpr (KG > 1) {
@@ -809,36 +825,62 @@ constexpr int kLdsPerCu = 160 * 1024;
 // One launch of an instantiation of the wide kernel.  SZL kernels take 256 * gp * 4 bytes of
 // dynamic LDS next to their static activation buffers; the per-kernel limit on dynamic LDS
 // (64 KB by default) is raised on every launch.
-template <bool HZ, int BITS, bool SPLIT, int MS, int KG, bool SZL>
-hipError_t launch_wide_k(dim3 grid, const LinearArgs& a, float* part, int spl, int gp, hipStream_t st) {
+template <bool HZ, int BITS, bool SPLIT, int MS, int KG, bool SZL, bool PH = false>
+hipError_t launch_wide_k(dim3 grid, const LinearArgs& a, float* part, int spl, int gp, hipStream_t st,
+                         int pst = 0) {
     const int dyn = SZL ? 256 * gp * 4 : 0;
     if constexpr (SZL) {
         const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&prefill_f16_wide_kernel<HZ, BITS, SPLIT, MS, KG, SZL>),
+            reinterpret_cast<const void*>(&prefill_f16_wide_kernel<HZ, BITS, SPLIT, MS, KG, SZL, PH>),
             hipFuncAttributeMaxDynamicSharedMemorySize, dyn);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((prefill_f16_wide_kernel<HZ, BITS, SPLIT, MS, KG, SZL>), grid, dim3(256 * KG), dyn, st,
+    hipLaunchKernelGGL((prefill_f16_wide_kernel<HZ, BITS, SPLIT, MS, KG, SZL, PH>), grid, dim3(256 * KG), dyn, st,
                        static_cast<const uint16_t*>(a.X), a.qw, a.scales, a.zeros, static_cast<uint16_t*>(a.Y),
-                       a.M, a.N, a.K, a.G, a.gshift, part, spl, gp);
+                       a.M, a.N, a.K, a.G, a.gshift, part, spl, gp, pst);
     return hipGetLastError();
 }
 
-// Row stride (dwords, odd) of the LDS-staged scales and zeros of a wide-kernel launch, or 0 when
-// they are loaded per step: the groups of a block's k-range (all of K, or the largest split)
-// must number at most 8 kSzStagePieces and fit the LDS next to the activation buffers.
-int wide_szl_stride(const LinearArgs& a, int ms, int kg, bool split, int spl) {
+// LDS staging of a wide-kernel launch's scales and zeros: gp, the row stride (dwords, odd), or
+// 0 when they are loaded per step; pst, the phase length in k-steps, or 0 for one phase.  The
+// groups of a phase must number at most 8 kSzStagePieces and fit the LDS next to the
+// activation buffers.  One phase covers a block's whole k-range (all of K, or the largest
+// split); a plain launch whose rows hold more groups runs phases that start on group
+// boundaries, of a multiple of 2 KG steps (the pipeline's step pairs), as few as fit.
+// Measured (fp16, g = 64, 172 groups per row, 11008 -> 4096; two phases against per-step
+// loads): M = 256: 158.1 -> 112.7 us, M = 1024: 163.3 -> 125.0 us, M = 2048: 218.3 -> 186.2 us,
+// M = 4096: 333.1 -> 313.5 us.
+struct SzlPlan {
+    int gp = 0, pst = 0;
+};
+SzlPlan wide_szl_plan(const LinearArgs& a, int ms, int kg, bool split, int spl) {
     const int nsteps = a.K / W_BK;
+    const bool deep = ms == 2 && !split && kg == 1;
+    const int stat = kg * 4096 * ms * (deep ? 3 : 2);
+    auto fits = [&](int gl) { return gl <= 8 * kSzStagePieces && stat + 256 * (gl | 1) * 4 <= kLdsPerCu; };
     int gl = 0;
     for (int sb = 0; sb < nsteps; sb += split ? spl : nsteps) {
         const int se = split ? std::min(nsteps, sb + spl) : nsteps;
         gl = std::max(gl, (((se * W_BK) - 1) >> a.gshift) + 1 - ((sb * W_BK) >> a.gshift));
     }
-    const int gp = gl | 1;
-    const bool deep = ms == 2 && !split && kg == 1;
-    const int stat = kg * 4096 * ms * (deep ? 3 : 2);
-    if (gl > 8 * kSzStagePieces || stat + 256 * gp * 4 > kLdsPerCu) return 0;
-    return gp;
+    SzlPlan p;
+    if (fits(gl)) {
+        p.gp = gl | 1;
+        return p;
+    }
+    if (split) return p;
+    const int q = std::max(2 * kg, a.g > W_BK ? a.g / W_BK : 1);      // steps: a multiple of q
+    for (int np = 2; np <= 16; ++np) {
+        const int pst = ((nsteps + np - 1) / np + q - 1) / q * q;
+        if (pst >= nsteps) continue;
+        const int glp = (((pst * W_BK) - 1) >> a.gshift) + 1;          // phases start on a group
+        if (fits(glp)) {
+            p.gp = glp | 1;
+            p.pst = pst;
+            return p;
+        }
+    }
+    return p;
 }
 
 
@@ -879,7 +921,7 @@ hipError_t launch_prefill_splitk(const LinearArgs& a, float* work, hipStream_t s
     if (S <= 1 || !work) return hipErrorInvalidValue;
     const int tiles = ((a.M + W_BM - 1) / W_BM) * ((a.N + W_BN - 1) / W_BN);
     const dim3 grid(8 * ((tiles + 7) / 8), S);
-    const int gp = wide_szl_stride(a, 8, 1, true, spl);
+    const int gp = wide_szl_plan(a, 8, 1, true, spl).gp;
     hipError_t e;
     if (a.zeros)
         e = gp > 0 ? launch_wide_k<true, 4, true, 8, 1, true>(grid, a, work, spl, gp, st)
@@ -909,8 +951,10 @@ int wide_ms(int M, int N) {
 }
 
 template <bool HZ, int BITS, int MS, int KG>
-hipError_t launch_wide_ms(dim3 grid, const LinearArgs& a, int gp, hipStream_t st) {
-    if (gp > 0) return launch_wide_k<HZ, BITS, false, MS, KG, true>(grid, a, nullptr, 0, gp, st);
+hipError_t launch_wide_ms(dim3 grid, const LinearArgs& a, const SzlPlan& sp, hipStream_t st) {
+    if (sp.gp > 0 && sp.pst > 0)
+        return launch_wide_k<HZ, BITS, false, MS, KG, true, true>(grid, a, nullptr, 0, sp.gp, st, sp.pst);
+    if (sp.gp > 0) return launch_wide_k<HZ, BITS, false, MS, KG, true>(grid, a, nullptr, 0, sp.gp, st);
     return launch_wide_k<HZ, BITS, false, MS, KG, false>(grid, a, nullptr, 0, 0, st);
 }
 
@@ -922,18 +966,18 @@ hipError_t launch_wide(const LinearArgs& a, hipStream_t st) {
     // Measured (fp16, g = 128, scales and zeros in LDS): M = 256, 4096 -> 11008: 54.9 -> 49.2 us;
     // M = 1024, 11008 -> 4096: 152.0 -> 139.1 us; M = 2048, 11008 -> 4096: 205.7 -> 196.6 us.
     const int kg = BITS == 4 && ms <= 4 && (a.K / W_BK) % 4 == 0 ? 2 : 1;
-    const int gp = wide_szl_stride(a, ms, kg, false, 0);
+    const SzlPlan sp = wide_szl_plan(a, ms, kg, false, 0);
     const int tiles = wide_blocks(a.M, a.N, ms);
     const dim3 grid(8 * ((tiles + 7) / 8));
     if constexpr (BITS == 4) {
         if (kg == 2) {
-            if (ms == 4) return launch_wide_ms<HZ, 4, 4, 2>(grid, a, gp, st);
-            if (ms == 2) return launch_wide_ms<HZ, 4, 2, 2>(grid, a, gp, st);
+            if (ms == 4) return launch_wide_ms<HZ, 4, 4, 2>(grid, a, sp, st);
+            if (ms == 2) return launch_wide_ms<HZ, 4, 2, 2>(grid, a, sp, st);
         }
     }
-    if (ms == 8) return launch_wide_ms<HZ, BITS, 8, 1>(grid, a, gp, st);
-    if (ms == 4) return launch_wide_ms<HZ, BITS, 4, 1>(grid, a, gp, st);
-    return launch_wide_ms<HZ, BITS, 2, 1>(grid, a, gp, st);
+    if (ms == 8) return launch_wide_ms<HZ, BITS, 8, 1>(grid, a, sp, st);
+    if (ms == 4) return launch_wide_ms<HZ, BITS, 4, 1>(grid, a, sp, st);
+    return launch_wide_ms<HZ, BITS, 2, 1>(grid, a, sp, st);
 }
 
 // Time of the plain fp16 4-bit launch: a block round costs s(rows) us per k-step, growing with

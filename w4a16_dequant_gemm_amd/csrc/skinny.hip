@@ -163,7 +163,7 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int has_zeros,
     uint16_t* __restrict__ Y, int M, int N, int K, int G, int gshift, int KS, int gp) {
     // the waves' partial tiles at the end; during the k-loop (SZL) the block's scales and zeros,
-    // 16 NB rows x gp dwords (gp <= 97 fits: the buffer holds 8 MT KB per row-block)
+    // 16 NB rows x gp dwords (gp <= 16 W MT fits: the buffer holds W MT KB per row-block)
     __shared__ f32x4 red[W][NB][MT][64];
     uint32_t* szl = reinterpret_cast<uint32_t*>(&red[0][0][0][0]);
     const int tid = threadIdx.x;
@@ -208,7 +208,8 @@ __global__ __launch_bounds__(64 * W) void skinny_kernel(
         for (int mt = 0; mt < MT; ++mt) tile[nb][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     if constexpr (SZL) {
-        stage_sz_rows<4 * W / NB>(szl, gp, tid, 16 * NB, row0, N, G, 0, G, has_zeros != 0, src.s, src.z, src.none);
+        stage_sz_rows<4 * W / NB, 2 * W * MT>(szl, gp, tid, 16 * NB, row0, N, G, 0, G, has_zeros != 0, src.s, src.z,
+                                              src.none);
         __syncthreads();
     }
     const int kb0 = wave * KS;
@@ -279,10 +280,11 @@ SkinnyCfg pick_skinny(const LinearArgs& a) {
 
 template <int DT, int NB, int MT>
 hipError_t run(const LinearArgs& a, const SkinnyCfg& c, hipStream_t st) {
-    // scales and zeros staged in LDS when the row's groups fit the staging (G <= 96); measured
-    // (fp16, g = 128): M = 256, 11008 -> 4096: 109.5 -> 92.4 us; M = 128, 4096 -> 4096: 24.2 ->
-    // 18.1 us; M = 32, 4096 -> 11008: 31.6 -> 25.7 us (the address unit was 75 % busy)
-    const bool szl = a.G <= 8 * kSzStagePieces;
+    // scales and zeros staged in LDS when the row's groups fit the reduction buffer (gp = G | 1
+    // <= 16 W MT words per row: G < 128 MT); measured (fp16, g = 128): M = 256, 11008 -> 4096:
+    // 109.5 -> 92.4 us; M = 128, 4096 -> 4096: 24.2 -> 18.1 us; M = 32, 4096 -> 11008: 31.6 ->
+    // 25.7 us (the address unit was 75 % busy)
+    const bool szl = (a.G | 1) <= 16 * kSkinnyWaves * MT;
     if (szl)
         hipLaunchKernelGGL((skinny_kernel<DT, NB, MT, kSkinnyWaves, true>), dim3(c.blocks, c.mblocks),
                            dim3(64 * kSkinnyWaves), 0, st, static_cast<const uint16_t*>(a.X), a.qw,
