@@ -13,12 +13,15 @@
 // 127); output = out(fp32(fp32(acc) * sx[m]) * sw[n]) from the exact int32 sum.
 //
 // GEMM.  qx [M, K] and qw [N, K] int8, K contiguous ("NT"), K % 128 == 0.  Block tile 256 x 256,
-// k-step 128 bytes, 4 waves in 2 x 2 (128 x 128 each), MFMA 32x32x32 i8 (lane (r, h) holds
+// k-step 128 bytes, 8 waves in 2 x 4 (128 x 64 each), MFMA 32x32x32 i8 (lane (r, h) holds
 // bytes 16 h .. + 15 of the 32-byte k-slice; for the j-th slice of a step it reads 16-byte
 // piece 4 h + j of the row, a consistent k assignment for both operands).  Both operand tiles
 // go global -> LDS with buffer-load-to-LDS into XOR-swizzled double buffers (piece c of row r
 // at slot c ^ (r / 2 % 8), conflict-free 32-row fragment reads); 128 KB of LDS, one block per
-// CU; tiles assigned XCD-major.
+// CU; tiles assigned XCD-major.  Two waves per SIMD (186 registers each) keep the matrix cores
+// fed while the other wave waits at a step's end; measured against 4 waves of 128 x 128 (one
+// per SIMD, 6 fragment reads per 8 MFMAs here against 8 per 16): M = 4096, 4096 -> 11008:
+// 288 -> 237-246 us; 11008 -> 4096: 205 -> 185-189 us (the same bits).
 #include "common.h"
 #include "launch.h"
 #include "tile.h"
@@ -211,7 +214,7 @@ constexpr int I_BM = 256, I_BN = 256, I_BK = 128;      // bytes of K per step
 constexpr int kGemmLds = 4 * I_BM * 8 * 16;            // A and B, two buffers each: 128 KB
 
 template <int DT>
-__global__ __launch_bounds__(256, 1) void w8a8_gemm_kernel(const int8_t* __restrict__ qx, const float* __restrict__ sx,
+__global__ __launch_bounds__(512, 1) void w8a8_gemm_kernel(const int8_t* __restrict__ qx, const float* __restrict__ sx,
                                                            const int8_t* __restrict__ qw, const float* __restrict__ sw,
                                                            uint16_t* __restrict__ Y, int M, int N, int K) {
     extern __shared__ __attribute__((aligned(16))) u32x4 lds8[];
@@ -223,7 +226,7 @@ __global__ __launch_bounds__(256, 1) void w8a8_gemm_kernel(const int8_t* __restr
     const int wave = tid >> 6;
     const int l32 = lane & 31;
     const int h = lane >> 5;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
     int mt, nt;
     if (!xcd_tile(blockIdx.x, (M + I_BM - 1) / I_BM, (N + I_BN - 1) / I_BN, mt, nt)) return;
     const int m0 = mt * I_BM;
@@ -232,23 +235,23 @@ __global__ __launch_bounds__(256, 1) void w8a8_gemm_kernel(const int8_t* __restr
 
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(qx), 0, 0x7FFFFFFF, 0x00020000);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(qw), 0, 0x7FFFFFFF, 0x00020000);
-    // instruction j of wave w fills slots (8 w + j) * 64 + lane: row r = (8 w + j) * 8 + lane / 8,
+    // instruction j of wave w fills slots (4 w + j) * 64 + lane: row r = (4 w + j) * 8 + lane / 8,
     // slot lane % 8 holding piece (lane % 8) ^ (r / 2 % 8); rows past M / N are clamped
-    int aoff[8], boff[8];
+    int aoff[4], boff[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int r = (8 * wave + j) * 8 + (lane >> 3);
+    for (int j = 0; j < 4; ++j) {
+        const int r = (4 * wave + j) * 8 + (lane >> 3);
         const int c = (lane & 7) ^ ((r >> 1) & 7);
         aoff[j] = min(m0 + r, M - 1) * K + 16 * c;
         boff[j] = min(n0 + r, N - 1) * K + 16 * c;
     }
     auto load = [&](int buf, int step) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 4; ++j) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ra, (__attribute__((address_space(3))) void*)(As(buf) + (8 * wave + j) * 64), 16, aoff[j], step * I_BK, 0, 0);
+                ra, (__attribute__((address_space(3))) void*)(As(buf) + (4 * wave + j) * 64), 16, aoff[j], step * I_BK, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rb, (__attribute__((address_space(3))) void*)(Bs(buf) + (8 * wave + j) * 64), 16, boff[j], step * I_BK, 0, 0);
+                rb, (__attribute__((address_space(3))) void*)(Bs(buf) + (4 * wave + j) * 64), 16, boff[j], step * I_BK, 0, 0);
         }
     };
     // fragment slots: tile row rr = 32 t + l32, piece 4 h + j -> slot rr * 8 + ((4 h + j) ^ (rr / 2 % 8))
@@ -256,46 +259,47 @@ __global__ __launch_bounds__(256, 1) void w8a8_gemm_kernel(const int8_t* __restr
 #pragma unroll
     for (int j = 0; j < 4; ++j) fslot[j] = l32 * 8 + ((4 * h + j) ^ ((l32 >> 1) & 7));
 
-    v16i acc[4][4];
+    v16i acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int jn = 0; jn < 4; ++jn)
+        for (int jn = 0; jn < 2; ++jn)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][jn][e] = 0;
 
     auto compute = [&](int buf) {
         const u32x4* A = As(buf) + wm * 128 * 8;
-        const u32x4* B = Bs(buf) + wn * 128 * 8;
-        u32x4 fa[2][4], fb[2][4];
+        const u32x4* B = Bs(buf) + wn * 64 * 8;
+        u32x4 fa[2][4], fb[2][2];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            fa[0][t] = A[t * 256 + fslot[0]];
-            fb[0][t] = B[t * 256 + fslot[0]];
-        }
+        for (int t = 0; t < 4; ++t) fa[0][t] = A[t * 256 + fslot[0]];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) fb[0][t] = B[t * 256 + fslot[0]];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int cur = j & 1;
             if (j < 3) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    fa[cur ^ 1][t] = A[t * 256 + fslot[j + 1]];
-                    fb[cur ^ 1][t] = B[t * 256 + fslot[j + 1]];
-                }
+                for (int t = 0; t < 4; ++t) fa[cur ^ 1][t] = A[t * 256 + fslot[j + 1]];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) fb[cur ^ 1][t] = B[t * 256 + fslot[j + 1]];
             }
 #pragma unroll
             for (int tm = 0; tm < 4; ++tm) {
                 const v4i av = __builtin_bit_cast(v4i, fa[cur][tm]);
 #pragma unroll
-                for (int tn = 0; tn < 4; ++tn)
+                for (int tn = 0; tn < 2; ++tn)
                     acc[tm][tn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, __builtin_bit_cast(v4i, fb[cur][tn]),
                                                                         acc[tm][tn], 0, 0, 0);
             }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if (j < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);              // MFMA
+            for (int i = 0; i < 4; ++i) {
+                if (j < 3) {
+                    if (i < 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+                    else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                  // MFMA
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -313,10 +317,10 @@ __global__ __launch_bounds__(256, 1) void w8a8_gemm_kernel(const int8_t* __restr
     }
 
     // epilogue: lane (l32, h) element e of tile (tm, tn) is row 32 tm + 8 (e / 4) + 4 h + e % 4,
-    // column 32 tn + l32 of the wave's 128 x 128
+    // column 32 tn + l32 of the wave's 128 x 64
 #pragma unroll
-    for (int tn = 0; tn < 4; ++tn) {
-        const int n = n0 + wn * 128 + tn * 32 + l32;
+    for (int tn = 0; tn < 2; ++tn) {
+        const int n = n0 + wn * 64 + tn * 32 + l32;
         if (n >= N) continue;
         const float swn = sw[n];
 #pragma unroll
@@ -399,10 +403,10 @@ hipError_t launch_w8a8_linear(const int8_t* qx, const float* sx, int M, int N, i
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
     if (e != hipSuccess) return e;
     if (dtype == DT_F16)
-        hipLaunchKernelGGL(w8a8_gemm_kernel<DT_F16>, dim3(grid), dim3(256), kGemmLds, st, qx, sx, qw, sw,
+        hipLaunchKernelGGL(w8a8_gemm_kernel<DT_F16>, dim3(grid), dim3(512), kGemmLds, st, qx, sx, qw, sw,
                            static_cast<uint16_t*>(Y), M, N, K);
     else
-        hipLaunchKernelGGL(w8a8_gemm_kernel<DT_BF16>, dim3(grid), dim3(256), kGemmLds, st, qx, sx, qw, sw,
+        hipLaunchKernelGGL(w8a8_gemm_kernel<DT_BF16>, dim3(grid), dim3(512), kGemmLds, st, qx, sx, qw, sw,
                            static_cast<uint16_t*>(Y), M, N, K);
     return hipGetLastError();
 }
