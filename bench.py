@@ -541,12 +541,11 @@ def counter_summary(run_dirs, out_path: str, header: str = ""):
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             with open(f) as fh:
                 for r in csv.DictReader(fh):
-                    k = r["Kernel_Name"]
-                    if not _library_kernel(k):
+                    if not _library_kernel(r["Kernel_Name"]):
                         continue
+                    k = (r["Kernel_Name"], r.get("Grid_Size") or "?")     # one entry per launch shape
                     sums.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
-                    if r.get("Grid_Size"):
-                        grid[k] = r["Grid_Size"]
+                    grid[k] = k[1]
     if not sums:
         raise SystemExit(f"no counter_collection csv under {run_dirs}")
 
@@ -556,7 +555,7 @@ def counter_summary(run_dirs, out_path: str, header: str = ""):
     lines = [header.rstrip("\n")] if header else []
     for k in sorted(sums, key=lambda k: -max(sum(v) for v in sums[k].values())):
         c = {n: sum(v) / len(v) for n, v in sums[k].items()}
-        lines.append(f"{short(k)}  (grid {grid.get(k, '?')} threads)")
+        lines.append(f"{short(k[0])}  (grid {grid.get(k, '?')} threads)")
         lines.append("  raw: " + ", ".join(f"{n}={c[n]:.0f}" for n in sorted(c)))
         d = []
         if "SQ_VALU_MFMA_BUSY_CYCLES" in c and c.get("GRBM_GUI_ACTIVE"):
