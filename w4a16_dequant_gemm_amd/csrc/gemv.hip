@@ -260,7 +260,8 @@ __device__ __forceinline__ void load_batch(RowBatch<DT, M, CPL, RB>& bt, const S
 template <int DT, int M, int CPL, int RB>
 __device__ __forceinline__ void compute_batch(const RowBatch<DT, M, CPL, RB>& bt, const uint32_t* xp,
                                               const float* xsum, const float2* szl, int szrow, int G,
-                                              int nrows, const int lgrp[CPL], int lane, float acc[RB][M]) {
+                                              int nrows, const int lgrp[CPL], int C, int gshift, int lane,
+                                              float acc[RB][M]) {
     constexpr int CH = CPL * 64;
 #pragma unroll
     for (int r = 0; r < RB; ++r)
@@ -289,7 +290,10 @@ __device__ __forceinline__ void compute_batch(const RowBatch<DT, M, CPL, RB>& bt
         for (int r = 0; r < RB; ++r) {
             // rows past the batch's last real row (zeros loaded, result not stored) read
             // that row's factors, so every LDS read stays inside the staged words
-            const float2 f = szl[szrow + (r < nrows ? r : nrows - 1) * G + lgrp[i]];
+            // one row: recomputed, so that no register holds it across the loads (the grouped
+            // kernel's allocation stays at 64 VGPRs); more rows: kept, as recomputing cost more
+            const int grp = M == 1 ? group_of((c < C ? c : 0) << 5, gshift) : lgrp[i];
+            const float2 f = szl[szrow + (r < nrows ? r : nrows - 1) * G + grp];
             if constexpr (DT == DT_F16) {
                 float pa[M], pb[M];
 #pragma unroll
@@ -351,8 +355,10 @@ __host__ __device__ constexpr int sz_lds_offset(int M, int CPL) { return (lds_by
 constexpr int kSzPiecesPerThread = 2;     // 16-byte pieces of scales (and of zeros) per thread
 
 // The work of one block of the streaming kernel (block index `blk`), shared by the plain
-// kernel and the grouped kernel (several independent layers in one launch).
-template <int DT, int M, int CPL, int RB, int W, int NB>
+// kernel and the grouped kernel (several independent layers in one launch).  JSZ: 16-byte
+// pieces of scales (and of zeros) each thread stages; the launcher checks that the block's
+// pieces fit.
+template <int DT, int M, int CPL, int RB, int W, int NB, int JSZ>
 __device__ __forceinline__ void stream_block(
     uint32_t* __restrict__ lds, const uint16_t* __restrict__ X, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int has_zeros,
@@ -361,7 +367,6 @@ __device__ __forceinline__ void stream_block(
     constexpr int NT = 64 * W;
     constexpr int JOBS = M * CH * 4;                   // 8-column staging jobs
     constexpr int JPT = (JOBS + NT - 1) / NT;
-    constexpr int JSZ = kSzPiecesPerThread;
     uint32_t* xp = lds;                  // [M][4 pieces][CH] x 16 B pairs, then one spare slot
     float* xsum = reinterpret_cast<float*>(lds + (M * CH + 1) * 16);   // [M*CH + 1]
     float2* szs = reinterpret_cast<float2*>(lds + sz_lds_offset(M, CPL) / 4);   // staged group factors
@@ -519,7 +524,7 @@ __device__ __forceinline__ void stream_block(
         // all loads are in flight; compute in load order so each chunk waits only for itself
         if (nbatch > 0) {
             compute_batch<DT, M, CPL, RB>(buf[0], xp, xsum, szs, szrow0 + (first - row_begin) * G, G,
-                                          wave_end - first, lgrp, lane, acc);
+                                          wave_end - first, lgrp, C, gshift, lane, acc);
             store_batch<DT, M, RB>(acc, first, wave_end, N, lane, Y);
         }
     } else {
@@ -529,7 +534,7 @@ __device__ __forceinline__ void stream_block(
             for (int i = 0; i < NB; ++i) {
                 const int row = first + (b + i) * W * RB;
                 compute_batch<DT, M, CPL, RB>(buf[i], xp, xsum, szs, szrow0 + (row - row_begin) * G, G,
-                                              row_end - row, lgrp, lane, acc);
+                                              row_end - row, lgrp, C, gshift, lane, acc);
                 load_batch<DT, M, CPL, RB, false>(buf[i], src, first + (b + i + NB) * W * RB,
                                                   b + i + NB < nbatch, N, vw);
                 store_batch<DT, M, RB>(acc, row, row_end, N, lane, Y);
@@ -540,7 +545,7 @@ __device__ __forceinline__ void stream_block(
             if (b + i < nbatch) {
                 const int row = first + (b + i) * W * RB;
                 compute_batch<DT, M, CPL, RB>(buf[i], xp, xsum, szs, szrow0 + (row - row_begin) * G, G,
-                                              row_end - row, lgrp, lane, acc);
+                                              row_end - row, lgrp, C, gshift, lane, acc);
                 store_batch<DT, M, RB>(acc, row, row_end, N, lane, Y);
             }
         }
@@ -553,8 +558,8 @@ __global__ __launch_bounds__(64 * W) void gemv_stream_kernel(
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int has_zeros,
     uint16_t* __restrict__ Y, int N, int K, int G, int gshift, int rows_per_block) {
     extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-    stream_block<DT, M, CPL, RB, W, NB>(lds, X, qw, scales, zeros, has_zeros, Y, N, K, G, gshift,
-                                        rows_per_block, blockIdx.x);
+    stream_block<DT, M, CPL, RB, W, NB, kSzPiecesPerThread>(lds, X, qw, scales, zeros, has_zeros, Y, N, K, G,
+                                                            gshift, rows_per_block, blockIdx.x);
 }
 
 struct GemvCfg {
@@ -776,16 +781,26 @@ hipError_t run_lds(const LinearArgs& a, const LdsCfg& c, hipStream_t st) {
 // up, drain), which at decode is comparable to streaming a whole 7B-sized layer; one grid
 // over the layers pays it once.  Block b works for the layer whose block range holds b and
 // runs the streaming block body for that layer, so every output is computed exactly as by
-// the layer's own launch (same lane-to-chunk mapping, same order of sums).  Blocks of 4
-// waves, each wave loading all of its rows at once: two rows per wave for up to 3 chunks
-// per lane (K <= 6144), one row for 4 .. 6 chunks (K <= 12288), which keeps the kernel's
-// register count at that of the one-row 6-chunk body.  Measured on the 7B-like step
-// (4096 x 4096, 4096 -> 11008, 11008 -> 4096): 8-wave blocks 14.1 us, 4-wave 14.2 us, 4-wave
-// with the long-row layer dispatched first 13.5 us, one row per wave for N <= 4096 15.0 us,
-// two rows per wave everywhere (150 VGPRs) 15.1 us.
+// the layer's own launch (same lane-to-chunk mapping, same order of sums).
+//
+// The kernel is bound by the weight bytes a CU keeps in flight: a wave's loads are all
+// issued at its start and its registers hold them until it has computed, so the rate
+// follows the number of resident waves.  Every variant of the switch below shares one
+// register allocation, the largest; the variants are chosen so that it stays at 64 VGPRs,
+// which lets 8 waves share a SIMD: two rows per wave for up to 2 chunks per lane
+// (K <= 4096), one row for 3 .. 6 chunks (K <= 12288; two rows at 3 chunks took 79 VGPRs).
+// Blocks of 8 waves stage the activations once for twice the rows of 4-wave blocks, and each
+// thread stages at most one 16-byte piece of scales and one of zeros.  Measured on the
+// 7B-like step (4096 x 4096, 4096 -> 11008, 11008 -> 4096), 200 launches per graph replay:
+// 4-wave blocks at 89 VGPRs (5 waves per SIMD) 14.3 us; 8-wave blocks at 82 VGPRs 14.3 us;
+// the same capped at 80 VGPRs (6 per SIMD, two registers spilled) 12.6-12.8 us; this form
+// (64 VGPRs, 8 per SIMD, no spills) 12.5 us; a plain read of the same 56.8 MB in one
+// launch takes 9.9 us at best.
 constexpr int kGroupMax = 16;
-constexpr int kGroupWaves = 4;        // waves per block of the grouped kernel
+constexpr int kGroupWaves = 8;        // waves per block of the grouped kernel
+constexpr int kGroupSzPieces = 1;     // staged 16-byte scale (and zero) pieces per thread
 constexpr int kGroupMaxCpl = 6;       // chunks per lane of the kernel's variants (K <= 12288)
+constexpr int group_rows_per_wave(int cpl) { return cpl <= 2 ? 2 : 1; }
 
 struct GroupItem {
     const uint16_t* X;
@@ -796,7 +811,7 @@ struct GroupItem {
     int N, K, G, gshift;
     int rows_per_block;
     int block_begin;       // first grid block of this layer
-    int variant;           // group_variant(CPL, RB)
+    int variant;           // chunks per lane: the case of the kernel's switch
     int has_zeros;
 };
 
@@ -805,7 +820,6 @@ struct GroupArgs {
     int count;
 };
 
-constexpr int group_variant(int cpl, int rb) { return cpl <= 3 ? 2 * (cpl - 1) + (rb - 1) : 6 + (cpl - 4); }
 
 template <int DT>
 __global__ __launch_bounds__(64 * kGroupWaves) void gemv_group_kernel(const GroupArgs ga) {
@@ -817,18 +831,18 @@ __global__ __launch_bounds__(64 * kGroupWaves) void gemv_group_kernel(const Grou
         if (j < ga.count && b >= ga.it[j].block_begin) i = j;
     const GroupItem& t = ga.it[i];
     const int lb = b - t.block_begin;
-#define W4A16_GROUP_CASE(CPL, RB)                                                                          \
-    case group_variant(CPL, RB):                                                                        \
-        stream_block<DT, 1, CPL, RB, kGroupWaves, 0>(lds, t.X, t.qw, t.scales, t.zeros, t.has_zeros, t.Y, \
-                                                      t.N, t.K, t.G, t.gshift, t.rows_per_block, lb);     \
+#define W4A16_GROUP_CASE(CPL)                                                                             \
+    case CPL:                                                                                          \
+        stream_block<DT, 1, CPL, group_rows_per_wave(CPL), kGroupWaves, 0, kGroupSzPieces>(              \
+            lds, t.X, t.qw, t.scales, t.zeros, t.has_zeros, t.Y, t.N, t.K, t.G, t.gshift, t.rows_per_block, lb); \
         break;
     switch (t.variant) {
-        W4A16_GROUP_CASE(1, 2)
-        W4A16_GROUP_CASE(2, 2)
-        W4A16_GROUP_CASE(3, 2)
-        W4A16_GROUP_CASE(4, 1)
-        W4A16_GROUP_CASE(5, 1)
-        W4A16_GROUP_CASE(6, 1)
+        W4A16_GROUP_CASE(1)
+        W4A16_GROUP_CASE(2)
+        W4A16_GROUP_CASE(3)
+        W4A16_GROUP_CASE(4)
+        W4A16_GROUP_CASE(5)
+        W4A16_GROUP_CASE(6)
         default: break;
     }
 #undef W4A16_GROUP_CASE
@@ -841,10 +855,10 @@ LdsCfg pick_group(const LinearArgs& a, int* rb) {
     const int cpl = (a.K / 32 + 63) / 64;
     if (cpl > kGroupMaxCpl) return c;
     if ((long long)a.N * (a.K / 2) >= (1LL << 31)) return c;
-    *rb = cpl > 3 ? 1 : 2;
+    *rb = group_rows_per_wave(cpl);
     const int rpb = *rb * kGroupWaves;
     const long long pieces = ((long long)rpb * a.G + 7) / 8 + 1;
-    if (pieces > (long long)kSzPiecesPerThread * 64 * kGroupWaves) return c;
+    if (pieces > (long long)kGroupSzPieces * 64 * kGroupWaves) return c;
     const long long lds = sz_lds_offset(1, cpl) + 64 * pieces;
     if (lds > kLdsBudget) return c;
     c.cpl = cpl;
@@ -890,7 +904,7 @@ hipError_t launch_gemv_group(const LinearArgs* items, int count, hipStream_t st)
         t.gshift = a.gshift;
         t.rows_per_block = c.rows_per_block;
         t.block_begin = (int)blocks;
-        t.variant = group_variant(c.cpl, rb);
+        t.variant = c.cpl;
         t.has_zeros = a.zeros ? 1 : 0;
         blocks += c.blocks;
         lds = lds > c.lds ? lds : c.lds;
