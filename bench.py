@@ -142,6 +142,46 @@ def time_loop(fn, iters, torch, graph=True, repeats: int = REPEATS):
     return e0.elapsed_time(e1) / iters   # ms per iteration
 
 
+PROBE_LIB = os.path.join(ROOT, "w4a16_dequant_gemm_amd", "libw4a16_probe.so")
+
+
+def read_ceiling(nbytes: int, torch) -> dict:
+    """The fastest plain read of ``nbytes`` in one launch (libw4a16_probe.so: every thread
+    issues 4, 8 or 16 16-byte loads at once, then XORs them; the best of the three), over
+    rotating buffers of >= 1 GiB, 200 launches per graph replay, median of 5 replays: the
+    rate one launch of that size reaches on this GPU, the practical ceiling of a kernel that
+    streams those bytes."""
+    import ctypes
+    if not os.path.exists(PROBE_LIB):
+        raise SystemExit(f"{PROBE_LIB} is missing: build with `python -m w4a16_dequant_gemm_amd.build`")
+    L = ctypes.CDLL(PROBE_LIB)
+    L.w4a16_probe_blocks.restype = ctypes.c_longlong
+    L.w4a16_probe_blocks.argtypes = [ctypes.c_longlong, ctypes.c_int]
+    L.w4a16_probe_read.restype = ctypes.c_int
+    L.w4a16_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    copies = max(2, -(-(1 << 30) // nbytes))
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    best = None
+    for per in (4, 8, 16):
+        out = torch.empty(L.w4a16_probe_blocks(nbytes, per) * 256, dtype=torch.int32, device="cuda")
+
+        def f(i, per=per, out=out):
+            rc = L.w4a16_probe_read(bufs[i % copies].data_ptr(), nbytes, per, out.data_ptr(),
+                                    torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"w4a16_probe_read failed ({rc})")
+        f(0)
+        torch.cuda.synchronize()
+        us = time_loop(f, 200, torch) * 1e3
+        if best is None or us < best["us"]:
+            best = {"us": round(us, 3), "GBps": round(nbytes / us / 1e3, 1), "loads_per_thread": per}
+    del bufs
+    torch.cuda.empty_cache()
+    best["bytes"] = nbytes
+    return best
+
+
 def check_samples(samples, oracle, np):
     """The oracle on the sampled rows of every timed extra configuration: packing bit-exact
     (codes, scales, zero points) and outputs within the bar (relative Frobenius <= 1e-3,
@@ -739,6 +779,10 @@ def main():
                 "launches_timed": ss_steps}
     if traffic:
         roofline["traffic_source"] = traffic["source"]
+    ceiling = read_ceiling(step_bytes, torch)
+    roofline["read_ceiling"] = dict(ceiling, frac_of_ceiling=round(achieved / ceiling["GBps"], 4))
+    log(f"plain read of the step's bytes in one launch: {ceiling['us']} us, {ceiling['GBps']} GB/s; "
+        f"the grouped kernel reaches {achieved / ceiling['GBps']:.1%} of it")
 
     extras = {"per_layer_m1": per_layer}
     samples = []
@@ -834,6 +878,11 @@ def run_comparators(W4, synth, torch, w4_step_ms):
     log(f"  prefill M=4096 fused vs unfused: {pf}")
     del packed
     torch.cuda.empty_cache()
+    # read ceilings at the sizes of single layers: 7B-like (8.9 and 24.0 MB) and 70B-like (35.7 and
+    # 124.8 MB) packed weights with their scales and zeros
+    res["read_ceiling_by_size"] = [read_ceiling(weight_bytes(N, K, GROUP), torch)
+                                   for K, N in ((4096, 4096), (4096, 11008), (8192, 8192), (8192, 28672))]
+    log(f"  plain-read ceilings: {res['read_ceiling_by_size']}")
     # launch gap
     one = torch.zeros(1, dtype=torch.float32, device="cuda")
     ms_l = time_loop(lambda i: one.add_(1.0), 200, torch)

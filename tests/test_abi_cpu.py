@@ -361,3 +361,24 @@ def test_linear_batch_rejects_invalid_arguments(lib):
     assert lib.w4a16_linear_batch(items, 2, 7, None) == L.ERR_DTYPE
     assert lib.w4a16_linear_batch(None, 1, 0, None) == L.ERR_NULL
     assert lib.w4a16_linear_batch(items, 0, 0, None) == L.ERR_SHAPE
+
+
+def test_read_probe_library_loads_and_sizes_its_launch():
+    """The benchmark's plain-read reference (libw4a16_probe.so, outside the W4A16 ABI) loads
+    without a GPU and sizes its grid on the host: ceil(bytes / (per * 256 threads * 16 B))
+    blocks, 0 for unsupported sizes."""
+    import ctypes
+    from w4a16_dequant_gemm_amd import build
+    if not os.path.exists(build.PROBE_LIB):
+        pytest.skip("libw4a16_probe.so not built")
+    P = ctypes.CDLL(build.PROBE_LIB)
+    P.w4a16_probe_blocks.restype = ctypes.c_longlong
+    P.w4a16_probe_blocks.argtypes = [ctypes.c_longlong, ctypes.c_int]
+    P.w4a16_probe_read.restype = ctypes.c_int
+    P.w4a16_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    assert P.w4a16_probe_blocks(56819712, 8) == -(-56819712 // (8 * 256 * 16))
+    assert P.w4a16_probe_blocks(1, 16) == 1
+    for bytes_, per in ((0, 8), (1 << 31, 8), (4096, 3), (4096, 32)):
+        assert P.w4a16_probe_blocks(bytes_, per) == 0
+    assert P.w4a16_probe_read(None, 4096, 8, None, None) == -1      # rejected before any launch

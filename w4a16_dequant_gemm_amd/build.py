@@ -3,7 +3,9 @@
 ``python -m w4a16_dequant_gemm_amd.build`` or ``build()`` from Python.  Every source is
 compiled to its own object in parallel (no device code crosses files: each file holds its
 kernels and their host launchers), then the objects are linked into one shared library
-written next to this file, so it travels with the source tree.
+written next to this file, so it travels with the source tree.  A second small library,
+``libw4a16_probe.so`` (``csrc/probe.hip``), holds the plain-read reference kernel that the
+benchmark times beside the weight-streaming kernels; it is not part of the W4A16 C ABI.
 """
 
 from __future__ import annotations
@@ -16,6 +18,10 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw4a16.so")
+# read-rate reference timed by the benchmark beside the weight-streaming kernels (its own
+# library: not part of the W4A16 C ABI)
+PROBE_LIB = os.path.join(HERE, "libw4a16_probe.so")
+PROBE_SOURCE = "probe.hip"
 OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["api.cpp", "quantize.hip", "gemv.hip", "skinny.hip", "decode.hip", "prefill.hip", "gptq.hip",
            "awq.hip", "w8a8.hip", "kv.hip", "w8a16.hip", "scratch.hip"]
@@ -68,6 +74,15 @@ def build(verbose: bool = False) -> str:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed linking libw4a16.so")
     os.replace(tmp, LIB)
+    probe_tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, "-shared", "-x", "hip", os.path.join(CSRC, PROBE_SOURCE), "-o", probe_tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building libw4a16_probe.so")
+    os.replace(probe_tmp, PROBE_LIB)
     return LIB
 
 
