@@ -46,11 +46,17 @@ def _layer(M, N, K, g, dtype, seed, scheme=ASYM, zeros_none=False):
 
 
 # (M, N, K, g, scheme, zeros_none): the three 7B-like layers, short and ragged rows, two rows
-# per wave (N > 4096), per-channel groups, symmetric weights without zero points, N = 1
+# per wave (N > 4096), per-channel groups, symmetric weights without zero points, N = 1, and
+# every chunks-per-lane case of the grouped kernel (1 .. 6: K up to 2048, 4096, 6144, 8192,
+# 10240, 12288), with a row whose last chunks per lane run past its end (K = 4352) and
+# 32-column groups
 ONE_ROW = [(1, 4096, 4096, 128, ASYM, False), (1, 11008, 4096, 128, ASYM, False),
            (1, 4096, 11008, 128, ASYM, False), (1, 300, 2048, 64, ASYM, False),
            (1, 4097, 1024, 128, ASYM, False), (1, 50, 11008, 11008, ASYM, False),
-           (1, 192, 1024, 128, SYM, True), (1, 1, 32, 32, ASYM, False), (1, 777, 12288, 256, ASYM, False)]
+           (1, 192, 1024, 128, SYM, True), (1, 1, 32, 32, ASYM, False), (1, 777, 12288, 256, ASYM, False),
+           (1, 1000, 6144, 128, ASYM, False), (1, 129, 4352, 128, ASYM, False),
+           (1, 520, 5120, 32, SYM, True), (1, 3000, 8192, 128, ASYM, False),
+           (1, 333, 10240, 64, ASYM, False)]
 
 
 @pytest.mark.parametrize("dtype", [FP16, BF16])
