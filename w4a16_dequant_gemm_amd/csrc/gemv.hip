@@ -213,7 +213,13 @@ __global__ __launch_bounds__(launch_limit(M, CPL, RB)) void gemv_kernel(
 // wave owns whole rows: one DPP reduction per row, no cross-wave traffic.
 constexpr int kLdsBudget = 65536;
 
-__host__ __device__ constexpr int lds_bytes(int M, int CPL) { return (M * CPL * 64 + 1) * (64 + 4); }
+// Staged activations: per row, four planes (one per 16-byte piece of a 32-column chunk) of
+// CPL * 64 chunk slots plus one pad slot, so that the four lanes staging one chunk write four
+// different banks (planes exactly CPL * 1 KB apart put all four in the same banks); then one
+// spare slot, then the chunk sums (M * CPL * 64 + 1 floats).
+__host__ __device__ constexpr int x_plane(int CPL) { return CPL * 64 + 1; }
+__host__ __device__ constexpr int x_slots(int M, int CPL) { return 4 * M * x_plane(CPL) + 1; }
+__host__ __device__ constexpr int lds_bytes(int M, int CPL) { return x_slots(M, CPL) * 16 + (M * CPL * 64 + 1) * 4; }
 
 template <int DT, int M, int CPL, int RB>
 struct RowBatch {
@@ -275,10 +281,10 @@ __device__ __forceinline__ void compute_batch(const RowBatch<DT, M, CPL, RB>& bt
 #pragma unroll
         for (int m = 0; m < M; ++m) {
             // piece-major layout [m][piece][chunk]: a wave reads 64 consecutive 16-byte slots
-            const u32x4* src = reinterpret_cast<const u32x4*>(xp) + (size_t)m * 4 * CH + c;
+            const u32x4* src = reinterpret_cast<const u32x4*>(xp) + (size_t)m * 4 * x_plane(CPL) + c;
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                const u32x4 v = src[b * CH];
+                const u32x4 v = src[b * x_plane(CPL)];
                 xr[m][4 * b + 0] = v.x;
                 xr[m][4 * b + 1] = v.y;
                 xr[m][4 * b + 2] = v.z;
@@ -367,8 +373,9 @@ __device__ __forceinline__ void stream_block(
     constexpr int NT = 64 * W;
     constexpr int JOBS = M * CH * 4;                   // 8-column staging jobs
     constexpr int JPT = (JOBS + NT - 1) / NT;
-    uint32_t* xp = lds;                  // [M][4 pieces][CH] x 16 B pairs, then one spare slot
-    float* xsum = reinterpret_cast<float*>(lds + (M * CH + 1) * 16);   // [M*CH + 1]
+    constexpr int PS = x_plane(CPL);                   // slots per piece plane (one pad slot)
+    uint32_t* xp = lds;                  // [M][4 pieces][PS] x 16 B pairs, then one spare slot
+    float* xsum = reinterpret_cast<float*>(lds + x_slots(M, CPL) * 4);   // [M*CH + 1]
     float2* szs = reinterpret_cast<float2*>(lds + sz_lds_offset(M, CPL) / 4);   // staged group factors
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -461,7 +468,7 @@ __device__ __forceinline__ void stream_block(
     for (int j = 0; j < JPT; ++j) {
         const int job0 = tid + NT * j;
         const bool real = job0 < JOBS;
-        const int job = real ? job0 : JOBS;            // spare: 4 slots past the last chunk
+        const int job = real ? job0 : JOBS;            // spare: the slot past the last plane
         const int e = job % (CH * 4);
         const bool ok = real && (e >> 2) < C;
         const u32x4 v = xv[j];
@@ -479,8 +486,8 @@ __device__ __forceinline__ void stream_block(
         sum += dpp_mov<0x4E>(sum);                     // quad_perm [2,3,0,1]
         const int slot = real ? job >> 2 : M * CH;
         const int mrow = job / (CH * 4);
-        const int piece_major = (mrow * 4 + (e & 3)) * CH + (e >> 2);
-        reinterpret_cast<u32x4*>(xp)[real ? piece_major : 4 * M * CH] =
+        const int piece_major = (mrow * 4 + (e & 3)) * PS + (e >> 2);
+        reinterpret_cast<u32x4*>(xp)[real ? piece_major : 4 * M * PS] =
             ok ? u32x4{o[0], o[1], o[2], o[3]} : u32x4{0u, 0u, 0u, 0u};
         if ((job0 & 3) == 0)
             xsum[slot] = ok ? (DT == DT_F16 ? sum * 5.9604644775390625e-8f : sum) : 0.0f;
