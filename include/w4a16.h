@@ -140,9 +140,10 @@ int w4a16_linear_ex(const void* X, int dtype, int64_t M, int64_t N, int64_t K,
  * (K <= 12288, packed weights < 2 GiB) share launches of up to 16 layers, in item order: one
  * grid streams all of their weights, so the fixed cost of a launch (dispatch, ramp-up and
  * drain, about as long as streaming a 7B-sized layer at decode) is paid once per group.
- * Items with 2 <= M <= 8 that w4a16_linear runs on its small-batch path, with N and K at most
- * 12288 (K % 256 == 0, group_size % 128 == 0), likewise share launches of up to 16 layers of
- * the MFMA ring decode kernel, one 16-row tile per block, so the layers' blocks overlap.  The
+ * Items with 2 <= M <= 8 that w4a16_linear runs on its small-batch path or on the GEMV (two
+ * rows of K <= 4096), with N and K at most 12288 (K % 256 == 0, group_size % 128 == 0),
+ * likewise share launches of up to 16 layers of the MFMA ring decode kernel, one 16-row tile
+ * per block, so the layers' blocks overlap (a group of one runs as w4a16_linear).  The
  * other items run as w4a16_linear, in item order.  Grouped outputs meet w4a16_linear's
  * accuracy contract; they are computed with the arithmetic of the kernel the group runs, in
  * the same order, so where w4a16_linear takes that kernel for the layer (the weight-streaming

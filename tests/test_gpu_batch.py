@@ -129,11 +129,12 @@ def test_batch_graph_replay_matches_eager():
 
 # (M, N, K, g, scheme, zeros_none): layers the ring decode kernel takes in a group (M <= 8, N and K
 # <= 12288, K % 256 == 0, g % 128 == 0): the 7B-like shapes, ragged N, per-channel groups,
-# symmetric weights without zero points
+# symmetric weights without zero points, two-row layers whose single call runs the GEMV
 RING = [(8, 4096, 4096, 128, ASYM, False), (8, 11008, 4096, 128, ASYM, False),
         (8, 4096, 11008, 128, ASYM, False), (5, 1000, 2048, 128, ASYM, False),
         (7, 777, 4096, 4096, ASYM, False), (6, 300, 12288, 256, SYM, True), (4, 1040, 4096, 128, ASYM, False),
-        (3, 500, 8192, 128, ASYM, False), (2, 2000, 6144, 128, SYM, True)]
+        (3, 500, 8192, 128, ASYM, False), (2, 2000, 6144, 128, SYM, True), (2, 4096, 4096, 128, ASYM, False),
+        (2, 1100, 2048, 128, ASYM, False)]
 
 
 @pytest.mark.parametrize("dtype", [FP16, BF16])

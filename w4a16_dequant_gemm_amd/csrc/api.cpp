@@ -469,7 +469,10 @@ int w4a16_linear_batch(const w4a16_linear_item* items, int count, int dtype, voi
         const LinearArgs& a = args[(size_t)i];
         const int p = paths[(size_t)i];
         const bool g1 = w4a16::gemv_group_supports(a);
-        const bool g2 = !g1 && p == W4A16_PATH_SKINNY && w4a16::skinny_supports(a) && w4a16::ring_group_supports(a);
+        // 2-8 rows: the ring group also takes layers whose single call runs the GEMV (two rows of
+        // K <= 4096), so a decode step's layers share one launch instead of one launch each
+        const bool g2 = !g1 && a.M >= 2 && w4a16::ring_group_supports(a) &&
+                        ((p == W4A16_PATH_SKINNY && w4a16::skinny_supports(a)) || p == W4A16_PATH_GEMV);
         if (g1 || g2) {
             std::vector<LinearArgs>& group = g1 ? rows1 : ring;
             group.push_back(a);
