@@ -466,6 +466,19 @@ template <int MASK, int N>
 __device__ __forceinline__ void sched_group() {
     __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
 }
+// Wait until at most N vector-memory loads of this wave are in flight.  Written as an asm
+// statement with a memory clobber, it is also a compiler barrier: no load moves across it,
+// so N counts exactly the loads issued after the ones waited for.
+template <int N>
+struct VmWait {
+    static constexpr int value = N;
+};
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"I"(N) : "memory");
+}
+// Keeps the loads before it ahead of the loads after it in issue order.
+__device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
 
 constexpr int W_BM = 256, W_BN = 256, W_BK = 64;     // K % 128 == 0: steps in pairs
 
@@ -672,15 +685,20 @@ __global__ __launch_bounds__(256 * KG, (MS >= 8 || BITS == 8 || (MS == 2 && !SPL
     // activation tile is in LDS (step_end), leaving the weight loads in flight: they are needed
     // one step later.  Loads past the last step re-read it (harmless, unused).
     // End of a step: this wave's loads into the next activation buffer must have landed
-    // before the barrier (other waves read them after it).  A read of one of this wave's own
-    // words of that buffer makes the compiler wait for exactly those loads (it tracks the
-    // LDS-destination loads per LDS object), whatever order it gave the loads; the bare
-    // s_barrier then leaves the weight loads in flight (__syncthreads() would drain them).
-    auto step_end = [&](const u32x4* next) {
-        const u32x4 v = next[abase + (MS * wave) * 64 + lane];
-        asm volatile("" ::"v"(v.x));
+    // before the barrier (other waves read them after it).  The wait is explicit: each step
+    // issues its activation loads (MS), a fence, then its weight loads (NWL), so the number
+    // of loads allowed in flight is exact (W: the loads issued after the tile waited for);
+    // the bare s_barrier leaves those weight loads in flight.  (Leaving the wait to the
+    // compiler's tracking of loads into LDS failed where it issued the activation loads in a
+    // waterfall loop and rotated the k-loop: one step end of the three-step pipeline carried
+    // no wait at all, and a step now and then computed on the previous activation tile.)
+    constexpr int NWL = 2 * (WL + (SZL ? 0 : 2));     // loads of one load_w
+    auto step_end = [&](auto w) {
+        wait_vmcnt<decltype(w)::value>();
         __builtin_amdgcn_s_barrier();
     };
+    using After1 = VmWait<NWL>;                       // tile issued this step: its weight loads
+    using After2 = VmWait<MS + 2 * NWL>;              // tile issued a step earlier (three-step)
     for (;;) {                                            // phases
     if constexpr (SZL) {
         const __amdgpu_buffer_rsrc_t rnull =
@@ -711,22 +729,25 @@ __global__ __launch_bounds__(256 * KG, (MS >= 8 || BITS == 8 || (MS == 2 && !SPL
         int t = 0;
         for (; t + 3 <= L; t += 3) {
             load_a(As2, gstep(t + 2));
+            issue_fence();
             load_w(p0, gstep(t + 3));
             compute(As0 + abase, b0, p1, b1);
-            step_end(As1);
+            step_end(After2{});                           // As1
             load_a(As0, gstep(t + 3));
+            issue_fence();
             load_w(p1, gstep(t + 4));
             compute(As1 + abase, b1, p2, b2);
-            step_end(As2);
+            step_end(After2{});                           // As2
             load_a(As1, gstep(t + 4));
+            issue_fence();
             load_w(p2, gstep(t + 5));
             compute(As2 + abase, b2, p0, b0);
-            step_end(As0);
+            step_end(After2{});                           // As0
         }
         // the last one or two steps: their activations and weights are already in flight
         if (t < L) {                                      // uniform
             compute(As0 + abase, b0, p1, b1);
-            step_end(As1);
+            step_end(VmWait<0>{});                        // As1, the last tile issued
             if (t + 1 < L) compute(As1 + abase, b1, p2, b2);
         }
     } else {
@@ -741,13 +762,15 @@ __global__ __launch_bounds__(256 * KG, (MS >= 8 || BITS == 8 || (MS == 2 && !SPL
         __syncthreads();
         for (int t = 0; t < L; t += 2) {
             load_a(As1, gstep(t + 1));
+            issue_fence();
             load_w(p0, gstep(t + 2));
             compute(As0 + abase, b0, p1, b1);
-            step_end(As1);
+            step_end(After1{});                           // As1
             load_a(As0, gstep(t + 2));
+            issue_fence();
             load_w(p1, gstep(t + 3));
             compute(As1 + abase, b1, p0, b0);
-            step_end(As0);
+            step_end(After1{});                           // As0
         }
     }
     if (!PH || pe >= se) break;                           // uniform
