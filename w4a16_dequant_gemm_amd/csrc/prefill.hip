@@ -582,8 +582,11 @@ __global__ __launch_bounds__(256 * KG, (MS >= 8 || BITS == 8 || (MS == 2 && !SPL
         szoff[ns] = wrow * G * 2;
     }
     auto load_a = [&](u32x4* As, int step) {
+        // the step offset is wave-uniform; saying so keeps it in an SGPR (held in a VGPR, the
+        // compiler wrapped each load in a waterfall loop)
+        const int so = __builtin_amdgcn_readfirstlane(step * W_BK * 2);
 #pragma unroll
-        for (int j = 0; j < MS; ++j) lds_load16(rx, &As[abase + (MS * wave + j) * 64], xoff[j], step * W_BK * 2);
+        for (int j = 0; j < MS; ++j) lds_load16(rx, &As[abase + (MS * wave + j) * 64], xoff[j], so);
     };
     constexpr int WL = BITS == 4 ? 1 : 2;        // 16-byte weight loads per row and step
     struct WStage {
